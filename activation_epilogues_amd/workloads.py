@@ -1,0 +1,158 @@
+"""Seeded synthetic workloads for the transposed-convolution + epilogue path.
+
+This module is the only code shared by the oracle side and the HIP side: it
+describes the five workload shapes and draws their inputs.  It holds none of
+the method's arithmetic (no output-size formula, no convolution, no
+normalisation); it only names shapes and draws random numbers.
+
+Shapes follow the three problems the pages work on:
+  * p61 page (ConvTranspose3d 64->128, k=3, then ReLU and GroupNorm(8)),
+  * p49 page (ConvTranspose3d 32->64, k=3, stride 2, pad 1, output_padding 1,
+    then softmax over channels and sigmoid),
+  * p77 page (ConvTranspose3d 64->128, k=5, then x2.0, training-mode
+    BatchNorm3d and AdaptiveAvgPool3d(1)),
+plus a tiny GroupNorm case and a stride-2, k=4 GroupNorm case at 128 channels.
+
+Input recipe (every workload): numpy ``default_rng(seed)`` draws, in this
+order and as float64, x ~ N(0,1); w ~ U(-a, a) and b ~ U(-a, a) with
+a = 1/sqrt(cin*k^3); gamma ~ U(0.5, 1.5); beta ~ N(0, 0.1).  All five arrays
+are always drawn (so the streams do not depend on which are used) and then
+cast to float32.  The same float32 arrays feed the oracle and the GPU.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+
+EPI_NONE = 0
+EPI_RELU_GROUPNORM = 1
+EPI_SOFTMAX_SIGMOID = 2
+EPI_SCALE_BN_TRAIN_AVGPOOL = 3
+
+EPI_NAMES = {
+    EPI_NONE: "none",
+    EPI_RELU_GROUPNORM: "relu_groupnorm",
+    EPI_SOFTMAX_SIGMOID: "softmax_sigmoid",
+    EPI_SCALE_BN_TRAIN_AVGPOOL: "scale_bn_train_avgpool",
+}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One transposed-convolution + epilogue problem (NCDHW, cubic kernel)."""
+
+    name: str
+    n: int
+    cin: int
+    cout: int
+    d: int
+    h: int
+    w: int
+    k: int
+    stride: int = 1
+    pad: int = 0
+    out_pad: int = 0
+    bias: bool = True
+    epi: int = EPI_RELU_GROUPNORM
+    groups: int = 1
+    eps: float = 1e-5
+    scale: float = 1.0
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    @property
+    def x_shape(self):
+        return (self.n, self.cin, self.d, self.h, self.w)
+
+    @property
+    def w_shape(self):
+        return (self.cin, self.cout, self.k, self.k, self.k)
+
+
+# The five workloads.  Seeds are 20260 + (position in this list, from 1).
+WORKLOADS = [
+    Workload("tiny_gn", 2, 8, 16, 8, 8, 8, k=3, stride=1, pad=0, bias=True,
+             epi=EPI_RELU_GROUPNORM, groups=4, seed=20261,
+             note="tiny GroupNorm case the oracle finishes in well under a second"),
+    Workload("k3s1_gn", 16, 64, 128, 32, 32, 32, k=3, stride=1, pad=0, bias=False,
+             epi=EPI_RELU_GROUPNORM, groups=8, seed=20262,
+             note="p61 page shape: ConvTranspose3d 64->128 k3 (no bias), ReLU, GroupNorm(8)"),
+    Workload("k3s2_softmax", 16, 32, 64, 16, 32, 32, k=3, stride=2, pad=1, out_pad=1,
+             bias=True, epi=EPI_SOFTMAX_SIGMOID, seed=20263,
+             note="p49 page shape: ConvTranspose3d 32->64 k3 s2 p1 op1, softmax(dim=1), sigmoid"),
+    Workload("k5s1_bnpool", 16, 64, 128, 16, 32, 32, k=5, stride=1, pad=0, bias=True,
+             epi=EPI_SCALE_BN_TRAIN_AVGPOOL, scale=2.0, seed=20264,
+             note="p77 page shape: ConvTranspose3d 64->128 k5, x2, BatchNorm3d (train), avgpool"),
+    Workload("k4s2_gn", 8, 128, 128, 32, 32, 32, k=4, stride=2, pad=1, bias=True,
+             epi=EPI_RELU_GROUPNORM, groups=16, seed=20265,
+             note="stride-2 k4 GroupNorm(16) case at 128 channels"),
+]
+
+BY_NAME = {wl.name: wl for wl in WORKLOADS}
+
+
+@dataclass
+class Inputs:
+    x: np.ndarray
+    w: np.ndarray
+    b: Optional[np.ndarray]
+    gamma: Optional[np.ndarray]
+    beta: Optional[np.ndarray]
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None, x_dist: str = "normal") -> Inputs:
+    """Draw the float32 inputs of ``wl`` from ``default_rng(seed or wl.seed)``.
+
+    ``x_dist`` may be "normal" (N(0,1), the default) or "uniform" (U[0,1)).
+    Returned bias/gamma/beta are None when the workload does not use them.
+    """
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    a = 1.0 / np.sqrt(wl.cin * wl.k ** 3)
+    if x_dist == "normal":
+        x = rng.standard_normal(wl.x_shape)
+    elif x_dist == "uniform":
+        x = rng.random(wl.x_shape)
+    else:
+        raise ValueError(x_dist)
+    w = rng.uniform(-a, a, size=wl.w_shape)
+    b = rng.uniform(-a, a, size=(wl.cout,))
+    gamma = rng.uniform(0.5, 1.5, size=(wl.cout,))
+    beta = rng.normal(0.0, 0.1, size=(wl.cout,))
+    f32 = lambda arr: np.ascontiguousarray(arr, dtype=np.float32)
+    uses_affine = wl.epi in (EPI_RELU_GROUPNORM, EPI_SCALE_BN_TRAIN_AVGPOOL)
+    return Inputs(
+        x=f32(x),
+        w=f32(w),
+        b=f32(b) if wl.bias else None,
+        gamma=f32(gamma) if uses_affine else None,
+        beta=f32(beta) if uses_affine else None,
+    )
+
+
+def random_geometry(rng: np.random.Generator, max_in: int = 6, max_ch: int = 7,
+                    epi: int = EPI_NONE) -> Workload:
+    """A small random geometry for sweeps: k in 1..5, stride in 1..3,
+    pad < k, out_pad < stride, odd sizes and channel counts that are not powers
+    of two.  Some draws have an empty output; the caller decides (with its own
+    size formula) whether to keep a draw."""
+    k = int(rng.integers(1, 6))
+    s = int(rng.integers(1, 4))
+    p = int(rng.integers(0, k))
+    op = int(rng.integers(0, s))
+    d, h, w = (int(v) for v in rng.integers(1, max_in + 1, size=3))
+    cin = int(rng.integers(1, max_ch + 1))
+    cout = int(rng.integers(1, max_ch + 1))
+    groups = 1
+    if epi == EPI_RELU_GROUPNORM:
+        divs = [g for g in range(1, cout + 1) if cout % g == 0]
+        groups = int(rng.choice(divs))
+    n = int(rng.integers(1, 4))
+    return Workload("rand", n, cin, cout, d, h, w, k=k, stride=s, pad=p, out_pad=op,
+                    bias=bool(rng.integers(0, 2)), epi=epi, groups=groups,
+                    scale=float(rng.choice([1.0, 2.0, -0.5])),
+                    seed=int(rng.integers(0, 2**31)))

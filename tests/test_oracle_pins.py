@@ -1,0 +1,367 @@
+"""Pins of the fp64 CPU oracle to things other than itself.
+
+Each test ties one oracle function to something fixed outside it: values the
+pages print for worked examples (fixtures under tests/golden/), library
+routines that compute the same operation (torch fp64 on the CPU), closed
+forms, identities, invariants and special cases.  They are chosen so that a
+plausible slip in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, a biased/unbiased mix-up, the wrong softmax axis) fails at
+least one of them.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from activation_epilogues_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def t64(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+def rand_case(rng, n=2, cin=3, cout=5, dims=(4, 5, 3), k=3, s=1, p=0, op=0, bias=True):
+    x = rng.standard_normal((n, cin) + tuple(dims)).astype(np.float32)
+    w = rng.uniform(-1, 1, (cin, cout, k, k, k)).astype(np.float32)
+    b = rng.uniform(-1, 1, cout).astype(np.float32) if bias else None
+    return x, w, b
+
+
+def sweep_geometries(count, seed=1234, max_in=6, max_ch=6):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        wl = W.random_geometry(rng, max_in=max_in, max_ch=max_ch)
+        if min(oracle.out_dims(wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)) <= 0:
+            continue
+        out.append(wl)
+    return out
+
+
+# ---------------------------------------------------------------- geometry pins
+
+def test_output_sizes_printed_on_pages():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "page_output_sizes.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            rows.append([int(v) for v in line.split()])
+    assert len(rows) == 5
+    for n_in, k, s, p, op, n_out in rows:
+        assert oracle.out_dim(n_in, k, s, p, op) == n_out
+
+
+def test_output_shapes_of_the_five_workloads():
+    # shapes stated with the workloads: [2,16,10,10,10], [16,128,34,34,34],
+    # [16,64,32,64,64], [16,128,20,36,36], [8,128,64,64,64]
+    expect = {"tiny_gn": (10, 10, 10), "k3s1_gn": (34, 34, 34), "k3s2_softmax": (32, 64, 64),
+              "k5s1_bnpool": (20, 36, 36), "k4s2_gn": (64, 64, 64)}
+    for wl in W.WORKLOADS:
+        assert oracle.out_dims(wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad) == expect[wl.name]
+
+
+def test_p49_stride2_gather_table():
+    """The (input, tap) -> output table the p49 page enumerates for k=3, s=2, p=1."""
+    table = {}
+    boundary = {}
+    for line in open(os.path.join(GOLDEN, "p49_stride2_k3_p1_gather_table.txt")):
+        line = line.split("#")[0].strip()
+        m = re.match(r"^(\d+): (.*)$", line)
+        if m:
+            table[int(m.group(1))] = sorted(tuple(int(v) for v in pr.strip("()").split(","))
+                                            for pr in m.group(2).split())
+        m = re.match(r"^in (\d+) -> (.*)$", line)
+        if m:
+            boundary[int(m.group(1))] = [int(v) for v in m.group(2).split()]
+    assert len(table) == 4 and len(boundary) == 2
+    k, s, p, n_in = 3, 2, 1, 16
+    # along D: with H=W=1 and taps (kh, kw) = (1, 1) the other dims map 0 -> 0 at p=1
+    for axis in range(3):
+        found = {}
+        for i in range(n_in):
+            for tap in range(k):
+                dims = [1, 1, 1]
+                dims[axis] = n_in
+                x = np.zeros((1, 1) + tuple(dims), np.float32)
+                idx = [0, 0, 0]
+                idx[axis] = i
+                x[(0, 0) + tuple(idx)] = 1.0
+                w = np.zeros((1, 1, k, k, k), np.float32)
+                tt = [1, 1, 1]
+                tt[axis] = tap
+                w[(0, 0) + tuple(tt)] = 1.0
+                # output_padding 1: the tested axis gets length 32, the length-1
+                # axes get length 2 and tap 1 maps their input 0 to output 0
+                y = oracle.convt3d(x, w, None, s, p, 1)
+                sl = [slice(0, 1)] * 3
+                sl[axis] = slice(None)
+                line = y[(0, 0) + tuple(sl)].reshape(-1)
+                # with tap 1 on a length-1 dim, output index 0 receives the value
+                nz = np.nonzero(line)[0]
+                assert len(nz) <= 1
+                if i in boundary:
+                    boundary_found = found.setdefault(("b", i), [])
+                    boundary_found.append(int(nz[0]) if len(nz) else -1)
+                for o in nz:
+                    found.setdefault(int(o), []).append((i, tap))
+        for o, pairs in table.items():
+            assert sorted(found[o]) == pairs, (axis, o)
+        for i, outs in boundary.items():
+            assert found[("b", i)] == outs, (axis, i)
+        # 1 and 2 taps alternate along a dimension (average 1.5); the last output row
+        # (added by output_padding) is reached only from the last input voxel (tap 2)
+        counts = [len(found.get(o, [])) for o in range(2 * n_in)]
+        assert counts == [1, 2] * (n_in - 1) + [1, 1]
+        assert found[2 * n_in - 1] == [(n_in - 1, 2)]
+
+
+def test_p61_worked_1d_examples():
+    """Stride-1, pad-0, k=3 one-dimensional examples of the p61 page, along each axis."""
+    ex_a, ex_b = {}, None
+    for line in open(os.path.join(GOLDEN, "p61_convT1d_examples.txt")):
+        line = line.split("#")[0].strip()
+        m = re.match(r"^(\d+): (.*)$", line)
+        if m:
+            ex_a[int(m.group(1))] = [tuple(int(v) for v in pr.strip("()").split(","))
+                                     for pr in m.group(2).split()]
+        m = re.match(r"^out: (.*)$", line)
+        if m:
+            ex_b = m.group(1).split()
+    rng = np.random.default_rng(7)
+    wv = rng.uniform(0.5, 2.0, 3)
+    zv = rng.uniform(0.5, 2.0, 3)
+    for axis in range(3):
+        dims = [1, 1, 1]
+        dims[axis] = 3
+        x = zv.reshape([1, 1] + dims).astype(np.float32)
+        w = np.zeros((1, 1, 3, 3, 3), np.float32)
+        sl = [0, 0, 0]
+        for t in range(3):
+            sl[axis] = t
+            w[(0, 0) + tuple(sl)] = wv[t]
+        y = oracle.convt3d(x, w, None, 1, 0, 0)
+        sel = [0, 0, 0]
+        sel[axis] = slice(None)
+        line = y[(0, 0) + tuple(sel)]
+        assert line.shape == (5,)
+        xf, wf = x.astype(np.float64).reshape(-1), w.astype(np.float64)
+        for o, terms in ex_a.items():
+            want = 0.0
+            for tap, i in terms:
+                tt = [0, 0, 0]
+                tt[axis] = tap
+                want += wf[(0, 0) + tuple(tt)] * xf[i]
+            assert abs(line[o] - want) < 1e-12
+        # example (b): input (1, 0) -> (k0, k1, k2, 0)
+        dims[axis] = 2
+        xb = np.zeros([1, 1] + dims, np.float32)
+        idx = [0, 0, 0]
+        xb[(0, 0) + tuple(idx)] = 1.0
+        yb = oracle.convt3d(xb, w, None, 1, 0, 0)
+        lb = yb[(0, 0) + tuple(sel)]
+        assert lb.shape == (4,)
+        for o, tok in enumerate(ex_b):
+            want = 0.0 if tok == "-" else float(np.float32(wv[int(tok)]))
+            assert abs(lb[o] - want) < 1e-12
+
+
+# ---------------------------------------------------------------- convolution pins
+
+@pytest.mark.parametrize("wl", sweep_geometries(40), ids=lambda wl: f"k{wl.k}s{wl.stride}p{wl.pad}op{wl.out_pad}")
+def test_matches_torch_conv_transpose3d(wl):
+    """Library routine for the same operation: torch conv_transpose3d in fp64 on the CPU."""
+    rng = np.random.default_rng(wl.seed)
+    x, w, b = rand_case(rng, wl.n, wl.cin, wl.cout, (wl.d, wl.h, wl.w), wl.k, wl.stride,
+                        wl.pad, wl.out_pad, wl.bias)
+    y = oracle.convt3d(x, w, b, wl.stride, wl.pad, wl.out_pad)
+    ref = F.conv_transpose3d(t64(x), t64(w), None if b is None else t64(b), stride=wl.stride,
+                             padding=wl.pad, output_padding=wl.out_pad).numpy()
+    assert y.shape == ref.shape
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("wl", sweep_geometries(25, seed=99), ids=lambda wl: f"k{wl.k}s{wl.stride}p{wl.pad}op{wl.out_pad}")
+def test_scatter_equals_gather(wl):
+    rng = np.random.default_rng(wl.seed)
+    x, w, b = rand_case(rng, wl.n, wl.cin, wl.cout, (wl.d, wl.h, wl.w), wl.k, wl.stride,
+                        wl.pad, wl.out_pad, wl.bias)
+    ys = oracle.convt3d(x, w, b, wl.stride, wl.pad, wl.out_pad)
+    yg = oracle.convt3d_gather(x, w, b, wl.stride, wl.pad, wl.out_pad)
+    np.testing.assert_allclose(ys, yg, rtol=0, atol=1e-12)
+    # and single points
+    for _ in range(5):
+        idx = tuple(int(rng.integers(0, n)) for n in ys.shape)
+        v = oracle.convt3d_point(x, w, b, wl.stride, wl.pad, wl.out_pad, *idx)
+        assert abs(v - ys[idx]) < 1e-12
+
+
+@pytest.mark.parametrize("k,p", [(1, 0), (3, 0), (3, 1), (3, 2), (4, 1), (5, 0), (5, 3)])
+def test_stride1_identity_flipped_kernel(k, p):
+    """Stride 1: convT(x, w, pad p) equals an ordinary correlation of x with the kernel
+    rotated by 180 degrees in all three dims and in/out channels swapped, padded by
+    k-1-p on every side (p61 page's matrix-transpose argument, extended to 3-D)."""
+    rng = np.random.default_rng(k * 10 + p)
+    x, w, b = rand_case(rng, 2, 3, 4, (5, 6, 4), k, 1, p, 0, True)
+    y = oracle.convt3d(x, w, b, 1, p, 0)
+    wf = t64(w).permute(1, 0, 2, 3, 4).flip(2, 3, 4).contiguous()
+    ref = F.conv3d(t64(x), wf, t64(b), stride=1, padding=k - 1 - p).numpy()
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("k,s,p,op", [(3, 1, 0, 0), (3, 2, 1, 1), (4, 2, 1, 0), (5, 3, 2, 2), (2, 2, 0, 1), (1, 2, 0, 1)])
+def test_adjoint_identity(k, s, p, op):
+    """<convT(x; w), z> == <x, conv3d(z; w, stride s, pad p)>: the transposed convolution
+    is the adjoint of the strided convolution that uses the same weight tensor."""
+    rng = np.random.default_rng(100 + k + 10 * s + 100 * p)
+    x, w, _ = rand_case(rng, 2, 3, 4, (4, 5, 3), k, s, p, op, False)
+    y = oracle.convt3d(x, w, None, s, p, op)
+    z = rng.standard_normal(y.shape)
+    lhs = float((y * z).sum())
+    cz = F.conv3d(t64(z), t64(w), None, stride=s, padding=p).numpy()
+    assert cz.shape == x.shape
+    rhs = float((x.astype(np.float64) * cz).sum())
+    assert abs(lhs - rhs) < 1e-10 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("k,s,op", [(3, 1, 0), (5, 1, 0), (3, 2, 1), (4, 2, 0), (2, 3, 2)])
+def test_spatial_sum_closed_form_pad0(k, s, op):
+    """With pad 0 every (input voxel, tap) pair lands inside the output, so
+    sum over space of y[n, co] = sum_ci Xsum[n, ci] * Wsum[ci, co] + b[co] * |out|
+    (p77 page's spatial-sum argument, with the bias term)."""
+    rng = np.random.default_rng(k + 7 * s)
+    x, w, b = rand_case(rng, 3, 4, 5, (4, 3, 5), k, s, 0, op, True)
+    y = oracle.convt3d(x, w, b, s, 0, op)
+    S = int(np.prod(y.shape[2:]))
+    xs = x.astype(np.float64).sum(axis=(2, 3, 4))
+    ws = w.astype(np.float64).sum(axis=(2, 3, 4))
+    want = xs @ ws + b.astype(np.float64)[None, :] * S
+    np.testing.assert_allclose(y.sum(axis=(2, 3, 4)), want, rtol=0, atol=1e-10)
+
+
+def test_k1_is_a_per_voxel_matrix_product():
+    """k=1, s=1, p=0: y[n, :, v] = w^T x[n, :, v] + b (textbook special case)."""
+    rng = np.random.default_rng(5)
+    x, w, b = rand_case(rng, 2, 6, 7, (3, 4, 5), 1, 1, 0, 0, True)
+    y = oracle.convt3d(x, w, b, 1, 0, 0)
+    ref = np.einsum("ncdhw,co->nodhw", x.astype(np.float64), w[:, :, 0, 0, 0].astype(np.float64))
+    ref += b.astype(np.float64)[None, :, None, None, None]
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
+
+
+def test_unreached_outputs_keep_only_the_bias():
+    """stride > k leaves output voxels no tap reaches; they hold the bias."""
+    rng = np.random.default_rng(3)
+    x, w, b = rand_case(rng, 1, 2, 3, (3, 3, 3), 1, 3, 0, 2, True)
+    y = oracle.convt3d(x, w, b, 3, 0, 2)
+    assert y.shape[2:] == (9, 9, 9)
+    mask = np.zeros((9, 9, 9), bool)
+    mask[::3, ::3, ::3] = True
+    for co in range(3):
+        assert np.all(y[0, co][~mask] == np.float64(b[co]))
+
+
+# ---------------------------------------------------------------- epilogue pins
+
+def test_relu_groupnorm_matches_torch_and_invariants():
+    rng = np.random.default_rng(11)
+    y = rng.standard_normal((3, 12, 3, 4, 5))
+    gamma = rng.uniform(0.5, 1.5, 12).astype(np.float32)
+    beta = rng.normal(0, 0.1, 12).astype(np.float32)
+    for G in (1, 3, 4, 12):
+        out, st = oracle.relu_groupnorm(y, G, 1e-5, gamma, beta)
+        ref = F.group_norm(torch.relu(t64(y)), G, t64(gamma), t64(beta), eps=1e-5).numpy()
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+        # invariants before the affine step: per (n, g) mean 0, variance var/(var+eps)
+        r = np.maximum(y, 0).reshape(3, G, -1)
+        var = r.var(axis=2)  # biased
+        z = ((out - beta.astype(np.float64)[None, :, None, None, None]) /
+             gamma.astype(np.float64)[None, :, None, None, None]).reshape(3, G, -1)
+        np.testing.assert_allclose(z.mean(axis=2), 0, atol=1e-12)
+        np.testing.assert_allclose(z.var(axis=2), var / (var + 1e-5), rtol=1e-12)
+        np.testing.assert_allclose(st[..., 0], r.mean(axis=2), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(st[..., 1], 1 / np.sqrt(var + 1e-5), rtol=1e-12)
+
+
+def test_groupnorm_with_one_channel_per_group_is_instance_norm():
+    rng = np.random.default_rng(12)
+    y = rng.standard_normal((2, 5, 3, 3, 4))
+    out, _ = oracle.relu_groupnorm(y, 5, 1e-5, None, None)
+    ref = F.instance_norm(torch.relu(t64(y)), eps=1e-5).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_softmax_sigmoid_matches_torch_and_invariants():
+    rng = np.random.default_rng(13)
+    y = rng.standard_normal((2, 64, 3, 4, 5)) * 0.5
+    out, p = oracle.softmax_sigmoid(y)
+    ref = torch.sigmoid(torch.softmax(t64(y), dim=1)).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    # sigmoid of a probability lies in (0.5, sigmoid(1)]  (p49 page's range remark)
+    assert out.min() > 0.5 and out.max() <= 1 / (1 + np.exp(-1.0)) + 1e-15
+    # a softmax taken along W instead of C (the failure the p49 page chased) differs
+    wrong = torch.sigmoid(torch.softmax(t64(y), dim=4)).numpy()
+    assert np.abs(wrong - out).max() > 1e-3
+
+
+def test_softmax_single_channel_is_sigmoid_of_one():
+    y = np.random.default_rng(14).standard_normal((2, 1, 2, 3, 3))
+    out, _ = oracle.softmax_sigmoid(y)
+    np.testing.assert_allclose(out, 1 / (1 + np.exp(-1.0)), rtol=0, atol=1e-15)
+
+
+def test_scale_bn_avgpool_matches_torch_and_invariants():
+    rng = np.random.default_rng(15)
+    y = rng.standard_normal((4, 6, 3, 4, 5)) + rng.standard_normal((1, 6, 1, 1, 1))
+    gamma = rng.uniform(0.5, 1.5, 6).astype(np.float32)
+    beta = rng.normal(0, 0.1, 6).astype(np.float32)
+    for scale in (2.0, -0.5, 1.0):
+        out, st = oracle.scale_bn_avgpool(y, scale, 1e-5, gamma, beta)
+        z = scale * t64(y)
+        bn = F.batch_norm(z, None, None, t64(gamma), t64(beta), training=True, eps=1e-5)
+        ref = bn.mean(dim=(2, 3, 4)).numpy()
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+        # batch statistics: biased variance over (N, D, H, W) of z
+        zz = z.numpy()
+        np.testing.assert_allclose(st[:, 0], zz.mean(axis=(0, 2, 3, 4)), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(st[:, 1], zz.var(axis=(0, 2, 3, 4)), rtol=1e-12)
+        # the batch mean of the pooled output is beta (mean_c is the mean of per-sample means)
+        np.testing.assert_allclose(out.mean(axis=0), beta.astype(np.float64), rtol=0, atol=1e-12)
+        # collapsed form: (mean_dhw z - mean_c) * rstd * gamma + beta
+        mz = zz.mean(axis=(2, 3, 4))
+        coll = (mz - st[None, :, 0]) / np.sqrt(st[None, :, 1] + 1e-5) * gamma + beta
+        np.testing.assert_allclose(out, coll, rtol=0, atol=1e-12)
+
+
+def test_scale_does_not_factor_out_of_bn_because_of_eps():
+    """Statistics are taken of z = scale*y, so eps enters as sqrt(scale^2 var + eps) (p77 page)."""
+    rng = np.random.default_rng(16)
+    y = rng.standard_normal((2, 3, 2, 2, 2)) * 1e-3
+    o2, _ = oracle.scale_bn_avgpool(y, 2.0, 1e-5, None, None)
+    o1, _ = oracle.scale_bn_avgpool(y, 1.0, 1e-5, None, None)
+    assert np.abs(o2 - o1).max() > 1e-3
+
+
+def test_tiny_workload_whole_path_against_torch():
+    wl = W.BY_NAME["tiny_gn"]
+    inp = W.make_inputs(wl)
+    res = oracle.run_workload(wl, inp)
+    y = F.conv_transpose3d(t64(inp.x), t64(inp.w), t64(inp.b))
+    ref = F.group_norm(torch.relu(y), wl.groups, t64(inp.gamma), t64(inp.beta), eps=wl.eps).numpy()
+    np.testing.assert_allclose(res.out, ref, rtol=0, atol=1e-12)
+
+
+def test_input_recipe_is_reproducible():
+    wl = W.BY_NAME["tiny_gn"]
+    a, b = W.make_inputs(wl), W.make_inputs(wl)
+    assert np.array_equal(a.x, b.x) and np.array_equal(a.w, b.w)
+    assert a.x.dtype == np.float32 and a.x.shape == (2, 8, 8, 8, 8)
+    lim = 1 / np.sqrt(8 * 27)
+    assert np.abs(a.w).max() <= lim and np.abs(a.b).max() <= lim
+    assert 0.5 <= a.gamma.min() and a.gamma.max() <= 1.5
