@@ -1,0 +1,48 @@
+"""Build libconvt3d.so in-tree with hipcc for gfx950.
+
+    python -m activation_epilogues_amd.build
+
+Every HIP source is compiled with ``-Xclang -target-feature -Xclang
+-packed-fp32-ops`` (no packed FP32 instructions are generated).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libconvt3d.so")
+SOURCES = ["plan.cpp", "api.cpp", "kernels.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libconvt3d)")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libconvt3d.so (always rebuilds)."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-O3", "--offload-arch=" + ARCH, "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I" + INCLUDE, "-I" + CSRC, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libconvt3d")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

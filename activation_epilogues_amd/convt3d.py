@@ -1,0 +1,221 @@
+"""Thin ctypes binding of libconvt3d (include/convt3d.h).
+
+The functions keep the C names and only marshal arguments: torch tensors (or
+raw integers) become device pointers, a torch stream becomes a hipStream_t.
+All computation happens in the library's HIP kernels; if the library is not
+built, every call raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libconvt3d.so")
+
+EPI_NONE = 0
+EPI_RELU_GROUPNORM = 1
+EPI_SOFTMAX_SIGMOID = 2
+EPI_SCALE_BN_TRAIN_AVGPOOL = 3
+
+STATUS = {
+    0: "OK", 1: "ERR_NULL", 2: "ERR_GEOMETRY", 3: "ERR_GROUPS", 4: "ERR_ALIGNMENT",
+    5: "ERR_WORKSPACE", 6: "ERR_UNSUPPORTED", 7: "ERR_LAUNCH", 8: "ERR_TOO_LARGE", 9: "ERR_ALIAS",
+}
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in
+                ("n", "cin", "cout", "d", "h", "w", "k", "stride", "pad", "out_pad")]
+
+
+class Epilogue(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("groups", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("scale", ctypes.c_float), ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("stats_out", ctypes.c_void_p)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("co_blocks_per_wave", ctypes.c_int32),
+                ("pos_blocks_per_wave", ctypes.c_int32), ("w_phases_per_wave", ctypes.c_int32),
+                ("waves_co", ctypes.c_int32), ("waves_pos", ctypes.c_int32),
+                ("tile_q", ctypes.c_int32 * 3), ("ci_chunk", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("workgroups", ctypes.c_int64),
+                ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64)]
+
+
+class Convt3dError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libconvt3d.so (built in-tree by activation_epilogues_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libconvt3d is not built ({LIB_PATH} missing); run "
+                               "python -m activation_epilogues_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.convt3d_status_string.restype = ctypes.c_char_p
+        L.convt3d_status_string.argtypes = [ctypes.c_int]
+        L.convt3d_output_dims.restype = ctypes.c_int
+        L.convt3d_output_dims.argtypes = [P(Geom), P(ctypes.c_int32)]
+        L.convt3d_output_elems.restype = ctypes.c_int64
+        L.convt3d_output_elems.argtypes = [P(Geom), P(Epilogue)]
+        L.convt3d_packed_weight_bytes.restype = sz
+        L.convt3d_packed_weight_bytes.argtypes = [P(Geom)]
+        L.convt3d_prepack_weights.restype = ctypes.c_int
+        L.convt3d_prepack_weights.argtypes = [P(Geom), vp, vp, vp]
+        L.convt3d_workspace_size.restype = sz
+        L.convt3d_workspace_size.argtypes = [P(Geom), P(Epilogue)]
+        L.convt3d_fused.restype = ctypes.c_int
+        L.convt3d_fused.argtypes = [vp, vp, vp, P(Geom), P(Epilogue), vp, vp, sz, vp]
+        L.convt3d_get_plan_info.restype = ctypes.c_int
+        L.convt3d_get_plan_info.argtypes = [P(Geom), P(Epilogue), P(PlanInfo)]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ["convt3d_status_string", "convt3d_output_dims", "convt3d_output_elems",
+            "convt3d_packed_weight_bytes", "convt3d_prepack_weights", "convt3d_workspace_size",
+            "convt3d_fused", "convt3d_get_plan_info"]
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (or an int / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_geom(n, cin, cout, d, h, w, k, stride=1, pad=0, out_pad=0) -> Geom:
+    return Geom(n, cin, cout, d, h, w, k, stride, pad, out_pad)
+
+
+def make_epilogue(kind, groups=1, eps=1e-5, scale=1.0, gamma=None, beta=None, stats_out=None) -> Epilogue:
+    return Epilogue(kind, groups, eps, scale, _ptr(gamma), _ptr(beta), _ptr(stats_out))
+
+
+def status_string(status: int) -> str:
+    return lib().convt3d_status_string(status).decode()
+
+
+def convt3d_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def convt3d_output_dims(geom: Geom):
+    arr = (ctypes.c_int32 * 3)()
+    st = lib().convt3d_output_dims(ctypes.byref(geom), arr)
+    if st:
+        raise Convt3dError(st, "convt3d_output_dims")
+    return tuple(arr)
+
+
+def convt3d_output_elems(geom: Geom, epi: Epilogue) -> int:
+    return int(lib().convt3d_output_elems(ctypes.byref(geom), ctypes.byref(epi)))
+
+
+def convt3d_packed_weight_bytes(geom: Geom) -> int:
+    return int(lib().convt3d_packed_weight_bytes(ctypes.byref(geom)))
+
+
+def convt3d_workspace_size(geom: Geom, epi: Epilogue) -> int:
+    return int(lib().convt3d_workspace_size(ctypes.byref(geom), ctypes.byref(epi)))
+
+
+def convt3d_prepack_weights(geom: Geom, w, w_packed, stream=None, check=True) -> int:
+    st = lib().convt3d_prepack_weights(ctypes.byref(geom), _ptr(w), _ptr(w_packed), _stream(stream))
+    if check and st:
+        raise Convt3dError(st, "convt3d_prepack_weights")
+    return st
+
+
+def convt3d_fused(x, w_packed, bias, geom: Geom, epi: Epilogue, out, workspace, workspace_bytes: int,
+                  stream=None, check=True) -> int:
+    st = lib().convt3d_fused(_ptr(x), _ptr(w_packed), _ptr(bias), ctypes.byref(geom), ctypes.byref(epi),
+                             _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream))
+    if check and st:
+        raise Convt3dError(st, "convt3d_fused")
+    return st
+
+
+def convt3d_get_plan_info(geom: Geom, epi: Epilogue) -> dict:
+    info = PlanInfo()
+    st = lib().convt3d_get_plan_info(ctypes.byref(geom), ctypes.byref(epi), ctypes.byref(info))
+    if st:
+        raise Convt3dError(st, "convt3d_get_plan_info")
+    d = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+    d["tile_q"] = tuple(info.tile_q)
+    return d
+
+
+# ----------------------------------------------------------------------------
+# Device-memory plumbing with torch (allocation only; no arithmetic).
+
+class FusedCall:
+    """Holds the device buffers of one geometry/epilogue and calls the library.
+
+    Allocates with torch (packed weights, workspace, output, stats); every step
+    of the computation runs in libconvt3d.
+    """
+
+    def __init__(self, geom: Geom, kind: int, groups: int = 1, eps: float = 1e-5, scale: float = 1.0,
+                 device="cuda", want_stats: bool = False):
+        import torch
+        self.geom = geom
+        self.kind = kind
+        self.groups, self.eps, self.scale = groups, eps, scale
+        probe = make_epilogue(kind, groups, eps, scale)
+        self.out_dims = convt3d_output_dims(geom)
+        self.out_elems = convt3d_output_elems(geom, probe)
+        if self.out_elems < 0:
+            raise Convt3dError(2, "convt3d_output_elems")
+        self.ws_bytes = convt3d_workspace_size(geom, probe)
+        self.packed_bytes = convt3d_packed_weight_bytes(geom)
+        self.w_packed = torch.empty(max(1, self.packed_bytes // 4), dtype=torch.float32, device=device)
+        self.workspace = torch.empty(max(1, self.ws_bytes // 4), dtype=torch.float32, device=device)
+        if kind == EPI_SCALE_BN_TRAIN_AVGPOOL:
+            self.out = torch.empty((geom.n, geom.cout, 1, 1, 1), dtype=torch.float32, device=device)
+        else:
+            self.out = torch.empty((geom.n, geom.cout) + tuple(self.out_dims), dtype=torch.float32,
+                                   device=device)
+        self.stats = None
+        if want_stats:
+            if kind == EPI_RELU_GROUPNORM:
+                self.stats = torch.empty((geom.n, groups, 2), dtype=torch.float32, device=device)
+            elif kind == EPI_SCALE_BN_TRAIN_AVGPOOL:
+                self.stats = torch.empty((geom.cout, 2), dtype=torch.float32, device=device)
+
+    def epilogue(self, gamma=None, beta=None) -> Epilogue:
+        return make_epilogue(self.kind, self.groups, self.eps, self.scale, gamma, beta, self.stats)
+
+    def prepack(self, w, stream=None):
+        convt3d_prepack_weights(self.geom, w, self.w_packed, stream)
+
+    def __call__(self, x, bias=None, gamma=None, beta=None, stream=None):
+        convt3d_fused(x, self.w_packed, bias, self.geom, self.epilogue(gamma, beta), self.out,
+                      self.workspace, self.ws_bytes, stream)
+        return self.out
+
+    def plan_info(self) -> dict:
+        return convt3d_get_plan_info(self.geom, self.epilogue())

@@ -1,0 +1,186 @@
+// C ABI of libconvt3d (include/convt3d.h): argument checks, plan cache and the
+// kernel sequence of each epilogue.  All work is enqueued on the caller's
+// stream; nothing here allocates device memory or waits on the device.
+#include <hip/hip_runtime_api.h>
+
+#include <cstring>
+#include <list>
+#include <mutex>
+
+#include "convt3d_internal.hpp"
+
+using namespace convt3d;
+
+namespace {
+
+// Plans depend on the geometry and on the epilogue kind / groups only.
+struct CacheKey {
+    convt3d_geom g;
+    int kind, groups;
+    bool operator==(const CacheKey &o) const {
+        return std::memcmp(&g, &o.g, sizeof(g)) == 0 && kind == o.kind && groups == o.groups;
+    }
+};
+
+std::mutex g_mu;
+std::list<std::pair<CacheKey, Plan>> g_cache;  // most recent first, bounded
+
+int cached_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *out) {
+    if (!g || !e) return CONVT3D_ERR_NULL;
+    CacheKey key;
+    std::memset(&key, 0, sizeof(key));
+    key.g = *g;
+    key.kind = e->kind;
+    key.groups = e->kind == CONVT3D_EPI_RELU_GROUPNORM ? e->groups : 0;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        for (auto it = g_cache.begin(); it != g_cache.end(); ++it)
+            if (it->first == key) {
+                *out = it->second;
+                out->e = *e;  // pointers / eps / scale of this call
+                if (it != g_cache.begin()) g_cache.splice(g_cache.begin(), g_cache, it);
+                return CONVT3D_OK;
+            }
+    }
+    Plan pl;
+    int st = make_plan(g, e, &pl);
+    if (st) return st;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_cache.emplace_front(key, pl);
+        if (g_cache.size() > 64) g_cache.pop_back();
+    }
+    *out = pl;
+    return CONVT3D_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *convt3d_status_string(int status) {
+    switch (status) {
+        case CONVT3D_OK: return "ok";
+        case CONVT3D_ERR_NULL: return "a required pointer is NULL";
+        case CONVT3D_ERR_GEOMETRY: return "invalid geometry (size out of range or empty output)";
+        case CONVT3D_ERR_GROUPS: return "GroupNorm groups must be >= 1 and divide cout";
+        case CONVT3D_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
+        case CONVT3D_ERR_WORKSPACE: return "workspace missing or smaller than convt3d_workspace_size";
+        case CONVT3D_ERR_UNSUPPORTED: return "unsupported epilogue or geometry combination";
+        case CONVT3D_ERR_LAUNCH: return "HIP kernel launch failed";
+        case CONVT3D_ERR_TOO_LARGE: return "tensor too large (more than 2^31 elements)";
+        case CONVT3D_ERR_ALIAS: return "out overlaps x";
+        default: return "unknown status";
+    }
+}
+
+int convt3d_output_dims(const convt3d_geom *geom, int32_t out_dhw[3]) {
+    if (!geom || !out_dhw) return CONVT3D_ERR_NULL;
+    const int st = validate_geom(geom);
+    if (st) return st;
+    out_dhw[0] = (int32_t)out_dim(geom->d, geom->k, geom->stride, geom->pad, geom->out_pad);
+    out_dhw[1] = (int32_t)out_dim(geom->h, geom->k, geom->stride, geom->pad, geom->out_pad);
+    out_dhw[2] = (int32_t)out_dim(geom->w, geom->k, geom->stride, geom->pad, geom->out_pad);
+    return CONVT3D_OK;
+}
+
+int64_t convt3d_output_elems(const convt3d_geom *geom, const convt3d_epilogue *epi) {
+    int32_t od[3];
+    if (!epi || convt3d_output_dims(geom, od) != CONVT3D_OK) return -1;
+    if (epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) return (int64_t)geom->n * geom->cout;
+    return (int64_t)geom->n * geom->cout * od[0] * od[1] * od[2];
+}
+
+size_t convt3d_packed_weight_bytes(const convt3d_geom *geom) {
+    Plan pl;
+    if (make_geometry(geom, &pl) != CONVT3D_OK) return 0;
+    return (size_t)pl.packed_floats * sizeof(float);
+}
+
+int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_packed, void *stream) {
+    if (!geom || !w || !w_packed) return CONVT3D_ERR_NULL;
+    if (!aligned16(w_packed)) return CONVT3D_ERR_ALIGNMENT;
+    Plan pl;
+    const int st = make_geometry(geom, &pl);
+    if (st) return st;
+    if (launch_prepack(pl, w, static_cast<float *>(w_packed), stream) != (int)hipSuccess)
+        return CONVT3D_ERR_LAUNCH;
+    return CONVT3D_OK;
+}
+
+size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *epi) {
+    Plan pl;
+    if (cached_plan(geom, epi, &pl) != CONVT3D_OK) return 0;
+    return pl.ws_bytes;
+}
+
+int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi, convt3d_plan_info *info) {
+    if (!info) return CONVT3D_ERR_NULL;
+    Plan pl;
+    const int st = cached_plan(geom, epi, &pl);
+    if (st) return st;
+    std::memset(info, 0, sizeof(*info));
+    info->variant = pl.variant;
+    info->co_blocks_per_wave = pl.CBW;
+    info->pos_blocks_per_wave = pl.PBW;
+    info->w_phases_per_wave = pl.NPH;
+    info->waves_co = pl.WCO;
+    info->waves_pos = pl.WPOS;
+    for (int i = 0; i < 3; ++i) info->tile_q[i] = pl.TQ[i];
+    info->ci_chunk = pl.CI_T;
+    info->lds_bytes = pl.lds_bytes;
+    info->workgroups = pl.grid_x * pl.grid_y * pl.grid_z;
+    info->issued_macs = pl.issued_macs;
+    info->valid_macs = pl.valid_macs;
+    return CONVT3D_OK;
+}
+
+int convt3d_fused(const float *x, const void *w_packed, const float *bias, const convt3d_geom *geom,
+                  const convt3d_epilogue *epi, float *out, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    if (!geom || !epi) return CONVT3D_ERR_NULL;
+    Plan pl;
+    int st = cached_plan(geom, epi, &pl);
+    if (st) return st;
+    if (geom->n == 0) return CONVT3D_OK;  // empty batch
+    if (!x || !w_packed || !out) return CONVT3D_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w_packed) || !aligned16(out) || (bias && !aligned16(bias)))
+        return CONVT3D_ERR_ALIGNMENT;
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+        return CONVT3D_ERR_WORKSPACE;
+    {
+        const char *xb = reinterpret_cast<const char *>(x);
+        const char *xe = xb + (size_t)geom->n * geom->cin * geom->d * geom->h * geom->w * sizeof(float);
+        const char *ob = reinterpret_cast<const char *>(out);
+        const char *oe = ob + (size_t)convt3d_output_elems(geom, epi) * sizeof(float);
+        if (ob < xe && xb < oe) return CONVT3D_ERR_ALIAS;
+    }
+    char *ws = static_cast<char *>(workspace);
+    const bool stats = epi->kind == CONVT3D_EPI_RELU_GROUPNORM || epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
+    float *partials = stats ? reinterpret_cast<float *>(ws + pl.ws_partials) : nullptr;
+
+    ConvParams cp;
+    fill_conv_params(pl, &cp);
+    cp.x = x;
+    cp.wp = static_cast<const float *>(w_packed);
+    cp.bias = bias;
+    cp.out = out;
+    cp.partials = partials;
+    if (launch_conv(pl, cp, stream) != (int)hipSuccess) return CONVT3D_ERR_LAUNCH;
+
+    if (epi->kind == CONVT3D_EPI_RELU_GROUPNORM) {
+        float *ab = reinterpret_cast<float *>(ws + pl.ws_ab);
+        if (launch_gn_finalize(pl, partials, epi->gamma, epi->beta, ab, epi->stats_out, stream) != (int)hipSuccess)
+            return CONVT3D_ERR_LAUNCH;
+        if (launch_normalize(pl, out, ab, stream) != (int)hipSuccess) return CONVT3D_ERR_LAUNCH;
+    } else if (epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) {
+        if (launch_bn_finalize(pl, partials, epi->gamma, epi->beta, out, epi->stats_out, stream) !=
+            (int)hipSuccess)
+            return CONVT3D_ERR_LAUNCH;
+    }
+    return CONVT3D_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal declarations shared by the planner, the C-ABI and the kernels of
+// libconvt3d.  Not part of the public interface (include/convt3d.h is).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "convt3d.h"
+
+namespace convt3d {
+
+constexpr int kMaxStride = 4;
+constexpr int kMaxPhases = kMaxStride * kMaxStride * kMaxStride;
+constexpr int kOctet = 8;          // input channels per packed weight group (4 MFMA k-steps)
+constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
+constexpr int kMaxLdsBytes = 80 * 1024;  // two workgroups per CU
+
+// Per-dimension stride-phase description.  Output index o = s*q + rho; the
+// taps that reach it are k = r + s*j (j = 0..J-1) from input i = q + c - j.
+struct DimPhase {
+    int r;   // first kernel tap of the phase: (rho + pad) mod s
+    int c;   // carry: (rho + pad) div s
+    int J;   // number of taps: ceil((k - r) / s), 0 if r >= k
+    int nq;  // number of q with s*q + rho < Out
+};
+
+// Arguments of the convolution kernel (passed by value).
+struct ConvParams {
+    const float *x;
+    const float *wp;      // packed weights
+    const float *bias;    // may be null
+    float *out;
+    float *partials;      // [n][tiles_per_n][cout][2] or null
+    int N, Cin, Cout, D, H, W, Do, Ho, Wo;
+    int s;
+    int Qd, Qh, Qw;
+    int TQd, TQh, TQw;
+    int ntd, nth, ntw;
+    int CI_T;             // input channels per LDS chunk (multiple of 8)
+    int octets;           // ceil(Cin / 8)
+    int nchunks;          // ceil(octets * 8 / CI_T)
+    int cb_total;         // ceil(Cout / 32)
+    int WCO, WPOS;        // wave grid
+    int co_tiles;
+    int nwgroups;         // w-phase groups per (rho_d, rho_h): s / NPH
+    int HWp;              // LDS row pitch (floats)
+    int CISTR;            // LDS stride between staged input channels (floats)
+    int epi;
+    float scale;
+    int tiles_per_n;
+    int pr[3][kMaxStride], pc[3][kMaxStride], pJ[3][kMaxStride];
+    int ntaps[kMaxPhases];
+    int wp_off[kMaxPhases];   // float offset of each phase's packed block
+    int steps4[kMaxPhases];   // packed float4 groups per co-block of each phase = octets*ntaps
+};
+
+struct Plan {
+    convt3d_geom g{};
+    convt3d_epilogue e{};
+    int Do = 0, Ho = 0, Wo = 0;
+    int64_t S = 0;            // output voxels per channel
+    int s = 1;
+    int Q[3] = {0, 0, 0};     // ceil(Out / s)
+    DimPhase ph[3][kMaxStride]{};
+    int ntaps[kMaxPhases]{};
+    int64_t wp_off[kMaxPhases]{};
+    int steps4[kMaxPhases]{};
+    int cb_total = 0, octets = 0;
+    int64_t packed_floats = 0;
+    // kernel choice
+    int variant = -1;
+    int CBW = 1, NPH = 1, PBW = 1, WCO = 1, WPOS = 1;
+    int TQ[3] = {1, 1, 1};
+    int ntile[3] = {1, 1, 1};
+    int CI_T = 8, nchunks = 1;
+    int HWp = 1, CISTR = 1, lds_bytes = 0;
+    int co_tiles = 1, nwgroups = 1;
+    int64_t tiles_per_n = 0;
+    int64_t grid_x = 0, grid_y = 0, grid_z = 0;
+    int64_t issued_macs = 0, valid_macs = 0;
+    // workspace layout (bytes)
+    size_t ws_partials = 0, ws_ab = 0, ws_bytes = 0;
+};
+
+// Kernel variants the library is built with.
+struct Variant {
+    int CBW, NPH, PBW;
+};
+extern const Variant kVariants[];
+extern const int kNumVariants;
+
+int64_t out_dim(int64_t in, int64_t k, int64_t s, int64_t p, int64_t op);
+int validate_geom(const convt3d_geom *g);
+int make_geometry(const convt3d_geom *g, Plan *pl);        // phases + packing only
+int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl);
+void fill_conv_params(const Plan &pl, ConvParams *cp);
+
+// Launchers (kernels.hip).  Return a hipError_t as int.
+int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream);
+int launch_conv(const Plan &pl, const ConvParams &cp, void *stream);
+int launch_gn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta,
+                       float *ab, float *stats_out, void *stream);
+int launch_normalize(const Plan &pl, float *out, const float *ab, void *stream);
+int launch_bn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta,
+                       float *out, float *stats_out, void *stream);
+
+}  // namespace convt3d

@@ -1,0 +1,648 @@
+// HIP kernels of libconvt3d for gfx950 (CDNA4, wave64).
+//
+//  * prepack_kernel      -- nn.ConvTranspose3d weight [Cin, Cout, k, k, k] to
+//                           per-stride-phase MFMA A-operand order.
+//  * convt3d_mfma_kernel -- the transposed convolution as an output-stationary
+//                           implicit GEMM per stride phase on FP32 MFMA
+//                           (v_mfma_f32_32x32x2_f32), input halo staged in LDS,
+//                           with the epilogue fused on the accumulators:
+//                           bias (+ReLU) store with per-tile channel sums for
+//                           GroupNorm, in-register channel softmax + sigmoid,
+//                           or per-tile channel sums of scale*y for BatchNorm.
+//  * gn_finalize_kernel  -- per (n, group) fp64 merge of the tile partials,
+//                           mean / biased variance / rstd, per-channel a, b.
+//  * normalize_kernel    -- out = a[n,c] * out + b[n,c], in place, float4.
+//  * bn_finalize_kernel  -- per channel fp64 batch mean / biased variance and
+//                           the pooled output (mean over voxels of the
+//                           normalised values = (mean_nc - mean_c)*rstd*g + b).
+//
+// MFMA 32x32x2 f32 operand layout (checked on the device): lane l supplies
+// A[row = l%32][k = l/32] and B[k = l/32][col = l%32]; accumulator register r
+// of lane l holds D[row = 8*(r/4) + 4*(l/32) + r%4][col = l%32].  Rows are
+// output channels, columns are output voxels, k runs over (input channel, tap).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "convt3d_internal.hpp"
+
+namespace convt3d {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16f mfma32x32x2(float a, float b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Weight pre-pack.  Packed order per phase: [co_block][octet][tap][lane][4]
+// (as float4 groups [co_block][octet*ntaps + tap][lane]); element e of lane l
+// of group (octet, tap) is w[ci = 8*octet + 2*e + l/32][co = 32*co_block + l%32]
+// at kernel tap (r_d + s*j_d, r_h + s*j_h, r_w + s*j_w), zero outside
+// [0, Cin) x [0, Cout).
+struct PackParams {
+    const float *w;
+    float *wp;
+    int Cin, Cout, k, s, cb_total, nph;
+    int pr[3][kMaxStride], pJ[3][kMaxStride];
+    int ntaps[kMaxPhases], steps4[kMaxPhases], wp_off[kMaxPhases];
+    int total4;
+};
+
+__global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
+    for (int i4 = blockIdx.x * blockDim.x + threadIdx.x; i4 < P.total4; i4 += gridDim.x * blockDim.x) {
+        const int f = i4 * 4;
+        int ph = 0;
+        for (int q = 0; q < P.nph; ++q) {
+            const int beg = P.wp_off[q];
+            const int end = beg + P.cb_total * P.steps4[q] * 256;
+            if (f >= beg && f < end) { ph = q; break; }
+        }
+        const int local = (f - P.wp_off[ph]) >> 2;
+        const int lane = local & 63;
+        const int t = local >> 6;
+        const int steps4 = P.steps4[ph];
+        const int G = t % steps4;
+        const int cb = t / steps4;
+        const int ntp = P.ntaps[ph];
+        const int octet = G / ntp, tap = G % ntp;
+        const int s = P.s;
+        const int rd = ph / (s * s), rh = (ph / s) % s, rw = ph % s;
+        const int Jh = P.pJ[1][rh], Jw = P.pJ[2][rw];
+        const int jw = tap % Jw, jh = (tap / Jw) % Jh, jd = tap / (Jw * Jh);
+        const int kd = P.pr[0][rd] + s * jd, kh = P.pr[1][rh] + s * jh, kw = P.pr[2][rw] + s * jw;
+        const int co = cb * 32 + (lane & 31);
+        const int k = P.k;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ci = octet * 8 + 2 * e + (lane >> 5);
+            v[e] = (ci < P.Cin && co < P.Cout)
+                       ? P.w[((((size_t)ci * P.Cout + co) * k + kd) * k + kh) * k + kw]
+                       : 0.0f;
+        }
+        *reinterpret_cast<float4 *>(P.wp + f) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Transposed convolution on FP32 MFMA.
+//
+// Workgroup = 4 waves = WCO (co direction) x WPOS (position direction).  It
+// owns: one sample n, one (rho_d, rho_h) phase pair, NPH consecutive w-phases,
+// a box of TQd x TQh x TQw stride-phase positions q, and WCO*CBW blocks of 32
+// output channels.  Each wave owns CBW co-blocks x PBW blocks of 32 positions
+// for each of its NPH w-phases.  Input channels are consumed in chunks of CI_T:
+// the input halo of the box for those channels is staged in LDS, then every
+// live tap of every phase runs 4 MFMA k-steps per 8 input channels.
+template <int CBW, int NPH, int PBW>
+__global__ __launch_bounds__(kBlockThreads) void convt3d_mfma_kernel(const ConvParams P) {
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    const int wave = tid >> 6;
+    const int wco = wave % P.WCO;
+    const int wpos = wave / P.WCO;
+
+    // ---- workgroup -> tile
+    int bx = blockIdx.x;
+    const int tw_i = bx % P.ntw;
+    bx /= P.ntw;
+    const int th_i = bx % P.nth;
+    const int td_i = bx / P.nth;
+    int by = blockIdx.y;
+    const int co_tile = by % P.co_tiles;
+    by /= P.co_tiles;
+    const int wgrp = by % P.nwgroups;
+    by /= P.nwgroups;
+    const int s = P.s;
+    const int rho_h = by % s;
+    const int rho_d = by / s;
+    const int n = blockIdx.z;
+
+    const int TQd = P.TQd, TQh = P.TQh, TQw = P.TQw;
+    const int q0d = td_i * TQd, q0h = th_i * TQh, q0w = tw_i * TQw;
+    const int Jd = P.pJ[0][rho_d], cd = P.pc[0][rho_d];
+    const int Jh = P.pJ[1][rho_h], ch = P.pc[1][rho_h];
+    int Jw[NPH], cw[NPH], rw[NPH];
+    int lo_w_rel = INT_MAX, hi_w_rel = INT_MIN;
+#pragma unroll
+    for (int p = 0; p < NPH; ++p) {
+        rw[p] = wgrp * NPH + p;
+        Jw[p] = P.pJ[2][rw[p]];
+        cw[p] = P.pc[2][rw[p]];
+        if (Jw[p] > 0) {
+            lo_w_rel = min(lo_w_rel, cw[p] - Jw[p] + 1);
+            hi_w_rel = max(hi_w_rel, TQw - 1 + cw[p]);
+        }
+    }
+    const bool any_taps = Jd > 0 && Jh > 0 && lo_w_rel <= hi_w_rel;
+
+    // ---- halo box in input coordinates
+    const int HD = TQd + (Jd > 0 ? Jd : 1) - 1;
+    const int HH = TQh + (Jh > 0 ? Jh : 1) - 1;
+    const int HW = any_taps ? hi_w_rel - lo_w_rel + 1 : TQw;
+    const int lo_d = q0d + cd - Jd + 1;
+    const int lo_h = q0h + ch - Jh + 1;
+    const int lo_w = q0w + lo_w_rel;
+    const int HWp = P.HWp;
+    const int CISTR = P.CISTR;
+    const int ROW = HH * HWp;
+
+    // ---- taps that touch the input for this box (border tiles skip the rest)
+    const int TQd_e = min(TQd, P.Qd - q0d), TQh_e = min(TQh, P.Qh - q0h), TQw_e = min(TQw, P.Qw - q0w);
+    const int jd_lo = max(0, q0d + cd - (P.D - 1)), jd_hi = min(Jd - 1, q0d + TQd_e - 1 + cd);
+    const int jh_lo = max(0, q0h + ch - (P.H - 1)), jh_hi = min(Jh - 1, q0h + TQh_e - 1 + ch);
+    int jw_lo[NPH], jw_hi[NPH];
+#pragma unroll
+    for (int p = 0; p < NPH; ++p) {
+        jw_lo[p] = max(0, q0w + cw[p] - (P.W - 1));
+        jw_hi[p] = min(Jw[p] - 1, q0w + TQw_e - 1 + cw[p]);
+    }
+
+    // ---- per-lane position decode (B operand base offsets)
+    const int vol = TQd * TQh * TQw;
+    const int plane = TQh * TQw;
+    int lane_off[PBW];
+    int pos_t[PBW][3];
+    bool pos_ok[PBW];
+#pragma unroll
+    for (int pb = 0; pb < PBW; ++pb) {
+        const int pidx = (wpos * PBW + pb) * 32 + col;
+        pos_ok[pb] = pidx < vol;
+        const int pi = pos_ok[pb] ? pidx : 0;
+        const int td = pi / plane;
+        const int rem = pi - td * plane;
+        const int th = rem / TQw;
+        const int tw = rem - th * TQw;
+        pos_t[pb][0] = td;
+        pos_t[pb][1] = th;
+        pos_t[pb][2] = tw;
+        lane_off[pb] = (td * HH + th) * HWp + tw + half * CISTR;
+    }
+
+    const int CO_T = P.WCO * CBW;                   // co blocks per workgroup
+    const int cb0 = co_tile * CO_T + wco * CBW;     // first co block of this wave
+
+    v16f acc[NPH][CBW][PBW];
+#pragma unroll
+    for (int p = 0; p < NPH; ++p)
+#pragma unroll
+        for (int c = 0; c < CBW; ++c)
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[p][c][pb][r] = 0.0f;
+
+    bool work = any_taps && jd_lo <= jd_hi && jh_lo <= jh_hi;
+    {
+        bool anyw = false;
+#pragma unroll
+        for (int p = 0; p < NPH; ++p) anyw = anyw || (Jw[p] > 0 && jw_lo[p] <= jw_hi[p]);
+        work = work && anyw;
+    }
+    if (work) {
+        const float4 *wp4 = reinterpret_cast<const float4 *>(P.wp);
+        const int G4 = P.CI_T >> 3;
+        const int nthreads = blockDim.x;
+        const size_t HWin = (size_t)P.H * P.W;
+        for (int chunk = 0; chunk < P.nchunks; ++chunk) {
+            __syncthreads();
+            // ---- stage the input halo of CI_T channels
+            {
+                const int ci0 = chunk * P.CI_T;
+                const int total = P.CI_T * HD * HH * HW;
+                const float *xn = P.x + (size_t)n * P.Cin * P.D * HWin;
+                for (int e = tid; e < total; e += nthreads) {
+                    const int hw = e % HW;
+                    int t = e / HW;
+                    const int hh = t % HH;
+                    t /= HH;
+                    const int hd = t % HD;
+                    const int cl = t / HD;
+                    const int ci = ci0 + cl;
+                    const int id = lo_d + hd, ih = lo_h + hh, iw = lo_w + hw;
+                    float v = 0.0f;
+                    if (ci < P.Cin && (unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H &&
+                        (unsigned)iw < (unsigned)P.W)
+                        v = xn[((size_t)ci * P.D + id) * HWin + (size_t)ih * P.W + iw];
+                    lds[cl * CISTR + (hd * HH + hh) * HWp + hw] = v;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < NPH; ++p) {
+                if (Jw[p] == 0 || jw_lo[p] > jw_hi[p]) continue;
+                const int ph = (rho_d * s + rho_h) * s + rw[p];
+                const int ntp = P.ntaps[ph];
+                const int jwl = jw_lo[p], jwh = jw_hi[p], jwn = Jw[p], cwp = cw[p];
+                const float4 *wb[CBW];
+#pragma unroll
+                for (int c = 0; c < CBW; ++c) {
+                    const int cb = min(cb0 + c, P.cb_total - 1);
+                    wb[c] = wp4 + (P.wp_off[ph] >> 2) + (size_t)cb * P.steps4[ph] * 64 + lane;
+                }
+                const int n_it = (jd_hi - jd_lo + 1) * (jh_hi - jh_lo + 1) * (jwh - jwl + 1) * G4;
+                int jd = jd_lo, jh = jh_lo, jw = jwl, g4 = 0;
+                float4 a_cur[CBW];
+                int b_cur;
+                {
+                    const int gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
+#pragma unroll
+                    for (int c = 0; c < CBW; ++c) a_cur[c] = wb[c][gi];
+                    b_cur = (Jd - 1 - jd) * ROW + (Jh - 1 - jh) * HWp + (cwp - jw - lo_w_rel) + 8 * g4 * CISTR;
+                    if (++g4 == G4) { g4 = 0; if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } } }
+                }
+                for (int it = 0; it < n_it; ++it) {
+                    float4 a_nxt[CBW];
+                    int b_nxt = 0;
+                    if (it + 1 < n_it) {
+                        const int gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
+#pragma unroll
+                        for (int c = 0; c < CBW; ++c) a_nxt[c] = wb[c][gi];
+                        b_nxt = (Jd - 1 - jd) * ROW + (Jh - 1 - jh) * HWp + (cwp - jw - lo_w_rel) + 8 * g4 * CISTR;
+                        if (++g4 == G4) { g4 = 0; if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } } }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float b[PBW];
+#pragma unroll
+                        for (int pb = 0; pb < PBW; ++pb) b[pb] = lds[lane_off[pb] + b_cur + 2 * e * CISTR];
+#pragma unroll
+                        for (int c = 0; c < CBW; ++c) {
+                            const float a = a_cur[c][e];
+#pragma unroll
+                            for (int pb = 0; pb < PBW; ++pb) acc[p][c][pb] = mfma32x32x2(a, b[pb], acc[p][c][pb]);
+                        }
+                    }
+#pragma unroll
+                    for (int c = 0; c < CBW; ++c) a_cur[c] = a_nxt[c];
+                    b_cur = b_nxt;
+                }
+            }
+        }
+    }
+
+    // ------------------------------------------------------------------ epilogue
+    const int Do = P.Do, Ho = P.Ho, Wo = P.Wo;
+    const size_t S = (size_t)Do * Ho * Wo;
+    int sp[NPH][PBW];
+    bool ok[NPH][PBW];
+#pragma unroll
+    for (int pb = 0; pb < PBW; ++pb) {
+        const int od = s * (q0d + pos_t[pb][0]) + rho_d;
+        const int oh = s * (q0h + pos_t[pb][1]) + rho_h;
+#pragma unroll
+        for (int p = 0; p < NPH; ++p) {
+            const int ow = s * (q0w + pos_t[pb][2]) + rw[p];
+            ok[p][pb] = pos_ok[pb] && od < Do && oh < Ho && ow < Wo;
+            sp[p][pb] = (od * Ho + oh) * Wo + ow;
+        }
+    }
+    const int Cout = P.Cout;
+    const float *bias = P.bias;
+    float *outn = P.out + (size_t)n * Cout * S;
+
+    if (P.epi == CONVT3D_EPI_SOFTMAX_SIGMOID) {
+        // The wave holds every channel of its columns (planner: WCO == 1 and
+        // CBW*32 >= Cout); lane l and lane l^32 hold complementary halves.
+        float bv[CBW][16];
+#pragma unroll
+        for (int c = 0; c < CBW; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                bv[c][r] = (co < Cout) ? (bias ? bias[co] : 0.0f) : -INFINITY;
+            }
+#pragma unroll
+        for (int p = 0; p < NPH; ++p)
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int c = 0; c < CBW; ++c)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = acc[p][c][pb][r] + bv[c][r];  // -inf for padding rows
+                        acc[p][c][pb][r] = v;
+                        m = fmaxf(m, v);
+                    }
+                m = fmaxf(m, __shfl_xor(m, 32));
+                float sum = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CBW; ++c)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float e = __expf(acc[p][c][pb][r] - m);  // 0 for padding rows
+                        acc[p][c][pb][r] = e;
+                        sum += e;
+                    }
+                sum += __shfl_xor(sum, 32);
+                const float inv = 1.0f / sum;
+                if (ok[p][pb]) {
+#pragma unroll
+                    for (int c = 0; c < CBW; ++c)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                            if (co < Cout) {
+                                const float pr = acc[p][c][pb][r] * inv;
+                                outn[(size_t)co * S + sp[p][pb]] = 1.0f / (1.0f + __expf(-pr));
+                            }
+                        }
+                }
+            }
+        return;
+    }
+
+    const bool gn = P.epi == CONVT3D_EPI_RELU_GROUPNORM;
+    const bool bn = P.epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
+    const float scale = P.scale;
+    float s1[CBW][16], s2[CBW][16];
+#pragma unroll
+    for (int c = 0; c < CBW; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool cok = co < Cout;
+            const float bco = (cok && bias) ? bias[co] : 0.0f;
+            float a1 = 0.0f, a2 = 0.0f;
+#pragma unroll
+            for (int p = 0; p < NPH; ++p)
+#pragma unroll
+                for (int pb = 0; pb < PBW; ++pb) {
+                    float v = acc[p][c][pb][r] + bco;
+                    if (gn) v = fmaxf(v, 0.0f);
+                    if (bn) v = scale * v;
+                    if (cok && ok[p][pb]) {
+                        if (!bn) outn[(size_t)co * S + sp[p][pb]] = v;
+                        a1 += v;
+                        a2 += v * v;
+                    }
+                }
+            s1[c][r] = a1;
+            s2[c][r] = a2;
+        }
+    if (!(gn || bn)) return;
+
+    // ---- per-channel sums over the tile: 32 columns of each half, then waves
+#pragma unroll
+    for (int c = 0; c < CBW; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) {
+                s1[c][r] += __shfl_xor(s1[c][r], off);
+                s2[c][r] += __shfl_xor(s2[c][r], off);
+            }
+        }
+    __syncthreads();  // every wave is done with the halo LDS
+    float *red = lds;  // [WPOS][CO_T*32][2]
+    const int CO32 = CO_T * 32;
+    if (col == 0) {
+#pragma unroll
+        for (int c = 0; c < CBW; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = (wco * CBW + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                red[(wpos * CO32 + row) * 2 + 0] = s1[c][r];
+                red[(wpos * CO32 + row) * 2 + 1] = s2[c][r];
+            }
+    }
+    __syncthreads();
+    const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * (P.ntd * P.nth * P.ntw) + (int)blockIdx.x;
+    for (int row = tid; row < CO32; row += blockDim.x) {
+        const int co = co_tile * CO32 + row;
+        if (co >= Cout) continue;
+        float t1 = 0.0f, t2 = 0.0f;
+        for (int w = 0; w < P.WPOS; ++w) {
+            t1 += red[(w * CO32 + row) * 2 + 0];
+            t2 += red[(w * CO32 + row) * 2 + 1];
+        }
+        float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * Cout + co) * 2;
+        pp[0] = t1;
+        pp[1] = t2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GroupNorm statistics: one workgroup per (n, group); fp64 sums of the fp32
+// tile partials in a fixed order, then mean, biased variance E[r^2] - mean^2,
+// rstd = 1/sqrt(var + eps), and per channel a = gamma*rstd, b = beta - mean*a.
+__global__ __launch_bounds__(256) void gn_finalize_kernel(const float *partials, int tiles_per_n, int C,
+                                                          int G, float eps, const float *gamma,
+                                                          const float *beta, float *ab, float *stats_out,
+                                                          double count) {
+    const int n = blockIdx.x / G, g = blockIdx.x % G;
+    const int cpg = C / G;
+    const int items = tiles_per_n * cpg;
+    double a1 = 0.0, a2 = 0.0;
+    for (int i = threadIdx.x; i < items; i += blockDim.x) {
+        const int t = i / cpg, cc = i - t * cpg;
+        const float *pp = partials + (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2;
+        a1 += (double)pp[0];
+        a2 += (double)pp[1];
+    }
+    __shared__ double r1[256], r2[256];
+    __shared__ double mean_s, rstd_s;
+    r1[threadIdx.x] = a1;
+    r2[threadIdx.x] = a2;
+    __syncthreads();
+    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) {
+            r1[threadIdx.x] += r1[threadIdx.x + off];
+            r2[threadIdx.x] += r2[threadIdx.x + off];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double mean = r1[0] / count;
+        double var = r2[0] / count - mean * mean;
+        if (var < 0.0) var = 0.0;
+        mean_s = mean;
+        rstd_s = 1.0 / sqrt(var + (double)eps);
+        if (stats_out) {
+            stats_out[((size_t)n * G + g) * 2 + 0] = (float)mean;
+            stats_out[((size_t)n * G + g) * 2 + 1] = (float)rstd_s;
+        }
+    }
+    __syncthreads();
+    for (int cc = threadIdx.x; cc < cpg; cc += blockDim.x) {
+        const int c = g * cpg + cc;
+        const double ga = gamma ? (double)gamma[c] : 1.0;
+        const double be = beta ? (double)beta[c] : 0.0;
+        const double a = ga * rstd_s;
+        ab[((size_t)n * C + c) * 2 + 0] = (float)a;
+        ab[((size_t)n * C + c) * 2 + 1] = (float)(be - mean_s * a);
+    }
+}
+
+// out = a[row] * out + b[row] for rows of S elements (S % 4 == 0: float4 path).
+__global__ __launch_bounds__(256) void normalize4_kernel(float4 *out, const float2 *ab, int n4, int S4) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
+        const float2 p = ab[i / S4];
+        float4 v = out[i];
+        v.x = fmaf(p.x, v.x, p.y);
+        v.y = fmaf(p.x, v.y, p.y);
+        v.z = fmaf(p.x, v.z, p.y);
+        v.w = fmaf(p.x, v.w, p.y);
+        out[i] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void normalize1_kernel(float *out, const float2 *ab, int n1, int S) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n1; i += gridDim.x * blockDim.x) {
+        const float2 p = ab[i / S];
+        out[i] = fmaf(p.x, out[i], p.y);
+    }
+}
+
+// BatchNorm (training) + average pool: one workgroup per channel.
+__global__ __launch_bounds__(256) void bn_finalize_kernel(const float *partials, int N, int tiles_per_n, int C,
+                                                          double S, float eps, const float *gamma,
+                                                          const float *beta, float *out, float *stats_out) {
+    const int c = blockIdx.x;
+    double a1 = 0.0, a2 = 0.0;
+    const int items = N * tiles_per_n;
+    for (int i = threadIdx.x; i < items; i += blockDim.x) {
+        const float *pp = partials + ((size_t)i * C + c) * 2;  // i = n*tiles_per_n + t
+        a1 += (double)pp[0];
+        a2 += (double)pp[1];
+    }
+    __shared__ double r1[256], r2[256];
+    __shared__ double mean_s, rstd_s;
+    r1[threadIdx.x] = a1;
+    r2[threadIdx.x] = a2;
+    __syncthreads();
+    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) {
+            r1[threadIdx.x] += r1[threadIdx.x + off];
+            r2[threadIdx.x] += r2[threadIdx.x + off];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double cnt = (double)N * S;
+        const double mean = r1[0] / cnt;
+        double var = r2[0] / cnt - mean * mean;
+        if (var < 0.0) var = 0.0;
+        mean_s = mean;
+        rstd_s = 1.0 / sqrt(var + (double)eps);
+        if (stats_out) {
+            stats_out[(size_t)c * 2 + 0] = (float)mean;
+            stats_out[(size_t)c * 2 + 1] = (float)var;
+        }
+    }
+    __syncthreads();
+    const double ga = gamma ? (double)gamma[c] : 1.0;
+    const double be = beta ? (double)beta[c] : 0.0;
+    for (int n = threadIdx.x; n < N; n += blockDim.x) {
+        double m = 0.0;
+        for (int t = 0; t < tiles_per_n; ++t) m += (double)partials[(((size_t)n * tiles_per_n + t) * C + c) * 2];
+        m /= S;
+        out[(size_t)n * C + c] = (float)((m - mean_s) * rstd_s * ga + be);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+static int grid_for(int64_t items, int per_block, int cap) {
+    int64_t g = (items + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream) {
+    PackParams P{};
+    P.w = w;
+    P.wp = wp;
+    P.Cin = pl.g.cin;
+    P.Cout = pl.g.cout;
+    P.k = pl.g.k;
+    P.s = pl.s;
+    P.cb_total = pl.cb_total;
+    P.nph = pl.s * pl.s * pl.s;
+    for (int d = 0; d < 3; ++d)
+        for (int r = 0; r < kMaxStride; ++r) {
+            P.pr[d][r] = pl.ph[d][r].r;
+            P.pJ[d][r] = pl.ph[d][r].J;
+        }
+    for (int q = 0; q < kMaxPhases; ++q) {
+        P.ntaps[q] = pl.ntaps[q];
+        P.steps4[q] = pl.steps4[q];
+        P.wp_off[q] = (int)pl.wp_off[q];
+    }
+    P.total4 = (int)(pl.packed_floats / 4);
+    if (P.total4 == 0) return (int)hipSuccess;
+    hipLaunchKernelGGL(prepack_kernel, dim3(grid_for(P.total4, 256, 65536)), dim3(256), 0,
+                       (hipStream_t)stream, P);
+    return (int)hipGetLastError();
+}
+
+template <int CBW, int NPH, int PBW>
+static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
+    auto fn = convt3d_mfma_kernel<CBW, NPH, PBW>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxLdsBytes);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)pl.grid_x, (unsigned)pl.grid_y, (unsigned)pl.grid_z),
+                       dim3(kBlockThreads), pl.lds_bytes, (hipStream_t)stream, cp);
+    return (int)hipGetLastError();
+}
+
+int launch_conv(const Plan &pl, const ConvParams &cp, void *stream) {
+    const Variant v = kVariants[pl.variant];
+#define CONVT3D_VARIANT(a, b, c) \
+    if (v.CBW == a && v.NPH == b && v.PBW == c) return launch_conv_t<a, b, c>(pl, cp, stream);
+    CONVT3D_VARIANT(1, 1, 8)
+    CONVT3D_VARIANT(1, 1, 4)
+    CONVT3D_VARIANT(1, 1, 2)
+    CONVT3D_VARIANT(1, 2, 4)
+    CONVT3D_VARIANT(1, 2, 2)
+    CONVT3D_VARIANT(2, 1, 4)
+    CONVT3D_VARIANT(2, 2, 2)
+    CONVT3D_VARIANT(4, 1, 2)
+    CONVT3D_VARIANT(4, 2, 1)
+#undef CONVT3D_VARIANT
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_gn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta, float *ab,
+                       float *stats_out, void *stream) {
+    const int G = pl.e.groups;
+    const double count = (double)(pl.g.cout / G) * (double)pl.S;
+    hipLaunchKernelGGL(gn_finalize_kernel, dim3(pl.g.n * G), dim3(256), 0, (hipStream_t)stream, partials,
+                       (int)pl.tiles_per_n, pl.g.cout, G, pl.e.eps, gamma, beta, ab, stats_out, count);
+    return (int)hipGetLastError();
+}
+
+int launch_normalize(const Plan &pl, float *out, const float *ab, void *stream) {
+    const int64_t total = (int64_t)pl.g.n * pl.g.cout * pl.S;
+    if (pl.S % 4 == 0) {
+        const int n4 = (int)(total / 4);
+        hipLaunchKernelGGL(normalize4_kernel, dim3(grid_for(n4, 256, 256 * 64)), dim3(256), 0,
+                           (hipStream_t)stream, reinterpret_cast<float4 *>(out),
+                           reinterpret_cast<const float2 *>(ab), n4, (int)(pl.S / 4));
+    } else {
+        hipLaunchKernelGGL(normalize1_kernel, dim3(grid_for(total, 256, 256 * 64)), dim3(256), 0,
+                           (hipStream_t)stream, out, reinterpret_cast<const float2 *>(ab), (int)total,
+                           (int)pl.S);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_bn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta, float *out,
+                       float *stats_out, void *stream) {
+    hipLaunchKernelGGL(bn_finalize_kernel, dim3(pl.g.cout), dim3(256), 0, (hipStream_t)stream, partials, pl.g.n,
+                       (int)pl.tiles_per_n, pl.g.cout, (double)pl.S, pl.e.eps, gamma, beta, out, stats_out);
+    return (int)hipGetLastError();
+}
+
+}  // namespace convt3d

@@ -1,0 +1,151 @@
+/*
+ * convt3d.h -- C ABI of libconvt3d: ConvTranspose3d (NCDHW, fp32) fused with
+ * its epilogue, on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the three pages work on:
+ *   y[n, co, o] = bias[co] + sum_ci sum_taps x[n, ci, i] * w[ci, co, tap]
+ * over every (input voxel i, kernel tap) pair with o = stride*i - pad + tap in
+ * each spatial dimension (p49 page, its scatter statement of the transposed
+ * convolution; p77 page and p49 page, the output size
+ * (in - 1)*stride - 2*pad + k + out_pad), followed by one epilogue:
+ *   - ReLU then GroupNorm (p61 page's statement of GroupNorm: per (n, group)
+ *     mean and biased variance over channels of the group and all voxels, eps
+ *     inside the square root, per-channel gamma/beta);
+ *   - softmax over the channel dimension then sigmoid (p49 page: max-subtracted
+ *     softmax, then 1/(1+exp(-v)));
+ *   - multiply by `scale`, training-mode BatchNorm3d with batch statistics
+ *     over (N, D, H, W) and the biased variance, then AdaptiveAvgPool3d(1)
+ *     (p77 page); only the pooled [n, cout] result is produced.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are caller-owned, contiguous, fp32, in DEVICE memory of the
+ *     current HIP device, 16-byte aligned.  The library never allocates or
+ *     frees device memory and never synchronises the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every kernel is enqueued on it; results are ready in stream order.
+ *   - A nonzero return is an error code (see convt3d_status_string); errors
+ *     found from the arguments are returned before anything is launched and
+ *     leave every output untouched.
+ *   - Calls that share a workspace on overlapping streams race; give each
+ *     concurrent call its own workspace.
+ */
+#ifndef CONVT3D_H
+#define CONVT3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Geometry.  Input x is [n, cin, d, h, w]; weight is [cin, cout, k, k, k] (the
+ * layout nn.ConvTranspose3d stores); cubic kernel, same stride / pad /
+ * out_pad in all three dims, dilation 1, groups 1.  Limits: n >= 0 (n == 0 is
+ * an empty batch: nothing is launched), every other size >= 1, 1 <= stride
+ * <= 4, 0 <= pad, 0 <= out_pad < stride, and each output dim >= 1. */
+typedef struct convt3d_geom {
+    int32_t n, cin, cout, d, h, w;
+    int32_t k, stride, pad, out_pad;
+} convt3d_geom;
+
+enum convt3d_epi_kind {
+    CONVT3D_EPI_NONE = 0,                    /* out = y                                   */
+    CONVT3D_EPI_RELU_GROUPNORM = 1,          /* out = GroupNorm(ReLU(y))                  */
+    CONVT3D_EPI_SOFTMAX_SIGMOID = 2,         /* out = sigmoid(softmax_channels(y))        */
+    CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL = 3   /* out[n,c] = mean_dhw BN_train(scale * y)   */
+};
+
+/* Epilogue description.
+ *   kind      one of convt3d_epi_kind.
+ *   groups    GroupNorm groups (cout % groups == 0); ignored otherwise.
+ *   eps       GroupNorm / BatchNorm epsilon (added to the variance).
+ *   scale     multiplier applied before BatchNorm; ignored otherwise.
+ *   gamma     [cout] device, per-channel scale for GN/BN; NULL means 1.
+ *   beta      [cout] device, per-channel shift for GN/BN; NULL means 0.
+ *   stats_out optional device output, NULL to skip:
+ *               GroupNorm: [n, groups, 2] = (mean, 1/sqrt(var + eps)) of ReLU(y);
+ *               BatchNorm: [cout, 2]      = (batch mean, biased batch variance)
+ *                                           of scale*y;
+ *               others: ignored. */
+typedef struct convt3d_epilogue {
+    int32_t kind;
+    int32_t groups;
+    float eps;
+    float scale;
+    const float *gamma;
+    const float *beta;
+    float *stats_out;
+} convt3d_epilogue;
+
+enum convt3d_status {
+    CONVT3D_OK = 0,
+    CONVT3D_ERR_NULL = 1,          /* a required pointer is NULL                      */
+    CONVT3D_ERR_GEOMETRY = 2,      /* a size out of range or an empty output          */
+    CONVT3D_ERR_GROUPS = 3,        /* GroupNorm groups < 1 or cout % groups != 0      */
+    CONVT3D_ERR_ALIGNMENT = 4,     /* a tensor pointer is not 16-byte aligned         */
+    CONVT3D_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required         */
+    CONVT3D_ERR_UNSUPPORTED = 6,   /* epilogue kind unknown, or softmax with cout>128 */
+    CONVT3D_ERR_LAUNCH = 7,        /* HIP reported an error when launching            */
+    CONVT3D_ERR_TOO_LARGE = 8,     /* a tensor exceeds 2^31 elements                  */
+    CONVT3D_ERR_ALIAS = 9          /* out overlaps x                                  */
+};
+
+/* Human-readable text for a status code (static storage). */
+const char *convt3d_status_string(int status);
+
+/* Output spatial size (Do, Ho, Wo) of the geometry.  Returns a status. */
+int convt3d_output_dims(const convt3d_geom *geom, int32_t out_dhw[3]);
+
+/* Number of fp32 elements `out` must hold: n*cout*Do*Ho*Wo for NONE / GN /
+ * softmax, n*cout for the pooled BatchNorm epilogue; -1 on invalid input. */
+int64_t convt3d_output_elems(const convt3d_geom *geom, const convt3d_epilogue *epi);
+
+/* Bytes of the pre-packed weight buffer for this geometry (0 on invalid input). */
+size_t convt3d_packed_weight_bytes(const convt3d_geom *geom);
+
+/* Re-lay the nn.ConvTranspose3d weight w [cin, cout, k, k, k] (device) into the
+ * per-stride-phase, matrix-core operand order the convolution kernel reads
+ * (w_packed, device, convt3d_packed_weight_bytes bytes).  Enqueued on stream;
+ * w_packed depends only on the geometry's cin, cout, k, stride and pad. */
+int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_packed,
+                            void *stream);
+
+/* Bytes of device workspace convt3d_fused needs for (geom, epi) (statistics
+ * partials and per-channel scale/shift).  May be 0 (then workspace may be NULL). */
+size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *epi);
+
+/* The fused forward pass.
+ *   x          [n, cin, d, h, w] device input.
+ *   w_packed   output of convt3d_prepack_weights for this geometry.
+ *   bias       [cout] device, or NULL for no bias.
+ *   out        device output, convt3d_output_elems(geom, epi) floats; must not
+ *              overlap x.  For GroupNorm it is also used as the staging buffer
+ *              of ReLU(y) before normalisation in place.
+ *   workspace  device scratch of at least convt3d_workspace_size bytes.
+ * Enqueues 1 to 3 kernels on stream and returns without waiting. */
+int convt3d_fused(const float *x, const void *w_packed, const float *bias,
+                  const convt3d_geom *geom, const convt3d_epilogue *epi, float *out,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Planner's choices for (geom, epi), for reporting and tests. */
+typedef struct convt3d_plan_info {
+    int32_t variant;           /* kernel variant id                                   */
+    int32_t co_blocks_per_wave, pos_blocks_per_wave, w_phases_per_wave;
+    int32_t waves_co, waves_pos; /* wave grid of one workgroup                       */
+    int32_t tile_q[3];         /* box of stride-phase positions per workgroup (d,h,w) */
+    int32_t ci_chunk;          /* input channels staged in LDS per step               */
+    int32_t lds_bytes;         /* dynamic LDS per workgroup                           */
+    int64_t workgroups;        /* conv kernel grid size                               */
+    int64_t issued_macs;       /* multiply-adds the matrix cores execute (incl. padding) */
+    int64_t valid_macs;        /* multiply-adds whose input voxel is in range          */
+} convt3d_plan_info;
+
+int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
+                          convt3d_plan_info *info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVT3D_H */

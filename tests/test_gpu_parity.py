@@ -1,0 +1,98 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64 CPU
+oracle on the same seeded inputs, max |err| <= 1e-4 on every output."""
+import numpy as np
+import pytest
+
+import oracle
+from activation_epilogues_amd import workloads as W
+
+from gpu_helpers import TOL, max_err, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [W.EPI_NONE, W.EPI_RELU_GROUPNORM, W.EPI_SOFTMAX_SIGMOID, W.EPI_SCALE_BN_TRAIN_AVGPOOL]
+
+
+def oracle_for(wl, inp, kind):
+    return oracle.run_workload(wl.with_(epi=kind), inp)
+
+
+def check(wl, kind, inp=None, tag=""):
+    inp = W.make_inputs(wl.with_(epi=kind)) if inp is None else inp
+    say(f"[case] {tag} {wl.name} kind={kind} n={wl.n} cin={wl.cin} cout={wl.cout} "
+        f"in={wl.d}x{wl.h}x{wl.w} k={wl.k} s={wl.stride} p={wl.pad} op={wl.out_pad} "
+        f"groups={wl.groups} seed={wl.seed}")
+    out, st, call = run_gpu(wl.with_(epi=kind), inp, kind)
+    ref = oracle_for(wl, inp, kind)
+    want = ref.out.reshape(out.shape)
+    err = max_err(out, want)
+    assert np.isfinite(out).all()
+    assert err <= TOL, f"max|err| {err:.3e}"
+    if kind == W.EPI_RELU_GROUPNORM:
+        np.testing.assert_allclose(st[..., 0], ref.stats[..., 0], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(st[..., 1], ref.stats[..., 1], rtol=1e-5, atol=1e-6)
+    if kind == W.EPI_SCALE_BN_TRAIN_AVGPOOL:
+        np.testing.assert_allclose(st[:, 0], ref.stats[:, 0], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(st[:, 1], ref.stats[:, 1], rtol=1e-5, atol=1e-6)
+    return out, ref, call
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_tiny_workload_every_epilogue(kind):
+    wl = W.BY_NAME["tiny_gn"]
+    check(wl, kind, tag="tiny")
+
+
+def sweep(seed, count, epi):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        wl = W.random_geometry(rng, max_in=9, max_ch=40, epi=epi)
+        if min(oracle.out_dims(wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)) <= 0:
+            continue
+        if epi == W.EPI_SOFTMAX_SIGMOID and wl.cout > 128:
+            continue
+        out.append(wl.with_(name=f"rand{len(out)}"))
+    return out
+
+
+@pytest.mark.parametrize("wl", sweep(2024, 24, W.EPI_NONE), ids=lambda w: w.name)
+def test_random_geometry_raw_conv(wl):
+    check(wl, W.EPI_NONE, tag="sweep")
+
+
+@pytest.mark.parametrize("wl", sweep(77, 8, W.EPI_RELU_GROUPNORM), ids=lambda w: w.name)
+def test_random_geometry_groupnorm(wl):
+    check(wl, W.EPI_RELU_GROUPNORM, tag="sweep-gn")
+
+
+@pytest.mark.parametrize("wl", sweep(78, 8, W.EPI_SOFTMAX_SIGMOID), ids=lambda w: w.name)
+def test_random_geometry_softmax(wl):
+    check(wl, W.EPI_SOFTMAX_SIGMOID, tag="sweep-sm")
+
+
+@pytest.mark.parametrize("wl", sweep(79, 8, W.EPI_SCALE_BN_TRAIN_AVGPOOL), ids=lambda w: w.name)
+def test_random_geometry_bnpool(wl):
+    check(wl, W.EPI_SCALE_BN_TRAIN_AVGPOOL, tag="sweep-bn")
+
+
+# the five workloads at reduced batch: every tile shape, ragged tails and the
+# full channel / kernel sizes, with an oracle that finishes in seconds
+REDUCED = {"tiny_gn": 2, "k3s1_gn": 1, "k3s2_softmax": 1, "k5s1_bnpool": 2, "k4s2_gn": 1}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_workload_reduced_batch_final_and_raw(name):
+    wl = W.BY_NAME[name].with_(n=REDUCED[name])
+    inp = W.make_inputs(wl)
+    check(wl, wl.epi, inp, tag="reduced")
+    check(wl, W.EPI_NONE, inp, tag="reduced-raw")
+
+
+def test_run_twice_is_bitwise_identical():
+    wl = W.BY_NAME["k3s1_gn"].with_(n=1, d=12, h=10, w=9)
+    inp = W.make_inputs(wl)
+    say("[case] determinism k3s1_gn n=1 12x10x9")
+    a, sa, _ = run_gpu(wl, inp)
+    b, sb, _ = run_gpu(wl, inp)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
