@@ -45,6 +45,11 @@ class PlanInfo(ctypes.Structure):
                 ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64)]
 
 
+class Profile(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int32), ("conv_ms", ctypes.c_double), ("finalize_ms", ctypes.c_double),
+                ("normalize_ms", ctypes.c_double)]
+
+
 class Convt3dError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -80,13 +85,17 @@ def lib():
         L.convt3d_fused.argtypes = [vp, vp, vp, P(Geom), P(Epilogue), vp, vp, sz, vp]
         L.convt3d_get_plan_info.restype = ctypes.c_int
         L.convt3d_get_plan_info.argtypes = [P(Geom), P(Epilogue), P(PlanInfo)]
+        L.convt3d_profile_begin.restype = ctypes.c_int
+        L.convt3d_profile_begin.argtypes = []
+        L.convt3d_profile_end.restype = ctypes.c_int
+        L.convt3d_profile_end.argtypes = [P(Profile)]
         _lib = L
     return _lib
 
 
 EXPORTED = ["convt3d_status_string", "convt3d_output_dims", "convt3d_output_elems",
             "convt3d_packed_weight_bytes", "convt3d_prepack_weights", "convt3d_workspace_size",
-            "convt3d_fused", "convt3d_get_plan_info"]
+            "convt3d_fused", "convt3d_get_plan_info", "convt3d_profile_begin", "convt3d_profile_end"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -167,6 +176,20 @@ def convt3d_get_plan_info(geom: Geom, epi: Epilogue) -> dict:
     d = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
     d["tile_q"] = tuple(info.tile_q)
     return d
+
+
+def convt3d_profile_begin() -> None:
+    st = lib().convt3d_profile_begin()
+    if st:
+        raise Convt3dError(st, "convt3d_profile_begin")
+
+
+def convt3d_profile_end() -> dict:
+    p = Profile()
+    st = lib().convt3d_profile_end(ctypes.byref(p))
+    if st:
+        raise Convt3dError(st, "convt3d_profile_end")
+    return {f: getattr(p, f) for f, _ in Profile._fields_}
 
 
 # ----------------------------------------------------------------------------

@@ -6,6 +6,7 @@
 #include <cstring>
 #include <list>
 #include <mutex>
+#include <vector>
 
 #include "convt3d_internal.hpp"
 
@@ -55,6 +56,48 @@ int cached_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *out) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- optional per-kernel timing with HIP events (measurement only)
+struct Timed {
+    int kind;  // 0 conv, 1 finalize, 2 normalize
+    hipEvent_t beg, end;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+int g_prof_calls = 0;
+std::vector<Timed> g_prof_used;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch `fn` bracketed by events when profiling is on.
+template <class F>
+int timed(int kind, void *stream, F fn) {
+    hipEvent_t b = nullptr, e = nullptr;
+    bool on;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        on = g_prof_on;
+        if (on) { b = prof_event(); e = prof_event(); }
+    }
+    if (on && b && e) hipEventRecord(b, (hipStream_t)stream);
+    const int rc = fn();
+    if (on && b && e) {
+        hipEventRecord(e, (hipStream_t)stream);
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_prof_used.push_back(Timed{kind, b, e});
+    }
+    return rc;
+}
 
 }  // namespace
 
@@ -168,19 +211,63 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias, const
     cp.bias = bias;
     cp.out = out;
     cp.partials = partials;
-    if (launch_conv(pl, cp, stream) != (int)hipSuccess) return CONVT3D_ERR_LAUNCH;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (g_prof_on) ++g_prof_calls;
+    }
+    if (timed(0, stream, [&] { return launch_conv(pl, cp, stream); }) != (int)hipSuccess)
+        return CONVT3D_ERR_LAUNCH;
 
     if (epi->kind == CONVT3D_EPI_RELU_GROUPNORM) {
         float *ab = reinterpret_cast<float *>(ws + pl.ws_ab);
-        if (launch_gn_finalize(pl, partials, epi->gamma, epi->beta, ab, epi->stats_out, stream) != (int)hipSuccess)
+        if (timed(1, stream, [&] {
+                return launch_gn_finalize(pl, partials, epi->gamma, epi->beta, ab, epi->stats_out, stream);
+            }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
-        if (launch_normalize(pl, out, ab, stream) != (int)hipSuccess) return CONVT3D_ERR_LAUNCH;
+        if (timed(2, stream, [&] { return launch_normalize(pl, out, ab, stream); }) != (int)hipSuccess)
+            return CONVT3D_ERR_LAUNCH;
     } else if (epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) {
-        if (launch_bn_finalize(pl, partials, epi->gamma, epi->beta, out, epi->stats_out, stream) !=
-            (int)hipSuccess)
+        if (timed(1, stream, [&] {
+                return launch_bn_finalize(pl, partials, epi->gamma, epi->beta, out, epi->stats_out, stream);
+            }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
     }
     return CONVT3D_OK;
+}
+
+int convt3d_profile_begin(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto &t : g_prof_used) {
+        g_prof_pool.push_back(t.beg);
+        g_prof_pool.push_back(t.end);
+    }
+    g_prof_used.clear();
+    g_prof_calls = 0;
+    g_prof_on = true;
+    return CONVT3D_OK;
+}
+
+int convt3d_profile_end(convt3d_profile *out) {
+    if (!out) return CONVT3D_ERR_NULL;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = false;
+    std::memset(out, 0, sizeof(*out));
+    out->calls = g_prof_calls;
+    int status = CONVT3D_OK;
+    for (auto &t : g_prof_used) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(t.end) != hipSuccess || hipEventElapsedTime(&ms, t.beg, t.end) != hipSuccess) {
+            status = CONVT3D_ERR_LAUNCH;
+            continue;
+        }
+        if (t.kind == 0) out->conv_ms += ms;
+        else if (t.kind == 1) out->finalize_ms += ms;
+        else out->normalize_ms += ms;
+        g_prof_pool.push_back(t.beg);
+        g_prof_pool.push_back(t.end);
+    }
+    g_prof_used.clear();
+    return status;
 }
 
 }  // extern "C"

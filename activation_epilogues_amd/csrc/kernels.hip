@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // the input halo of the box for those channels is staged in LDS, then every
 // live tap of every phase runs 4 MFMA k-steps per 8 input channels.
 template <int CBW, int NPH, int PBW>
-__global__ __launch_bounds__(kBlockThreads) void convt3d_mfma_kernel(const ConvParams P) {
+__global__ __launch_bounds__(kBlockThreads, (CBW * NPH * PBW <= 8) ? 2 : 1) void convt3d_mfma_kernel(const ConvParams P) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -245,41 +245,64 @@ __global__ __launch_bounds__(kBlockThreads) void convt3d_mfma_kernel(const ConvP
                     wb[c] = wp4 + (P.wp_off[ph] >> 2) + (size_t)cb * P.steps4[ph] * 64 + lane;
                 }
                 const int n_it = (jd_hi - jd_lo + 1) * (jh_hi - jh_lo + 1) * (jwh - jwl + 1) * G4;
+                // Iteration state (jd, jh, jw, g4) of the next group to load; every
+                // group is 4 MFMA k-steps = 8 input channels of one tap.
                 int jd = jd_lo, jh = jh_lo, jw = jwl, g4 = 0;
-                float4 a_cur[CBW];
-                int b_cur;
-                {
-                    const int gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
-#pragma unroll
-                    for (int c = 0; c < CBW; ++c) a_cur[c] = wb[c][gi];
-                    b_cur = (Jd - 1 - jd) * ROW + (Jh - 1 - jh) * HWp + (cwp - jw - lo_w_rel) + 8 * g4 * CISTR;
-                    if (++g4 == G4) { g4 = 0; if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } } }
-                }
-                for (int it = 0; it < n_it; ++it) {
-                    float4 a_nxt[CBW];
-                    int b_nxt = 0;
-                    if (it + 1 < n_it) {
-                        const int gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
-#pragma unroll
-                        for (int c = 0; c < CBW; ++c) a_nxt[c] = wb[c][gi];
-                        b_nxt = (Jd - 1 - jd) * ROW + (Jh - 1 - jh) * HWp + (cwp - jw - lo_w_rel) + 8 * g4 * CISTR;
-                        if (++g4 == G4) { g4 = 0; if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } } }
+                auto next_group = [&](int &gi, int &bo) {
+                    gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
+                    bo = (Jd - 1 - jd) * ROW + (Jh - 1 - jh) * HWp + (cwp - jw - lo_w_rel) + 8 * g4 * CISTR;
+                    if (++g4 == G4) {
+                        g4 = 0;
+                        if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } }
                     }
+                };
+                // One group = 4 MFMA k-steps.  While the MFMAs of step e run, the B
+                // values of step e+1 (or of step 0 of the next group) are read from
+                // LDS into the other half of bq.
+                float bq[2][PBW];
+                auto group_mfma = [&](const float4 (&a)[CBW], int bo, int bo_next) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float b[PBW];
+                        const int ro = (e < 3) ? bo + 2 * (e + 1) * CISTR : bo_next;
 #pragma unroll
-                        for (int pb = 0; pb < PBW; ++pb) b[pb] = lds[lane_off[pb] + b_cur + 2 * e * CISTR];
+                        for (int pb = 0; pb < PBW; ++pb) bq[(e + 1) & 1][pb] = lds[lane_off[pb] + ro];
 #pragma unroll
                         for (int c = 0; c < CBW; ++c) {
-                            const float a = a_cur[c][e];
+                            const float av = a[c][e];
 #pragma unroll
-                            for (int pb = 0; pb < PBW; ++pb) acc[p][c][pb] = mfma32x32x2(a, b[pb], acc[p][c][pb]);
+                            for (int pb = 0; pb < PBW; ++pb)
+                                acc[p][c][pb] = mfma32x32x2(av, bq[e & 1][pb], acc[p][c][pb]);
+                        }
+#pragma unroll
+                        for (int pb = 0; pb < PBW; ++pb) {
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                            __builtin_amdgcn_sched_group_barrier(0x008, CBW, 0);  // CBW MFMAs
                         }
                     }
+                };
+                // Two A register sets in flight; loads are always issued (the last
+                // ones repeat a valid group) so the wait counts stay static.
+                float4 aA[CBW], aB[CBW];
+                int giA, boA, giB, boB;
+                next_group(giA, boA);
 #pragma unroll
-                    for (int c = 0; c < CBW; ++c) a_cur[c] = a_nxt[c];
-                    b_cur = b_nxt;
+                for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+#pragma unroll
+                for (int pb = 0; pb < PBW; ++pb) bq[0][pb] = lds[lane_off[pb] + boA];
+                for (int it = 0; it < n_it; it += 2) {
+                    if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
+#pragma unroll
+                    for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
+                    __builtin_amdgcn_sched_barrier(0);
+                    group_mfma(aA, boA, boB);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (it + 1 >= n_it) break;
+                    if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
+#pragma unroll
+                    for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                    __builtin_amdgcn_sched_barrier(0);
+                    group_mfma(aB, boB, boA);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }

@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused ConvTranspose3d + epilogue path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: re-lay the weights for the matrix cores
+(convt3d_prepack_weights), then convt3d_fused (convolution with the fused
+epilogue, statistics, normalisation).  The default workload is the
+[16,64,32,32,32] -> ConvTranspose3d(64->128, k3) -> ReLU -> GroupNorm(8) case.
+
+Prints ONE JSON line.  ``value`` is algorithmic GFLOP/s = 2 * (multiply-adds
+whose input voxel is in range) / time per step.  ``roofline`` describes the
+dominant kernel (the convolution kernel, FP32 MFMA bound): its duration comes
+from HIP events the library records on the launch stream over the timed
+region.  ``cpu_baseline`` times the fp64 CPU oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+METRIC = "ConvTranspose3d+epilogue GFLOP/s and ms/forward; % FP32 MFMA peak"
+KERNEL_SRC = os.path.join(ROOT, "activation_epilogues_amd", "csrc", "kernels.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per conv launch from the committed rocprofv3 --pmc summary, if it
+    was taken from the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"convt3d_mfma_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, inp, max_samples: int):
+    """The oracle (fp64, OpenMP) on the first samples of the same workload."""
+    import numpy as np
+    import oracle
+    from activation_epilogues_amd import workloads as W
+    n = min(wl.n, max_samples)
+    sub = wl.with_(n=n)
+    sub_inp = W.Inputs(x=np.ascontiguousarray(inp.x[:n]), w=inp.w, b=inp.b, gamma=inp.gamma, beta=inp.beta)
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.run_workload(sub, sub_inp)
+    dt = time.perf_counter() - t0
+    return n, dt, oracle.num_threads()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k3s1_gn")
+    ap.add_argument("--cpu-samples", type=int, default=16,
+                    help="batch samples the CPU oracle baseline runs (bounded)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from activation_epilogues_amd import convt3d as C
+    from activation_epilogues_amd import workloads as W
+
+    wl = W.BY_NAME[args.workload]
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    g = C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)
+    call = C.FusedCall(g, wl.epi, wl.groups, wl.eps, wl.scale, device=dev)
+    x = torch.from_numpy(inp.x).to(dev)
+    w = torch.from_numpy(inp.w).to(dev)
+    b = None if inp.b is None else torch.from_numpy(inp.b).to(dev)
+    gamma = None if inp.gamma is None else torch.from_numpy(inp.gamma).to(dev)
+    beta = None if inp.beta is None else torch.from_numpy(inp.beta).to(dev)
+    stream = torch.cuda.current_stream()
+    info = call.plan_info()
+    flops = 2.0 * info["valid_macs"]
+
+    def step():
+        call.prepack(w, stream)
+        call(x, b, gamma, beta, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    C.convt3d_profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = C.convt3d_profile_end()
+    ms = (t1 - t0) * 1e3 / args.steps
+    gflops = flops / (ms * 1e-3) / 1e9
+    print(f"[bench] timed region done: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    conv_ms = prof["conv_ms"] / max(1, prof["calls"])
+    conv_tflops = flops / (conv_ms * 1e-3) / 1e12
+    traffic = stored_traffic(wl.name)
+    roofline = {
+        "kernel": "convt3d_mfma_kernel",
+        "bound": "mfma",
+        "achieved": round(conv_tflops, 3),
+        "peak": PEAK_FP32_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(conv_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        "traffic": traffic,
+        "algorithmic_flop_per_launch": flops,
+        "avg_launch_ms": round(conv_ms, 4),
+    }
+    kernels = {
+        "conv_ms": round(conv_ms, 4),
+        "finalize_ms": round(prof["finalize_ms"] / max(1, prof["calls"]), 4),
+        "normalize_ms": round(prof["normalize_ms"] / max(1, prof["calls"]), 4),
+    }
+    if prof["normalize_ms"] > 0:
+        norm_bytes = 2.0 * 4 * call.out.numel()  # read + write of the output
+        kernels["normalize_GBps"] = round(norm_bytes / (kernels["normalize_ms"] * 1e-3) / 1e9, 1)
+        kernels["normalize_frac_hbm"] = round(kernels["normalize_GBps"] / PEAK_HBM_GBS, 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        n_cpu, dt, cores = cpu_baseline(wl, inp, args.cpu_samples)
+        cpu_flops = flops * n_cpu / wl.n
+        cpu = {"value": round(cpu_flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+               "sample": f"{n_cpu} of {wl.n} samples of {wl.name}, whole path (conv + epilogue), fp64",
+               "seconds": round(dt, 2)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(gflops, 2),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) input, U(+-1/sqrt(cin*k^3)) weights)",
+        "config": {"workload": wl.name, "x": list(wl.x_shape), "cout": wl.cout, "k": wl.k, "stride": wl.stride,
+                   "pad": wl.pad, "out_pad": wl.out_pad, "bias": wl.bias,
+                   "epilogue": W.EPI_NAMES[wl.epi], "groups": wl.groups, "scale": wl.scale},
+        "pct_fp32_mfma_peak_whole_step": round(100 * gflops / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
+        "roofline": roofline,
+        "kernels": kernels,
+        "plan": {k: v for k, v in info.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -144,6 +144,22 @@ typedef struct convt3d_plan_info {
 int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
                           convt3d_plan_info *info);
 
+/* Kernel timing for measurement.  Between convt3d_profile_begin() and
+ * convt3d_profile_end(), every convt3d_fused call records HIP events on its
+ * stream around each kernel it launches.  convt3d_profile_end() waits for the
+ * recorded events (it synchronises on them, so call it after the timed
+ * region), fills `out` with the summed per-kernel durations and stops
+ * recording.  Not thread-safe with respect to concurrent recording sessions. */
+typedef struct convt3d_profile {
+    int32_t calls;        /* convt3d_fused calls recorded                       */
+    double conv_ms;       /* convolution (+ fused epilogue) kernel, summed      */
+    double finalize_ms;   /* GroupNorm / BatchNorm statistics kernels, summed   */
+    double normalize_ms;  /* GroupNorm in-place normalisation kernels, summed   */
+} convt3d_profile;
+
+int convt3d_profile_begin(void);
+int convt3d_profile_end(convt3d_profile *out);
+
 #ifdef __cplusplus
 }
 #endif
