@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // the input halo of the box for those channels is staged in LDS, then every
 // live tap of every phase runs 4 MFMA k-steps per 8 input channels.
 template <int CBW, int NPH, int PBW>
-__global__ __launch_bounds__(kBlockThreads, (CBW * NPH * PBW <= 8) ? 2 : 1) void convt3d_mfma_kernel(const ConvParams P) {
+__global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1) void convt3d_mfma_kernel(const ConvParams P) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -208,20 +208,23 @@ __global__ __launch_bounds__(kBlockThreads, (CBW * NPH * PBW <= 8) ? 2 : 1) void
         const int G4 = P.CI_T >> 3;
         const int nthreads = blockDim.x;
         const size_t HWin = (size_t)P.H * P.W;
+        const float *xn = P.x + (size_t)n * P.Cin * P.D * HWin;
+        // digits of tid and of nthreads in the radix (CI_T, HD, HH, HW)
+        const int st_total = P.CI_T * HD * HH * HW;
+        const int st_hw = tid % HW, st_hh = (tid / HW) % HH, st_hd = (tid / (HW * HH)) % HD,
+                  st_cl = tid / (HW * HH * HD);
+        const int inc_hw = nthreads % HW, inc_hh = (nthreads / HW) % HH, inc_hd = (nthreads / (HW * HH)) % HD,
+                  inc_cl = nthreads / (HW * HH * HD);
         for (int chunk = 0; chunk < P.nchunks; ++chunk) {
             __syncthreads();
-            // ---- stage the input halo of CI_T channels
+            // ---- stage the input halo of CI_T channels: thread t covers flat
+            // elements t, t + nthreads, ...; the (cl, hd, hh, hw) digits advance by
+            // the mixed-radix digits of nthreads, so no division in the loop.
             {
                 const int ci0 = chunk * P.CI_T;
-                const int total = P.CI_T * HD * HH * HW;
-                const float *xn = P.x + (size_t)n * P.Cin * P.D * HWin;
-                for (int e = tid; e < total; e += nthreads) {
-                    const int hw = e % HW;
-                    int t = e / HW;
-                    const int hh = t % HH;
-                    t /= HH;
-                    const int hd = t % HD;
-                    const int cl = t / HD;
+                int hw = st_hw, hh = st_hh, hd = st_hd, cl = st_cl;
+#pragma unroll 4
+                for (int e = tid; e < st_total; e += nthreads) {
                     const int ci = ci0 + cl;
                     const int id = lo_d + hd, ih = lo_h + hh, iw = lo_w + hw;
                     float v = 0.0f;
@@ -229,6 +232,13 @@ __global__ __launch_bounds__(kBlockThreads, (CBW * NPH * PBW <= 8) ? 2 : 1) void
                         (unsigned)iw < (unsigned)P.W)
                         v = xn[((size_t)ci * P.D + id) * HWin + (size_t)ih * P.W + iw];
                     lds[cl * CISTR + (hd * HH + hh) * HWp + hw] = v;
+                    hw += inc_hw;
+                    if (hw >= HW) { hw -= HW; ++hh; }
+                    hh += inc_hh;
+                    if (hh >= HH) { hh -= HH; ++hd; }
+                    hd += inc_hd;
+                    if (hd >= HD) { hd -= HD; ++cl; }
+                    cl += inc_cl;
                 }
             }
             __syncthreads();

@@ -240,8 +240,27 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                                                (int64_t)nchunks * CI_T * taps;
                         const int64_t grid = nn * co_tiles * s * s * nwg *
                                              ntile[0] * ntile[1] * ntile[2];
-                        // per-workgroup fixed cost (staging, epilogue) ~ 64 MACs per output
-                        double cost = (double)issued + (double)grid * CO_T * 32 * PT * v.NPH * 64.0;
+                        // input elements staged into LDS by all workgroups (halo per phase group)
+                        int64_t staged = 0;
+                        for (int rd = 0; rd < s; ++rd)
+                            for (int rh = 0; rh < s; ++rh)
+                                for (int wg = 0; wg < nwg; ++wg) {
+                                    int lo = INT_MAX, hi = INT_MIN;
+                                    for (int p = 0; p < v.NPH; ++p) {
+                                        const DimPhase &d = pl->ph[2][wg * v.NPH + p];
+                                        if (d.J == 0) continue;
+                                        lo = std::min(lo, d.c - d.J + 1);
+                                        hi = std::max(hi, TQw - 1 + d.c);
+                                    }
+                                    if (lo > hi || pl->ph[0][rd].J == 0 || pl->ph[1][rh].J == 0) continue;
+                                    staged += (int64_t)(TQd + pl->ph[0][rd].J - 1) * (TQh + pl->ph[1][rh].J - 1) *
+                                              (hi - lo + 1);
+                                }
+                        staged *= nn * co_tiles * (int64_t)ntile[0] * ntile[1] * ntile[2] * nchunks * CI_T;
+                        // cost in MAC-equivalents: issued MFMA work, ~24 per staged element
+                        // (address arithmetic, load, LDS store), ~64 per output of the epilogue
+                        double cost = (double)issued + 24.0 * (double)staged +
+                                      (double)grid * CO_T * 32 * PT * v.NPH * 64.0;
                         const double fill = std::min(1.0, (double)grid / 512.0);
                         cost /= fill;
                         if (cost < best) {
