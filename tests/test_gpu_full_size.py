@@ -1,0 +1,82 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (same geometry -> same plan).  Expected values were written by
+tests/golden/make_full_size_golden.py, which runs only the fp64 oracle:
+sampled voxels of the raw convolution and of the final output, the exported
+statistics, and for the pooled BatchNorm path the whole [n, cout] output.
+Properties that hold at any size are checked on the whole GPU output."""
+import os
+
+import numpy as np
+import pytest
+
+from activation_epilogues_amd import workloads as W
+
+from gpu_helpers import TOL, max_err, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NAMES = ["k3s1_gn", "k3s2_softmax", "k5s1_bnpool", "k4s2_gn"]
+
+
+def load_golden(name):
+    path = os.path.join(GOLDEN, f"full_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    return np.load(path, allow_pickle=False)
+
+
+def check_inputs(g, inp):
+    for k in ("x", "w", "b", "gamma", "beta"):
+        a = getattr(inp, k)
+        if "sum_" + k in g.files:
+            assert a is not None
+            assert np.array_equal(a.reshape(-1)[:8], g["head_" + k]), k
+            assert a.astype(np.float64).sum() == g["sum_" + k], k
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_final_output(name):
+    wl = W.BY_NAME[name]
+    g = load_golden(name)
+    inp = W.make_inputs(wl)
+    check_inputs(g, inp)
+    say(f"[case] full-size {name} epilogue={W.EPI_NAMES[wl.epi]} x={wl.x_shape}")
+    out, st, _ = run_gpu(wl, inp)
+    assert np.isfinite(out).all()
+    idx = g["sample_index"]
+    if wl.epi == W.EPI_SCALE_BN_TRAIN_AVGPOOL:
+        o2 = out.reshape(wl.n, wl.cout)
+        assert max_err(o2, g["out"]) <= TOL
+        np.testing.assert_allclose(st[:, 0], g["stats"][:, 0], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(st[:, 1], g["stats"][:, 1], rtol=1e-5, atol=1e-6)
+        # the batch mean of the pooled output is beta
+        np.testing.assert_allclose(o2.astype(np.float64).mean(axis=0), inp.beta.astype(np.float64), atol=1e-5)
+        return
+    assert max_err(out[tuple(idx.T)], g["out_at_samples"]) <= TOL
+    if wl.epi == W.EPI_RELU_GROUPNORM:
+        np.testing.assert_allclose(st[..., 0], g["stats"][..., 0], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(st[..., 1], g["stats"][..., 1], rtol=1e-5, atol=1e-6)
+        # per (n, group): mean 0 and variance var/(var+eps) before the affine step
+        ga = inp.gamma.astype(np.float64)[None, :, None]
+        be = inp.beta.astype(np.float64)[None, :, None]
+        z = (out.reshape(wl.n, wl.cout, -1).astype(np.float64) - be) / ga
+        z = z.reshape(wl.n, wl.groups, -1)
+        rstd = g["stats"][..., 1]
+        var = 1.0 / rstd ** 2 - wl.eps
+        np.testing.assert_allclose(z.mean(axis=2), 0.0, atol=2e-5)
+        np.testing.assert_allclose(z.var(axis=2), var / (var + wl.eps), rtol=1e-4)
+    if wl.epi == W.EPI_SOFTMAX_SIGMOID:
+        # sigmoid of a probability lies in (0.5, sigmoid(1)]
+        assert out.min() > 0.5 and out.max() <= 1.0 / (1.0 + np.exp(-1.0)) + 1e-6
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_raw_convolution(name):
+    wl = W.BY_NAME[name]
+    g = load_golden(name)
+    inp = W.make_inputs(wl)
+    say(f"[case] full-size raw conv {name} x={wl.x_shape}")
+    raw, _, _ = run_gpu(wl.with_(epi=W.EPI_NONE), inp, kind=W.EPI_NONE, want_stats=False)
+    idx = g["sample_index"]
+    assert max_err(raw[tuple(idx.T)], g["raw_at_samples"]) <= TOL
