@@ -3,6 +3,7 @@
 // stream; nothing here allocates device memory or waits on the device.
 #include <hip/hip_runtime_api.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <list>
 #include <mutex>
@@ -18,8 +19,10 @@ namespace {
 struct CacheKey {
     convt3d_geom g;
     int kind, groups;
+    char plan_env[64];  // CONVT3D_PLAN tile override, if any
     bool operator==(const CacheKey &o) const {
-        return std::memcmp(&g, &o.g, sizeof(g)) == 0 && kind == o.kind && groups == o.groups;
+        return std::memcmp(&g, &o.g, sizeof(g)) == 0 && kind == o.kind && groups == o.groups &&
+               std::strncmp(plan_env, o.plan_env, sizeof(plan_env)) == 0;
     }
 };
 
@@ -33,6 +36,7 @@ int cached_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *out) {
     key.g = *g;
     key.kind = e->kind;
     key.groups = e->kind == CONVT3D_EPI_RELU_GROUPNORM ? e->groups : 0;
+    if (const char *env = std::getenv("CONVT3D_PLAN")) std::strncpy(key.plan_env, env, sizeof(key.plan_env) - 1);
     {
         std::lock_guard<std::mutex> lk(g_mu);
         for (auto it = g_cache.begin(); it != g_cache.end(); ++it)

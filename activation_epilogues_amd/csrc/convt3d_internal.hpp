@@ -12,8 +12,9 @@ namespace convt3d {
 constexpr int kMaxStride = 4;
 constexpr int kMaxPhases = kMaxStride * kMaxStride * kMaxStride;
 constexpr int kOctet = 8;          // input channels per packed weight group (4 MFMA k-steps)
+constexpr int kMaxRegions = 27;    // tiling regions: (low border, interior, high border)^3
 constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
-constexpr int kMaxLdsBytes = 80 * 1024;  // two workgroups per CU
+constexpr int kMaxLdsBytes = 80 * 1024;  // at least two workgroups per CU
 
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
 // taps that reach it are k = r + s*j (j = 0..J-1) from input i = q + c - j.
@@ -34,8 +35,13 @@ struct ConvParams {
     int N, Cin, Cout, D, H, W, Do, Ho, Wo;
     int s;
     int Qd, Qh, Qw;
-    int TQd, TQh, TQw;
-    int ntd, nth, ntw;
+    // Tiling regions.  rg[r] = {start d,h,w; end d,h,w; box d,h,w; tiles d,h,w}
+    // in stride-phase coordinates q; workgroup x-index b belongs to region r when
+    // rg_off[r] <= b < rg_off[r+1].
+    int nreg;
+    int rg[kMaxRegions][12];
+    int rg_off[kMaxRegions + 1];
+    int tiles_total;      // rg_off[nreg]
     int CI_T;             // input channels per LDS chunk (multiple of 8)
     int octets;           // ceil(Cin / 8)
     int nchunks;          // ceil(octets * 8 / CI_T)
@@ -70,8 +76,11 @@ struct Plan {
     // kernel choice
     int variant = -1;
     int CBW = 1, NPH = 1, PBW = 1, WCO = 1, WPOS = 1;
-    int TQ[3] = {1, 1, 1};
-    int ntile[3] = {1, 1, 1};
+    int TQ[3] = {1, 1, 1};    // box of the largest region (for reporting)
+    int nreg = 0;
+    int rg[kMaxRegions][12]{};
+    int rg_off[kMaxRegions + 1]{};
+    int tiles_total = 0;
     int CI_T = 8, nchunks = 1;
     int HWp = 1, CISTR = 1, lds_bytes = 0;
     int co_tiles = 1, nwgroups = 1;
@@ -85,6 +94,7 @@ struct Plan {
 // Kernel variants the library is built with.
 struct Variant {
     int CBW, NPH, PBW;
+    int waves_per_simd;
 };
 extern const Variant kVariants[];
 extern const int kNumVariants;

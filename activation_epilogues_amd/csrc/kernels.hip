@@ -106,12 +106,15 @@ __global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1
     const int wco = wave % P.WCO;
     const int wpos = wave / P.WCO;
 
-    // ---- workgroup -> tile
-    int bx = blockIdx.x;
-    const int tw_i = bx % P.ntw;
-    bx /= P.ntw;
-    const int th_i = bx % P.nth;
-    const int td_i = bx / P.nth;
+    // ---- workgroup -> tile: find the region, then the tile inside it
+    const int bx = blockIdx.x;
+    int reg = 0;
+    while (reg + 1 < P.nreg && bx >= P.rg_off[reg + 1]) ++reg;
+    const int *RG = P.rg[reg];
+    const int local = bx - P.rg_off[reg];
+    const int tw_i = local % RG[11];
+    const int th_i = (local / RG[11]) % RG[10];
+    const int td_i = local / (RG[11] * RG[10]);
     int by = blockIdx.y;
     const int co_tile = by % P.co_tiles;
     by /= P.co_tiles;
@@ -122,8 +125,10 @@ __global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1
     const int rho_d = by / s;
     const int n = blockIdx.z;
 
-    const int TQd = P.TQd, TQh = P.TQh, TQw = P.TQw;
-    const int q0d = td_i * TQd, q0h = th_i * TQh, q0w = tw_i * TQw;
+    const int TQd = RG[6], TQh = RG[7], TQw = RG[8];
+    const int q0d = RG[0] + td_i * TQd, q0h = RG[1] + th_i * TQh, q0w = RG[2] + tw_i * TQw;
+    // extent of this tile inside its region (the box may overhang the region end)
+    const int TQd_e = min(TQd, RG[3] - q0d), TQh_e = min(TQh, RG[4] - q0h), TQw_e = min(TQw, RG[5] - q0w);
     const int Jd = P.pJ[0][rho_d], cd = P.pc[0][rho_d];
     const int Jh = P.pJ[1][rho_h], ch = P.pc[1][rho_h];
     int Jw[NPH], cw[NPH], rw[NPH];
@@ -147,12 +152,11 @@ __global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1
     const int lo_d = q0d + cd - Jd + 1;
     const int lo_h = q0h + ch - Jh + 1;
     const int lo_w = q0w + lo_w_rel;
-    const int HWp = P.HWp;
+    const int HWp = HW;  // compact rows
     const int CISTR = P.CISTR;
     const int ROW = HH * HWp;
 
     // ---- taps that touch the input for this box (border tiles skip the rest)
-    const int TQd_e = min(TQd, P.Qd - q0d), TQh_e = min(TQh, P.Qh - q0h), TQw_e = min(TQw, P.Qw - q0w);
     const int jd_lo = max(0, q0d + cd - (P.D - 1)), jd_hi = min(Jd - 1, q0d + TQd_e - 1 + cd);
     const int jh_lo = max(0, q0h + ch - (P.H - 1)), jh_hi = min(Jh - 1, q0h + TQh_e - 1 + ch);
     int jw_lo[NPH], jw_hi[NPH];
@@ -171,12 +175,12 @@ __global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
         const int pidx = (wpos * PBW + pb) * 32 + col;
-        pos_ok[pb] = pidx < vol;
-        const int pi = pos_ok[pb] ? pidx : 0;
+        const int pi = pidx < vol ? pidx : 0;
         const int td = pi / plane;
         const int rem = pi - td * plane;
         const int th = rem / TQw;
         const int tw = rem - th * TQw;
+        pos_ok[pb] = pidx < vol && td < TQd_e && th < TQh_e && tw < TQw_e;
         pos_t[pb][0] = td;
         pos_t[pb][1] = th;
         pos_t[pb][2] = tw;
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1
             }
     }
     __syncthreads();
-    const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * (P.ntd * P.nth * P.ntw) + (int)blockIdx.x;
+    const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + (int)blockIdx.x;
     for (int row = tid; row < CO32; row += blockDim.x) {
         const int co = co_tile * CO32 + row;
         if (co >= Cout) continue;

@@ -10,6 +10,9 @@
 // can never be valid is ever multiplied.
 #include <algorithm>
 #include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -20,11 +23,13 @@ namespace convt3d {
 // Kernel variants compiled into the library (co-blocks per wave, w-phases per
 // wave, position blocks per wave).  Keep in sync with the instantiations in
 // kernels.hip.
+// The last field is the waves per SIMD the compiled kernel's register count
+// allows (used only by the cost model).
 const Variant kVariants[] = {
-    {1, 1, 8}, {1, 1, 4}, {1, 1, 2},
-    {1, 2, 4}, {1, 2, 2},
-    {2, 1, 4}, {2, 2, 2},
-    {4, 1, 2}, {4, 2, 1},
+    {1, 1, 8, 2}, {1, 1, 4, 3}, {1, 1, 2, 4},
+    {1, 2, 4, 2}, {1, 2, 2, 3},
+    {2, 1, 4, 1}, {2, 2, 2, 1},
+    {4, 1, 2, 1}, {4, 2, 1, 1},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -94,23 +99,6 @@ int make_geometry(const convt3d_geom *g, Plan *pl) {
     return CONVT3D_OK;
 }
 
-// Taps of a phase that touch the input for a tile starting at q0 (tile length
-// tq, q extent Q), along one dim: count of j in [max(0, q0+c-(in-1)),
-// min(J-1, q0+tq_eff-1+c)].
-static int live_taps(const DimPhase &d, int q0, int tq, int Q, int in) {
-    if (d.J == 0) return 0;
-    const int te = std::min(tq, Q - q0);
-    const int lo = std::max(0, q0 + d.c - (in - 1));
-    const int hi = std::min(d.J - 1, q0 + te - 1 + d.c);
-    return hi >= lo ? hi - lo + 1 : 0;
-}
-
-static int64_t sum_live(const DimPhase &d, int tq, int Q, int in) {
-    int64_t t = 0;
-    for (int q0 = 0; q0 < Q; q0 += tq) t += live_taps(d, q0, tq, Q, in);
-    return t;
-}
-
 static int64_t valid_taps_dim(int out, int in, int k, int s, int p) {
     int64_t t = 0;
     for (int o = 0; o < out; ++o)
@@ -159,15 +147,57 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                      valid_taps_dim(pl->Ho, g->h, g->k, s, g->pad) *
                      valid_taps_dim(pl->Wo, g->w, g->k, s, g->pad);
 
-    // sum over tiles of live taps, per (dim, phase, tile length)
-    const int tqmax = 4 * 8 * 32;
-    std::vector<int64_t> live[3][kMaxStride];
-    for (int dim = 0; dim < 3; ++dim)
+    // ---- tiling regions.  Along each dim, positions q whose every phase has all
+    // of its taps on the input form the interior [lo, hi); the borders around it
+    // have fewer live taps.  Tiling each (border/interior)^3 region with its own
+    // box lets border tiles skip the taps that cannot reach the input.
+    struct Seg { int a, b; };
+    Seg segs_split[3][3], segs_whole[3][1];
+    int nseg_split[3];
+    for (int dim = 0; dim < 3; ++dim) {
+        int lo = 0, hi = pl->Q[dim];
         for (int rho = 0; rho < s; ++rho) {
-            live[dim][rho].assign(std::min(pl->Q[dim], tqmax) + 1, 0);
-            for (int tq = 1; tq < (int)live[dim][rho].size(); ++tq)
-                live[dim][rho][tq] = sum_live(pl->ph[dim][rho], tq, pl->Q[dim], ins[dim]);
+            const DimPhase &d = pl->ph[dim][rho];
+            if (d.J == 0) continue;
+            lo = std::max(lo, d.J - 1 - d.c);
+            hi = std::min(hi, ins[dim] - d.c);
         }
+        lo = std::min(std::max(lo, 0), pl->Q[dim]);
+        hi = std::max(std::min(hi, pl->Q[dim]), lo);
+        int &ns = nseg_split[dim];
+        ns = 0;
+        if (lo > 0) segs_split[dim][ns++] = {0, lo};
+        if (hi > lo) segs_split[dim][ns++] = {lo, hi};
+        if (pl->Q[dim] > hi) segs_split[dim][ns++] = {hi, pl->Q[dim]};
+        segs_whole[dim][0] = {0, pl->Q[dim]};
+    }
+    // live taps summed over the tiles of a segment for a tile length
+    auto seg_live = [&](int dim, int rho, const Seg &sg, int tq) {
+        const DimPhase &d = pl->ph[dim][rho];
+        if (d.J == 0) return (int64_t)0;
+        int64_t t = 0;
+        for (int q0 = sg.a; q0 < sg.b; q0 += tq) {
+            const int te = std::min(tq, sg.b - q0);
+            const int lo = std::max(0, q0 + d.c - (ins[dim] - 1));
+            const int hi = std::min(d.J - 1, q0 + te - 1 + d.c);
+            if (hi >= lo) t += hi - lo + 1;
+        }
+        return t;
+    };
+
+    // Optional override for tile sweeps: CONVT3D_PLAN="variant,WCO,TQd,TQh,TQw,CI_T[,split]"
+    // restricts the search to that variant / wave grid / chunk, with that box in
+    // the largest region and (bit 0 d, 1 h, 2 w) those dims split into border /
+    // interior segments (ignored if it does not fit).
+    int force[7] = {-1, -1, -1, -1, -1, -1, -1};
+    if (const char *env = std::getenv("CONVT3D_PLAN")) {
+        const int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &force[0], &force[1], &force[2], &force[3],
+                                    &force[4], &force[5], &force[6]);
+        if (got < 6) force[0] = -1;
+    }
+    const bool forced = force[0] >= 0;
+    const int64_t nn = std::max(g->n, 1);  // plan an empty batch like n = 1
+    const int CI_pad = pl->octets * kOctet;
 
     double best = 1e300;
     Plan bestp = *pl;
@@ -175,117 +205,204 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
     for (int vi = 0; vi < kNumVariants; ++vi) {
         const Variant v = kVariants[vi];
         if (s % v.NPH != 0) continue;
+        if (forced && vi != force[0]) continue;
         if (softmax && v.CBW < pl->cb_total) continue;
         if (softmax && v.CBW >= 2 * pl->cb_total) continue;  // keep only the tightest fit
         for (int WCO = 1; WCO <= 4; WCO *= 2) {
-            const int WPOS = 4 / WCO;
+          const int WPOS = 4 / WCO;
+          if (forced && WCO != force[1]) continue;
+          // which dims are split into border / interior segments
+          for (int split = 0; split < 8; ++split) {
+            if (forced && force[6] >= 0 && split != force[6]) continue;
+            Seg segs[3][3];
+            int nseg[3];
+            bool redundant = false;
+            for (int dim = 0; dim < 3; ++dim) {
+                const bool sp = (split >> dim) & 1;
+                if (sp && nseg_split[dim] == 1) redundant = true;  // same as unsplit
+                nseg[dim] = sp ? nseg_split[dim] : 1;
+                for (int i = 0; i < nseg[dim]; ++i) segs[dim][i] = sp ? segs_split[dim][i] : segs_whole[dim][0];
+            }
+            if (redundant) continue;
             if (softmax && WCO != 1) continue;
             const int CO_T = WCO * v.CBW;  // co blocks per workgroup
             if (CO_T > pl->cb_total && WCO > 1) continue;  // do not waste whole waves on padding
             const int co_tiles = (int)ceil_div(pl->cb_total, CO_T);
             const int PT = WPOS * v.PBW * 32;
             const int nwg = s / v.NPH;
-            // halo extents along w over each group of NPH w-phases
-            // rows of at least 16 positions keep LDS reads and output stores contiguous
-            const int TQw_min = std::min(pl->Q[2], 16);
-            for (int TQw = TQw_min; TQw <= std::min(pl->Q[2], PT); ++TQw) {
-                for (int TQh = 1; TQh <= std::min(pl->Q[1], PT / TQw); ++TQh) {
-                    // boxes that leave a whole position block empty are skipped unless
-                    // the box cannot grow any more along d
-                    const int maxd = std::min(pl->Q[0], PT / (TQw * TQh));
-                    int mind = std::max(1, (PT - 32) / (TQw * TQh));
-                    if (mind > maxd) mind = maxd;
-                    for (int TQd = mind; TQd <= maxd; ++TQd) {
-                        // LDS halo size (max over phases)
-                        int HD = 1, HH = 1, HW = TQw;
-                        for (int rho = 0; rho < s; ++rho) {
-                            HD = std::max(HD, TQd + std::max(pl->ph[0][rho].J, 1) - 1);
-                            HH = std::max(HH, TQh + std::max(pl->ph[1][rho].J, 1) - 1);
-                        }
-                        for (int wg = 0; wg < nwg; ++wg) {
-                            int lo = INT_MAX, hi = INT_MIN;
-                            for (int p = 0; p < v.NPH; ++p) {
-                                const DimPhase &d = pl->ph[2][wg * v.NPH + p];
-                                if (d.J == 0) continue;
-                                lo = std::min(lo, d.c - d.J + 1);
-                                hi = std::max(hi, TQw - 1 + d.c);
-                            }
-                            if (lo <= hi) HW = std::max(HW, hi - lo + 1);
-                        }
-                        const int HWp = HW;
-                        const int slab = HD * HH * HWp;
-                        int CI_T = 0;
-                        for (int m = 4; m >= 1; m /= 2) {
-                            if (pl->octets % m != 0) continue;  // chunks never pass the packed octets
-                            if ((int64_t)m * kOctet * slab * 4 <= kMaxLdsBytes) { CI_T = m * kOctet; break; }
-                        }
-                        if (CI_T == 0) continue;
-                        const int nchunks = (int)ceil_div(pl->octets * kOctet, CI_T);
-                        const int ntile[3] = {(int)ceil_div(pl->Q[0], TQd), (int)ceil_div(pl->Q[1], TQh),
-                                              (int)ceil_div(pl->Q[2], TQw)};
-                        // issued MACs: per workgroup CO_T*32 x PT x CI_pad x sum_p live taps
-                        int64_t taps = 0;
-                        for (int rd = 0; rd < s; ++rd) {
-                            const int64_t ld = live[0][rd][TQd];
-                            for (int rh = 0; rh < s; ++rh) {
-                                const int64_t lh = live[1][rh][TQh];
-                                int64_t lw = 0;
-                                for (int rw = 0; rw < s; ++rw)
-                                    lw += live[2][rw][TQw];
-                                taps += ld * lh * lw;
-                            }
-                        }
-                        const int64_t nn = std::max(g->n, 1);  // plan an empty batch like n = 1
-                        const int64_t issued = nn * co_tiles * CO_T * 32 * PT *
-                                               (int64_t)nchunks * CI_T * taps;
-                        const int64_t grid = nn * co_tiles * s * s * nwg *
-                                             ntile[0] * ntile[1] * ntile[2];
-                        // input elements staged into LDS by all workgroups (halo per phase group)
-                        int64_t staged = 0;
-                        for (int rd = 0; rd < s; ++rd)
-                            for (int rh = 0; rh < s; ++rh)
-                                for (int wg = 0; wg < nwg; ++wg) {
-                                    int lo = INT_MAX, hi = INT_MIN;
-                                    for (int p = 0; p < v.NPH; ++p) {
-                                        const DimPhase &d = pl->ph[2][wg * v.NPH + p];
-                                        if (d.J == 0) continue;
-                                        lo = std::min(lo, d.c - d.J + 1);
-                                        hi = std::max(hi, TQw - 1 + d.c);
-                                    }
-                                    if (lo > hi || pl->ph[0][rd].J == 0 || pl->ph[1][rh].J == 0) continue;
-                                    staged += (int64_t)(TQd + pl->ph[0][rd].J - 1) * (TQh + pl->ph[1][rh].J - 1) *
-                                              (hi - lo + 1);
-                                }
-                        staged *= nn * co_tiles * (int64_t)ntile[0] * ntile[1] * ntile[2] * nchunks * CI_T;
-                        // cost in MAC-equivalents: issued MFMA work, ~24 per staged element
-                        // (address arithmetic, load, LDS store), ~64 per output of the epilogue
-                        double cost = (double)issued + 24.0 * (double)staged +
-                                      (double)grid * CO_T * 32 * PT * v.NPH * 64.0;
-                        const double fill = std::min(1.0, (double)grid / 512.0);
-                        cost /= fill;
-                        if (cost < best) {
-                            best = cost;
-                            found = true;
-                            Plan c = *pl;
-                            c.variant = vi;
-                            c.CBW = v.CBW; c.NPH = v.NPH; c.PBW = v.PBW;
-                            c.WCO = WCO; c.WPOS = WPOS;
-                            c.TQ[0] = TQd; c.TQ[1] = TQh; c.TQ[2] = TQw;
-                            for (int i = 0; i < 3; ++i) c.ntile[i] = ntile[i];
-                            c.CI_T = CI_T; c.nchunks = nchunks;
-                            c.HWp = HWp; c.CISTR = slab;
-                            c.lds_bytes = CI_T * slab * 4;
-                            c.co_tiles = co_tiles; c.nwgroups = nwg;
-                            c.tiles_per_n = (int64_t)s * s * nwg * ntile[0] * ntile[1] * ntile[2];
-                            c.grid_x = (int64_t)ntile[0] * ntile[1] * ntile[2];
-                            c.grid_y = (int64_t)co_tiles * s * s * nwg;
-                            c.grid_z = g->n;
-                            c.issued_macs = issued / nn * g->n;
-                            bestp = c;
-                        }
-                    }
+            // halo width along w of a box for each w-phase group
+            auto halo_w = [&](int TQw, int wg) {
+                int lo = INT_MAX, hi = INT_MIN;
+                for (int p = 0; p < v.NPH; ++p) {
+                    const DimPhase &d = pl->ph[2][wg * v.NPH + p];
+                    if (d.J == 0) continue;
+                    lo = std::min(lo, d.c - d.J + 1);
+                    hi = std::max(hi, TQw - 1 + d.c);
                 }
+                return lo <= hi ? hi - lo + 1 : 0;
+            };
+            // largest region (the one a forced box applies to)
+            int big = 0, big_vol = -1, ri = 0;
+            for (int i0 = 0; i0 < nseg[0]; ++i0)
+                for (int i1 = 0; i1 < nseg[1]; ++i1)
+                    for (int i2 = 0; i2 < nseg[2]; ++i2, ++ri) {
+                        const int vol = (segs[0][i0].b - segs[0][i0].a) * (segs[1][i1].b - segs[1][i1].a) *
+                                        (segs[2][i2].b - segs[2][i2].a);
+                        if (vol > big_vol) { big_vol = vol; big = ri; }
+                    }
+            // best box per region
+            struct RChoice { int box[3], nt[3]; int64_t tiles, issued, staged; int slab; double cost; };
+            RChoice rc[kMaxRegions];
+            int nreg = 0;
+            bool ok_all = true;
+            for (int i0 = 0; i0 < nseg[0] && ok_all; ++i0)
+                for (int i1 = 0; i1 < nseg[1] && ok_all; ++i1)
+                    for (int i2 = 0; i2 < nseg[2] && ok_all; ++i2) {
+                        const Seg sd = segs[0][i0], sh = segs[1][i1], sw = segs[2][i2];
+                        const int ext[3] = {sd.b - sd.a, sh.b - sh.a, sw.b - sw.a};
+                        RChoice bestr{};
+                        bestr.cost = 1e300;
+                        // rows of at least 16 positions keep LDS reads and stores contiguous
+                        const int TQw_min = std::min(ext[2], 16);
+                        for (int TQw = TQw_min; TQw <= std::min(ext[2], PT); ++TQw) {
+                            for (int TQh = 1; TQh <= std::min(ext[1], PT / TQw); ++TQh) {
+                                // boxes that leave a whole position block empty are skipped
+                                // unless the box cannot grow any more along d
+                                const int maxd = std::min(ext[0], PT / (TQw * TQh));
+                                int mind = std::max(1, (PT - 32) / (TQw * TQh));
+                                if (mind > maxd) mind = maxd;
+                                for (int TQd = mind; TQd <= maxd; ++TQd) {
+                                    if (forced && nreg == big &&
+                                        (TQd != force[2] || TQh != force[3] || TQw != force[4]))
+                                        continue;
+                                    int HD = 1, HH = 1, HW = TQw;
+                                    for (int rho = 0; rho < s; ++rho) {
+                                        HD = std::max(HD, TQd + std::max(pl->ph[0][rho].J, 1) - 1);
+                                        HH = std::max(HH, TQh + std::max(pl->ph[1][rho].J, 1) - 1);
+                                    }
+                                    for (int wg = 0; wg < nwg; ++wg) HW = std::max(HW, halo_w(TQw, wg));
+                                    const int slab = HD * HH * HW;
+                                    if ((int64_t)kOctet * slab * 4 > kMaxLdsBytes) continue;
+                                    const int nt[3] = {(int)ceil_div(ext[0], TQd), (int)ceil_div(ext[1], TQh),
+                                                       (int)ceil_div(ext[2], TQw)};
+                                    const int64_t tiles = (int64_t)nt[0] * nt[1] * nt[2];
+                                    int64_t taps = 0, halo = 0;
+                                    for (int rd = 0; rd < s; ++rd) {
+                                        const int64_t ld = seg_live(0, rd, sd, TQd);
+                                        for (int rh = 0; rh < s; ++rh) {
+                                            const int64_t lh = seg_live(1, rh, sh, TQh);
+                                            int64_t lw = 0;
+                                            for (int rw = 0; rw < s; ++rw) lw += seg_live(2, rw, sw, TQw);
+                                            taps += ld * lh * lw;
+                                            if (pl->ph[0][rd].J == 0 || pl->ph[1][rh].J == 0) continue;
+                                            for (int wg = 0; wg < nwg; ++wg)
+                                                halo += (int64_t)(TQd + pl->ph[0][rd].J - 1) *
+                                                        (TQh + pl->ph[1][rh].J - 1) * halo_w(TQw, wg);
+                                        }
+                                    }
+                                    const int64_t issued = nn * co_tiles * CO_T * 32 * (int64_t)PT * CI_pad * taps;
+                                    const int64_t staged = nn * co_tiles * tiles * CI_pad * halo;
+                                    const int64_t wgs = nn * co_tiles * s * s * nwg * tiles;
+                                    // MAC-equivalents: issued MFMA work, ~24 per staged element
+                                    // (address arithmetic, load, LDS store), ~64 per output of
+                                    // the epilogue
+                                    const double cost = (double)issued + 24.0 * (double)staged +
+                                                        (double)wgs * CO_T * 32 * PT * v.NPH * 64.0;
+                                    if (cost < bestr.cost) {
+                                        bestr.cost = cost;
+                                        bestr.box[0] = TQd; bestr.box[1] = TQh; bestr.box[2] = TQw;
+                                        for (int i = 0; i < 3; ++i) bestr.nt[i] = nt[i];
+                                        bestr.tiles = tiles;
+                                        bestr.issued = issued;
+                                        bestr.staged = staged;
+                                        bestr.slab = slab;
+                                    }
+                                }
+                            }
+                        }
+                        if (bestr.cost >= 1e300) { ok_all = false; break; }
+                        rc[nreg++] = bestr;
+                    }
+            if (!ok_all) continue;
+            int max_slab = 0;
+            int64_t tiles_total = 0, issued = 0;
+            double cost = 0.0;
+            for (int r = 0; r < nreg; ++r) {
+                max_slab = std::max(max_slab, rc[r].slab);
+                tiles_total += rc[r].tiles;
+                issued += rc[r].issued;
+                cost += rc[r].cost;
             }
+            // largest channel chunk whose LDS still lets the register-limited number
+            // of workgroups share a CU (measured: occupancy beats fewer barriers)
+            int CI_T = 0;
+            for (int m = 4; m >= 1; m /= 2) {
+                if (pl->octets % m != 0) continue;  // chunks never pass the packed octets
+                const int64_t bytes = (int64_t)m * kOctet * max_slab * 4;
+                if (bytes > kMaxLdsBytes) continue;
+                if (m > 1 && bytes * v.waves_per_simd > 160 * 1024) continue;
+                CI_T = m * kOctet;
+                break;
+            }
+            if (forced && force[5] > 0) {
+                if (force[5] % kOctet || pl->octets % (force[5] / kOctet) ||
+                    (int64_t)force[5] * max_slab * 4 > kMaxLdsBytes)
+                    continue;
+                CI_T = force[5];
+            }
+            if (CI_T == 0) continue;
+            const int64_t grid = nn * co_tiles * s * s * nwg * tiles_total;
+            // whole rounds of workgroups over the CUs; workgroups per CU from the
+            // variant's register occupancy and the LDS size
+            const int lds_wg = std::max(CI_T * max_slab * 4, 1);
+            const int per_cu = std::max(1, std::min(v.waves_per_simd, 160 * 1024 / lds_wg));
+            const double slots = 256.0 * per_cu;
+            const double rounds = std::ceil((double)grid / slots);
+            cost *= rounds * slots / (double)grid;
+            // few waves per SIMD hide less latency; fewer MFMA tiles per wave mean
+            // more operand traffic per MFMA
+            // (measured on MI355X: 3 workgroups per CU reach ~67% MFMA busy, 2 ~60%)
+            cost *= per_cu == 1 ? 1.35 : per_cu == 2 ? 1.15 : per_cu == 3 ? 1.04 : 1.0;
+            cost *= 1.0 + 0.15 / (v.CBW * v.PBW * v.NPH);
+            if (cost < best) {
+                best = cost;
+                found = true;
+                Plan c = *pl;
+                c.variant = vi;
+                c.CBW = v.CBW; c.NPH = v.NPH; c.PBW = v.PBW;
+                c.WCO = WCO; c.WPOS = WPOS;
+                c.nreg = nreg;
+                int64_t off = 0;
+                int r = 0;
+                for (int i0 = 0; i0 < nseg[0]; ++i0)
+                    for (int i1 = 0; i1 < nseg[1]; ++i1)
+                        for (int i2 = 0; i2 < nseg[2]; ++i2, ++r) {
+                            const Seg sg[3] = {segs[0][i0], segs[1][i1], segs[2][i2]};
+                            for (int dim = 0; dim < 3; ++dim) {
+                                c.rg[r][dim] = sg[dim].a;
+                                c.rg[r][3 + dim] = sg[dim].b;
+                                c.rg[r][6 + dim] = rc[r].box[dim];
+                                c.rg[r][9 + dim] = rc[r].nt[dim];
+                            }
+                            c.rg_off[r] = (int)off;
+                            off += rc[r].tiles;
+                        }
+                c.rg_off[nreg] = (int)off;
+                c.tiles_total = (int)tiles_total;
+                for (int dim = 0; dim < 3; ++dim) c.TQ[dim] = rc[big].box[dim];
+                c.CI_T = CI_T; c.nchunks = (int)ceil_div(CI_pad, CI_T);
+                c.HWp = 0;  // per-tile (compact rows)
+                c.CISTR = max_slab;
+                c.lds_bytes = CI_T * max_slab * 4;
+                c.co_tiles = co_tiles; c.nwgroups = nwg;
+                c.tiles_per_n = (int64_t)s * s * nwg * tiles_total;
+                c.grid_x = tiles_total;
+                c.grid_y = (int64_t)co_tiles * s * s * nwg;
+                c.grid_z = g->n;
+                c.issued_macs = issued / nn * g->n;
+                bestp = c;
+            }
+          }
         }
     }
     if (!found) return CONVT3D_ERR_UNSUPPORTED;
@@ -307,8 +424,11 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->Do = pl.Do; cp->Ho = pl.Ho; cp->Wo = pl.Wo;
     cp->s = pl.s;
     cp->Qd = pl.Q[0]; cp->Qh = pl.Q[1]; cp->Qw = pl.Q[2];
-    cp->TQd = pl.TQ[0]; cp->TQh = pl.TQ[1]; cp->TQw = pl.TQ[2];
-    cp->ntd = pl.ntile[0]; cp->nth = pl.ntile[1]; cp->ntw = pl.ntile[2];
+    cp->nreg = pl.nreg;
+    for (int r = 0; r < kMaxRegions; ++r)
+        for (int i = 0; i < 12; ++i) cp->rg[r][i] = pl.rg[r][i];
+    for (int r = 0; r <= kMaxRegions; ++r) cp->rg_off[r] = pl.rg_off[r];
+    cp->tiles_total = pl.tiles_total;
     cp->CI_T = pl.CI_T; cp->octets = pl.octets; cp->nchunks = pl.nchunks;
     cp->cb_total = pl.cb_total;
     cp->WCO = pl.WCO; cp->WPOS = pl.WPOS;
