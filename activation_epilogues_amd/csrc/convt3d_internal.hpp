@@ -94,7 +94,8 @@ struct Plan {
 // Kernel variants the library is built with.
 struct Variant {
     int CBW, NPH, PBW;
-    int waves_per_simd;
+    bool softmax;        // compiled with the softmax epilogue (else NONE / GN / BN)
+    int waves_per_simd;  // register-limited occupancy of the compiled kernel
 };
 extern const Variant kVariants[];
 extern const int kNumVariants;

@@ -95,8 +95,11 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // for each of its NPH w-phases.  Input channels are consumed in chunks of CI_T:
 // the input halo of the box for those channels is staged in LDS, then every
 // live tap of every phase runs 4 MFMA k-steps per 8 input channels.
-template <int CBW, int NPH, int PBW>
-__global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1) void convt3d_mfma_kernel(const ConvParams P) {
+template <int CBW, int NPH, int PBW, bool SM>
+__global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
+                                          : (CBW * NPH * PBW <= 2) ? 4 : (CBW * NPH * PBW <= 4) ? 3
+                                          : (CBW * NPH * PBW <= 8) ? 2 : 1)
+void convt3d_mfma_kernel(const ConvParams P) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -338,21 +341,36 @@ __global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1
             sp[p][pb] = (od * Ho + oh) * Wo + ow;
         }
     }
+    // both w-phases of a lane land in one aligned float pair (w even, w + 1)
+    bool pair_ok[PBW];
+#pragma unroll
+    for (int pb = 0; pb < PBW; ++pb) {
+        pair_ok[pb] = false;
+        if constexpr (NPH == 2)
+            pair_ok[pb] = ok[0][pb] && ok[1][pb] && (Wo % 2 == 0);  // rw[0] is even when NPH == 2
+    }
     const int Cout = P.Cout;
     const float *bias = P.bias;
     float *outn = P.out + (size_t)n * Cout * S;
 
-    if (P.epi == CONVT3D_EPI_SOFTMAX_SIGMOID) {
-        // The wave holds every channel of its columns (planner: WCO == 1 and
-        // CBW*32 >= Cout); lane l and lane l^32 hold complementary halves.
-        float bv[CBW][16];
+    if constexpr (SM) {
+        // Channel softmax + sigmoid.  The wave holds every channel of its columns
+        // (planner: WCO == 1 and CBW*32 >= Cout); lane l and lane l^32 hold
+        // complementary halves.  Bias first (padding rows -> -inf, so they add 0).
 #pragma unroll
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                bv[c][r] = (co < Cout) ? (bias ? bias[co] : 0.0f) : -INFINITY;
+                const float bco = (co < Cout) ? (bias ? bias[co] : 0.0f) : -INFINITY;
+#pragma unroll
+                for (int p = 0; p < NPH; ++p)
+#pragma unroll
+                    for (int pb = 0; pb < PBW; ++pb) acc[p][c][pb][r] += bco;
             }
+        // exp(x) = 2^(x*log2 e) on the hardware exp2, 1/x on the hardware
+        // reciprocal (about 1 ulp each); the max is taken on the scaled values.
+        constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
         for (int p = 0; p < NPH; ++p)
 #pragma unroll
@@ -361,106 +379,121 @@ __global__ __launch_bounds__(kBlockThreads, (CBW == 1 && NPH * PBW <= 8) ? 2 : 1
 #pragma unroll
                 for (int c = 0; c < CBW; ++c)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float v = acc[p][c][pb][r] + bv[c][r];  // -inf for padding rows
-                        acc[p][c][pb][r] = v;
-                        m = fmaxf(m, v);
-                    }
+                    for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[p][c][pb][r]);
                 m = fmaxf(m, __shfl_xor(m, 32));
+                const float ml = m * kLog2e;
                 float sum = 0.0f;
 #pragma unroll
                 for (int c = 0; c < CBW; ++c)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float e = __expf(acc[p][c][pb][r] - m);  // 0 for padding rows
+                        // 0 for padding rows (-inf)
+                        const float e = __builtin_amdgcn_exp2f(fmaf(acc[p][c][pb][r], kLog2e, -ml));
                         acc[p][c][pb][r] = e;
                         sum += e;
                     }
                 sum += __shfl_xor(sum, 32);
-                const float inv = 1.0f / sum;
-                if (ok[p][pb]) {
+                const float inv = __builtin_amdgcn_rcpf(sum);
 #pragma unroll
-                    for (int c = 0; c < CBW; ++c)
+                for (int c = 0; c < CBW; ++c)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                            if (co < Cout) {
-                                const float pr = acc[p][c][pb][r] * inv;
-                                outn[(size_t)co * S + sp[p][pb]] = 1.0f / (1.0f + __expf(-pr));
-                            }
-                        }
-                }
-            }
-        return;
-    }
-
-    const bool gn = P.epi == CONVT3D_EPI_RELU_GROUPNORM;
-    const bool bn = P.epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
-    const float scale = P.scale;
-    float s1[CBW][16], s2[CBW][16];
-#pragma unroll
-    for (int c = 0; c < CBW; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool cok = co < Cout;
-            const float bco = (cok && bias) ? bias[co] : 0.0f;
-            float a1 = 0.0f, a2 = 0.0f;
-#pragma unroll
-            for (int p = 0; p < NPH; ++p)
-#pragma unroll
-                for (int pb = 0; pb < PBW; ++pb) {
-                    float v = acc[p][c][pb][r] + bco;
-                    if (gn) v = fmaxf(v, 0.0f);
-                    if (bn) v = scale * v;
-                    if (cok && ok[p][pb]) {
-                        if (!bn) outn[(size_t)co * S + sp[p][pb]] = v;
-                        a1 += v;
-                        a2 += v * v;
+                    for (int r = 0; r < 16; ++r) {
+                        const float pr = acc[p][c][pb][r] * inv;
+                        acc[p][c][pb][r] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-pr * kLog2e));
                     }
-                }
-            s1[c][r] = a1;
-            s2[c][r] = a2;
-        }
-    if (!(gn || bn)) return;
-
-    // ---- per-channel sums over the tile: 32 columns of each half, then waves
-#pragma unroll
-    for (int c = 0; c < CBW; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) {
-                s1[c][r] += __shfl_xor(s1[c][r], off);
-                s2[c][r] += __shfl_xor(s2[c][r], off);
             }
-        }
-    __syncthreads();  // every wave is done with the halo LDS
-    float *red = lds;  // [WPOS][CO_T*32][2]
-    const int CO32 = CO_T * 32;
-    if (col == 0) {
+        // stores: with two w-phases the lane holds outputs at w and w+1
+#pragma unroll
+        for (int pb = 0; pb < PBW; ++pb)
+#pragma unroll
+            for (int c = 0; c < CBW; ++c)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (co >= Cout) continue;
+                    float *dst = outn + (size_t)co * S;
+                    if constexpr (NPH == 2) {
+                        if (pair_ok[pb]) {
+                            *reinterpret_cast<float2 *>(dst + sp[0][pb]) =
+                                make_float2(acc[0][c][pb][r], acc[1][c][pb][r]);
+                            continue;
+                        }
+                    }
+#pragma unroll
+                    for (int p = 0; p < NPH; ++p)
+                        if (ok[p][pb]) dst[sp[p][pb]] = acc[p][c][pb][r];
+                }
+    } else {
+        // bias (+ReLU) and store, or scale; per-channel sums over the tile: the
+        // lane's columns, then the 32 columns of each half (xor shuffles), then
+        // the waves (LDS), one (sum, sum of squares) per (tile, channel).
+        const bool gn = P.epi == CONVT3D_EPI_RELU_GROUPNORM;
+        const bool bn = P.epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
+        const float scale = P.scale;
+        const int CO32 = CO_T * 32;
+        float *red = lds;  // [WPOS][CO_T*32][2], reuses the halo LDS
+        if (gn || bn) __syncthreads();  // every wave is done with the halo LDS
 #pragma unroll
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = (wco * CBW + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                red[(wpos * CO32 + row) * 2 + 0] = s1[c][r];
-                red[(wpos * CO32 + row) * 2 + 1] = s2[c][r];
+                const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const bool cok = co < Cout;
+                const float bco = (cok && bias) ? bias[co] : 0.0f;
+                float a1 = 0.0f, a2 = 0.0f;
+                float *dst = outn + (size_t)co * S;
+#pragma unroll
+                for (int pb = 0; pb < PBW; ++pb) {
+                    float v[NPH];
+#pragma unroll
+                    for (int p = 0; p < NPH; ++p) {
+                        v[p] = acc[p][c][pb][r] + bco;
+                        if (gn) v[p] = fmaxf(v[p], 0.0f);
+                        if (bn) v[p] = scale * v[p];
+                        if (cok && ok[p][pb]) {
+                            a1 += v[p];
+                            a2 += v[p] * v[p];
+                        }
+                    }
+                    if (!cok || bn) continue;
+                    if constexpr (NPH == 2) {
+                        if (pair_ok[pb]) {
+                            *reinterpret_cast<float2 *>(dst + sp[0][pb]) = make_float2(v[0], v[1]);
+                            continue;
+                        }
+                    }
+#pragma unroll
+                    for (int p = 0; p < NPH; ++p)
+                        if (ok[p][pb]) dst[sp[p][pb]] = v[p];
+                }
+                if (gn || bn) {
+#pragma unroll
+                    for (int off = 16; off >= 1; off >>= 1) {
+                        a1 += __shfl_xor(a1, off);
+                        a2 += __shfl_xor(a2, off);
+                    }
+                    if (col == 0) {
+                        const int row = (wco * CBW + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        red[(wpos * CO32 + row) * 2 + 0] = a1;
+                        red[(wpos * CO32 + row) * 2 + 1] = a2;
+                    }
+                }
             }
-    }
-    __syncthreads();
-    const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + (int)blockIdx.x;
-    for (int row = tid; row < CO32; row += blockDim.x) {
-        const int co = co_tile * CO32 + row;
-        if (co >= Cout) continue;
-        float t1 = 0.0f, t2 = 0.0f;
-        for (int w = 0; w < P.WPOS; ++w) {
-            t1 += red[(w * CO32 + row) * 2 + 0];
-            t2 += red[(w * CO32 + row) * 2 + 1];
+        if (!(gn || bn)) return;
+        __syncthreads();
+        const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + (int)blockIdx.x;
+        for (int row = tid; row < CO32; row += blockDim.x) {
+            const int co = co_tile * CO32 + row;
+            if (co >= Cout) continue;
+            float t1 = 0.0f, t2 = 0.0f;
+            for (int w = 0; w < P.WPOS; ++w) {
+                t1 += red[(w * CO32 + row) * 2 + 0];
+                t2 += red[(w * CO32 + row) * 2 + 1];
+            }
+            float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * Cout + co) * 2;
+            pp[0] = t1;
+            pp[1] = t2;
         }
-        float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * Cout + co) * 2;
-        pp[0] = t1;
-        pp[1] = t2;
     }
 }
 
@@ -620,9 +653,9 @@ int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream) {
     return (int)hipGetLastError();
 }
 
-template <int CBW, int NPH, int PBW>
+template <int CBW, int NPH, int PBW, bool SM>
 static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
-    auto fn = convt3d_mfma_kernel<CBW, NPH, PBW>;
+    auto fn = convt3d_mfma_kernel<CBW, NPH, PBW, SM>;
     static bool attr_set = false;
     if (!attr_set) {
         hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -636,17 +669,23 @@ static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
 
 int launch_conv(const Plan &pl, const ConvParams &cp, void *stream) {
     const Variant v = kVariants[pl.variant];
-#define CONVT3D_VARIANT(a, b, c) \
-    if (v.CBW == a && v.NPH == b && v.PBW == c) return launch_conv_t<a, b, c>(pl, cp, stream);
-    CONVT3D_VARIANT(1, 1, 8)
-    CONVT3D_VARIANT(1, 1, 4)
-    CONVT3D_VARIANT(1, 1, 2)
-    CONVT3D_VARIANT(1, 2, 4)
-    CONVT3D_VARIANT(1, 2, 2)
-    CONVT3D_VARIANT(2, 1, 4)
-    CONVT3D_VARIANT(2, 2, 2)
-    CONVT3D_VARIANT(4, 1, 2)
-    CONVT3D_VARIANT(4, 2, 1)
+#define CONVT3D_VARIANT(a, b, c, d) \
+    if (v.CBW == a && v.NPH == b && v.PBW == c && v.softmax == d) return launch_conv_t<a, b, c, d>(pl, cp, stream);
+    CONVT3D_VARIANT(1, 1, 8, false)
+    CONVT3D_VARIANT(1, 1, 4, false)
+    CONVT3D_VARIANT(1, 1, 2, false)
+    CONVT3D_VARIANT(1, 2, 4, false)
+    CONVT3D_VARIANT(1, 2, 2, false)
+    CONVT3D_VARIANT(1, 1, 4, true)
+    CONVT3D_VARIANT(1, 1, 2, true)
+    CONVT3D_VARIANT(1, 2, 2, true)
+    CONVT3D_VARIANT(2, 1, 4, true)
+    CONVT3D_VARIANT(2, 2, 2, true)
+    CONVT3D_VARIANT(2, 1, 2, true)
+    CONVT3D_VARIANT(2, 2, 1, true)
+    CONVT3D_VARIANT(4, 1, 2, true)
+    CONVT3D_VARIANT(4, 2, 1, true)
+    CONVT3D_VARIANT(4, 1, 1, true)
 #undef CONVT3D_VARIANT
     return (int)hipErrorInvalidValue;
 }

@@ -26,10 +26,11 @@ namespace convt3d {
 // The last field is the waves per SIMD the compiled kernel's register count
 // allows (used only by the cost model).
 const Variant kVariants[] = {
-    {1, 1, 8, 2}, {1, 1, 4, 3}, {1, 1, 2, 4},
-    {1, 2, 4, 2}, {1, 2, 2, 3},
-    {2, 1, 4, 1}, {2, 2, 2, 1},
-    {4, 1, 2, 1}, {4, 2, 1, 1},
+    {1, 1, 8, false, 2}, {1, 1, 4, false, 4}, {1, 1, 2, false, 7},
+    {1, 2, 4, false, 2}, {1, 2, 2, false, 4},
+    {1, 1, 4, true, 4}, {1, 1, 2, true, 6}, {1, 2, 2, true, 4},
+    {2, 1, 4, true, 2}, {2, 2, 2, true, 2}, {2, 1, 2, true, 3}, {2, 2, 1, true, 3},
+    {4, 1, 2, true, 1}, {4, 2, 1, true, 1}, {4, 1, 1, true, 2},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -206,6 +207,7 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
         const Variant v = kVariants[vi];
         if (s % v.NPH != 0) continue;
         if (forced && vi != force[0]) continue;
+        if (v.softmax != softmax) continue;
         if (softmax && v.CBW < pl->cb_total) continue;
         if (softmax && v.CBW >= 2 * pl->cb_total) continue;  // keep only the tightest fit
         for (int WCO = 1; WCO <= 4; WCO *= 2) {
@@ -306,8 +308,11 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                                     // MAC-equivalents: issued MFMA work, ~24 per staged element
                                     // (address arithmetic, load, LDS store), ~64 per output of
                                     // the epilogue
-                                    const double cost = (double)issued + 24.0 * (double)staged +
-                                                        (double)wgs * CO_T * 32 * PT * v.NPH * 64.0;
+                                    double cost = (double)issued + 24.0 * (double)staged +
+                                                  (double)wgs * CO_T * 32 * PT * v.NPH * 64.0;
+                                    // rows that break inside a 32-position block split its
+                                    // stores into more memory segments
+                                    if (32 % TQw != 0 && TQw % 32 != 0) cost *= 1.05;
                                     if (cost < bestr.cost) {
                                         bestr.cost = cost;
                                         bestr.box[0] = TQd; bestr.box[1] = TQh; bestr.box[2] = TQw;
@@ -364,6 +369,9 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
             // (measured on MI355X: 3 workgroups per CU reach ~67% MFMA busy, 2 ~60%)
             cost *= per_cu == 1 ? 1.35 : per_cu == 2 ? 1.15 : per_cu == 3 ? 1.04 : 1.0;
             cost *= 1.0 + 0.15 / (v.CBW * v.PBW * v.NPH);
+            // measured: splitting the output channels over fewer waves (WCO < 4)
+            // costs MFMA issue rate when the channels could fill four waves
+            if (!softmax && WCO < 4 && pl->cb_total >= 4) cost *= WCO == 2 ? 1.1 : 1.2;
             if (cost < best) {
                 best = cost;
                 found = true;
