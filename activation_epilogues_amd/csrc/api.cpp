@@ -19,7 +19,7 @@ namespace {
 struct CacheKey {
     convt3d_geom g;
     int kind, groups;
-    char plan_env[64];  // CONVT3D_PLAN tile override, if any
+    char plan_env[64];  // CONVT3D_PLAN tile override and CONVT3D_PHASE_LOOP, if any
     bool operator==(const CacheKey &o) const {
         return std::memcmp(&g, &o.g, sizeof(g)) == 0 && kind == o.kind && groups == o.groups &&
                std::strncmp(plan_env, o.plan_env, sizeof(plan_env)) == 0;
@@ -36,7 +36,11 @@ int cached_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *out) {
     key.g = *g;
     key.kind = e->kind;
     key.groups = e->kind == CONVT3D_EPI_RELU_GROUPNORM ? e->groups : 0;
-    if (const char *env = std::getenv("CONVT3D_PLAN")) std::strncpy(key.plan_env, env, sizeof(key.plan_env) - 1);
+    if (const char *env = std::getenv("CONVT3D_PLAN")) std::strncpy(key.plan_env, env, 48);
+    if (const char *env = std::getenv("CONVT3D_PHASE_LOOP")) {
+        key.plan_env[60] = '|';
+        key.plan_env[61] = env[0];
+    }
     {
         std::lock_guard<std::mutex> lk(g_mu);
         for (auto it = g_cache.begin(); it != g_cache.end(); ++it)
@@ -181,6 +185,7 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
     info->workgroups = pl.grid_x * pl.grid_y * pl.grid_z;
     info->issued_macs = pl.issued_macs;
     info->valid_macs = pl.valid_macs;
+    info->phase_loop = pl.phase_loop;
     return CONVT3D_OK;
 }
 

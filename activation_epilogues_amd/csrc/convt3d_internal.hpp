@@ -51,6 +51,8 @@ struct ConvParams {
     int nwgroups;         // w-phase groups per (rho_d, rho_h): s / NPH
     int HWp;              // LDS row pitch (floats)
     int CISTR;            // LDS stride between staged input channels (floats)
+    int phase_loop;       // 1: each workgroup loops over all (rho_d, rho_h) groups
+    int red_off;          // LDS float offset of the epilogue's reduction scratch
     int epi;
     float scale;
     int tiles_per_n;
@@ -84,6 +86,7 @@ struct Plan {
     int CI_T = 8, nchunks = 1;
     int HWp = 1, CISTR = 1, lds_bytes = 0;
     int co_tiles = 1, nwgroups = 1;
+    int phase_loop = 0, red_off = 0;
     int64_t tiles_per_n = 0;
     int64_t grid_x = 0, grid_y = 0, grid_z = 0;
     int64_t issued_macs = 0, valid_macs = 0;
@@ -96,6 +99,7 @@ struct Variant {
     int CBW, NPH, PBW;
     bool softmax;        // compiled with the softmax epilogue (else NONE / GN / BN)
     int waves_per_simd;  // register-limited occupancy of the compiled kernel
+    bool phase_loop;     // also compiled with the (rho_d, rho_h) phase-group loop
 };
 extern const Variant kVariants[];
 extern const int kNumVariants;

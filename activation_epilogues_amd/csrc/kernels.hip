@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // for each of its NPH w-phases.  Input channels are consumed in chunks of CI_T:
 // the input halo of the box for those channels is staged in LDS, then every
 // live tap of every phase runs 4 MFMA k-steps per 8 input channels.
-template <int CBW, int NPH, int PBW, bool SM>
+template <int CBW, int NPH, int PBW, bool SM, bool PL>
 __global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
                                           : (CBW * NPH * PBW <= 2) ? 4 : (CBW * NPH * PBW <= 4) ? 3
                                           : (CBW * NPH * PBW <= 8) ? 2 : 1)
@@ -124,16 +124,31 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int wgrp = by % P.nwgroups;
     by /= P.nwgroups;
     const int s = P.s;
-    const int rho_h = by % s;
-    const int rho_d = by / s;
     const int n = blockIdx.z;
 
     const int TQd = RG[6], TQh = RG[7], TQw = RG[8];
     const int q0d = RG[0] + td_i * TQd, q0h = RG[1] + th_i * TQh, q0w = RG[2] + tw_i * TQw;
     // extent of this tile inside its region (the box may overhang the region end)
     const int TQd_e = min(TQd, RG[3] - q0d), TQh_e = min(TQh, RG[4] - q0h), TQw_e = min(TQw, RG[5] - q0w);
-    const int Jd = P.pJ[0][rho_d], cd = P.pc[0][rho_d];
-    const int Jh = P.pJ[1][rho_h], ch = P.pc[1][rho_h];
+
+    // (rho_d, rho_h) phase groups of this workgroup: one (from the grid), or all
+    // s*s of them over one staged halo when the whole channel range fits in
+    // one LDS chunk.  The staged box is the union of the groups' footprints.
+    constexpr bool ploop = PL;  // == (P.phase_loop != 0): the launcher picks the instantiation
+    const int npg = ploop ? s * s : 1;
+    const int pg0 = ploop ? 0 : by;
+    int lo_d_rel = 0, lo_h_rel = 0, HD = TQd, HH = TQh;
+    {
+        int dlo = INT_MAX, dhi = INT_MIN, hlo = INT_MAX, hhi = INT_MIN;
+        for (int g = pg0; g < pg0 + npg; ++g) {
+            const int rd = g / s, rh = g % s;
+            const int Jd_ = P.pJ[0][rd], cd_ = P.pc[0][rd], Jh_ = P.pJ[1][rh], ch_ = P.pc[1][rh];
+            if (Jd_ > 0) { dlo = min(dlo, cd_ - Jd_ + 1); dhi = max(dhi, TQd - 1 + cd_); }
+            if (Jh_ > 0) { hlo = min(hlo, ch_ - Jh_ + 1); hhi = max(hhi, TQh - 1 + ch_); }
+        }
+        if (dlo <= dhi) { lo_d_rel = dlo; HD = dhi - dlo + 1; }
+        if (hlo <= hhi) { lo_h_rel = hlo; HH = hhi - hlo + 1; }
+    }
     int Jw[NPH], cw[NPH], rw[NPH];
     int lo_w_rel = INT_MAX, hi_w_rel = INT_MIN;
 #pragma unroll
@@ -146,22 +161,16 @@ void convt3d_mfma_kernel(const ConvParams P) {
             hi_w_rel = max(hi_w_rel, TQw - 1 + cw[p]);
         }
     }
-    const bool any_taps = Jd > 0 && Jh > 0 && lo_w_rel <= hi_w_rel;
+    const bool w_taps = lo_w_rel <= hi_w_rel;
 
     // ---- halo box in input coordinates
-    const int HD = TQd + (Jd > 0 ? Jd : 1) - 1;
-    const int HH = TQh + (Jh > 0 ? Jh : 1) - 1;
-    const int HW = any_taps ? hi_w_rel - lo_w_rel + 1 : TQw;
-    const int lo_d = q0d + cd - Jd + 1;
-    const int lo_h = q0h + ch - Jh + 1;
+    const int HW = w_taps ? hi_w_rel - lo_w_rel + 1 : TQw;
+    const int lo_d = q0d + lo_d_rel;
+    const int lo_h = q0h + lo_h_rel;
     const int lo_w = q0w + lo_w_rel;
     const int HWp = HW;  // compact rows
     const int CISTR = P.CISTR;
     const int ROW = HH * HWp;
-
-    // ---- taps that touch the input for this box (border tiles skip the rest)
-    const int jd_lo = max(0, q0d + cd - (P.D - 1)), jd_hi = min(Jd - 1, q0d + TQd_e - 1 + cd);
-    const int jh_lo = max(0, q0h + ch - (P.H - 1)), jh_hi = min(Jh - 1, q0h + TQh_e - 1 + ch);
     int jw_lo[NPH], jw_hi[NPH];
 #pragma unroll
     for (int p = 0; p < NPH; ++p) {
@@ -192,6 +201,55 @@ void convt3d_mfma_kernel(const ConvParams P) {
 
     const int CO_T = P.WCO * CBW;                   // co blocks per workgroup
     const int cb0 = co_tile * CO_T + wco * CBW;     // first co block of this wave
+    const float4 *wp4 = reinterpret_cast<const float4 *>(P.wp);
+    const int G4 = P.CI_T >> 3;
+    const int nthreads = blockDim.x;
+    const size_t HWin = (size_t)P.H * P.W;
+    const float *xn = P.x + (size_t)n * P.Cin * P.D * HWin;
+    // digits of tid and of nthreads in the radix (CI_T, HD, HH, HW)
+    const int st_total = P.CI_T * HD * HH * HW;
+    const int st_hw = tid % HW, st_hh = (tid / HW) % HH, st_hd = (tid / (HW * HH)) % HD,
+              st_cl = tid / (HW * HH * HD);
+    const int inc_hw = nthreads % HW, inc_hh = (nthreads / HW) % HH, inc_hd = (nthreads / (HW * HH)) % HD,
+              inc_cl = nthreads / (HW * HH * HD);
+    // ---- stage the input halo of CI_T channels: thread t covers flat elements
+    // t, t + nthreads, ...; the (cl, hd, hh, hw) digits advance by the
+    // mixed-radix digits of nthreads, so no division in the loop.
+    auto stage = [&](int chunk) {
+        const int ci0 = chunk * P.CI_T;
+        int hw = st_hw, hh = st_hh, hd = st_hd, cl = st_cl;
+#pragma unroll 4
+        for (int e = tid; e < st_total; e += nthreads) {
+            const int ci = ci0 + cl;
+            const int id = lo_d + hd, ih = lo_h + hh, iw = lo_w + hw;
+            float v = 0.0f;
+            if (ci < P.Cin && (unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H &&
+                (unsigned)iw < (unsigned)P.W)
+                v = xn[((size_t)ci * P.D + id) * HWin + (size_t)ih * P.W + iw];
+            lds[cl * CISTR + (hd * HH + hh) * HWp + hw] = v;
+            hw += inc_hw;
+            if (hw >= HW) { hw -= HW; ++hh; }
+            hh += inc_hh;
+            if (hh >= HH) { hh -= HH; ++hd; }
+            hd += inc_hd;
+            if (hd >= HD) { hd -= HD; ++cl; }
+            cl += inc_cl;
+        }
+    };
+    if constexpr (PL) {  // one chunk (planner guarantee), staged once for every phase group
+        stage(0);
+        __syncthreads();
+    }
+
+  for (int pgi = 0; pgi < npg; ++pgi) {
+    const int pg = pg0 + pgi;
+    const int rho_h = pg % s;
+    const int rho_d = pg / s;
+    const int Jd = P.pJ[0][rho_d], cd = P.pc[0][rho_d];
+    const int Jh = P.pJ[1][rho_h], ch = P.pc[1][rho_h];
+    // ---- taps that touch the input for this box (border tiles skip the rest)
+    const int jd_lo = max(0, q0d + cd - (P.D - 1)), jd_hi = min(Jd - 1, q0d + TQd_e - 1 + cd);
+    const int jh_lo = max(0, q0h + ch - (P.H - 1)), jh_hi = min(Jh - 1, q0h + TQh_e - 1 + ch);
 
     v16f acc[NPH][CBW][PBW];
 #pragma unroll
@@ -203,7 +261,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[p][c][pb][r] = 0.0f;
 
-    bool work = any_taps && jd_lo <= jd_hi && jh_lo <= jh_hi;
+    bool work = Jd > 0 && Jh > 0 && w_taps && jd_lo <= jd_hi && jh_lo <= jh_hi;
     {
         bool anyw = false;
 #pragma unroll
@@ -211,44 +269,12 @@ void convt3d_mfma_kernel(const ConvParams P) {
         work = work && anyw;
     }
     if (work) {
-        const float4 *wp4 = reinterpret_cast<const float4 *>(P.wp);
-        const int G4 = P.CI_T >> 3;
-        const int nthreads = blockDim.x;
-        const size_t HWin = (size_t)P.H * P.W;
-        const float *xn = P.x + (size_t)n * P.Cin * P.D * HWin;
-        // digits of tid and of nthreads in the radix (CI_T, HD, HH, HW)
-        const int st_total = P.CI_T * HD * HH * HW;
-        const int st_hw = tid % HW, st_hh = (tid / HW) % HH, st_hd = (tid / (HW * HH)) % HD,
-                  st_cl = tid / (HW * HH * HD);
-        const int inc_hw = nthreads % HW, inc_hh = (nthreads / HW) % HH, inc_hd = (nthreads / (HW * HH)) % HD,
-                  inc_cl = nthreads / (HW * HH * HD);
         for (int chunk = 0; chunk < P.nchunks; ++chunk) {
+          if constexpr (!PL) {
             __syncthreads();
-            // ---- stage the input halo of CI_T channels: thread t covers flat
-            // elements t, t + nthreads, ...; the (cl, hd, hh, hw) digits advance by
-            // the mixed-radix digits of nthreads, so no division in the loop.
-            {
-                const int ci0 = chunk * P.CI_T;
-                int hw = st_hw, hh = st_hh, hd = st_hd, cl = st_cl;
-#pragma unroll 4
-                for (int e = tid; e < st_total; e += nthreads) {
-                    const int ci = ci0 + cl;
-                    const int id = lo_d + hd, ih = lo_h + hh, iw = lo_w + hw;
-                    float v = 0.0f;
-                    if (ci < P.Cin && (unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H &&
-                        (unsigned)iw < (unsigned)P.W)
-                        v = xn[((size_t)ci * P.D + id) * HWin + (size_t)ih * P.W + iw];
-                    lds[cl * CISTR + (hd * HH + hh) * HWp + hw] = v;
-                    hw += inc_hw;
-                    if (hw >= HW) { hw -= HW; ++hh; }
-                    hh += inc_hh;
-                    if (hh >= HH) { hh -= HH; ++hd; }
-                    hd += inc_hd;
-                    if (hd >= HD) { hd -= HD; ++cl; }
-                    cl += inc_cl;
-                }
-            }
+            stage(chunk);
             __syncthreads();
+          }
 #pragma unroll
             for (int p = 0; p < NPH; ++p) {
                 if (Jw[p] == 0 || jw_lo[p] > jw_hi[p]) continue;
@@ -267,7 +293,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 int jd = jd_lo, jh = jh_lo, jw = jwl, g4 = 0;
                 auto next_group = [&](int &gi, int &bo) {
                     gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
-                    bo = (Jd - 1 - jd) * ROW + (Jh - 1 - jh) * HWp + (cwp - jw - lo_w_rel) + 8 * g4 * CISTR;
+                    bo = (cd - jd - lo_d_rel) * ROW + (ch - jh - lo_h_rel) * HWp + (cwp - jw - lo_w_rel) +
+                         8 * g4 * CISTR;
                     if (++g4 == G4) {
                         g4 = 0;
                         if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } }
@@ -350,6 +377,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
             pair_ok[pb] = ok[0][pb] && ok[1][pb] && (Wo % 2 == 0);  // rw[0] is even when NPH == 2
     }
     const int Cout = P.Cout;
+    // first output channel of the lane's accumulator rows; inside the phase-group
+    // loop it is made opaque so the per-row channel indices and store addresses
+    // are formed here, not hoisted out of the loop and kept live across the MFMAs
+    int co_lane = cb0 * 32 + 4 * half;
+    if constexpr (PL) asm volatile("" : "+v"(co_lane));
     const float *bias = P.bias;
     float *outn = P.out + (size_t)n * Cout * S;
 
@@ -361,7 +393,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int co = co_lane + c * 32 + 8 * (r >> 2) + (r & 3);
                 const float bco = (co < Cout) ? (bias ? bias[co] : 0.0f) : -INFINITY;
 #pragma unroll
                 for (int p = 0; p < NPH; ++p)
@@ -409,7 +441,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
             for (int c = 0; c < CBW; ++c)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const int co = co_lane + c * 32 + 8 * (r >> 2) + (r & 3);
                     if (co >= Cout) continue;
                     float *dst = outn + (size_t)co * S;
                     if constexpr (NPH == 2) {
@@ -431,13 +463,13 @@ void convt3d_mfma_kernel(const ConvParams P) {
         const bool bn = P.epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
         const float scale = P.scale;
         const int CO32 = CO_T * 32;
-        float *red = lds;  // [WPOS][CO_T*32][2], reuses the halo LDS
-        if (gn || bn) __syncthreads();  // every wave is done with the halo LDS
+        float *red = lds + P.red_off;  // [WPOS][CO_T*32][2], after the halo
+        if (gn || bn) __syncthreads();  // the previous phase group's readers are done
 #pragma unroll
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = (cb0 + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const int co = co_lane + c * 32 + 8 * (r >> 2) + (r & 3);
                 const bool cok = co < Cout;
                 const float bco = (cok && bias) ? bias[co] : 0.0f;
                 float a1 = 0.0f, a2 = 0.0f;
@@ -479,22 +511,24 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     }
                 }
             }
-        if (!(gn || bn)) return;
-        __syncthreads();
-        const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + (int)blockIdx.x;
-        for (int row = tid; row < CO32; row += blockDim.x) {
-            const int co = co_tile * CO32 + row;
-            if (co >= Cout) continue;
-            float t1 = 0.0f, t2 = 0.0f;
-            for (int w = 0; w < P.WPOS; ++w) {
-                t1 += red[(w * CO32 + row) * 2 + 0];
-                t2 += red[(w * CO32 + row) * 2 + 1];
+        if (gn || bn) {
+            __syncthreads();
+            const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + (int)blockIdx.x;
+            for (int row = tid; row < CO32; row += blockDim.x) {
+                const int co = co_tile * CO32 + row;
+                if (co >= Cout) continue;
+                float t1 = 0.0f, t2 = 0.0f;
+                for (int w = 0; w < P.WPOS; ++w) {
+                    t1 += red[(w * CO32 + row) * 2 + 0];
+                    t2 += red[(w * CO32 + row) * 2 + 1];
+                }
+                float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * Cout + co) * 2;
+                pp[0] = t1;
+                pp[1] = t2;
             }
-            float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * Cout + co) * 2;
-            pp[0] = t1;
-            pp[1] = t2;
         }
     }
+  }  // phase groups
 }
 
 // ---------------------------------------------------------------------------
@@ -653,9 +687,9 @@ int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream) {
     return (int)hipGetLastError();
 }
 
-template <int CBW, int NPH, int PBW, bool SM>
+template <int CBW, int NPH, int PBW, bool SM, bool PL>
 static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
-    auto fn = convt3d_mfma_kernel<CBW, NPH, PBW, SM>;
+    auto fn = convt3d_mfma_kernel<CBW, NPH, PBW, SM, PL>;
     static bool attr_set = false;
     if (!attr_set) {
         hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -669,8 +703,13 @@ static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
 
 int launch_conv(const Plan &pl, const ConvParams &cp, void *stream) {
     const Variant v = kVariants[pl.variant];
+    const bool pl_ = pl.phase_loop != 0;
 #define CONVT3D_VARIANT(a, b, c, d) \
-    if (v.CBW == a && v.NPH == b && v.PBW == c && v.softmax == d) return launch_conv_t<a, b, c, d>(pl, cp, stream);
+    if (v.CBW == a && v.NPH == b && v.PBW == c && v.softmax == d && !pl_) \
+        return launch_conv_t<a, b, c, d, false>(pl, cp, stream);
+#define CONVT3D_VARIANT_PL(a, b, c, d) \
+    if (v.CBW == a && v.NPH == b && v.PBW == c && v.softmax == d && pl_) \
+        return launch_conv_t<a, b, c, d, true>(pl, cp, stream);
     CONVT3D_VARIANT(1, 1, 8, false)
     CONVT3D_VARIANT(1, 1, 4, false)
     CONVT3D_VARIANT(1, 1, 2, false)
@@ -686,7 +725,19 @@ int launch_conv(const Plan &pl, const ConvParams &cp, void *stream) {
     CONVT3D_VARIANT(4, 1, 2, true)
     CONVT3D_VARIANT(4, 2, 1, true)
     CONVT3D_VARIANT(4, 1, 1, true)
+    // phase-group loop instantiations (stride > 1, one channel chunk)
+    CONVT3D_VARIANT_PL(1, 1, 4, false)
+    CONVT3D_VARIANT_PL(1, 2, 2, false)
+    CONVT3D_VARIANT_PL(1, 2, 4, false)
+    CONVT3D_VARIANT_PL(1, 1, 2, true)
+    CONVT3D_VARIANT_PL(1, 2, 2, true)
+    CONVT3D_VARIANT_PL(2, 2, 2, true)
+    CONVT3D_VARIANT_PL(2, 2, 1, true)
+    CONVT3D_VARIANT_PL(2, 1, 2, true)
+    CONVT3D_VARIANT_PL(4, 2, 1, true)
+    CONVT3D_VARIANT_PL(4, 1, 1, true)
 #undef CONVT3D_VARIANT
+#undef CONVT3D_VARIANT_PL
     return (int)hipErrorInvalidValue;
 }
 

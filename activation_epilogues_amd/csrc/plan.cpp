@@ -23,14 +23,16 @@ namespace convt3d {
 // Kernel variants compiled into the library (co-blocks per wave, w-phases per
 // wave, position blocks per wave).  Keep in sync with the instantiations in
 // kernels.hip.
-// The last field is the waves per SIMD the compiled kernel's register count
-// allows (used only by the cost model).
+// waves_per_simd is the occupancy the compiled kernel's register count allows
+// (used only by the cost model; the phase-loop build of a variant has the
+// same occupancy as the plain one).
 const Variant kVariants[] = {
-    {1, 1, 8, false, 2}, {1, 1, 4, false, 4}, {1, 1, 2, false, 7},
-    {1, 2, 4, false, 2}, {1, 2, 2, false, 4},
-    {1, 1, 4, true, 4}, {1, 1, 2, true, 6}, {1, 2, 2, true, 4},
-    {2, 1, 4, true, 2}, {2, 2, 2, true, 2}, {2, 1, 2, true, 3}, {2, 2, 1, true, 3},
-    {4, 1, 2, true, 1}, {4, 2, 1, true, 1}, {4, 1, 1, true, 2},
+    {1, 1, 8, false, 2, false}, {1, 1, 4, false, 4, true},  {1, 1, 2, false, 7, false},
+    {1, 2, 4, false, 2, true},  {1, 2, 2, false, 4, true},
+    {1, 1, 4, true, 4, false},  {1, 1, 2, true, 6, true},   {1, 2, 2, true, 4, true},
+    {2, 1, 4, true, 2, false},  {2, 2, 2, true, 2, true},   {2, 1, 2, true, 3, true},
+    {2, 2, 1, true, 3, true},
+    {4, 1, 2, true, 1, false},  {4, 2, 1, true, 1, true},   {4, 1, 1, true, 2, true},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -197,6 +199,9 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
         if (got < 6) force[0] = -1;
     }
     const bool forced = force[0] >= 0;
+    // CONVT3D_PHASE_LOOP=0|1 restricts the phase-group loop choice (tests, sweeps)
+    int ploop_only = -1;
+    if (const char *env = std::getenv("CONVT3D_PHASE_LOOP")) ploop_only = std::atoi(env) ? 1 : 0;
     const int64_t nn = std::max(g->n, 1);  // plan an empty batch like n = 1
     const int CI_pad = pl->octets * kOctet;
 
@@ -215,7 +220,13 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
           if (forced && WCO != force[1]) continue;
           // which dims are split into border / interior segments
           for (int split = 0; split < 8; ++split) {
+           // ploop: one workgroup loops over every (rho_d, rho_h) group on one staged
+           // halo (needs the whole channel range in one LDS chunk)
+           for (int ploop = 0; ploop < (s > 1 ? 2 : 1); ++ploop) {
             if (forced && force[6] >= 0 && split != force[6]) continue;
+            if (ploop_only >= 0 && ploop != ploop_only) continue;
+            if (ploop && !v.phase_loop) continue;
+            const int npg = ploop ? s * s : 1;
             Seg segs[3][3];
             int nseg[3];
             bool redundant = false;
@@ -278,13 +289,24 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                                         (TQd != force[2] || TQh != force[3] || TQw != force[4]))
                                         continue;
                                     int HD = 1, HH = 1, HW = TQw;
-                                    for (int rho = 0; rho < s; ++rho) {
-                                        HD = std::max(HD, TQd + std::max(pl->ph[0][rho].J, 1) - 1);
-                                        HH = std::max(HH, TQh + std::max(pl->ph[1][rho].J, 1) - 1);
+                                    if (ploop) {  // union of the groups' footprints
+                                        int dlo = INT_MAX, dhi = INT_MIN, hlo = INT_MAX, hhi = INT_MIN;
+                                        for (int rho = 0; rho < s; ++rho) {
+                                            const DimPhase &a = pl->ph[0][rho], &b = pl->ph[1][rho];
+                                            if (a.J) { dlo = std::min(dlo, a.c - a.J + 1); dhi = std::max(dhi, TQd - 1 + a.c); }
+                                            if (b.J) { hlo = std::min(hlo, b.c - b.J + 1); hhi = std::max(hhi, TQh - 1 + b.c); }
+                                        }
+                                        HD = dlo <= dhi ? dhi - dlo + 1 : TQd;
+                                        HH = hlo <= hhi ? hhi - hlo + 1 : TQh;
+                                    } else {
+                                        for (int rho = 0; rho < s; ++rho) {
+                                            HD = std::max(HD, TQd + std::max(pl->ph[0][rho].J, 1) - 1);
+                                            HH = std::max(HH, TQh + std::max(pl->ph[1][rho].J, 1) - 1);
+                                        }
                                     }
                                     for (int wg = 0; wg < nwg; ++wg) HW = std::max(HW, halo_w(TQw, wg));
                                     const int slab = HD * HH * HW;
-                                    if ((int64_t)kOctet * slab * 4 > kMaxLdsBytes) continue;
+                                    if ((int64_t)(ploop ? CI_pad : kOctet) * slab * 4 > kMaxLdsBytes) continue;
                                     const int nt[3] = {(int)ceil_div(ext[0], TQd), (int)ceil_div(ext[1], TQh),
                                                        (int)ceil_div(ext[2], TQw)};
                                     const int64_t tiles = (int64_t)nt[0] * nt[1] * nt[2];
@@ -296,7 +318,7 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                                             int64_t lw = 0;
                                             for (int rw = 0; rw < s; ++rw) lw += seg_live(2, rw, sw, TQw);
                                             taps += ld * lh * lw;
-                                            if (pl->ph[0][rd].J == 0 || pl->ph[1][rh].J == 0) continue;
+                                            if (ploop || pl->ph[0][rd].J == 0 || pl->ph[1][rh].J == 0) continue;
                                             for (int wg = 0; wg < nwg; ++wg)
                                                 halo += (int64_t)(TQd + pl->ph[0][rd].J - 1) *
                                                         (TQh + pl->ph[1][rh].J - 1) * halo_w(TQw, wg);
@@ -304,6 +326,8 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                                     }
                                     const int64_t issued = nn * co_tiles * CO_T * 32 * (int64_t)PT * CI_pad * taps;
                                     const int64_t staged = nn * co_tiles * tiles * CI_pad * halo;
+                                    if (ploop)
+                                        for (int wg = 0; wg < nwg; ++wg) halo += (int64_t)HD * HH * halo_w(TQw, wg);
                                     const int64_t wgs = nn * co_tiles * s * s * nwg * tiles;
                                     // MAC-equivalents: issued MFMA work, ~24 per staged element
                                     // (address arithmetic, load, LDS store), ~64 per output of
@@ -349,6 +373,7 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                 CI_T = m * kOctet;
                 break;
             }
+            if (ploop) CI_T = (int64_t)CI_pad * max_slab * 4 <= kMaxLdsBytes ? CI_pad : 0;
             if (forced && force[5] > 0) {
                 if (force[5] % kOctet || pl->octets % (force[5] / kOctet) ||
                     (int64_t)force[5] * max_slab * 4 > kMaxLdsBytes)
@@ -356,10 +381,11 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                 CI_T = force[5];
             }
             if (CI_T == 0) continue;
-            const int64_t grid = nn * co_tiles * s * s * nwg * tiles_total;
+            const int64_t grid = nn * co_tiles * (s * s / npg) * nwg * tiles_total;
             // whole rounds of workgroups over the CUs; workgroups per CU from the
             // variant's register occupancy and the LDS size
-            const int lds_wg = std::max(CI_T * max_slab * 4, 1);
+            const int red_floats = WPOS * CO_T * 32 * 2;
+            const int lds_wg = std::max((CI_T * max_slab + red_floats) * 4, 1);
             const int per_cu = std::max(1, std::min(v.waves_per_simd, 160 * 1024 / lds_wg));
             const double slots = 256.0 * per_cu;
             const double rounds = std::ceil((double)grid / slots);
@@ -401,22 +427,22 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                 c.CI_T = CI_T; c.nchunks = (int)ceil_div(CI_pad, CI_T);
                 c.HWp = 0;  // per-tile (compact rows)
                 c.CISTR = max_slab;
-                c.lds_bytes = CI_T * max_slab * 4;
+                c.phase_loop = ploop;
+                c.red_off = CI_T * max_slab;
+                c.lds_bytes = lds_wg;
                 c.co_tiles = co_tiles; c.nwgroups = nwg;
                 c.tiles_per_n = (int64_t)s * s * nwg * tiles_total;
                 c.grid_x = tiles_total;
-                c.grid_y = (int64_t)co_tiles * s * s * nwg;
+                c.grid_y = (int64_t)co_tiles * (s * s / npg) * nwg;
                 c.grid_z = g->n;
                 c.issued_macs = issued / nn * g->n;
                 bestp = c;
             }
+           }
           }
         }
     }
     if (!found) return CONVT3D_ERR_UNSUPPORTED;
-    // the reduction scratch of the epilogue reuses the halo LDS
-    const int red = bestp.WPOS * bestp.WCO * bestp.CBW * 32 * 2 * 4;
-    bestp.lds_bytes = std::max(bestp.lds_bytes, red);
     if (bestp.grid_x > INT32_MAX || bestp.grid_y > 65535 || bestp.grid_z > 65535)
         return CONVT3D_ERR_TOO_LARGE;
     *pl = bestp;
@@ -442,6 +468,7 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->WCO = pl.WCO; cp->WPOS = pl.WPOS;
     cp->co_tiles = pl.co_tiles; cp->nwgroups = pl.nwgroups;
     cp->HWp = pl.HWp; cp->CISTR = pl.CISTR;
+    cp->phase_loop = pl.phase_loop; cp->red_off = pl.red_off;
     cp->epi = pl.e.kind;
     cp->scale = pl.e.kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL ? pl.e.scale : 1.0f;
     cp->tiles_per_n = (int)pl.tiles_per_n;

@@ -96,3 +96,22 @@ def test_run_twice_is_bitwise_identical():
     a, sa, _ = run_gpu(wl, inp)
     b, sb, _ = run_gpu(wl, inp)
     assert np.array_equal(a, b) and np.array_equal(sa, sb)
+
+
+@pytest.mark.parametrize("epi", [W.EPI_NONE, W.EPI_RELU_GROUPNORM, W.EPI_SOFTMAX_SIGMOID,
+                                 W.EPI_SCALE_BN_TRAIN_AVGPOOL])
+def test_phase_group_loop(epi, monkeypatch):
+    """Workgroups that loop over every (d, h) stride phase on one staged halo."""
+    monkeypatch.setenv("CONVT3D_PHASE_LOOP", "1")
+    from activation_epilogues_amd import convt3d as C
+    rng = np.random.default_rng(500 + epi)
+    done = 0
+    while done < 4:
+        wl = W.random_geometry(rng, max_in=8, max_ch=20, epi=epi)
+        if wl.stride == 1 or min(oracle.out_dims(wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)) <= 0:
+            continue
+        g = C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)
+        info = C.convt3d_get_plan_info(g, C.make_epilogue(epi, wl.groups, wl.eps, wl.scale))
+        assert info["phase_loop"] == 1
+        check(wl, epi, tag="phase-loop")
+        done += 1
