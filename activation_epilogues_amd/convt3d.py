@@ -43,7 +43,7 @@ class PlanInfo(ctypes.Structure):
                 ("tile_q", ctypes.c_int32 * 3), ("ci_chunk", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("workgroups", ctypes.c_int64),
                 ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64),
-                ("phase_loop", ctypes.c_int32)]
+                ("phase_loop", ctypes.c_int32), ("halo_buffers", ctypes.c_int32)]
 
 
 class Profile(ctypes.Structure):

@@ -186,6 +186,7 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
     info->issued_macs = pl.issued_macs;
     info->valid_macs = pl.valid_macs;
     info->phase_loop = pl.phase_loop;
+    info->halo_buffers = pl.nbuf;
     return CONVT3D_OK;
 }
 

@@ -15,6 +15,7 @@ constexpr int kOctet = 8;          // input channels per packed weight group (4 
 constexpr int kMaxRegions = 27;    // tiling regions: (low border, interior, high border)^3
 constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
 constexpr int kMaxLdsBytes = 80 * 1024;  // at least two workgroups per CU
+constexpr int kNumXcd = 8;               // MI355X: 8 XCDs (256 CUs), one L2 each
 
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
 // taps that reach it are k = r + s*j (j = 0..J-1) from input i = q + c - j.
@@ -49,8 +50,9 @@ struct ConvParams {
     int WCO, WPOS;        // wave grid
     int co_tiles;
     int nwgroups;         // w-phase groups per (rho_d, rho_h): s / NPH
-    int HWp;              // LDS row pitch (floats)
-    int CISTR;            // LDS stride between staged input channels (floats)
+    int buf_stride;       // LDS floats per input-halo buffer (multiple of 256)
+    int nbuf;             // 2: chunk c + 1 is staged while chunk c is multiplied
+    int nxcd;             // XCDs the workgroups are dealt over round-robin
     int phase_loop;       // 1: each workgroup loops over all (rho_d, rho_h) groups
     int red_off;          // LDS float offset of the epilogue's reduction scratch
     int epi;
@@ -84,7 +86,7 @@ struct Plan {
     int rg_off[kMaxRegions + 1]{};
     int tiles_total = 0;
     int CI_T = 8, nchunks = 1;
-    int HWp = 1, CISTR = 1, lds_bytes = 0;
+    int buf_stride = 0, nbuf = 1, lds_bytes = 0;
     int co_tiles = 1, nwgroups = 1;
     int phase_loop = 0, red_off = 0;
     int64_t tiles_per_n = 0;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // live tap of every phase runs 4 MFMA k-steps per 8 input channels.
 template <int CBW, int NPH, int PBW, bool SM, bool PL>
 __global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
-                                          : (CBW * NPH * PBW <= 2) ? 4 : (CBW * NPH * PBW <= 4) ? 3
+                                          : (CBW * NPH * PBW <= 2) ? 6 : (CBW * NPH * PBW <= 4) ? 3
                                           : (CBW * NPH * PBW <= 8) ? 2 : 1)
 void convt3d_mfma_kernel(const ConvParams P) {
     extern __shared__ float lds[];
@@ -105,12 +105,29 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int col = lane & 31;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
     const int wco = wave % P.WCO;
     const int wpos = wave / P.WCO;
 
-    // ---- workgroup -> tile: find the region, then the tile inside it
-    const int bx = blockIdx.x;
+    // ---- workgroup -> work item.  Workgroups are handed to the XCDs round-robin
+    // (dispatch index i runs on XCD i % nxcd), each XCD with its own L2.  The
+    // dispatch index is mapped to a linear work index so that every XCD gets
+    // one contiguous range, in which the (co tile, phase) index varies fastest
+    // (those workgroups read the same input box), then the tile, then n: the
+    // halo overlap of neighbouring tiles then hits in one L2.
+    int bx, by, n;
+    {
+        const int gx = gridDim.x, gy = gridDim.y;
+        const int total = gx * gy * gridDim.z;
+        const int bid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+        const int nx = P.nxcd, q = total / nx, r = total % nx;
+        const int xcd = bid % nx, idx = bid / nx;
+        const int lin = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+        by = lin % gy;
+        bx = (lin / gy) % gx;
+        n = lin / (gx * gy);
+    }
+    // ---- tile: find the region, then the tile inside it
     int reg = 0;
     while (reg + 1 < P.nreg && bx >= P.rg_off[reg + 1]) ++reg;
     const int *RG = P.rg[reg];
@@ -118,13 +135,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int tw_i = local % RG[11];
     const int th_i = (local / RG[11]) % RG[10];
     const int td_i = local / (RG[11] * RG[10]);
-    int by = blockIdx.y;
     const int co_tile = by % P.co_tiles;
     by /= P.co_tiles;
     const int wgrp = by % P.nwgroups;
     by /= P.nwgroups;
     const int s = P.s;
-    const int n = blockIdx.z;
 
     const int TQd = RG[6], TQh = RG[7], TQw = RG[8];
     const int q0d = RG[0] + td_i * TQd, q0h = RG[1] + th_i * TQh, q0w = RG[2] + tw_i * TQw;
@@ -168,8 +183,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int lo_d = q0d + lo_d_rel;
     const int lo_h = q0h + lo_h_rel;
     const int lo_w = q0w + lo_w_rel;
-    const int HWp = HW;  // compact rows
-    const int CISTR = P.CISTR;
+    const int HWp = HW;            // compact rows
+    const int CISTR = HD * HH * HW;  // channel stride: the staged elements are dense
     const int ROW = HH * HWp;
     int jw_lo[NPH], jw_hi[NPH];
 #pragma unroll
@@ -181,21 +196,25 @@ void convt3d_mfma_kernel(const ConvParams P) {
     // ---- per-lane position decode (B operand base offsets)
     const int vol = TQd * TQh * TQw;
     const int plane = TQh * TQw;
+    // The tile position of a lane's column in position block pb; decoded again
+    // where it is needed (from an opaque copy of the lane's column index, so
+    // the decode is not hoisted and kept live across the MFMA loop).
+    auto decode_pos = [&](int pb, int &td, int &th, int &tw) -> bool {
+        int c = col;
+        asm volatile("" : "+v"(c));
+        const int pidx = (wpos * PBW + pb) * 32 + c;
+        const int pi = pidx < vol ? pidx : 0;
+        td = pi / plane;
+        const int rem = pi - td * plane;
+        th = rem / TQw;
+        tw = rem - th * TQw;
+        return pidx < vol && td < TQd_e && th < TQh_e && tw < TQw_e;
+    };
     int lane_off[PBW];
-    int pos_t[PBW][3];
-    bool pos_ok[PBW];
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
-        const int pidx = (wpos * PBW + pb) * 32 + col;
-        const int pi = pidx < vol ? pidx : 0;
-        const int td = pi / plane;
-        const int rem = pi - td * plane;
-        const int th = rem / TQw;
-        const int tw = rem - th * TQw;
-        pos_ok[pb] = pidx < vol && td < TQd_e && th < TQh_e && tw < TQw_e;
-        pos_t[pb][0] = td;
-        pos_t[pb][1] = th;
-        pos_t[pb][2] = tw;
+        int td, th, tw;
+        decode_pos(pb, td, th, tw);
         lane_off[pb] = (td * HH + th) * HWp + tw + half * CISTR;
     }
 
@@ -206,40 +225,74 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int nthreads = blockDim.x;
     const size_t HWin = (size_t)P.H * P.W;
     const float *xn = P.x + (size_t)n * P.Cin * P.D * HWin;
-    // digits of tid and of nthreads in the radix (CI_T, HD, HH, HW)
-    const int st_total = P.CI_T * HD * HH * HW;
-    const int st_hw = tid % HW, st_hh = (tid / HW) % HH, st_hd = (tid / (HW * HH)) % HD,
-              st_cl = tid / (HW * HH * HD);
-    const int inc_hw = nthreads % HW, inc_hh = (nthreads / HW) % HH, inc_hd = (nthreads / (HW * HH)) % HD,
-              inc_cl = nthreads / (HW * HH * HD);
-    // ---- stage the input halo of CI_T channels: thread t covers flat elements
-    // t, t + nthreads, ...; the (cl, hd, hh, hw) digits advance by the
-    // mixed-radix digits of nthreads, so no division in the loop.
-    auto stage = [&](int chunk) {
-        const int ci0 = chunk * P.CI_T;
-        int hw = st_hw, hh = st_hh, hd = st_hd, cl = st_cl;
+    // ---- halo staging.  Flat element e of a chunk (channel-major, then d, h, w)
+    // lands at LDS float e of the chunk's buffer; thread t covers e = t, t + 256,
+    // ...  The (cl, hd, hh, hw) digits advance by the mixed-radix digits of 256,
+    // so no division.  Elements outside the input (or past Cin) are zero.
+    // While chunk c is multiplied, chunk c + 1 is staged into the other buffer
+    // one element per MFMA group: each call writes the element loaded by the
+    // call before (one group of latency) and loads the next.
+    const int st_total = P.CI_T * CISTR;
+    const int inc_hw = kBlockThreads % HW, inc_hh = (kBlockThreads / HW) % HH,
+              inc_hd = (kBlockThreads / (HW * HH)) % HD, inc_cl = kBlockThreads / (HW * HH * HD);
+    // elements of this wave per chunk (wave-uniform loop count; tail lanes masked)
+    const int wave_first = wave * 64;
+    const int dma_n = __builtin_amdgcn_readfirstlane(
+        st_total > wave_first ? (st_total - wave_first + kBlockThreads - 1) / kBlockThreads : 0);
+    int dma_i = dma_n, d_hw = 0, d_hh = 0, d_hd = 0, d_cl = 0, d_ci0 = 0;
+    float *dma_buf = lds;
+    float pend_v = 0.0f;  // element dma_i - 1, loaded and not yet written
+    auto dma_begin = [&](int chunk, float *buf) {
+        dma_i = 0;
+        int t = tid;  // opaque: the digits of tid are formed here, not kept live
+        asm volatile("" : "+v"(t));
+        d_hw = t % HW; d_hh = (t / HW) % HH; d_hd = (t / (HW * HH)) % HD; d_cl = t / (HW * HH * HD);
+        d_ci0 = chunk * P.CI_T;
+        dma_buf = buf;
+    };
+    auto load_next = [&]() -> float {
+        const int ci = d_ci0 + d_cl;
+        const int id = lo_d + d_hd, ih = lo_h + d_hh, iw = lo_w + d_hw;
+        float v = 0.0f;
+        if (dma_i * kBlockThreads + tid < st_total && ci < P.Cin && (unsigned)id < (unsigned)P.D &&
+            (unsigned)ih < (unsigned)P.H && (unsigned)iw < (unsigned)P.W)
+            v = xn[((size_t)ci * P.D + id) * HWin + (size_t)ih * P.W + iw];
+        d_hw += inc_hw;
+        if (d_hw >= HW) { d_hw -= HW; ++d_hh; }
+        d_hh += inc_hh;
+        if (d_hh >= HH) { d_hh -= HH; ++d_hd; }
+        d_hd += inc_hd;
+        if (d_hd >= HD) { d_hd -= HD; ++d_cl; }
+        d_cl += inc_cl;
+        return v;
+    };
+    auto write_pending = [&]() {
+        const int e = (dma_i - 1) * kBlockThreads + tid;
+        if (dma_i > 0 && e < st_total) dma_buf[e] = pend_v;
+    };
+    auto dma_issue = [&]() {  // spread form: dma_i < dma_n
+        write_pending();
+        pend_v = load_next();
+        ++dma_i;
+    };
+    // the rest of the chunk, loads batched; the caller then syncs
+    auto dma_finish = [&]() {
+        write_pending();
 #pragma unroll 4
-        for (int e = tid; e < st_total; e += nthreads) {
-            const int ci = ci0 + cl;
-            const int id = lo_d + hd, ih = lo_h + hh, iw = lo_w + hw;
-            float v = 0.0f;
-            if (ci < P.Cin && (unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H &&
-                (unsigned)iw < (unsigned)P.W)
-                v = xn[((size_t)ci * P.D + id) * HWin + (size_t)ih * P.W + iw];
-            lds[cl * CISTR + (hd * HH + hh) * HWp + hw] = v;
-            hw += inc_hw;
-            if (hw >= HW) { hw -= HW; ++hh; }
-            hh += inc_hh;
-            if (hh >= HH) { hh -= HH; ++hd; }
-            hd += inc_hd;
-            if (hd >= HD) { hd -= HD; ++cl; }
-            cl += inc_cl;
+        for (; dma_i < dma_n; ++dma_i) {
+            const int e = dma_i * kBlockThreads + tid;
+            const float v = load_next();
+            if (e < st_total) dma_buf[e] = v;
         }
     };
-    if constexpr (PL) {  // one chunk (planner guarantee), staged once for every phase group
-        stage(0);
-        __syncthreads();
-    }
+    // two halo buffers (P.nbuf == 2): chunk c + 1 is loaded into the other
+    // buffer while chunk c is multiplied; with one, each chunk is staged at its
+    // start
+    float *const buf0 = lds;
+    float *const buf1 = lds + P.buf_stride;
+    dma_begin(0, buf0);
+    dma_finish();
+    __syncthreads();
 
   for (int pgi = 0; pgi < npg; ++pgi) {
     const int pg = pg0 + pgi;
@@ -270,11 +323,18 @@ void convt3d_mfma_kernel(const ConvParams P) {
     }
     if (work) {
         for (int chunk = 0; chunk < P.nchunks; ++chunk) {
-          if constexpr (!PL) {
-            __syncthreads();
-            stage(chunk);
-            __syncthreads();
-          }
+            const bool two = P.nbuf == 2;
+            const float *hb = (two && (chunk & 1)) ? buf1 : buf0;  // this chunk's halo
+            if constexpr (!PL) {
+                if (two) {
+                    if (chunk + 1 < P.nchunks) dma_begin(chunk + 1, (chunk & 1) ? buf0 : buf1);
+                } else if (chunk > 0) {  // one buffer: stage while the workgroup waits
+                    __syncthreads();
+                    dma_begin(chunk, buf0);
+                    dma_finish();
+                    __syncthreads();
+                }
+            }
 #pragma unroll
             for (int p = 0; p < NPH; ++p) {
                 if (Jw[p] == 0 || jw_lo[p] > jw_hi[p]) continue;
@@ -309,7 +369,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     for (int e = 0; e < 4; ++e) {
                         const int ro = (e < 3) ? bo + 2 * (e + 1) * CISTR : bo_next;
 #pragma unroll
-                        for (int pb = 0; pb < PBW; ++pb) bq[(e + 1) & 1][pb] = lds[lane_off[pb] + ro];
+                        for (int pb = 0; pb < PBW; ++pb) bq[(e + 1) & 1][pb] = hb[lane_off[pb] + ro];
 #pragma unroll
                         for (int c = 0; c < CBW; ++c) {
                             const float av = a[c][e];
@@ -332,11 +392,12 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                 for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
 #pragma unroll
-                for (int pb = 0; pb < PBW; ++pb) bq[0][pb] = lds[lane_off[pb] + boA];
+                for (int pb = 0; pb < PBW; ++pb) bq[0][pb] = hb[lane_off[pb] + boA];
                 for (int it = 0; it < n_it; it += 2) {
                     if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
 #pragma unroll
                     for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
+                    if (!PL && dma_i < dma_n) dma_issue();
                     __builtin_amdgcn_sched_barrier(0);
                     group_mfma(aA, boA, boB);
                     __builtin_amdgcn_sched_barrier(0);
@@ -344,9 +405,16 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
 #pragma unroll
                     for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                    if (!PL && dma_i < dma_n) dma_issue();
                     __builtin_amdgcn_sched_barrier(0);
                     group_mfma(aB, boB, boA);
                     __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (!PL) {
+                if (two && chunk + 1 < P.nchunks) {  // next chunk's halo is in; this one's readers are done
+                    dma_finish();
+                    __syncthreads();
                 }
             }
         }
@@ -359,12 +427,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
     bool ok[NPH][PBW];
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
-        const int od = s * (q0d + pos_t[pb][0]) + rho_d;
-        const int oh = s * (q0h + pos_t[pb][1]) + rho_h;
+        int td, th, tw;
+        const bool pos_ok = decode_pos(pb, td, th, tw);
+        const int od = s * (q0d + td) + rho_d;
+        const int oh = s * (q0h + th) + rho_h;
 #pragma unroll
         for (int p = 0; p < NPH; ++p) {
-            const int ow = s * (q0w + pos_t[pb][2]) + rw[p];
-            ok[p][pb] = pos_ok[pb] && od < Do && oh < Ho && ow < Wo;
+            const int ow = s * (q0w + tw) + rw[p];
+            ok[p][pb] = pos_ok && od < Do && oh < Ho && ow < Wo;
             sp[p][pb] = (od * Ho + oh) * Wo + ow;
         }
     }
@@ -513,7 +583,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
             }
         if (gn || bn) {
             __syncthreads();
-            const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + (int)blockIdx.x;
+            const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + bx;
             for (int row = tid; row < CO32; row += blockDim.x) {
                 const int co = co_tile * CO32 + row;
                 if (co >= Cout) continue;

@@ -140,6 +140,7 @@ typedef struct convt3d_plan_info {
     int64_t issued_macs;       /* multiply-adds the matrix cores execute (incl. padding) */
     int64_t valid_macs;        /* multiply-adds whose input voxel is in range          */
     int32_t phase_loop;        /* 1: a workgroup covers every (d, h) stride phase       */
+    int32_t halo_buffers;      /* 2: next channel chunk staged during this one's MFMAs  */
 } convt3d_plan_info;
 
 int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
