@@ -43,7 +43,13 @@ class PlanInfo(ctypes.Structure):
                 ("tile_q", ctypes.c_int32 * 3), ("ci_chunk", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("workgroups", ctypes.c_int64),
                 ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64),
-                ("phase_loop", ctypes.c_int32), ("halo_buffers", ctypes.c_int32)]
+                ("phase_loop", ctypes.c_int32), ("halo_buffers", ctypes.c_int32),
+                ("tuned", ctypes.c_int32), ("border_split", ctypes.c_int32)]
+
+
+class TuneResult(ctypes.Structure):
+    _fields_ = [("candidates", ctypes.c_int32), ("chosen", ctypes.c_int32), ("chosen_ms", ctypes.c_float),
+                ("model_choice_ms", ctypes.c_float)]
 
 
 class Profile(ctypes.Structure):
@@ -84,6 +90,8 @@ def lib():
         L.convt3d_workspace_size.argtypes = [P(Geom), P(Epilogue)]
         L.convt3d_fused.restype = ctypes.c_int
         L.convt3d_fused.argtypes = [vp, vp, vp, P(Geom), P(Epilogue), vp, vp, sz, vp]
+        L.convt3d_autotune.restype = ctypes.c_int
+        L.convt3d_autotune.argtypes = [vp, vp, vp, P(Geom), P(Epilogue), vp, vp, sz, vp, P(TuneResult)]
         L.convt3d_get_plan_info.restype = ctypes.c_int
         L.convt3d_get_plan_info.argtypes = [P(Geom), P(Epilogue), P(PlanInfo)]
         L.convt3d_profile_begin.restype = ctypes.c_int
@@ -96,7 +104,8 @@ def lib():
 
 EXPORTED = ["convt3d_status_string", "convt3d_output_dims", "convt3d_output_elems",
             "convt3d_packed_weight_bytes", "convt3d_prepack_weights", "convt3d_workspace_size",
-            "convt3d_fused", "convt3d_get_plan_info", "convt3d_profile_begin", "convt3d_profile_end"]
+            "convt3d_fused", "convt3d_autotune", "convt3d_get_plan_info", "convt3d_profile_begin",
+            "convt3d_profile_end"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -169,6 +178,16 @@ def convt3d_fused(x, w_packed, bias, geom: Geom, epi: Epilogue, out, workspace, 
     return st
 
 
+def convt3d_autotune(x, w_packed, bias, geom: Geom, epi: Epilogue, out, workspace, workspace_bytes: int,
+                     stream=None) -> dict:
+    res = TuneResult()
+    st = lib().convt3d_autotune(_ptr(x), _ptr(w_packed), _ptr(bias), ctypes.byref(geom), ctypes.byref(epi),
+                                _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream), ctypes.byref(res))
+    if st:
+        raise Convt3dError(st, "convt3d_autotune")
+    return {f: getattr(res, f) for f, _ in TuneResult._fields_}
+
+
 def convt3d_get_plan_info(geom: Geom, epi: Epilogue) -> dict:
     info = PlanInfo()
     st = lib().convt3d_get_plan_info(ctypes.byref(geom), ctypes.byref(epi), ctypes.byref(info))
@@ -177,6 +196,14 @@ def convt3d_get_plan_info(geom: Geom, epi: Epilogue) -> dict:
     d = {f: getattr(info, f) for f, _ in PlanInfo._fields_}
     d["tile_q"] = tuple(info.tile_q)
     return d
+
+
+def plan_string(info: dict) -> str:
+    """CONVT3D_PLAN value that selects this plan again (with CONVT3D_PHASE_LOOP
+    set to info["phase_loop"])."""
+    t = info["tile_q"]
+    return (f"{info['variant']},{info['waves_co']},{t[0]},{t[1]},{t[2]},{info['ci_chunk']},"
+            f"{info['border_split']},{info['halo_buffers']}")
 
 
 def convt3d_profile_begin() -> None:
@@ -240,6 +267,11 @@ class FusedCall:
         convt3d_fused(x, self.w_packed, bias, self.geom, self.epilogue(gamma, beta), self.out,
                       self.workspace, self.ws_bytes, stream)
         return self.out
+
+    def autotune(self, x, bias=None, gamma=None, beta=None, stream=None) -> dict:
+        """Time the candidate plans on these buffers and keep the fastest."""
+        return convt3d_autotune(x, self.w_packed, bias, self.geom, self.epilogue(gamma, beta), self.out,
+                                self.workspace, self.ws_bytes, stream)
 
     def plan_info(self) -> dict:
         return convt3d_get_plan_info(self.geom, self.epilogue())

@@ -1,8 +1,10 @@
 // C ABI of libconvt3d (include/convt3d.h): argument checks, plan cache and the
 // kernel sequence of each epilogue.  All work is enqueued on the caller's
-// stream; nothing here allocates device memory or waits on the device.
+// stream; nothing here allocates device memory, and only convt3d_autotune
+// waits on the device (it times candidate plans).
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <list>
@@ -26,11 +28,19 @@ struct CacheKey {
     }
 };
 
-std::mutex g_mu;
-std::list<std::pair<CacheKey, Plan>> g_cache;  // most recent first, bounded
+// Candidate plans convt3d_autotune times (the cost model's best ones).
+constexpr int kTuneCandidates = 8;
 
-int cached_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *out) {
-    if (!g || !e) return CONVT3D_ERR_NULL;
+struct CacheEntry {
+    Plan plan;         // the plan convt3d_fused runs
+    size_t ws_max;     // largest workspace of the candidate plans
+    bool tuned;        // chosen by timing (convt3d_autotune)
+};
+
+std::mutex g_mu;
+std::list<std::pair<CacheKey, CacheEntry>> g_cache;  // most recent first, bounded
+
+CacheKey make_key(const convt3d_geom *g, const convt3d_epilogue *e) {
     CacheKey key;
     std::memset(&key, 0, sizeof(key));
     key.g = *g;
@@ -41,26 +51,55 @@ int cached_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *out) {
         key.plan_env[60] = '|';
         key.plan_env[61] = env[0];
     }
+    return key;
+}
+
+// Plan of (geometry, epilogue): cached, else the cost model's choice.
+int cached_entry(const convt3d_geom *g, const convt3d_epilogue *e, CacheEntry *out) {
+    if (!g || !e) return CONVT3D_ERR_NULL;
+    const CacheKey key = make_key(g, e);
     {
         std::lock_guard<std::mutex> lk(g_mu);
         for (auto it = g_cache.begin(); it != g_cache.end(); ++it)
             if (it->first == key) {
                 *out = it->second;
-                out->e = *e;  // pointers / eps / scale of this call
+                out->plan.e = *e;  // pointers / eps / scale of this call
                 if (it != g_cache.begin()) g_cache.splice(g_cache.begin(), g_cache, it);
                 return CONVT3D_OK;
             }
     }
-    Plan pl;
-    int st = make_plan(g, e, &pl);
+    std::vector<Plan> cands;
+    const int st = plan_candidates(g, e, kTuneCandidates, &cands);
     if (st) return st;
+    CacheEntry ent{cands[0], 0, false};
+    for (const Plan &c : cands) ent.ws_max = std::max(ent.ws_max, c.ws_bytes);
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        g_cache.emplace_front(key, pl);
+        g_cache.emplace_front(key, ent);
         if (g_cache.size() > 64) g_cache.pop_back();
     }
-    *out = pl;
+    *out = ent;
+    out->plan.e = *e;
     return CONVT3D_OK;
+}
+
+int cached_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *out) {
+    CacheEntry ent;
+    const int st = cached_entry(g, e, &ent);
+    if (st) return st;
+    *out = ent.plan;
+    return CONVT3D_OK;
+}
+
+void store_tuned(const convt3d_geom *g, const convt3d_epilogue *e, const Plan &pl) {
+    const CacheKey key = make_key(g, e);
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto &kv : g_cache)
+        if (kv.first == key) {
+            kv.second.plan = pl;
+            kv.second.tuned = true;
+            return;
+        }
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -162,16 +201,17 @@ int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_pa
 }
 
 size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *epi) {
-    Plan pl;
-    if (cached_plan(geom, epi, &pl) != CONVT3D_OK) return 0;
-    return pl.ws_bytes;
+    CacheEntry ent;
+    if (cached_entry(geom, epi, &ent) != CONVT3D_OK) return 0;
+    return ent.ws_max;  // enough for every plan convt3d_autotune may choose
 }
 
 int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi, convt3d_plan_info *info) {
     if (!info) return CONVT3D_ERR_NULL;
-    Plan pl;
-    const int st = cached_plan(geom, epi, &pl);
+    CacheEntry ent;
+    const int st = cached_entry(geom, epi, &ent);
     if (st) return st;
+    const Plan &pl = ent.plan;
     std::memset(info, 0, sizeof(*info));
     info->variant = pl.variant;
     info->co_blocks_per_wave = pl.CBW;
@@ -187,29 +227,32 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
     info->valid_macs = pl.valid_macs;
     info->phase_loop = pl.phase_loop;
     info->halo_buffers = pl.nbuf;
+    info->tuned = ent.tuned ? 1 : 0;
+    info->border_split = pl.split;
     return CONVT3D_OK;
 }
 
-int convt3d_fused(const float *x, const void *w_packed, const float *bias, const convt3d_geom *geom,
-                  const convt3d_epilogue *epi, float *out, void *workspace, size_t workspace_bytes,
-                  void *stream) {
-    if (!geom || !epi) return CONVT3D_ERR_NULL;
-    Plan pl;
-    int st = cached_plan(geom, epi, &pl);
-    if (st) return st;
-    if (geom->n == 0) return CONVT3D_OK;  // empty batch
+// Argument checks shared by convt3d_fused and convt3d_autotune (pl: the plan
+// that will run; its workspace need is checked).
+static int check_call(const float *x, const void *w_packed, const float *bias, const convt3d_geom *geom,
+                      const convt3d_epilogue *epi, float *out, void *workspace, size_t workspace_bytes,
+                      size_t ws_need) {
     if (!x || !w_packed || !out) return CONVT3D_ERR_NULL;
     if (!aligned16(x) || !aligned16(w_packed) || !aligned16(out) || (bias && !aligned16(bias)))
         return CONVT3D_ERR_ALIGNMENT;
-    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned16(workspace)))
         return CONVT3D_ERR_WORKSPACE;
-    {
-        const char *xb = reinterpret_cast<const char *>(x);
-        const char *xe = xb + (size_t)geom->n * geom->cin * geom->d * geom->h * geom->w * sizeof(float);
-        const char *ob = reinterpret_cast<const char *>(out);
-        const char *oe = ob + (size_t)convt3d_output_elems(geom, epi) * sizeof(float);
-        if (ob < xe && xb < oe) return CONVT3D_ERR_ALIAS;
-    }
+    const char *xb = reinterpret_cast<const char *>(x);
+    const char *xe = xb + (size_t)geom->n * geom->cin * geom->d * geom->h * geom->w * sizeof(float);
+    const char *ob = reinterpret_cast<const char *>(out);
+    const char *oe = ob + (size_t)convt3d_output_elems(geom, epi) * sizeof(float);
+    if (ob < xe && xb < oe) return CONVT3D_ERR_ALIAS;
+    return CONVT3D_OK;
+}
+
+// Enqueue the kernels of one call with plan pl (arguments already checked).
+static int run_plan(const Plan &pl, const float *x, const void *w_packed, const float *bias,
+                    const convt3d_epilogue *epi, float *out, void *workspace, void *stream) {
     char *ws = static_cast<char *>(workspace);
     const bool stats = epi->kind == CONVT3D_EPI_RELU_GROUPNORM || epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
     float *partials = stats ? reinterpret_cast<float *>(ws + pl.ws_partials) : nullptr;
@@ -241,6 +284,77 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias, const
                 return launch_bn_finalize(pl, partials, epi->gamma, epi->beta, out, epi->stats_out, stream);
             }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
+    }
+    return CONVT3D_OK;
+}
+
+int convt3d_fused(const float *x, const void *w_packed, const float *bias, const convt3d_geom *geom,
+                  const convt3d_epilogue *epi, float *out, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+    if (!geom || !epi) return CONVT3D_ERR_NULL;
+    Plan pl;
+    int st = cached_plan(geom, epi, &pl);
+    if (st) return st;
+    if (geom->n == 0) return CONVT3D_OK;  // empty batch
+    st = check_call(x, w_packed, bias, geom, epi, out, workspace, workspace_bytes, pl.ws_bytes);
+    if (st) return st;
+    return run_plan(pl, x, w_packed, bias, epi, out, workspace, stream);
+}
+
+int convt3d_autotune(const float *x, const void *w_packed, const float *bias, const convt3d_geom *geom,
+                     const convt3d_epilogue *epi, float *out, void *workspace, size_t workspace_bytes,
+                     void *stream, convt3d_tune_result *result) {
+    if (!geom || !epi) return CONVT3D_ERR_NULL;
+    if (result) std::memset(result, 0, sizeof(*result));
+    CacheEntry ent;
+    int st = cached_entry(geom, epi, &ent);
+    if (st) return st;
+    if (geom->n == 0) return CONVT3D_OK;  // nothing to time
+    st = check_call(x, w_packed, bias, geom, epi, out, workspace, workspace_bytes, 0);
+    if (st) return st;
+    std::vector<Plan> cands;
+    st = plan_candidates(geom, epi, kTuneCandidates, &cands);
+    if (st) return st;
+    hipEvent_t b = nullptr, e = nullptr;
+    if (hipEventCreate(&b) != hipSuccess || hipEventCreate(&e) != hipSuccess) {
+        if (b) hipEventDestroy(b);
+        return CONVT3D_ERR_LAUNCH;
+    }
+    constexpr int kReps = 3;
+    int best = -1, timed_n = 0;
+    float best_ms = 0.0f, first_ms = 0.0f;
+    for (size_t i = 0; i < cands.size() && st == CONVT3D_OK; ++i) {
+        Plan &pl = cands[i];
+        pl.e = *epi;
+        if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+            continue;  // needs more workspace than the caller gave
+        st = run_plan(pl, x, w_packed, bias, epi, out, workspace, stream);  // warm-up
+        if (st) break;
+        hipEventRecord(b, (hipStream_t)stream);
+        for (int r = 0; r < kReps && st == CONVT3D_OK; ++r)
+            st = run_plan(pl, x, w_packed, bias, epi, out, workspace, stream);
+        hipEventRecord(e, (hipStream_t)stream);
+        if (st) break;
+        float ms = 0.0f;
+        if (hipEventSynchronize(e) != hipSuccess || hipEventElapsedTime(&ms, b, e) != hipSuccess) {
+            st = CONVT3D_ERR_LAUNCH;
+            break;
+        }
+        ms /= kReps;
+        if (i == 0) first_ms = ms;
+        ++timed_n;
+        if (best < 0 || ms < best_ms) { best = (int)i; best_ms = ms; }
+    }
+    hipEventDestroy(b);
+    hipEventDestroy(e);
+    if (st) return st;
+    if (best < 0) return CONVT3D_ERR_WORKSPACE;  // no candidate fits the workspace
+    store_tuned(geom, epi, cands[best]);
+    if (result) {
+        result->candidates = timed_n;
+        result->chosen = best;
+        result->chosen_ms = best_ms;
+        result->model_choice_ms = first_ms;
     }
     return CONVT3D_OK;
 }

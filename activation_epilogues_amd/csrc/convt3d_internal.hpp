@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "convt3d.h"
 
@@ -89,6 +90,7 @@ struct Plan {
     int buf_stride = 0, nbuf = 1, lds_bytes = 0;
     int co_tiles = 1, nwgroups = 1;
     int phase_loop = 0, red_off = 0;
+    int split = 0;            // dims split into border / interior segments (bit 0 d, 1 h, 2 w)
     int64_t tiles_per_n = 0;
     int64_t grid_x = 0, grid_y = 0, grid_z = 0;
     int64_t issued_macs = 0, valid_macs = 0;
@@ -110,6 +112,7 @@ int64_t out_dim(int64_t in, int64_t k, int64_t s, int64_t p, int64_t op);
 int validate_geom(const convt3d_geom *g);
 int make_geometry(const convt3d_geom *g, Plan *pl);        // phases + packing only
 int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl);
+int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k, std::vector<Plan> *out);
 void fill_conv_params(const Plan &pl, ConvParams *cp);
 
 // Launchers (kernels.hip).  Return a hipError_t as int.

@@ -134,9 +134,15 @@ static void ws_layout(Plan *pl) {
     pl->ws_bytes = off;
 }
 
-int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
-    if (!g || !e) return CONVT3D_ERR_NULL;
-    *pl = Plan{};
+// Search of the kernel configuration: every (variant, wave grid, border split,
+// phase loop, halo buffers) with its best box per region and channel chunk,
+// ranked by the cost model.  Returns the best max_k plans, cheapest first.
+int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k, std::vector<Plan> *out) {
+    if (!g || !e || !out) return CONVT3D_ERR_NULL;
+    out->clear();
+    if (max_k < 1) max_k = 1;
+    Plan base{};
+    Plan *pl = &base;
     int st = make_geometry(g, pl);
     if (st) return st;
     pl->e = *e;
@@ -210,9 +216,8 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
     const int64_t nn = std::max(g->n, 1);  // plan an empty batch like n = 1
     const int CI_pad = pl->octets * kOctet;
 
-    double best = 1e300;
-    Plan bestp = *pl;
-    bool found = false;
+    std::vector<std::pair<double, Plan>> top;  // cheapest first, at most max_k
+    bool found = false, too_large = false;
     for (int vi = 0; vi < kNumVariants; ++vi) {
         const Variant v = kVariants[vi];
         if (s % v.NPH != 0) continue;
@@ -419,8 +424,7 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
               // measured: splitting the output channels over fewer waves (WCO < 4)
               // costs MFMA issue rate when the channels could fill four waves
               if (!softmax && WCO < 4 && pl->cb_total >= 4) cost *= WCO == 2 ? 1.1 : 1.2;
-              if (cost < best) {
-                  best = cost;
+              if ((int)top.size() < max_k || cost < top.back().first) {
                   found = true;
                   Plan c = *pl;
                   c.variant = vi;
@@ -449,6 +453,7 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                   c.buf_stride = halo_floats(CI_T);
                   c.nbuf = nbuf_of(CI_T);
                   c.phase_loop = ploop;
+                  c.split = split;
                   c.red_off = c.nbuf * c.buf_stride;
                   c.lds_bytes = lds_wg;
                   c.co_tiles = co_tiles; c.nwgroups = nwg;
@@ -457,7 +462,17 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
                   c.grid_y = (int64_t)co_tiles * (s * s / npg) * nwg;
                   c.grid_z = g->n;
                   c.issued_macs = issued / nn * g->n;
-                  bestp = c;
+                  // the kernel forms a linear workgroup index in 32-bit arithmetic
+                  if (c.grid_x > INT32_MAX || c.grid_y > 65535 || c.grid_z > 65535 ||
+                      c.grid_x * c.grid_y * c.grid_z > INT32_MAX) {
+                      too_large = true;
+                      continue;
+                  }
+                  ws_layout(&c);
+                  auto at = top.begin();
+                  while (at != top.end() && at->first <= cost) ++at;
+                  top.insert(at, std::make_pair(cost, c));
+                  if ((int)top.size() > max_k) top.pop_back();
               }
             }
            }
@@ -465,12 +480,16 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
         }
     }
     if (!found) return CONVT3D_ERR_UNSUPPORTED;
-    // the kernel forms a linear workgroup index in 32-bit arithmetic
-    if (bestp.grid_x > INT32_MAX || bestp.grid_y > 65535 || bestp.grid_z > 65535 ||
-        bestp.grid_x * bestp.grid_y * bestp.grid_z > INT32_MAX)
-        return CONVT3D_ERR_TOO_LARGE;
-    *pl = bestp;
-    ws_layout(pl);
+    if (top.empty()) return too_large ? CONVT3D_ERR_TOO_LARGE : CONVT3D_ERR_UNSUPPORTED;
+    for (auto &t : top) out->push_back(t.second);
+    return CONVT3D_OK;
+}
+
+int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
+    std::vector<Plan> c;
+    const int st = plan_candidates(g, e, 1, &c);
+    if (st) return st;
+    *pl = c[0];
     return CONVT3D_OK;
 }
 

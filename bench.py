@@ -9,6 +9,12 @@ is already resident in HBM: re-lay the weights for the matrix cores
 epilogue, statistics, normalisation).  The default workload is the
 [16,64,32,32,32] -> ConvTranspose3d(64->128, k3) -> ReLU -> GroupNorm(8) case.
 
+Before the warm-up the plan is chosen once by timing (convt3d_autotune, as a
+caller would do once per geometry); ``--no-tune`` keeps the cost model's
+plan, and ``--plan`` / ``--phase-loop`` force one (the ``plan_string`` the
+output reports selects the timed plan again without tuning, e.g. for a
+profiler run whose kernel list should hold only the timed launches).
+
 Prints ONE JSON line.  ``value`` is algorithmic GFLOP/s = 2 * (multiply-adds
 whose input voxel is in range) / time per step.  ``roofline`` describes the
 dominant kernel (the convolution kernel, FP32 MFMA bound): its duration comes
@@ -82,7 +88,16 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=16,
                     help="batch samples the CPU oracle baseline runs (bounded)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true", help="keep the cost model's plan")
+    ap.add_argument("--plan", default=None, help="force a plan (CONVT3D_PLAN string); implies --no-tune")
+    ap.add_argument("--phase-loop", type=int, choices=(0, 1), default=None,
+                    help="force the phase-group loop off / on (with --plan)")
     args = ap.parse_args()
+    if args.plan is not None:
+        os.environ["CONVT3D_PLAN"] = args.plan
+        args.no_tune = True
+    if args.phase_loop is not None:
+        os.environ["CONVT3D_PHASE_LOOP"] = str(args.phase_loop)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -104,6 +119,11 @@ def main():
     gamma = None if inp.gamma is None else torch.from_numpy(inp.gamma).to(dev)
     beta = None if inp.beta is None else torch.from_numpy(inp.beta).to(dev)
     stream = torch.cuda.current_stream()
+    tune = None
+    if not args.no_tune:
+        call.prepack(w, stream)
+        tune = call.autotune(x, b, gamma, beta, stream)
+        print(f"[bench] plan tuned: {tune}", file=sys.stderr, flush=True)
     info = call.plan_info()
     flops = 2.0 * info["valid_macs"]
 
@@ -181,6 +201,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "plan": {k: v for k, v in info.items()},
+        "plan_string": C.plan_string(info),
+        "tune": tune,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

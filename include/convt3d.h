@@ -112,7 +112,8 @@ int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_pa
                             void *stream);
 
 /* Bytes of device workspace convt3d_fused needs for (geom, epi) (statistics
- * partials and per-channel scale/shift).  May be 0 (then workspace may be NULL). */
+ * partials and per-channel scale/shift), for every plan convt3d_autotune may
+ * choose.  May be 0 (then workspace may be NULL). */
 size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *epi);
 
 /* The fused forward pass.
@@ -128,6 +129,27 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias,
                   const convt3d_geom *geom, const convt3d_epilogue *epi, float *out,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/* Plan selection by timing.  The cost model ranks the kernel configurations
+ * for (geom, epi); this runs the best few of them on the caller's buffers
+ * (the same arguments as convt3d_fused; out and workspace are overwritten,
+ * epi->stats_out too) and keeps the fastest for every later convt3d_fused
+ * call with this geometry and epilogue kind in this process.  Every plan
+ * computes the same result up to float summation order.  Unlike
+ * convt3d_fused it waits on the device (it times the candidates with HIP
+ * events on `stream`).  Candidates needing more workspace than
+ * workspace_bytes are skipped.  result may be NULL. */
+typedef struct convt3d_tune_result {
+    int32_t candidates;      /* plans timed                                      */
+    int32_t chosen;          /* rank of the chosen plan in cost-model order (0 = the model's pick) */
+    float chosen_ms;         /* time per call of the chosen plan                 */
+    float model_choice_ms;   /* time per call of the cost model's pick           */
+} convt3d_tune_result;
+
+int convt3d_autotune(const float *x, const void *w_packed, const float *bias,
+                     const convt3d_geom *geom, const convt3d_epilogue *epi, float *out,
+                     void *workspace, size_t workspace_bytes, void *stream,
+                     convt3d_tune_result *result);
+
 /* Planner's choices for (geom, epi), for reporting and tests. */
 typedef struct convt3d_plan_info {
     int32_t variant;           /* kernel variant id                                   */
@@ -141,6 +163,8 @@ typedef struct convt3d_plan_info {
     int64_t valid_macs;        /* multiply-adds whose input voxel is in range          */
     int32_t phase_loop;        /* 1: a workgroup covers every (d, h) stride phase       */
     int32_t halo_buffers;      /* 2: next channel chunk staged during this one's MFMAs  */
+    int32_t tuned;             /* 1: chosen by convt3d_autotune                         */
+    int32_t border_split;      /* dims split into border / interior tile regions (bit 0 d, 1 h, 2 w) */
 } convt3d_plan_info;
 
 int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,

@@ -157,3 +157,39 @@ def test_empty_batch_is_a_no_op():
         e = C.make_epilogue(kind, 2)
         # null pointers are fine: nothing is launched for an empty batch
         assert C.convt3d_fused(None, None, None, g, e, None, None, 0, stream=0, check=False) == 0
+
+
+def test_autotune_argument_checks():
+    """convt3d_autotune checks its arguments like convt3d_fused before timing anything."""
+    g = C.make_geom(1, 4, 8, 3, 3, 3, 3)
+    e = C.make_epilogue(0)
+    out = FAKE * 64
+    lib = C.lib()
+    res = C.TuneResult()
+
+    def tune(x, wp, bias, out_, ws, ws_bytes, geom=g, epi=e):
+        return lib.convt3d_autotune(x, wp, bias, ctypes.byref(geom), ctypes.byref(epi), out_, ws, ws_bytes, 0,
+                                    ctypes.byref(res))
+
+    assert tune(None, FAKE, None, out, None, 0) == 1
+    assert tune(FAKE, None, None, out, None, 0) == 1
+    assert tune(FAKE + 4, FAKE, None, out, None, 0) == 4
+    assert tune(FAKE, FAKE * 2, None, FAKE + 64, None, 0) == 9
+    # an empty batch times nothing and succeeds with null buffers
+    g0 = C.make_geom(0, 4, 8, 3, 3, 3, 3)
+    assert tune(None, None, None, None, None, 0, geom=g0) == 0
+    assert res.candidates == 0
+
+
+
+def test_plan_string_selects_the_same_plan(monkeypatch):
+    """The CONVT3D_PLAN string a plan reports forces that plan again."""
+    for wl in W.WORKLOADS:
+        e = C.make_epilogue(wl.epi, wl.groups)
+        monkeypatch.delenv("CONVT3D_PLAN", raising=False)
+        monkeypatch.delenv("CONVT3D_PHASE_LOOP", raising=False)
+        info = C.convt3d_get_plan_info(geom_of(wl), e)
+        monkeypatch.setenv("CONVT3D_PLAN", C.plan_string(info))
+        monkeypatch.setenv("CONVT3D_PHASE_LOOP", str(info["phase_loop"]))
+        again = C.convt3d_get_plan_info(geom_of(wl), e)
+        assert again == info, wl.name
