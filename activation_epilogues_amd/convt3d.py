@@ -44,7 +44,7 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("workgroups", ctypes.c_int64),
                 ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64),
                 ("phase_loop", ctypes.c_int32), ("halo_buffers", ctypes.c_int32),
-                ("tuned", ctypes.c_int32), ("border_split", ctypes.c_int32)]
+                ("tuned", ctypes.c_int32), ("border_split", ctypes.c_int32), ("xcd_order", ctypes.c_int32)]
 
 
 class TuneResult(ctypes.Structure):

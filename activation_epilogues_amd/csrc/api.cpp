@@ -21,7 +21,7 @@ namespace {
 struct CacheKey {
     convt3d_geom g;
     int kind, groups;
-    char plan_env[64];  // CONVT3D_PLAN tile override and CONVT3D_PHASE_LOOP, if any
+    char plan_env[64];  // CONVT3D_PLAN tile override, CONVT3D_PHASE_LOOP, CONVT3D_ORDER, if any
     bool operator==(const CacheKey &o) const {
         return std::memcmp(&g, &o.g, sizeof(g)) == 0 && kind == o.kind && groups == o.groups &&
                std::strncmp(plan_env, o.plan_env, sizeof(plan_env)) == 0;
@@ -50,6 +50,10 @@ CacheKey make_key(const convt3d_geom *g, const convt3d_epilogue *e) {
     if (const char *env = std::getenv("CONVT3D_PHASE_LOOP")) {
         key.plan_env[60] = '|';
         key.plan_env[61] = env[0];
+    }
+    if (const char *env = std::getenv("CONVT3D_ORDER")) {
+        key.plan_env[62] = '|';
+        key.plan_env[63] = env[0];
     }
     return key;
 }
@@ -229,6 +233,7 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
     info->halo_buffers = pl.nbuf;
     info->tuned = ent.tuned ? 1 : 0;
     info->border_split = pl.split;
+    info->xcd_order = pl.order;
     return CONVT3D_OK;
 }
 

@@ -17,6 +17,7 @@ constexpr int kMaxRegions = 27;    // tiling regions: (low border, interior, hig
 constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
 constexpr int kMaxLdsBytes = 80 * 1024;  // at least two workgroups per CU
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs (256 CUs), one L2 each
+constexpr int64_t kL2Bytes = 4 << 20;    // L2 per XCD
 
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
 // taps that reach it are k = r + s*j (j = 0..J-1) from input i = q + c - j.
@@ -54,6 +55,7 @@ struct ConvParams {
     int buf_stride;       // LDS floats per input-halo buffer (multiple of 256)
     int nbuf;             // 2: chunk c + 1 is staged while chunk c is multiplied
     int nxcd;             // XCDs the workgroups are dealt over round-robin
+    int order;            // 0: (co tile, phase) index fastest, 1: tile fastest
     int phase_loop;       // 1: each workgroup loops over all (rho_d, rho_h) groups
     int red_off;          // LDS float offset of the epilogue's reduction scratch
     int epi;
@@ -91,6 +93,7 @@ struct Plan {
     int co_tiles = 1, nwgroups = 1;
     int phase_loop = 0, red_off = 0;
     int split = 0;            // dims split into border / interior segments (bit 0 d, 1 h, 2 w)
+    int order = 0;            // workgroup order within an XCD (see ConvParams::order)
     int64_t tiles_per_n = 0;
     int64_t grid_x = 0, grid_y = 0, grid_z = 0;
     int64_t issued_macs = 0, valid_macs = 0;

@@ -112,9 +112,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
     // ---- workgroup -> work item.  Workgroups are handed to the XCDs round-robin
     // (dispatch index i runs on XCD i % nxcd), each XCD with its own L2.  The
     // dispatch index is mapped to a linear work index so that every XCD gets
-    // one contiguous range, in which the (co tile, phase) index varies fastest
-    // (those workgroups read the same input box), then the tile, then n: the
-    // halo overlap of neighbouring tiles then hits in one L2.
+    // one contiguous range; the halo overlap of neighbouring tiles then hits in
+    // one L2.  Within it either the (co tile, phase) index varies fastest
+    // (those workgroups read the same input box; order 0) or the tile does
+    // (an XCD keeps to one phase's weights when all of them do not fit in its
+    // L2; order 1); n varies slowest.
     int bx, by, n;
     {
         const int gx = gridDim.x, gy = gridDim.y;
@@ -123,8 +125,13 @@ void convt3d_mfma_kernel(const ConvParams P) {
         const int nx = P.nxcd, q = total / nx, r = total % nx;
         const int xcd = bid % nx, idx = bid / nx;
         const int lin = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
-        by = lin % gy;
-        bx = (lin / gy) % gx;
+        if (P.order == 0) {
+            by = lin % gy;
+            bx = (lin / gy) % gx;
+        } else {
+            bx = lin % gx;
+            by = (lin / gx) % gy;
+        }
         n = lin / (gx * gy);
     }
     // ---- tile: find the region, then the tile inside it

@@ -210,6 +210,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         if (got < 6) force[0] = -1;
     }
     const bool forced = force[0] >= 0;
+    int order_env = -1;
+    if (const char *env = std::getenv("CONVT3D_ORDER")) order_env = std::atoi(env) ? 1 : 0;
     // CONVT3D_PHASE_LOOP=0|1 restricts the phase-group loop choice (tests, sweeps)
     int ploop_only = -1;
     if (const char *env = std::getenv("CONVT3D_PHASE_LOOP")) ploop_only = std::atoi(env) ? 1 : 0;
@@ -462,6 +464,10 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                   c.grid_y = (int64_t)co_tiles * (s * s / npg) * nwg;
                   c.grid_z = g->n;
                   c.issued_macs = issued / nn * g->n;
+                  // packed weights that do not fit in half an L2: keep each XCD on
+                  // one (co tile, phase) group at a time (CONVT3D_ORDER overrides)
+                  c.order = (c.grid_y > 1 && pl->packed_floats * 4 > kL2Bytes / 2) ? 1 : 0;
+                  if (order_env >= 0) c.order = order_env;
                   // the kernel forms a linear workgroup index in 32-bit arithmetic
                   if (c.grid_x > INT32_MAX || c.grid_y > 65535 || c.grid_z > 65535 ||
                       c.grid_x * c.grid_y * c.grid_z > INT32_MAX) {
@@ -512,6 +518,7 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->co_tiles = pl.co_tiles; cp->nwgroups = pl.nwgroups;
     cp->buf_stride = pl.buf_stride; cp->nbuf = pl.nbuf;
     cp->nxcd = kNumXcd;
+    cp->order = pl.order;
     cp->phase_loop = pl.phase_loop; cp->red_off = pl.red_off;
     cp->epi = pl.e.kind;
     cp->scale = pl.e.kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL ? pl.e.scale : 1.0f;

@@ -165,6 +165,7 @@ typedef struct convt3d_plan_info {
     int32_t halo_buffers;      /* 2: next channel chunk staged during this one's MFMAs  */
     int32_t tuned;             /* 1: chosen by convt3d_autotune                         */
     int32_t border_split;      /* dims split into border / interior tile regions (bit 0 d, 1 h, 2 w) */
+    int32_t xcd_order;         /* 0: phase / channel-tile index fastest per XCD, 1: tile fastest */
 } convt3d_plan_info;
 
 int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
