@@ -43,7 +43,7 @@ class PlanInfo(ctypes.Structure):
                 ("tile_q", ctypes.c_int32 * 3), ("ci_chunk", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("workgroups", ctypes.c_int64),
                 ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64),
-                ("phase_loop", ctypes.c_int32), ("halo_buffers", ctypes.c_int32),
+                ("phase_loop", ctypes.c_int32),
                 ("tuned", ctypes.c_int32), ("border_split", ctypes.c_int32), ("xcd_order", ctypes.c_int32)]
 
 
@@ -203,7 +203,7 @@ def plan_string(info: dict) -> str:
     set to info["phase_loop"])."""
     t = info["tile_q"]
     return (f"{info['variant']},{info['waves_co']},{t[0]},{t[1]},{t[2]},{info['ci_chunk']},"
-            f"{info['border_split']},{info['halo_buffers']}")
+            f"{info['border_split']}")
 
 
 def convt3d_profile_begin() -> None:

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <list>
@@ -28,8 +29,15 @@ struct CacheKey {
     }
 };
 
-// Candidate plans convt3d_autotune times (the cost model's best ones).
-constexpr int kTuneCandidates = 8;
+// Candidate plans convt3d_autotune times (the cost model's best ones);
+// CONVT3D_TUNE_CANDIDATES (1..64) overrides.
+int tune_candidates() {
+    if (const char *env = std::getenv("CONVT3D_TUNE_CANDIDATES")) {
+        const int k = std::atoi(env);
+        if (k >= 1 && k <= 64) return k;
+    }
+    return 8;
+}
 
 struct CacheEntry {
     Plan plan;         // the plan convt3d_fused runs
@@ -73,7 +81,7 @@ int cached_entry(const convt3d_geom *g, const convt3d_epilogue *e, CacheEntry *o
             }
     }
     std::vector<Plan> cands;
-    const int st = plan_candidates(g, e, kTuneCandidates, &cands);
+    const int st = plan_candidates(g, e, tune_candidates(), &cands);
     if (st) return st;
     CacheEntry ent{cands[0], 0, false};
     for (const Plan &c : cands) ent.ws_max = std::max(ent.ws_max, c.ws_bytes);
@@ -230,7 +238,6 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
     info->issued_macs = pl.issued_macs;
     info->valid_macs = pl.valid_macs;
     info->phase_loop = pl.phase_loop;
-    info->halo_buffers = pl.nbuf;
     info->tuned = ent.tuned ? 1 : 0;
     info->border_split = pl.split;
     info->xcd_order = pl.order;
@@ -318,7 +325,7 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     st = check_call(x, w_packed, bias, geom, epi, out, workspace, workspace_bytes, 0);
     if (st) return st;
     std::vector<Plan> cands;
-    st = plan_candidates(geom, epi, kTuneCandidates, &cands);
+    st = plan_candidates(geom, epi, tune_candidates(), &cands);
     if (st) return st;
     hipEvent_t b = nullptr, e = nullptr;
     if (hipEventCreate(&b) != hipSuccess || hipEventCreate(&e) != hipSuccess) {
@@ -326,6 +333,7 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
         return CONVT3D_ERR_LAUNCH;
     }
     constexpr int kReps = 3;
+    const bool log = std::getenv("CONVT3D_TUNE_LOG") != nullptr;  // one stderr line per candidate
     int best = -1, timed_n = 0;
     float best_ms = 0.0f, first_ms = 0.0f;
     for (size_t i = 0; i < cands.size() && st == CONVT3D_OK; ++i) {
@@ -346,6 +354,10 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
             break;
         }
         ms /= kReps;
+        if (log)
+            std::fprintf(stderr, "convt3d_autotune: rank %zu plan %d,%d,%d,%d,%d,%d,%d phase_loop %d order %d: %.4f ms\n",
+                         i, pl.variant, pl.WCO, pl.TQ[0], pl.TQ[1], pl.TQ[2], pl.CI_T, pl.split, pl.phase_loop,
+                         pl.order, ms);
         if (i == 0) first_ms = ms;
         ++timed_n;
         if (best < 0 || ms < best_ms) { best = (int)i; best_ms = ms; }

@@ -52,8 +52,6 @@ struct ConvParams {
     int WCO, WPOS;        // wave grid
     int co_tiles;
     int nwgroups;         // w-phase groups per (rho_d, rho_h): s / NPH
-    int buf_stride;       // LDS floats per input-halo buffer (multiple of 256)
-    int nbuf;             // 2: chunk c + 1 is staged while chunk c is multiplied
     int nxcd;             // XCDs the workgroups are dealt over round-robin
     int order;            // 0: (co tile, phase) index fastest, 1: tile fastest
     int phase_loop;       // 1: each workgroup loops over all (rho_d, rho_h) groups
@@ -89,7 +87,7 @@ struct Plan {
     int rg_off[kMaxRegions + 1]{};
     int tiles_total = 0;
     int CI_T = 8, nchunks = 1;
-    int buf_stride = 0, nbuf = 1, lds_bytes = 0;
+    int lds_bytes = 0;
     int co_tiles = 1, nwgroups = 1;
     int phase_loop = 0, red_off = 0;
     int split = 0;            // dims split into border / interior segments (bit 0 d, 1 h, 2 w)

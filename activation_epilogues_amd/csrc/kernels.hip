@@ -190,9 +190,6 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int lo_d = q0d + lo_d_rel;
     const int lo_h = q0h + lo_h_rel;
     const int lo_w = q0w + lo_w_rel;
-    const int HWp = HW;            // compact rows
-    const int CISTR = HD * HH * HW;  // channel stride: the staged elements are dense
-    const int ROW = HH * HWp;
     int jw_lo[NPH], jw_hi[NPH];
 #pragma unroll
     for (int p = 0; p < NPH; ++p) {
@@ -200,7 +197,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
         jw_hi[p] = min(Jw[p] - 1, q0w + TQw_e - 1 + cw[p]);
     }
 
-    // ---- per-lane position decode (B operand base offsets)
+    // ---- LDS layout of a staged chunk: [octet][d][h][w][8].  The 8 channels of
+    // an octet at one halo position are adjacent, in the order 0,2,4,6,1,3,5,7:
+    // the lanes that feed MFMA k-row h (h = lane/32) need channels h, h+2, h+4,
+    // h+6 for the 4 k-steps of a group, and read them with one 16-byte LDS read.
+    const int SLAB = HD * HH * HW;  // halo positions per octet
     const int vol = TQd * TQh * TQw;
     const int plane = TQh * TQw;
     // The tile position of a lane's column in position block pb; decoded again
@@ -217,88 +218,69 @@ void convt3d_mfma_kernel(const ConvParams P) {
         tw = rem - th * TQw;
         return pidx < vol && td < TQd_e && th < TQh_e && tw < TQw_e;
     };
-    int lane_off[PBW];
+    int lane_off[PBW];  // float offset of the lane's B reads at tap offset 0
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
         int td, th, tw;
         decode_pos(pb, td, th, tw);
-        lane_off[pb] = (td * HH + th) * HWp + tw + half * CISTR;
+        lane_off[pb] = ((td * HH + th) * HW + tw) * 8 + half * 4;
     }
 
     const int CO_T = P.WCO * CBW;                   // co blocks per workgroup
     const int cb0 = co_tile * CO_T + wco * CBW;     // first co block of this wave
     const float4 *wp4 = reinterpret_cast<const float4 *>(P.wp);
     const int G4 = P.CI_T >> 3;
-    const int nthreads = blockDim.x;
-    const size_t HWin = (size_t)P.H * P.W;
-    const float *xn = P.x + (size_t)n * P.Cin * P.D * HWin;
-    // ---- halo staging.  Flat element e of a chunk (channel-major, then d, h, w)
-    // lands at LDS float e of the chunk's buffer; thread t covers e = t, t + 256,
-    // ...  The (cl, hd, hh, hw) digits advance by the mixed-radix digits of 256,
-    // so no division.  Elements outside the input (or past Cin) are zero.
-    // While chunk c is multiplied, chunk c + 1 is staged into the other buffer
-    // one element per MFMA group: each call writes the element loaded by the
-    // call before (one group of latency) and loads the next.
-    const int st_total = P.CI_T * CISTR;
-    const int inc_hw = kBlockThreads % HW, inc_hh = (kBlockThreads / HW) % HH,
-              inc_hd = (kBlockThreads / (HW * HH)) % HD, inc_cl = kBlockThreads / (HW * HH * HD);
-    // elements of this wave per chunk (wave-uniform loop count; tail lanes masked)
-    const int wave_first = wave * 64;
-    const int dma_n = __builtin_amdgcn_readfirstlane(
-        st_total > wave_first ? (st_total - wave_first + kBlockThreads - 1) / kBlockThreads : 0);
-    int dma_i = dma_n, d_hw = 0, d_hh = 0, d_hd = 0, d_cl = 0, d_ci0 = 0;
-    float *dma_buf = lds;
-    float pend_v = 0.0f;  // element dma_i - 1, loaded and not yet written
-    auto dma_begin = [&](int chunk, float *buf) {
-        dma_i = 0;
-        int t = tid;  // opaque: the digits of tid are formed here, not kept live
+    const int DHWin = P.D * P.H * P.W;
+    const float *xn = P.x + (size_t)n * P.Cin * DHWin;
+
+    // ---- halo staging.  Thread t takes halo positions t, t + 256, ...; for each
+    // position inside the input it loads the 8 channels of every octet of the
+    // chunk (one address, channel planes apart) and writes them as two 16-byte
+    // LDS stores.  Positions outside the input are never written: when the box
+    // crosses the input border (or Cin is not a multiple of 8) the buffer is
+    // cleared once, and those positions stay zero for every chunk.
+    const bool clear = lo_d < 0 || lo_d + HD > P.D || lo_h < 0 || lo_h + HH > P.H || lo_w < 0 ||
+                       lo_w + HW > P.W || (P.Cin & 7) != 0;
+    if (clear) {
+        float4 *l4 = reinterpret_cast<float4 *>(lds);
+        const int n4 = (P.CI_T * SLAB) >> 2;
+        for (int i = tid; i < n4; i += kBlockThreads) l4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        __syncthreads();
+    }
+    const int inc_w = kBlockThreads % HW, inc_h = (kBlockThreads / HW) % HH, inc_d = kBlockThreads / (HW * HH);
+    auto stage = [&](int chunk) {
+        int t = tid;  // opaque: the digits are formed here, not kept live across the MFMA loop
         asm volatile("" : "+v"(t));
-        d_hw = t % HW; d_hh = (t / HW) % HH; d_hd = (t / (HW * HH)) % HD; d_cl = t / (HW * HH * HD);
-        d_ci0 = chunk * P.CI_T;
-        dma_buf = buf;
-    };
-    auto load_next = [&]() -> float {
-        const int ci = d_ci0 + d_cl;
-        const int id = lo_d + d_hd, ih = lo_h + d_hh, iw = lo_w + d_hw;
-        float v = 0.0f;
-        if (dma_i * kBlockThreads + tid < st_total && ci < P.Cin && (unsigned)id < (unsigned)P.D &&
-            (unsigned)ih < (unsigned)P.H && (unsigned)iw < (unsigned)P.W)
-            v = xn[((size_t)ci * P.D + id) * HWin + (size_t)ih * P.W + iw];
-        d_hw += inc_hw;
-        if (d_hw >= HW) { d_hw -= HW; ++d_hh; }
-        d_hh += inc_hh;
-        if (d_hh >= HH) { d_hh -= HH; ++d_hd; }
-        d_hd += inc_hd;
-        if (d_hd >= HD) { d_hd -= HD; ++d_cl; }
-        d_cl += inc_cl;
-        return v;
-    };
-    auto write_pending = [&]() {
-        const int e = (dma_i - 1) * kBlockThreads + tid;
-        if (dma_i > 0 && e < st_total) dma_buf[e] = pend_v;
-    };
-    auto dma_issue = [&]() {  // spread form: dma_i < dma_n
-        write_pending();
-        pend_v = load_next();
-        ++dma_i;
-    };
-    // the rest of the chunk, loads batched; the caller then syncs
-    auto dma_finish = [&]() {
-        write_pending();
-#pragma unroll 4
-        for (; dma_i < dma_n; ++dma_i) {
-            const int e = dma_i * kBlockThreads + tid;
-            const float v = load_next();
-            if (e < st_total) dma_buf[e] = v;
+        int w = t % HW, h = (t / HW) % HH, d = t / (HW * HH);
+        const int oct0 = chunk * G4;
+        for (int pos = t; pos < SLAB; pos += kBlockThreads) {
+            const int id = lo_d + d, ih = lo_h + h, iw = lo_w + w;
+            if ((unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H && (unsigned)iw < (unsigned)P.W) {
+                const int voff = (id * P.H + ih) * P.W + iw;
+                for (int g = 0; g < G4; ++g) {
+                    const int ci0 = (oct0 + g) * 8;
+                    const float *src = xn + (size_t)ci0 * DHWin + voff;
+                    float v[8];
+                    if (ci0 + 8 <= P.Cin) {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) v[c] = src[(size_t)c * DHWin];
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) v[c] = ci0 + c < P.Cin ? src[(size_t)c * DHWin] : 0.0f;
+                    }
+                    float4 *dst = reinterpret_cast<float4 *>(lds + ((size_t)g * SLAB + pos) * 8);
+                    dst[0] = make_float4(v[0], v[2], v[4], v[6]);
+                    dst[1] = make_float4(v[1], v[3], v[5], v[7]);
+                }
+            }
+            w += inc_w;
+            if (w >= HW) { w -= HW; ++h; }
+            h += inc_h;
+            if (h >= HH) { h -= HH; ++d; }
+            d += inc_d;
         }
     };
-    // two halo buffers (P.nbuf == 2): chunk c + 1 is loaded into the other
-    // buffer while chunk c is multiplied; with one, each chunk is staged at its
-    // start
-    float *const buf0 = lds;
-    float *const buf1 = lds + P.buf_stride;
-    dma_begin(0, buf0);
-    dma_finish();
+    stage(0);
     __syncthreads();
 
   for (int pgi = 0; pgi < npg; ++pgi) {
@@ -330,15 +312,10 @@ void convt3d_mfma_kernel(const ConvParams P) {
     }
     if (work) {
         for (int chunk = 0; chunk < P.nchunks; ++chunk) {
-            const bool two = P.nbuf == 2;
-            const float *hb = (two && (chunk & 1)) ? buf1 : buf0;  // this chunk's halo
             if constexpr (!PL) {
-                if (two) {
-                    if (chunk + 1 < P.nchunks) dma_begin(chunk + 1, (chunk & 1) ? buf0 : buf1);
-                } else if (chunk > 0) {  // one buffer: stage while the workgroup waits
+                if (chunk > 0) {  // stage the next chunk while the workgroup waits
                     __syncthreads();
-                    dma_begin(chunk, buf0);
-                    dma_finish();
+                    stage(chunk);
                     __syncthreads();
                 }
             }
@@ -356,72 +333,60 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 }
                 const int n_it = (jd_hi - jd_lo + 1) * (jh_hi - jh_lo + 1) * (jwh - jwl + 1) * G4;
                 // Iteration state (jd, jh, jw, g4) of the next group to load; every
-                // group is 4 MFMA k-steps = 8 input channels of one tap.
+                // group is 4 MFMA k-steps = 8 input channels of one tap.  gi: float4
+                // index of its A operands; bo: float offset of its B operands.
                 int jd = jd_lo, jh = jh_lo, jw = jwl, g4 = 0;
                 auto next_group = [&](int &gi, int &bo) {
                     gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
-                    bo = (cd - jd - lo_d_rel) * ROW + (ch - jh - lo_h_rel) * HWp + (cwp - jw - lo_w_rel) +
-                         8 * g4 * CISTR;
+                    bo = (((cd - jd - lo_d_rel) * HH + (ch - jh - lo_h_rel)) * HW + (cwp - jw - lo_w_rel) +
+                          g4 * SLAB) * 8;
                     if (++g4 == G4) {
                         g4 = 0;
                         if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } }
                     }
                 };
-                // One group = 4 MFMA k-steps.  While the MFMAs of step e run, the B
-                // values of step e+1 (or of step 0 of the next group) are read from
-                // LDS into the other half of bq.
-                float bq[2][PBW];
-                auto group_mfma = [&](const float4 (&a)[CBW], int bo, int bo_next) {
+                // One group = 4 MFMA k-steps; its B operands (4 per position block)
+                // come from one 16-byte LDS read per position block, issued one
+                // group ahead.
+                float4 bA[PBW], bB[PBW];
+                auto read_b = [&](float4 (&b)[PBW], int bo) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int ro = (e < 3) ? bo + 2 * (e + 1) * CISTR : bo_next;
+                    for (int pb = 0; pb < PBW; ++pb)
+                        b[pb] = *reinterpret_cast<const float4 *>(lds + lane_off[pb] + bo);
+                };
+                auto group_mfma = [&](const float4 (&a)[CBW], const float4 (&b)[PBW]) {
 #pragma unroll
-                        for (int pb = 0; pb < PBW; ++pb) bq[(e + 1) & 1][pb] = hb[lane_off[pb] + ro];
+                    for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) {
-                            const float av = a[c][e];
+                        for (int c = 0; c < CBW; ++c)
 #pragma unroll
                             for (int pb = 0; pb < PBW; ++pb)
-                                acc[p][c][pb] = mfma32x32x2(av, bq[e & 1][pb], acc[p][c][pb]);
-                        }
-#pragma unroll
-                        for (int pb = 0; pb < PBW; ++pb) {
-                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-                            __builtin_amdgcn_sched_group_barrier(0x008, CBW, 0);  // CBW MFMAs
-                        }
-                    }
+                                acc[p][c][pb] = mfma32x32x2(a[c][e], b[pb][e], acc[p][c][pb]);
                 };
-                // Two A register sets in flight; loads are always issued (the last
-                // ones repeat a valid group) so the wait counts stay static.
+                // Two A and two B register sets in flight; loads are always issued
+                // (the last ones repeat a valid group) so the wait counts stay static.
                 float4 aA[CBW], aB[CBW];
                 int giA, boA, giB, boB;
                 next_group(giA, boA);
 #pragma unroll
                 for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
-#pragma unroll
-                for (int pb = 0; pb < PBW; ++pb) bq[0][pb] = hb[lane_off[pb] + boA];
+                read_b(bA, boA);
                 for (int it = 0; it < n_it; it += 2) {
                     if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
 #pragma unroll
                     for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
-                    if (!PL && dma_i < dma_n) dma_issue();
+                    read_b(bB, boB);
                     __builtin_amdgcn_sched_barrier(0);
-                    group_mfma(aA, boA, boB);
+                    group_mfma(aA, bA);
                     __builtin_amdgcn_sched_barrier(0);
                     if (it + 1 >= n_it) break;
                     if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
 #pragma unroll
                     for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
-                    if (!PL && dma_i < dma_n) dma_issue();
+                    read_b(bA, boA);
                     __builtin_amdgcn_sched_barrier(0);
-                    group_mfma(aB, boB, boA);
+                    group_mfma(aB, bB);
                     __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            if constexpr (!PL) {
-                if (two && chunk + 1 < P.nchunks) {  // next chunk's halo is in; this one's readers are done
-                    dma_finish();
-                    __syncthreads();
                 }
             }
         }

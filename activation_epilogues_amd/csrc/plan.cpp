@@ -199,14 +199,14 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     };
 
     // Optional override for tile sweeps:
-    // CONVT3D_PLAN="variant,WCO,TQd,TQh,TQw,CI_T[,split[,nbuf]]" restricts the
-    // search to that variant / wave grid / chunk, with that box in the largest
-    // region, (bit 0 d, 1 h, 2 w) those dims split into border / interior
-    // segments and that many halo buffers (ignored if it does not fit).
-    int force[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    // CONVT3D_PLAN="variant,WCO,TQd,TQh,TQw,CI_T[,split]" restricts the search
+    // to that variant / wave grid / chunk, with that box in the largest region
+    // and (bit 0 d, 1 h, 2 w) those dims split into border / interior segments
+    // (ignored if it does not fit).
+    int force[7] = {-1, -1, -1, -1, -1, -1, -1};
     if (const char *env = std::getenv("CONVT3D_PLAN")) {
-        const int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d,%d", &force[0], &force[1], &force[2], &force[3],
-                                    &force[4], &force[5], &force[6], &force[7]);
+        const int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &force[0], &force[1], &force[2], &force[3],
+                                    &force[4], &force[5], &force[6]);
         if (got < 6) force[0] = -1;
     }
     const bool forced = force[0] >= 0;
@@ -374,112 +374,101 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                 issued += rc[r].issued;
                 cost_regions += rc[r].cost;
             }
-            for (int nb = 1; nb <= 2; ++nb) {
-              // nb = 1: each chunk is staged while the workgroup waits; nb = 2: two
-              // halo buffers, chunk c + 1 loads while chunk c is multiplied.
-              // LDS of a workgroup for a channel chunk: the halo (256-float rounded,
-              // 64 floats of guard) per buffer, then the reduction scratch
-              const int red_floats = WPOS * CO_T * 32 * 2;
-              auto halo_floats = [&](int ci_t) { return (int)ceil_div((int64_t)ci_t * max_slab + 64, 256) * 256; };
-              auto nbuf_of = [&](int ci_t) { return (nb == 2 && !ploop && CI_pad > ci_t) ? 2 : 1; };
-              auto lds_of = [&](int ci_t) {
-                  return (int64_t)(nbuf_of(ci_t) * halo_floats(ci_t) + red_floats) * 4;
-              };
-              // largest channel chunk whose LDS still lets the register-limited number
-              // of workgroups share a CU (measured: occupancy beats fewer barriers)
-              int CI_T = 0;
-              for (int m = 4; m >= 1; m /= 2) {
-                  if (pl->octets % m != 0) continue;  // chunks never pass the packed octets
-                  const int64_t bytes = lds_of(m * kOctet);
-                  if (bytes > kMaxLdsBytes) continue;
-                  if (m > 1 && bytes * v.waves_per_simd > 160 * 1024) continue;
-                  CI_T = m * kOctet;
-                  break;
-              }
-              if (ploop) CI_T = lds_of(CI_pad) <= kMaxLdsBytes ? CI_pad : 0;
-              if (forced && force[5] > 0) {
-                  if (force[5] % kOctet || pl->octets % (force[5] / kOctet) || lds_of(force[5]) > kMaxLdsBytes)
-                      continue;
-                  CI_T = force[5];
-              }
-              if (CI_T == 0) continue;
-              if (nb == 2 && nbuf_of(CI_T) == 1) continue;  // one chunk: same plan as nb = 1
-              if (forced && force[7] >= 1 && nb != force[7]) continue;
-              const int nchunks = (int)ceil_div(CI_pad, CI_T);
-              const int64_t grid = nn * co_tiles * (s * s / npg) * nwg * tiles_total;
-              // whole rounds of workgroups over the CUs; workgroups per CU from the
-              // variant's register occupancy and the LDS size
-              const int lds_wg = (int)lds_of(CI_T);
-              const int per_cu = std::max(1, std::min(v.waves_per_simd, 160 * 1024 / lds_wg));
-              const double slots = 256.0 * per_cu;
-              const double rounds = std::ceil((double)grid / slots);
-              // exposed staging waits: co-resident workgroups advance in lockstep on
-              // the shared MFMA pipe, so a synchronous stage idles the CU (measured
-              // about 2000 CU cycles = 250k MAC-equivalents per chunk and workgroup)
-              double cost = cost_regions + (double)grid * kStageWaitMacs * (nb == 2 ? 1 : nchunks);
-              cost *= rounds * slots / (double)grid;
-              // few waves per SIMD hide less latency; fewer MFMA tiles per wave mean
-              // more operand traffic per MFMA
-              // (measured on MI355X: 3 workgroups per CU reach ~67% MFMA busy, 2 ~60%)
-              cost *= per_cu == 1 ? 1.35 : per_cu == 2 ? 1.15 : per_cu == 3 ? 1.04 : 1.0;
-              cost *= 1.0 + 0.15 / (v.CBW * v.PBW * v.NPH);
-              // measured: splitting the output channels over fewer waves (WCO < 4)
-              // costs MFMA issue rate when the channels could fill four waves
-              if (!softmax && WCO < 4 && pl->cb_total >= 4) cost *= WCO == 2 ? 1.1 : 1.2;
-              if ((int)top.size() < max_k || cost < top.back().first) {
-                  found = true;
-                  Plan c = *pl;
-                  c.variant = vi;
-                  c.CBW = v.CBW; c.NPH = v.NPH; c.PBW = v.PBW;
-                  c.WCO = WCO; c.WPOS = WPOS;
-                  c.nreg = nreg;
-                  int64_t off = 0;
-                  int r = 0;
-                  for (int i0 = 0; i0 < nseg[0]; ++i0)
-                      for (int i1 = 0; i1 < nseg[1]; ++i1)
-                          for (int i2 = 0; i2 < nseg[2]; ++i2, ++r) {
-                              const Seg sg[3] = {segs[0][i0], segs[1][i1], segs[2][i2]};
-                              for (int dim = 0; dim < 3; ++dim) {
-                                  c.rg[r][dim] = sg[dim].a;
-                                  c.rg[r][3 + dim] = sg[dim].b;
-                                  c.rg[r][6 + dim] = rc[r].box[dim];
-                                  c.rg[r][9 + dim] = rc[r].nt[dim];
-                              }
-                              c.rg_off[r] = (int)off;
-                              off += rc[r].tiles;
-                          }
-                  c.rg_off[nreg] = (int)off;
-                  c.tiles_total = (int)tiles_total;
-                  for (int dim = 0; dim < 3; ++dim) c.TQ[dim] = rc[big].box[dim];
-                  c.CI_T = CI_T; c.nchunks = nchunks;
-                  c.buf_stride = halo_floats(CI_T);
-                  c.nbuf = nbuf_of(CI_T);
-                  c.phase_loop = ploop;
-                  c.split = split;
-                  c.red_off = c.nbuf * c.buf_stride;
-                  c.lds_bytes = lds_wg;
-                  c.co_tiles = co_tiles; c.nwgroups = nwg;
-                  c.tiles_per_n = (int64_t)s * s * nwg * tiles_total;
-                  c.grid_x = tiles_total;
-                  c.grid_y = (int64_t)co_tiles * (s * s / npg) * nwg;
-                  c.grid_z = g->n;
-                  c.issued_macs = issued / nn * g->n;
-                  // packed weights that do not fit in half an L2: keep each XCD on
-                  // one (co tile, phase) group at a time (CONVT3D_ORDER overrides)
-                  c.order = (c.grid_y > 1 && pl->packed_floats * 4 > kL2Bytes / 2) ? 1 : 0;
-                  if (order_env >= 0) c.order = order_env;
-                  // the kernel forms a linear workgroup index in 32-bit arithmetic
-                  if (c.grid_x > INT32_MAX || c.grid_y > 65535 || c.grid_z > 65535 ||
-                      c.grid_x * c.grid_y * c.grid_z > INT32_MAX) {
-                      too_large = true;
-                      continue;
-                  }
-                  ws_layout(&c);
-                  auto at = top.begin();
-                  while (at != top.end() && at->first <= cost) ++at;
-                  top.insert(at, std::make_pair(cost, c));
-                  if ((int)top.size() > max_k) top.pop_back();
-              }
+            // LDS of a workgroup for a channel chunk: the halo (rounded to 256
+            // floats), then the reduction scratch
+            const int red_floats = WPOS * CO_T * 32 * 2;
+            auto halo_floats = [&](int ci_t) { return (int)ceil_div((int64_t)ci_t * max_slab, 256) * 256; };
+            auto lds_of = [&](int ci_t) { return (int64_t)(halo_floats(ci_t) + red_floats) * 4; };
+            // largest channel chunk whose LDS still lets the register-limited number
+            // of workgroups share a CU (measured: occupancy beats fewer barriers)
+            int CI_T = 0;
+            for (int m = 4; m >= 1; m /= 2) {
+                if (pl->octets % m != 0) continue;  // chunks never pass the packed octets
+                const int64_t bytes = lds_of(m * kOctet);
+                if (bytes > kMaxLdsBytes) continue;
+                if (m > 1 && bytes * v.waves_per_simd > 160 * 1024) continue;
+                CI_T = m * kOctet;
+                break;
+            }
+            if (ploop) CI_T = lds_of(CI_pad) <= kMaxLdsBytes ? CI_pad : 0;
+            if (forced && force[5] > 0) {
+                if (force[5] % kOctet || pl->octets % (force[5] / kOctet) || lds_of(force[5]) > kMaxLdsBytes)
+                    continue;
+                CI_T = force[5];
+            }
+            if (CI_T == 0) continue;
+            const int nchunks = (int)ceil_div(CI_pad, CI_T);
+            const int64_t grid = nn * co_tiles * (s * s / npg) * nwg * tiles_total;
+            // whole rounds of workgroups over the CUs; workgroups per CU from the
+            // variant's register occupancy and the LDS size
+            const int lds_wg = (int)lds_of(CI_T);
+            const int per_cu = std::max(1, std::min(v.waves_per_simd, 160 * 1024 / lds_wg));
+            const double slots = 256.0 * per_cu;
+            const double rounds = std::ceil((double)grid / slots);
+            // exposed staging waits: co-resident workgroups advance in lockstep on
+            // the shared MFMA pipe, so a stage idles the CU (measured about 2000 CU
+            // cycles = 250k MAC-equivalents per chunk and workgroup)
+            double cost = cost_regions + (double)grid * kStageWaitMacs * nchunks;
+            cost *= rounds * slots / (double)grid;
+            // few waves per SIMD hide less latency; fewer MFMA tiles per wave mean
+            // more operand traffic per MFMA
+            // (measured on MI355X: 3 workgroups per CU reach ~67% MFMA busy, 2 ~60%)
+            cost *= per_cu == 1 ? 1.35 : per_cu == 2 ? 1.15 : per_cu == 3 ? 1.04 : 1.0;
+            cost *= 1.0 + 0.15 / (v.CBW * v.PBW * v.NPH);
+            // measured: splitting the output channels over fewer waves (WCO < 4)
+            // costs MFMA issue rate when the channels could fill four waves
+            if (!softmax && WCO < 4 && pl->cb_total >= 4) cost *= WCO == 2 ? 1.1 : 1.2;
+            if ((int)top.size() < max_k || cost < top.back().first) {
+                found = true;
+                Plan c = *pl;
+                c.variant = vi;
+                c.CBW = v.CBW; c.NPH = v.NPH; c.PBW = v.PBW;
+                c.WCO = WCO; c.WPOS = WPOS;
+                c.nreg = nreg;
+                int64_t off = 0;
+                int r = 0;
+                for (int i0 = 0; i0 < nseg[0]; ++i0)
+                    for (int i1 = 0; i1 < nseg[1]; ++i1)
+                        for (int i2 = 0; i2 < nseg[2]; ++i2, ++r) {
+                            const Seg sg[3] = {segs[0][i0], segs[1][i1], segs[2][i2]};
+                            for (int dim = 0; dim < 3; ++dim) {
+                                c.rg[r][dim] = sg[dim].a;
+                                c.rg[r][3 + dim] = sg[dim].b;
+                                c.rg[r][6 + dim] = rc[r].box[dim];
+                                c.rg[r][9 + dim] = rc[r].nt[dim];
+                            }
+                            c.rg_off[r] = (int)off;
+                            off += rc[r].tiles;
+                        }
+                c.rg_off[nreg] = (int)off;
+                c.tiles_total = (int)tiles_total;
+                for (int dim = 0; dim < 3; ++dim) c.TQ[dim] = rc[big].box[dim];
+                c.CI_T = CI_T; c.nchunks = nchunks;
+                c.phase_loop = ploop;
+                c.split = split;
+                c.red_off = halo_floats(CI_T);
+                c.lds_bytes = lds_wg;
+                c.co_tiles = co_tiles; c.nwgroups = nwg;
+                c.tiles_per_n = (int64_t)s * s * nwg * tiles_total;
+                c.grid_x = tiles_total;
+                c.grid_y = (int64_t)co_tiles * (s * s / npg) * nwg;
+                c.grid_z = g->n;
+                c.issued_macs = issued / nn * g->n;
+                // packed weights that do not fit in half an L2: keep each XCD on
+                // one (co tile, phase) group at a time (CONVT3D_ORDER overrides)
+                c.order = (c.grid_y > 1 && pl->packed_floats * 4 > kL2Bytes / 2) ? 1 : 0;
+                if (order_env >= 0) c.order = order_env;
+                // the kernel forms a linear workgroup index in 32-bit arithmetic
+                if (c.grid_x > INT32_MAX || c.grid_y > 65535 || c.grid_z > 65535 ||
+                    c.grid_x * c.grid_y * c.grid_z > INT32_MAX) {
+                    too_large = true;
+                    continue;
+                }
+                ws_layout(&c);
+                auto at = top.begin();
+                while (at != top.end() && at->first <= cost) ++at;
+                top.insert(at, std::make_pair(cost, c));
+                if ((int)top.size() > max_k) top.pop_back();
             }
            }
           }
@@ -516,7 +505,7 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->cb_total = pl.cb_total;
     cp->WCO = pl.WCO; cp->WPOS = pl.WPOS;
     cp->co_tiles = pl.co_tiles; cp->nwgroups = pl.nwgroups;
-    cp->buf_stride = pl.buf_stride; cp->nbuf = pl.nbuf;
+
     cp->nxcd = kNumXcd;
     cp->order = pl.order;
     cp->phase_loop = pl.phase_loop; cp->red_off = pl.red_off;

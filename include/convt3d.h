@@ -137,7 +137,9 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias,
  * computes the same result up to float summation order.  Unlike
  * convt3d_fused it waits on the device (it times the candidates with HIP
  * events on `stream`).  Candidates needing more workspace than
- * workspace_bytes are skipped.  result may be NULL. */
+ * workspace_bytes are skipped.  result may be NULL.  The best 8 candidates
+ * are timed (environment CONVT3D_TUNE_CANDIDATES=1..64 changes that;
+ * CONVT3D_TUNE_LOG prints one line per candidate to stderr). */
 typedef struct convt3d_tune_result {
     int32_t candidates;      /* plans timed                                      */
     int32_t chosen;          /* rank of the chosen plan in cost-model order (0 = the model's pick) */
@@ -162,7 +164,6 @@ typedef struct convt3d_plan_info {
     int64_t issued_macs;       /* multiply-adds the matrix cores execute (incl. padding) */
     int64_t valid_macs;        /* multiply-adds whose input voxel is in range          */
     int32_t phase_loop;        /* 1: a workgroup covers every (d, h) stride phase       */
-    int32_t halo_buffers;      /* 2: next channel chunk staged during this one's MFMAs  */
     int32_t tuned;             /* 1: chosen by convt3d_autotune                         */
     int32_t border_split;      /* dims split into border / interior tile regions (bit 0 d, 1 h, 2 w) */
     int32_t xcd_order;         /* 0: phase / channel-tile index fastest per XCD, 1: tile fastest */
