@@ -197,10 +197,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
         jw_hi[p] = min(Jw[p] - 1, q0w + TQw_e - 1 + cw[p]);
     }
 
-    // ---- LDS layout of a staged chunk: [octet][d][h][w][8].  The 8 channels of
-    // an octet at one halo position are adjacent, in the order 0,2,4,6,1,3,5,7:
-    // the lanes that feed MFMA k-row h (h = lane/32) need channels h, h+2, h+4,
-    // h+6 for the 4 k-steps of a group, and read them with one 16-byte LDS read.
+    // ---- LDS layout of a staged chunk: float4 [octet][k-row h][d][h][w].  The
+    // lanes that feed MFMA k-row h (h = lane/32) need channels h, h+2, h+4, h+6
+    // of an octet for the 4 k-steps of a group: they sit in one float4, read
+    // with one 16-byte LDS read, and the 32 lanes of a k-row read consecutive
+    // float4s along w (no bank conflicts).
     const int SLAB = HD * HH * HW;  // halo positions per octet
     const int vol = TQd * TQh * TQw;
     const int plane = TQh * TQw;
@@ -218,12 +219,12 @@ void convt3d_mfma_kernel(const ConvParams P) {
         tw = rem - th * TQw;
         return pidx < vol && td < TQd_e && th < TQh_e && tw < TQw_e;
     };
-    int lane_off[PBW];  // float offset of the lane's B reads at tap offset 0
+    int lane_off[PBW];  // float4 index of the lane's B reads at tap offset 0
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
         int td, th, tw;
         decode_pos(pb, td, th, tw);
-        lane_off[pb] = ((td * HH + th) * HW + tw) * 8 + half * 4;
+        lane_off[pb] = half * SLAB + (td * HH + th) * HW + tw;
     }
 
     const int CO_T = P.WCO * CBW;                   // co blocks per workgroup
@@ -268,9 +269,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                         for (int c = 0; c < 8; ++c) v[c] = ci0 + c < P.Cin ? src[(size_t)c * DHWin] : 0.0f;
                     }
-                    float4 *dst = reinterpret_cast<float4 *>(lds + ((size_t)g * SLAB + pos) * 8);
+                    float4 *dst = reinterpret_cast<float4 *>(lds) + (2 * g * SLAB + pos);
                     dst[0] = make_float4(v[0], v[2], v[4], v[6]);
-                    dst[1] = make_float4(v[1], v[3], v[5], v[7]);
+                    dst[SLAB] = make_float4(v[1], v[3], v[5], v[7]);
                 }
             }
             w += inc_w;
@@ -334,12 +335,12 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 const int n_it = (jd_hi - jd_lo + 1) * (jh_hi - jh_lo + 1) * (jwh - jwl + 1) * G4;
                 // Iteration state (jd, jh, jw, g4) of the next group to load; every
                 // group is 4 MFMA k-steps = 8 input channels of one tap.  gi: float4
-                // index of its A operands; bo: float offset of its B operands.
+                // index of its A operands; bo: float4 offset of its B operands.
                 int jd = jd_lo, jh = jh_lo, jw = jwl, g4 = 0;
                 auto next_group = [&](int &gi, int &bo) {
                     gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
-                    bo = (((cd - jd - lo_d_rel) * HH + (ch - jh - lo_h_rel)) * HW + (cwp - jw - lo_w_rel) +
-                          g4 * SLAB) * 8;
+                    bo = ((cd - jd - lo_d_rel) * HH + (ch - jh - lo_h_rel)) * HW + (cwp - jw - lo_w_rel) +
+                         2 * g4 * SLAB;
                     if (++g4 == G4) {
                         g4 = 0;
                         if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } }
@@ -349,10 +350,10 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 // come from one 16-byte LDS read per position block, issued one
                 // group ahead.
                 float4 bA[PBW], bB[PBW];
+                const float4 *lds4 = reinterpret_cast<const float4 *>(lds);
                 auto read_b = [&](float4 (&b)[PBW], int bo) {
 #pragma unroll
-                    for (int pb = 0; pb < PBW; ++pb)
-                        b[pb] = *reinterpret_cast<const float4 *>(lds + lane_off[pb] + bo);
+                    for (int pb = 0; pb < PBW; ++pb) b[pb] = lds4[lane_off[pb] + bo];
                 };
                 auto group_mfma = [&](const float4 (&a)[CBW], const float4 (&b)[PBW]) {
 #pragma unroll
