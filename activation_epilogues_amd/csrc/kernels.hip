@@ -394,9 +394,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
     }
 
     // ------------------------------------------------------------------ epilogue
+    // Accumulator register r of co block c holds output channel
+    // row0 + 32c + 8(r/4) + r%4 + 4*half at the lane's column position.  Store
+    // addresses are a wave-uniform row base (scalar registers) plus the lane's
+    // byte offset, formed once per position block: no vector address math per
+    // store.
     const int Do = P.Do, Ho = P.Ho, Wo = P.Wo;
-    const size_t S = (size_t)Do * Ho * Wo;
-    int sp[NPH][PBW];
+    const int S = Do * Ho * Wo;  // the planner keeps 20*S (the largest byte offset) below 2^32
+    unsigned vofs[NPH][PBW];     // byte offset of the lane's output from its row base
     bool ok[NPH][PBW];
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
@@ -408,7 +413,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
         for (int p = 0; p < NPH; ++p) {
             const int ow = s * (q0w + tw) + rw[p];
             ok[p][pb] = pos_ok && od < Do && oh < Ho && ow < Wo;
-            sp[p][pb] = (od * Ho + oh) * Wo + ow;
+            vofs[p][pb] = (unsigned)(4 * half * S + (od * Ho + oh) * Wo + ow) * 4u;
         }
     }
     // both w-phases of a lane land in one aligned float pair (w even, w + 1)
@@ -420,13 +425,31 @@ void convt3d_mfma_kernel(const ConvParams P) {
             pair_ok[pb] = ok[0][pb] && ok[1][pb] && (Wo % 2 == 0);  // rw[0] is even when NPH == 2
     }
     const int Cout = P.Cout;
-    // first output channel of the lane's accumulator rows; inside the phase-group
-    // loop it is made opaque so the per-row channel indices and store addresses
-    // are formed here, not hoisted out of the loop and kept live across the MFMAs
-    int co_lane = cb0 * 32 + 4 * half;
-    if constexpr (PL) asm volatile("" : "+v"(co_lane));
-    const float *bias = P.bias;
-    float *outn = P.out + (size_t)n * Cout * S;
+    // first output channel of the wave; inside the phase-group loop it is made
+    // opaque so the row bases are formed here, not hoisted out of the loop and
+    // kept live across the MFMAs
+    int row0 = cb0 * 32;
+    if constexpr (PL) asm volatile("" : "+s"(row0));
+    const bool rows_full = row0 + CBW * 32 <= Cout;  // every accumulator row is a channel
+    char *outb = reinterpret_cast<char *>(P.out + (size_t)n * Cout * S);
+    auto row_u = [&](int c, int r) { return row0 + c * 32 + 8 * (r >> 2) + (r & 3); };
+    auto row_ok = [&](int c, int r) { return rows_full || row_u(c, r) + 4 * half < Cout; };
+    auto rowp = [&](int c, int r) { return outb + (size_t)row_u(c, r) * S * 4; };
+    auto bias_of = [&](int c, int r, float dflt) {  // bias of the lane's row c, r (dflt: no bias)
+        return P.bias ? P.bias[row_u(c, r) + 4 * half] : dflt;
+    };
+    // the stores of one accumulator row (c, r) of position block pb
+    auto store_row = [&](char *rp, int pb, const float (&v)[NPH]) {
+        if constexpr (NPH == 2) {
+            if (pair_ok[pb]) {
+                *reinterpret_cast<float2 *>(rp + vofs[0][pb]) = make_float2(v[0], v[1]);
+                return;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NPH; ++p)
+            if (ok[p][pb]) *reinterpret_cast<float *>(rp + vofs[p][pb]) = v[p];
+    };
 
     if constexpr (SM) {
         // Channel softmax + sigmoid.  The wave holds every channel of its columns
@@ -436,8 +459,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = co_lane + c * 32 + 8 * (r >> 2) + (r & 3);
-                const float bco = (co < Cout) ? (bias ? bias[co] : 0.0f) : -INFINITY;
+                const float bco = row_ok(c, r) ? bias_of(c, r, 0.0f) : -INFINITY;
 #pragma unroll
                 for (int p = 0; p < NPH; ++p)
 #pragma unroll
@@ -468,36 +490,30 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         sum += e;
                     }
                 sum += __shfl_xor(sum, 32);
-                const float inv = __builtin_amdgcn_rcpf(sum);
+                // sigmoid(e/sum) = 1 / (1 + 2^(e * (-log2 e / sum)))
+                const float ninv = -kLog2e * __builtin_amdgcn_rcpf(sum);
 #pragma unroll
                 for (int c = 0; c < CBW; ++c)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float pr = acc[p][c][pb][r] * inv;
-                        acc[p][c][pb][r] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-pr * kLog2e));
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        acc[p][c][pb][r] =
+                            __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc[p][c][pb][r] * ninv));
             }
         // stores: with two w-phases the lane holds outputs at w and w+1
 #pragma unroll
-        for (int pb = 0; pb < PBW; ++pb)
+        for (int c = 0; c < CBW; ++c)
 #pragma unroll
-            for (int c = 0; c < CBW; ++c)
+            for (int r = 0; r < 16; ++r) {
+                if (!row_ok(c, r)) continue;
+                char *rp = rowp(c, r);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int co = co_lane + c * 32 + 8 * (r >> 2) + (r & 3);
-                    if (co >= Cout) continue;
-                    float *dst = outn + (size_t)co * S;
-                    if constexpr (NPH == 2) {
-                        if (pair_ok[pb]) {
-                            *reinterpret_cast<float2 *>(dst + sp[0][pb]) =
-                                make_float2(acc[0][c][pb][r], acc[1][c][pb][r]);
-                            continue;
-                        }
-                    }
+                for (int pb = 0; pb < PBW; ++pb) {
+                    float v[NPH];
 #pragma unroll
-                    for (int p = 0; p < NPH; ++p)
-                        if (ok[p][pb]) dst[sp[p][pb]] = acc[p][c][pb][r];
+                    for (int p = 0; p < NPH; ++p) v[p] = acc[p][c][pb][r];
+                    store_row(rp, pb, v);
                 }
+            }
     } else {
         // bias (+ReLU) and store, or scale; per-channel sums over the tile: the
         // lane's columns, then the 32 columns of each half (xor shuffles), then
@@ -512,11 +528,10 @@ void convt3d_mfma_kernel(const ConvParams P) {
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int co = co_lane + c * 32 + 8 * (r >> 2) + (r & 3);
-                const bool cok = co < Cout;
-                const float bco = (cok && bias) ? bias[co] : 0.0f;
+                const bool cok = row_ok(c, r);
+                const float bco = cok ? bias_of(c, r, 0.0f) : 0.0f;
                 float a1 = 0.0f, a2 = 0.0f;
-                float *dst = outn + (size_t)co * S;
+                char *rp = rowp(c, r);
 #pragma unroll
                 for (int pb = 0; pb < PBW; ++pb) {
                     float v[NPH];
@@ -525,21 +540,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         v[p] = acc[p][c][pb][r] + bco;
                         if (gn) v[p] = fmaxf(v[p], 0.0f);
                         if (bn) v[p] = scale * v[p];
-                        if (cok && ok[p][pb]) {
-                            a1 += v[p];
-                            a2 += v[p] * v[p];
-                        }
+                        const float vm = ok[p][pb] ? v[p] : 0.0f;
+                        a1 += vm;
+                        a2 = fmaf(vm, vm, a2);
                     }
-                    if (!cok || bn) continue;
-                    if constexpr (NPH == 2) {
-                        if (pair_ok[pb]) {
-                            *reinterpret_cast<float2 *>(dst + sp[0][pb]) = make_float2(v[0], v[1]);
-                            continue;
-                        }
-                    }
-#pragma unroll
-                    for (int p = 0; p < NPH; ++p)
-                        if (ok[p][pb]) dst[sp[p][pb]] = v[p];
+                    if (cok && !bn) store_row(rp, pb, v);
                 }
                 if (gn || bn) {
 #pragma unroll
@@ -547,7 +552,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         a1 += __shfl_xor(a1, off);
                         a2 += __shfl_xor(a2, off);
                     }
-                    if (col == 0) {
+                    if (col == 0 && cok) {
                         const int row = (wco * CBW + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                         red[(wpos * CO32 + row) * 2 + 0] = a1;
                         red[(wpos * CO32 + row) * 2 + 1] = a2;

@@ -144,6 +144,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     Plan base{};
     Plan *pl = &base;
     int st = make_geometry(g, pl);
+    // the conv kernel addresses an output row pair with 32-bit byte offsets
+    if (st == CONVT3D_OK && pl->S * 20 >= (int64_t(1) << 32)) st = CONVT3D_ERR_TOO_LARGE;
     if (st) return st;
     pl->e = *e;
     if (e->kind < CONVT3D_EPI_NONE || e->kind > CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL)
