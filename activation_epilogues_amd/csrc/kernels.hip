@@ -632,22 +632,39 @@ __global__ __launch_bounds__(256) void gn_finalize_kernel(const float *partials,
 }
 
 // out = a[row] * out + b[row] for rows of S elements (S % 4 == 0: float4 path).
-__global__ __launch_bounds__(256) void normalize4_kernel(float4 *out, const float2 *ab, int n4, int S4) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
-        const float2 p = ab[i / S4];
-        float4 v = out[i];
-        v.x = fmaf(p.x, v.x, p.y);
-        v.y = fmaf(p.x, v.y, p.y);
-        v.z = fmaf(p.x, v.z, p.y);
-        v.w = fmaf(p.x, v.w, p.y);
-        out[i] = v;
-    }
-}
-
-__global__ __launch_bounds__(256) void normalize1_kernel(float *out, const float2 *ab, int n1, int S) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n1; i += gridDim.x * blockDim.x) {
-        const float2 p = ab[i / S];
-        out[i] = fmaf(p.x, out[i], p.y);
+// GroupNorm normalisation in place, out = a[n,c] * out + b[n,c].  Block row y
+// is one (n, c) channel (rows beyond gridDim.y are taken in further passes),
+// so (a, b) is one scalar load; each thread issues kNormUnroll loads before
+// its stores to keep enough bytes in flight for HBM.
+constexpr int kNormUnroll = 4;
+template <class V>
+__global__ __launch_bounds__(256) void normalize_kernel(V *out, const float2 *ab, int rows, int row_len) {
+    for (int row = blockIdx.y; row < rows; row += gridDim.y) {
+        const float2 p = ab[row];
+        V *o = out + (size_t)row * row_len;
+        const int base = blockIdx.x * (256 * kNormUnroll) + threadIdx.x;
+        V v[kNormUnroll];
+#pragma unroll
+        for (int k = 0; k < kNormUnroll; ++k) {
+            const int i = base + k * 256;
+            if (i < row_len) v[k] = o[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kNormUnroll; ++k) {
+            const int i = base + k * 256;
+            if (i < row_len) {
+                if constexpr (sizeof(V) == 16) {
+                    float4 &x = reinterpret_cast<float4 &>(v[k]);
+                    x.x = fmaf(p.x, x.x, p.y);
+                    x.y = fmaf(p.x, x.y, p.y);
+                    x.z = fmaf(p.x, x.z, p.y);
+                    x.w = fmaf(p.x, x.w, p.y);
+                } else {
+                    reinterpret_cast<float &>(v[k]) = fmaf(p.x, reinterpret_cast<float &>(v[k]), p.y);
+                }
+                o[i] = v[k];
+            }
+        }
     }
 }
 
@@ -799,16 +816,18 @@ int launch_gn_finalize(const Plan &pl, const float *partials, const float *gamma
 }
 
 int launch_normalize(const Plan &pl, float *out, const float *ab, void *stream) {
-    const int64_t total = (int64_t)pl.g.n * pl.g.cout * pl.S;
+    const int rows = pl.g.n * pl.g.cout;
+    const int gy = rows < 65535 ? rows : 65535;
     if (pl.S % 4 == 0) {
-        const int n4 = (int)(total / 4);
-        hipLaunchKernelGGL(normalize4_kernel, dim3(grid_for(n4, 256, 256 * 64)), dim3(256), 0,
-                           (hipStream_t)stream, reinterpret_cast<float4 *>(out),
-                           reinterpret_cast<const float2 *>(ab), n4, (int)(pl.S / 4));
+        const int len = (int)(pl.S / 4);
+        const int gx = (len + 256 * kNormUnroll - 1) / (256 * kNormUnroll);
+        hipLaunchKernelGGL(normalize_kernel<float4>, dim3(gx, gy), dim3(256), 0, (hipStream_t)stream,
+                           reinterpret_cast<float4 *>(out), reinterpret_cast<const float2 *>(ab), rows, len);
     } else {
-        hipLaunchKernelGGL(normalize1_kernel, dim3(grid_for(total, 256, 256 * 64)), dim3(256), 0,
-                           (hipStream_t)stream, out, reinterpret_cast<const float2 *>(ab), (int)total,
-                           (int)pl.S);
+        const int len = (int)pl.S;
+        const int gx = (len + 256 * kNormUnroll - 1) / (256 * kNormUnroll);
+        hipLaunchKernelGGL(normalize_kernel<float>, dim3(gx, gy), dim3(256), 0, (hipStream_t)stream, out,
+                           reinterpret_cast<const float2 *>(ab), rows, len);
     }
     return (int)hipGetLastError();
 }
