@@ -97,7 +97,9 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // live tap of every phase runs 4 MFMA k-steps per 8 input channels.
 template <int CBW, int NPH, int PBW, bool SM, bool PL>
 __global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
-                                          : (CBW * NPH * PBW <= 2) ? 6 : (CBW * NPH * PBW <= 4) ? 3
+                                          : (CBW * NPH * PBW <= 2) ? 6
+                                          : (CBW * NPH * PBW == 4 && PBW == 4) ? 4
+                                          : (CBW * NPH * PBW <= 4) ? 3
                                           : (CBW * NPH * PBW <= 8) ? 2 : 1)
 void convt3d_mfma_kernel(const ConvParams P) {
     extern __shared__ float lds[];
@@ -349,45 +351,91 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 // One group = 4 MFMA k-steps; its B operands (4 per position block)
                 // come from one 16-byte LDS read per position block, issued one
                 // group ahead.
-                float4 bA[PBW], bB[PBW];
                 const float4 *lds4 = reinterpret_cast<const float4 *>(lds);
-                auto read_b = [&](float4 (&b)[PBW], int bo) {
-#pragma unroll
-                    for (int pb = 0; pb < PBW; ++pb) b[pb] = lds4[lane_off[pb] + bo];
-                };
-                auto group_mfma = [&](const float4 (&a)[CBW], const float4 (&b)[PBW]) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-#pragma unroll
-                        for (int c = 0; c < CBW; ++c)
-#pragma unroll
-                            for (int pb = 0; pb < PBW; ++pb)
-                                acc[p][c][pb] = mfma32x32x2(a[c][e], b[pb][e], acc[p][c][pb]);
-                };
-                // Two A and two B register sets in flight; loads are always issued
-                // (the last ones repeat a valid group) so the wait counts stay static.
                 float4 aA[CBW], aB[CBW];
                 int giA, boA, giB, boB;
                 next_group(giA, boA);
 #pragma unroll
                 for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
-                read_b(bA, boA);
-                for (int it = 0; it < n_it; it += 2) {
-                    if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
+                if constexpr (PBW >= 4) {
+                    // One B register set: a position block's registers are refilled
+                    // with the next group's B right after their last MFMA (k-step 3);
+                    // the other position blocks' MFMAs cover the LDS latency.
+                    float4 bq[PBW];
 #pragma unroll
-                    for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
-                    read_b(bB, boB);
-                    __builtin_amdgcn_sched_barrier(0);
-                    group_mfma(aA, bA);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (it + 1 >= n_it) break;
-                    if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
+                    for (int pb = 0; pb < PBW; ++pb) bq[pb] = lds4[lane_off[pb] + boA];
+                    auto group_mfma = [&](const float4 (&a)[CBW], int bo_next) {
 #pragma unroll
-                    for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                        for (int e = 0; e < 3; ++e)
+#pragma unroll
+                            for (int c = 0; c < CBW; ++c)
+#pragma unroll
+                                for (int pb = 0; pb < PBW; ++pb)
+                                    acc[p][c][pb] = mfma32x32x2(a[c][e], bq[pb][e], acc[p][c][pb]);
+#pragma unroll
+                        for (int pb = 0; pb < PBW; ++pb) {
+#pragma unroll
+                            for (int c = 0; c < CBW; ++c)
+                                acc[p][c][pb] = mfma32x32x2(a[c][3], bq[pb][3], acc[p][c][pb]);
+                            bq[pb] = lds4[lane_off[pb] + bo_next];
+                        }
+                        __builtin_amdgcn_sched_group_barrier(0x008, 3 * CBW * PBW, 0);
+#pragma unroll
+                        for (int pb = 0; pb < PBW; ++pb) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, CBW, 0);  // CBW MFMAs
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
+                        }
+                    };
+                    for (int it = 0; it < n_it; it += 2) {
+                        if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
+#pragma unroll
+                        for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
+                        __builtin_amdgcn_sched_barrier(0);
+                        group_mfma(aA, boB);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (it + 1 >= n_it) break;
+                        if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
+#pragma unroll
+                        for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                        __builtin_amdgcn_sched_barrier(0);
+                        group_mfma(aB, boA);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                } else {
+                    // Two B register sets: the next group's B is read before this
+                    // group's MFMAs.
+                    float4 bA[PBW], bB[PBW];
+                    auto read_b = [&](float4 (&b)[PBW], int bo) {
+#pragma unroll
+                        for (int pb = 0; pb < PBW; ++pb) b[pb] = lds4[lane_off[pb] + bo];
+                    };
+                    auto group_mfma = [&](const float4 (&a)[CBW], const float4 (&b)[PBW]) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+#pragma unroll
+                            for (int c = 0; c < CBW; ++c)
+#pragma unroll
+                                for (int pb = 0; pb < PBW; ++pb)
+                                    acc[p][c][pb] = mfma32x32x2(a[c][e], b[pb][e], acc[p][c][pb]);
+                    };
                     read_b(bA, boA);
-                    __builtin_amdgcn_sched_barrier(0);
-                    group_mfma(aB, bB);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int it = 0; it < n_it; it += 2) {
+                        if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
+#pragma unroll
+                        for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
+                        read_b(bB, boB);
+                        __builtin_amdgcn_sched_barrier(0);
+                        group_mfma(aA, bA);
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (it + 1 >= n_it) break;
+                        if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
+#pragma unroll
+                        for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                        read_b(bA, boA);
+                        __builtin_amdgcn_sched_barrier(0);
+                        group_mfma(aB, bB);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
         }
