@@ -538,14 +538,32 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         sum += e;
                     }
                 sum += __shfl_xor(sum, 32);
-                // sigmoid(e/sum) = 1 / (1 + 2^(e * (-log2 e / sum)))
-                const float ninv = -kLog2e * __builtin_amdgcn_rcpf(sum);
+                // sigmoid(q) for the probability q = e/sum in [0, 1]: the degree-6
+                // Chebyshev interpolant of sigmoid on [0, 1] (|error| < 1e-7; the
+                // coefficients are printed by sigmoid_poly.py beside this file),
+                // sum_k c_k q^k = sum_k (c_k / sum^k) e^k by Horner's rule in e.
+                const float inv = __builtin_amdgcn_rcpf(sum);
+                constexpr float kSig[7] = {5.000000000e-01f,  2.500010431e-01f, -1.699157474e-05f,
+                                           -2.072521672e-02f, -3.389832564e-04f, 2.655707300e-03f,
+                                           -5.169519573e-04f};
+                float d[7];
+                d[0] = kSig[0];
+                float ik = inv;
+#pragma unroll
+                for (int k = 1; k < 7; ++k) {
+                    d[k] = kSig[k] * ik;
+                    ik *= inv;
+                }
 #pragma unroll
                 for (int c = 0; c < CBW; ++c)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[p][c][pb][r] =
-                            __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc[p][c][pb][r] * ninv));
+                    for (int r = 0; r < 16; ++r) {
+                        const float e = acc[p][c][pb][r];
+                        float y = d[6];
+#pragma unroll
+                        for (int k = 5; k >= 0; --k) y = fmaf(y, e, d[k]);
+                        acc[p][c][pb][r] = y;
+                    }
             }
         // stores: with two w-phases the lane holds outputs at w and w+1
 #pragma unroll
