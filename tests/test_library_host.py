@@ -193,3 +193,23 @@ def test_plan_string_selects_the_same_plan(monkeypatch):
         monkeypatch.setenv("CONVT3D_PHASE_LOOP", str(info["phase_loop"]))
         again = C.convt3d_get_plan_info(geom_of(wl), e)
         assert again == info, wl.name
+
+
+def test_sigmoid_polynomial_matches_its_generator():
+    """The softmax epilogue's sigmoid coefficients are the ones sigmoid_poly.py
+    derives, and their float32 Horner evaluation stays within 1e-7 of the
+    definition on [0, 1]."""
+    import importlib.util
+    csrc = os.path.join(ROOT, "activation_epilogues_amd", "csrc")
+    spec = importlib.util.spec_from_file_location("sigmoid_poly", os.path.join(csrc, "sigmoid_poly.py"))
+    sp = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(sp)
+    want = sp.coefficients()
+    src = open(os.path.join(csrc, "kernels.hip")).read()
+    m = re.search(r"kSig\[7\]\s*=\s*\{([^}]*)\}", src)
+    assert m
+    got = np.array([float(t.strip().rstrip("f")) for t in m.group(1).split(",")], dtype=np.float32)
+    assert np.array_equal(got, want)
+    p = np.linspace(0.0, 1.0, 100001).astype(np.float32)
+    err = np.abs(sp.horner32(got, p).astype(np.float64) - 1.0 / (1.0 + np.exp(-p.astype(np.float64)))).max()
+    assert err < 1e-7
