@@ -24,8 +24,9 @@ struct CacheKey {
     int kind, groups;
     char plan_env[64];  // CONVT3D_PLAN tile override, CONVT3D_PHASE_LOOP, CONVT3D_ORDER, if any
     bool operator==(const CacheKey &o) const {
+        // plan_env holds NUL-separated fields (zero-filled): compare all bytes
         return std::memcmp(&g, &o.g, sizeof(g)) == 0 && kind == o.kind && groups == o.groups &&
-               std::strncmp(plan_env, o.plan_env, sizeof(plan_env)) == 0;
+               std::memcmp(plan_env, o.plan_env, sizeof(plan_env)) == 0;
     }
 };
 

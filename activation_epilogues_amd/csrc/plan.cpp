@@ -204,7 +204,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     // CONVT3D_PLAN="variant,WCO,TQd,TQh,TQw,CI_T[,split]" restricts the search
     // to that variant / wave grid / chunk, with that box in the largest region
     // and (bit 0 d, 1 h, 2 w) those dims split into border / interior segments
-    // (ignored if it does not fit).
+    // (ignored if it does not fit).  A negative field leaves that choice free
+    // (the box needs all three of TQd, TQh, TQw to be fixed).
     int force[7] = {-1, -1, -1, -1, -1, -1, -1};
     if (const char *env = std::getenv("CONVT3D_PLAN")) {
         const int got = std::sscanf(env, "%d,%d,%d,%d,%d,%d,%d", &force[0], &force[1], &force[2], &force[3],
@@ -231,7 +232,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         if (softmax && v.CBW >= 2 * pl->cb_total) continue;  // keep only the tightest fit
         for (int WCO = 1; WCO <= 4; WCO *= 2) {
           const int WPOS = 4 / WCO;
-          if (forced && WCO != force[1]) continue;
+          if (forced && force[1] >= 0 && WCO != force[1]) continue;
           // which dims are split into border / interior segments
           for (int split = 0; split < 8; ++split) {
            // ploop: one workgroup loops over every (rho_d, rho_h) group on one staged
@@ -299,7 +300,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                                 int mind = std::max(1, (PT - 32) / (TQw * TQh));
                                 if (mind > maxd) mind = maxd;
                                 for (int TQd = mind; TQd <= maxd; ++TQd) {
-                                    if (forced && nreg == big &&
+                                    if (forced && nreg == big && force[2] >= 0 && force[3] >= 0 && force[4] >= 0 &&
                                         (TQd != force[2] || TQh != force[3] || TQw != force[4]))
                                         continue;
                                     int HD = 1, HH = 1, HW = TQw;

@@ -213,3 +213,20 @@ def test_sigmoid_polynomial_matches_its_generator():
     p = np.linspace(0.0, 1.0, 100001).astype(np.float32)
     err = np.abs(sp.horner32(got, p).astype(np.float64) - 1.0 / (1.0 + np.exp(-p.astype(np.float64)))).max()
     assert err < 1e-7
+
+
+def test_plan_cache_keys_on_every_override(monkeypatch):
+    """A plan cached for a geometry is not reused under a different phase-loop or
+    work-order override (the overrides are part of the cache key)."""
+    g = C.make_geom(2, 20, 40, 7, 9, 11, 3, 2, 1, 1)
+    e = C.make_epilogue(1, 4)
+    monkeypatch.delenv("CONVT3D_PLAN", raising=False)
+    monkeypatch.setenv("CONVT3D_PHASE_LOOP", "0")
+    assert C.convt3d_get_plan_info(g, e)["phase_loop"] == 0
+    monkeypatch.setenv("CONVT3D_PHASE_LOOP", "1")
+    assert C.convt3d_get_plan_info(g, e)["phase_loop"] == 1
+    monkeypatch.delenv("CONVT3D_PHASE_LOOP")
+    monkeypatch.setenv("CONVT3D_ORDER", "0")
+    assert C.convt3d_get_plan_info(g, e)["xcd_order"] == 0
+    monkeypatch.setenv("CONVT3D_ORDER", "1")
+    assert C.convt3d_get_plan_info(g, e)["xcd_order"] == 1
