@@ -286,6 +286,10 @@ void convt3d_mfma_kernel(const ConvParams P) {
     stage(0);
     __syncthreads();
 
+    // a wave whose position blocks all lie past the box volume, or wholly in
+    // the d-overhang at a region's end (d is the slowest index), runs no MFMAs
+    const bool wave_live = min(vol, TQd_e * plane) > wpos * PBW * 32;
+
   for (int pgi = 0; pgi < npg; ++pgi) {
     const int pg = pg0 + pgi;
     const int rho_h = pg % s;
@@ -324,7 +328,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
             }
 #pragma unroll
             for (int p = 0; p < NPH; ++p) {
-                if (Jw[p] == 0 || jw_lo[p] > jw_hi[p]) continue;
+                if (!wave_live || Jw[p] == 0 || jw_lo[p] > jw_hi[p]) continue;
                 const int ph = (rho_d * s + rho_h) * s + rw[p];
                 const int ntp = P.ntaps[ph];
                 const int jwl = jw_lo[p], jwh = jw_hi[p], jwn = Jw[p], cwp = cw[p];

@@ -199,6 +199,22 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         }
         return t;
     };
+    // the same along d, each d-tile's live taps weighted by the output columns
+    // its workgroup runs MFMAs for: whole waves of wave_cols positions up to
+    // the rows the tile has (the kernel skips waves with no tile position)
+    auto seg_live_cols = [&](int rho, const Seg &sg, int tq, int plane, int wave_cols, int pt) {
+        const DimPhase &d = pl->ph[0][rho];
+        if (d.J == 0) return (int64_t)0;
+        int64_t t = 0;
+        for (int q0 = sg.a; q0 < sg.b; q0 += tq) {
+            const int te = std::min(tq, sg.b - q0);
+            const int lo = std::max(0, q0 + d.c - (ins[0] - 1));
+            const int hi = std::min(d.J - 1, q0 + te - 1 + d.c);
+            const int64_t cols = std::min<int64_t>(pt, ceil_div((int64_t)te * plane, wave_cols) * wave_cols);
+            if (hi >= lo) t += (hi - lo + 1) * cols;
+        }
+        return t;
+    };
 
     // Optional override for tile sweeps:
     // CONVT3D_PLAN="variant,WCO,TQd,TQh,TQw,CI_T[,split]" restricts the search
@@ -327,7 +343,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                                     const int64_t tiles = (int64_t)nt[0] * nt[1] * nt[2];
                                     int64_t taps = 0, halo = 0;
                                     for (int rd = 0; rd < s; ++rd) {
-                                        const int64_t ld = seg_live(0, rd, sd, TQd);
+                                        const int64_t ld = seg_live_cols(rd, sd, TQd, TQh * TQw, v.PBW * 32, PT);
                                         for (int rh = 0; rh < s; ++rh) {
                                             const int64_t lh = seg_live(1, rh, sh, TQh);
                                             int64_t lw = 0;
@@ -339,7 +355,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                                                         (TQh + pl->ph[1][rh].J - 1) * halo_w(TQw, wg);
                                         }
                                     }
-                                    const int64_t issued = nn * co_tiles * CO_T * 32 * (int64_t)PT * CI_pad * taps;
+                                    // taps already carries the live output columns of each tile
+                                    const int64_t issued = nn * co_tiles * CO_T * 32 * CI_pad * taps;
                                     const int64_t staged = nn * co_tiles * tiles * CI_pad * halo;
                                     if (ploop)
                                         for (int wg = 0; wg < nwg; ++wg) halo += (int64_t)HD * HH * halo_w(TQw, wg);
