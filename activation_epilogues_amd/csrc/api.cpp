@@ -37,7 +37,7 @@ int tune_candidates() {
         const int k = std::atoi(env);
         if (k >= 1 && k <= 64) return k;
     }
-    return 8;
+    return 12;
 }
 
 struct CacheEntry {

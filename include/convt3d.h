@@ -137,7 +137,7 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias,
  * computes the same result up to float summation order.  Unlike
  * convt3d_fused it waits on the device (it times the candidates with HIP
  * events on `stream`).  Candidates needing more workspace than
- * workspace_bytes are skipped.  result may be NULL.  The best 8 candidates
+ * workspace_bytes are skipped.  result may be NULL.  The best 12 candidates
  * are timed (environment CONVT3D_TUNE_CANDIDATES=1..64 changes that;
  * CONVT3D_TUNE_LOG prints one line per candidate to stderr). */
 typedef struct convt3d_tune_result {
