@@ -15,9 +15,12 @@ plus a tiny GroupNorm case and a stride-2, k=4 GroupNorm case at 128 channels.
 
 Input recipe (every workload): numpy ``default_rng(seed)`` draws, in this
 order and as float64, x ~ N(0,1); w ~ U(-a, a) and b ~ U(-a, a) with
-a = 1/sqrt(cin*k^3); gamma ~ U(0.5, 1.5); beta ~ N(0, 0.1).  All five arrays
-are always drawn (so the streams do not depend on which are used) and then
-cast to float32.  The same float32 arrays feed the oracle and the GPU.
+a = 1/sqrt(cin*k^3); gamma ~ U(0.5, 1.5); beta ~ N(0, 0.1); then the
+BatchNorm running statistics, running mean ~ N(0, 0.1) and running variance
+~ U(0.5, 1.5) (the state of a module some steps into training; a fresh one
+holds 0 and 1).  All seven arrays are always drawn (so the streams do not
+depend on which are used) and then cast to float32.  The same float32 arrays
+feed the oracle and the GPU.
 """
 from __future__ import annotations
 
@@ -30,12 +33,14 @@ EPI_NONE = 0
 EPI_RELU_GROUPNORM = 1
 EPI_SOFTMAX_SIGMOID = 2
 EPI_SCALE_BN_TRAIN_AVGPOOL = 3
+EPI_SCALE_BN_EVAL_AVGPOOL = 4
 
 EPI_NAMES = {
     EPI_NONE: "none",
     EPI_RELU_GROUPNORM: "relu_groupnorm",
     EPI_SOFTMAX_SIGMOID: "softmax_sigmoid",
     EPI_SCALE_BN_TRAIN_AVGPOOL: "scale_bn_train_avgpool",
+    EPI_SCALE_BN_EVAL_AVGPOOL: "scale_bn_eval_avgpool",
 }
 
 
@@ -59,6 +64,7 @@ class Workload:
     groups: int = 1
     eps: float = 1e-5
     scale: float = 1.0
+    momentum: float = 0.1
     seed: int = 0
     note: str = field(default="", compare=False)
 
@@ -93,7 +99,15 @@ WORKLOADS = [
              note="stride-2 k4 GroupNorm(16) case at 128 channels"),
 ]
 
-BY_NAME = {wl.name: wl for wl in WORKLOADS}
+# Further cases beyond the five: the p77 shape with BatchNorm in evaluation
+# mode (running statistics), seeded like the p77 case.
+EXTRA_WORKLOADS = [
+    Workload("k5s1_bnpool_eval", 16, 64, 128, 16, 32, 32, k=5, stride=1, pad=0, bias=True,
+             epi=EPI_SCALE_BN_EVAL_AVGPOOL, scale=2.0, seed=20264,
+             note="p77 page shape with BatchNorm3d in eval mode (running statistics)"),
+]
+
+BY_NAME = {wl.name: wl for wl in WORKLOADS + EXTRA_WORKLOADS}
 
 
 @dataclass
@@ -103,6 +117,8 @@ class Inputs:
     b: Optional[np.ndarray]
     gamma: Optional[np.ndarray]
     beta: Optional[np.ndarray]
+    rmean: Optional[np.ndarray] = None
+    rvar: Optional[np.ndarray] = None
 
 
 def make_inputs(wl: Workload, seed: Optional[int] = None, x_dist: str = "normal") -> Inputs:
@@ -123,14 +139,19 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, x_dist: str = "normal"
     b = rng.uniform(-a, a, size=(wl.cout,))
     gamma = rng.uniform(0.5, 1.5, size=(wl.cout,))
     beta = rng.normal(0.0, 0.1, size=(wl.cout,))
+    rmean = rng.normal(0.0, 0.1, size=(wl.cout,))
+    rvar = rng.uniform(0.5, 1.5, size=(wl.cout,))
     f32 = lambda arr: np.ascontiguousarray(arr, dtype=np.float32)
-    uses_affine = wl.epi in (EPI_RELU_GROUPNORM, EPI_SCALE_BN_TRAIN_AVGPOOL)
+    uses_affine = wl.epi in (EPI_RELU_GROUPNORM, EPI_SCALE_BN_TRAIN_AVGPOOL, EPI_SCALE_BN_EVAL_AVGPOOL)
+    uses_running = wl.epi in (EPI_SCALE_BN_TRAIN_AVGPOOL, EPI_SCALE_BN_EVAL_AVGPOOL)
     return Inputs(
         x=f32(x),
         w=f32(w),
         b=f32(b) if wl.bias else None,
         gamma=f32(gamma) if uses_affine else None,
         beta=f32(beta) if uses_affine else None,
+        rmean=f32(rmean) if uses_running else None,
+        rvar=f32(rvar) if uses_running else None,
     )
 
 

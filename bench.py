@@ -71,7 +71,8 @@ def cpu_baseline(wl, inp, max_samples: int):
     from activation_epilogues_amd import workloads as W
     n = min(wl.n, max_samples)
     sub = wl.with_(n=n)
-    sub_inp = W.Inputs(x=np.ascontiguousarray(inp.x[:n]), w=inp.w, b=inp.b, gamma=inp.gamma, beta=inp.beta)
+    sub_inp = W.Inputs(x=np.ascontiguousarray(inp.x[:n]), w=inp.w, b=inp.b, gamma=inp.gamma, beta=inp.beta,
+                       rmean=inp.rmean, rvar=inp.rvar)
     oracle.build()
     t0 = time.perf_counter()
     oracle.run_workload(sub, sub_inp)

@@ -14,7 +14,10 @@
  *                                    (p77 page, its statement of batch
  *                                     statistics over (N, D, H, W) with the
  *                                     biased variance, then the mean over
- *                                     D, H, W).
+ *                                     D, H, W), with the running-statistics
+ *                                     update of a training step, and the
+ *                                     evaluation-mode variant that uses the
+ *                                     running statistics.
  *
  * Every sum is accumulated in double precision; float inputs are widened on
  * read.  Only tests, the package smoke check and the benchmark's CPU-baseline
@@ -280,6 +283,57 @@ void oracle_scale_bn_avgpool(const double *y, int N, int C, long S, double scale
             double acc = 0.0;
             for (long i = 0; i < S; ++i)
                 acc += (scale * yc[i] - mean) * rstd * ga + be;
+            out[(size_t)n * C + c] = acc / (double)S;
+        }
+    }
+}
+
+/*
+ * BatchNorm running statistics after one training step (p77 page: in training
+ * mode BatchNorm3d normalises with the batch statistics and moves its running
+ * mean and variance toward them by the momentum, 0.1 there).  The variance
+ * folded in is the unbiased one, var * count / (count - 1), as nn.BatchNorm3d
+ * keeps it (the pages name that module; they fix the biased estimator only for
+ * the normalisation itself):
+ *   rmean = (1 - momentum) * rmean + momentum * mean_c
+ *   rvar  = (1 - momentum) * rvar  + momentum * var_c * count / (count - 1)
+ * stats is [C, 2] = (batch mean, biased batch variance); count = N*D*H*W > 1.
+ */
+void oracle_bn_running_update(const double *stats, int C, double count, double momentum,
+                              double *rmean, double *rvar)
+{
+    for (int c = 0; c < C; ++c) {
+        const double mean = stats[(size_t)c * 2 + 0];
+        const double unbiased = stats[(size_t)c * 2 + 1] * count / (count - 1.0);
+        rmean[c] = (1.0 - momentum) * rmean[c] + momentum * mean;
+        rvar[c] = (1.0 - momentum) * rvar[c] + momentum * unbiased;
+    }
+}
+
+/*
+ * x scale, BatchNorm3d in evaluation mode, AdaptiveAvgPool3d(1) (p77 page,
+ * where the model in eval mode normalises with its running mean and variance
+ * instead of batch statistics): z = scale * y;
+ * bn = (z - rmean[c]) / sqrt(rvar[c] + eps) * gamma[c] + beta[c];
+ * out[n, c] = mean over (d, h, w) of bn.  Every element is normalised and
+ * then averaged, as written; no shortcut through the spatial sum.
+ * gamma/beta NULL mean 1/0; rmean/rvar NULL mean 0/1 (a fresh module).
+ */
+void oracle_scale_bn_eval_avgpool(const double *y, int N, int C, long S, double scale, double eps,
+                                  const float *gamma, const float *beta,
+                                  const float *rmean, const float *rvar, double *out)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int n = 0; n < N; ++n) {
+        for (int c = 0; c < C; ++c) {
+            const double ga = gamma ? (double)gamma[c] : 1.0;
+            const double be = beta ? (double)beta[c] : 0.0;
+            const double rm = rmean ? (double)rmean[c] : 0.0;
+            const double rv = rvar ? (double)rvar[c] : 1.0;
+            const double *yc = y + ((size_t)n * C + c) * (size_t)S;
+            double acc = 0.0;
+            for (long i = 0; i < S; ++i)
+                acc += (scale * yc[i] - rm) / sqrt(rv + eps) * ga + be;
             out[(size_t)n * C + c] = acc / (double)S;
         }
     }

@@ -23,7 +23,8 @@ _lib = None
 
 __all__ = [
     "build", "out_dim", "out_dims", "convt3d", "convt3d_gather", "convt3d_point",
-    "relu_groupnorm", "softmax_sigmoid", "scale_bn_avgpool", "run_workload",
+    "relu_groupnorm", "softmax_sigmoid", "scale_bn_avgpool", "bn_running_update",
+    "scale_bn_eval_avgpool", "run_workload",
     "num_threads", "OracleResult",
 ]
 
@@ -60,6 +61,10 @@ def _load():
         lib.oracle_softmax_sigmoid.argtypes = [vp, i, i, l, vp, vp]
         lib.oracle_scale_bn_avgpool.restype = None
         lib.oracle_scale_bn_avgpool.argtypes = [vp, i, i, l, d, d, vp, vp, vp, vp]
+        lib.oracle_bn_running_update.restype = None
+        lib.oracle_bn_running_update.argtypes = [vp, i, d, d, vp, vp]
+        lib.oracle_scale_bn_eval_avgpool.restype = None
+        lib.oracle_scale_bn_eval_avgpool.argtypes = [vp, i, i, l, d, d, vp, vp, vp, vp, vp]
         lib.oracle_num_threads.restype = i
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -155,18 +160,45 @@ def scale_bn_avgpool(y, scale=1.0, eps=1e-5, gamma=None, beta=None):
     return out, stats
 
 
+def bn_running_update(stats, count, momentum=0.1, rmean=None, rvar=None):
+    """Running mean / variance after one training step from batch stats [C, 2]
+    (mean, biased variance) over ``count`` values per channel; rmean/rvar
+    default to a fresh module's 0 / 1.  Returns fp64 (rmean, rvar)."""
+    stats = np.ascontiguousarray(stats, dtype=np.float64)
+    C = stats.shape[0]
+    rm = np.zeros(C) if rmean is None else np.array(rmean, dtype=np.float64)
+    rv = np.ones(C) if rvar is None else np.array(rvar, dtype=np.float64)
+    _load().oracle_bn_running_update(_ptr(stats), C, float(count), float(momentum), _ptr(rm), _ptr(rv))
+    return rm, rv
+
+
+def scale_bn_eval_avgpool(y, scale=1.0, eps=1e-5, gamma=None, beta=None, rmean=None, rvar=None):
+    """x scale, BatchNorm3d with running statistics (eval mode), global average
+    pool; returns out[N, C] (fp64)."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    N, C = y.shape[:2]
+    S = int(np.prod(y.shape[2:]))
+    out = np.empty((N, C), dtype=np.float64)
+    _load().oracle_scale_bn_eval_avgpool(_ptr(y), N, C, S, scale, eps, _ptr(_f32(gamma)), _ptr(_f32(beta)),
+                                         _ptr(_f32(rmean)), _ptr(_f32(rvar)), _ptr(out))
+    return out
+
+
 @dataclass
 class OracleResult:
     y: np.ndarray                 # raw transposed-convolution output, fp64
     out: np.ndarray               # final output, fp64
     stats: Optional[np.ndarray]   # GN [N,G,2] (mean, rstd) | BN [C,2] (mean, var) | None
     p: Optional[np.ndarray] = None  # softmax values (softmax epilogue only)
+    running: Optional[tuple] = None  # BN training: updated (running mean, running var), fp64
 
 
 def run_workload(wl, inp) -> OracleResult:
     """The whole path for a workload description (epilogue codes as in
     ``activation_epilogues_amd.workloads``: 0 none, 1 ReLU+GroupNorm,
-    2 softmax+sigmoid, 3 scale+BatchNorm(train)+avgpool)."""
+    2 softmax+sigmoid, 3 scale+BatchNorm(train)+avgpool, 4 scale+BatchNorm(eval,
+    running statistics)+avgpool).  For code 3 with running statistics in the
+    inputs, the result also carries them after the step's update."""
     y = convt3d(inp.x, inp.w, inp.b, wl.stride, wl.pad, wl.out_pad)
     if wl.epi == 0:
         return OracleResult(y, y, None)
@@ -178,5 +210,12 @@ def run_workload(wl, inp) -> OracleResult:
         return OracleResult(y, out, None, p)
     if wl.epi == 3:
         out, st = scale_bn_avgpool(y, wl.scale, wl.eps, inp.gamma, inp.beta)
-        return OracleResult(y, out, st)
+        running = None
+        if inp.rmean is not None:
+            count = y.shape[0] * int(np.prod(y.shape[2:]))
+            running = bn_running_update(st, count, wl.momentum, inp.rmean, inp.rvar)
+        return OracleResult(y, out, st, running=running)
+    if wl.epi == 4:
+        out = scale_bn_eval_avgpool(y, wl.scale, wl.eps, inp.gamma, inp.beta, inp.rmean, inp.rvar)
+        return OracleResult(y, out, None)
     raise ValueError(wl.epi)

@@ -348,6 +348,80 @@ def test_scale_does_not_factor_out_of_bn_because_of_eps():
     assert np.abs(o2 - o1).max() > 1e-3
 
 
+def test_bn_running_update_matches_torch_and_special_cases():
+    """Running statistics of one training step: torch's batch_norm updates the
+    buffers it is given in place (momentum, unbiased variance), a library
+    routine for the same step; momentum 0 keeps, momentum 1 replaces, and the
+    result is affine in the momentum."""
+    rng = np.random.default_rng(17)
+    y = rng.standard_normal((3, 5, 2, 3, 4)) + rng.standard_normal((1, 5, 1, 1, 1))
+    rm0 = rng.normal(0, 0.1, 5)
+    rv0 = rng.uniform(0.5, 1.5, 5)
+    count = 3 * 2 * 3 * 4
+    for scale in (2.0, -0.5):
+        _, st = oracle.scale_bn_avgpool(y, scale, 1e-5, None, None)
+        z = scale * t64(y)
+        for m in (0.1, 0.37):
+            trm, trv = t64(rm0).clone(), t64(rv0).clone()
+            F.batch_norm(z, trm, trv, training=True, momentum=m, eps=1e-5)
+            rm, rv = oracle.bn_running_update(st, count, m, rm0, rv0)
+            np.testing.assert_allclose(rm, trm.numpy(), rtol=0, atol=1e-13)
+            np.testing.assert_allclose(rv, trv.numpy(), rtol=1e-12)
+        zz = z.numpy()
+        rm, rv = oracle.bn_running_update(st, count, 0.0, rm0, rv0)
+        assert np.array_equal(rm, rm0) and np.array_equal(rv, rv0)
+        rm, rv = oracle.bn_running_update(st, count, 1.0, rm0, rv0)
+        np.testing.assert_allclose(rm, zz.mean(axis=(0, 2, 3, 4)), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(rv, zz.var(axis=(0, 2, 3, 4), ddof=1), rtol=1e-12)
+        f0 = np.stack(oracle.bn_running_update(st, count, 0.0, rm0, rv0))
+        f1 = np.stack(oracle.bn_running_update(st, count, 1.0, rm0, rv0))
+        fm = np.stack(oracle.bn_running_update(st, count, 0.25, rm0, rv0))
+        np.testing.assert_allclose(fm, f0 + 0.25 * (f1 - f0), rtol=1e-13, atol=1e-15)
+    # a fresh module (no buffers given) starts from 0 and 1
+    _, st = oracle.scale_bn_avgpool(y, 1.0, 1e-5, None, None)
+    rm, rv = oracle.bn_running_update(st, count, 0.1)
+    np.testing.assert_allclose(rm, 0.1 * st[:, 0], rtol=1e-14)
+    np.testing.assert_allclose(rv, 0.9 + 0.1 * st[:, 1] * count / (count - 1), rtol=1e-14)
+
+
+def test_scale_bn_eval_avgpool_matches_torch_and_invariants():
+    rng = np.random.default_rng(18)
+    y = rng.standard_normal((3, 6, 3, 4, 5)) + rng.standard_normal((1, 6, 1, 1, 1))
+    gamma = rng.uniform(0.5, 1.5, 6).astype(np.float32)
+    beta = rng.normal(0, 0.1, 6).astype(np.float32)
+    rm = rng.normal(0, 0.1, 6).astype(np.float32)
+    rv = rng.uniform(0.5, 1.5, 6).astype(np.float32)
+    for scale, eps in ((2.0, 1e-5), (-0.7, 0.3)):
+        out = oracle.scale_bn_eval_avgpool(y, scale, eps, gamma, beta, rm, rv)
+        bn = F.batch_norm(scale * t64(y), t64(rm), t64(rv), t64(gamma), t64(beta), training=False, eps=eps)
+        np.testing.assert_allclose(out, bn.mean(dim=(2, 3, 4)).numpy(), rtol=0, atol=1e-12)
+        # with the running statistics set to this batch's (mean, biased variance)
+        # the evaluation-mode result is the training-mode one
+        tr, st = oracle.scale_bn_avgpool(y, scale, eps, gamma, beta)
+        ev = oracle.scale_bn_eval_avgpool(y, scale, eps, gamma, beta, st[:, 0], st[:, 1])
+        np.testing.assert_allclose(ev, tr, rtol=0, atol=1e-6)  # stats rounded to fp32
+    # fresh module and no affine: scale * spatial mean / sqrt(1 + eps)
+    out = oracle.scale_bn_eval_avgpool(y, 2.0, 0.5, None, None, None, None)
+    np.testing.assert_allclose(out, 2.0 * y.mean(axis=(2, 3, 4)) / np.sqrt(1.5), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("k,s,op", [(5, 1, 0), (3, 2, 1)])
+def test_bn_eval_pool_closed_form_through_the_conv(k, s, op):
+    """p77 page's closed form for evaluation mode: with pad 0 the pooled conv
+    output is Xsum @ Wsum / |out| + b, so the whole path reduces to BatchNorm
+    with running statistics on that [N, Cout] matrix."""
+    wl = W.Workload("eval", 2, 4, 6, 4, 3, 5, k=k, stride=s, pad=0, out_pad=op, bias=True,
+                    epi=W.EPI_SCALE_BN_EVAL_AVGPOOL, scale=2.0, eps=1e-5, seed=77)
+    inp = W.make_inputs(wl)
+    res = oracle.run_workload(wl, inp)
+    S = int(np.prod(res.y.shape[2:]))
+    m = (inp.x.astype(np.float64).sum(axis=(2, 3, 4)) @ inp.w.astype(np.float64).sum(axis=(2, 3, 4))) / S
+    m += inp.b.astype(np.float64)
+    f = lambda a: a.astype(np.float64)[None, :]
+    want = (2.0 * m - f(inp.rmean)) / np.sqrt(f(inp.rvar) + 1e-5) * f(inp.gamma) + f(inp.beta)
+    np.testing.assert_allclose(res.out, want, rtol=0, atol=1e-12)
+
+
 def test_tiny_workload_whole_path_against_torch():
     wl = W.BY_NAME["tiny_gn"]
     inp = W.make_inputs(wl)
