@@ -18,6 +18,8 @@ EPI_NONE = 0
 EPI_RELU_GROUPNORM = 1
 EPI_SOFTMAX_SIGMOID = 2
 EPI_SCALE_BN_TRAIN_AVGPOOL = 3
+EPI_SCALE_BN_EVAL_AVGPOOL = 4
+POOLED = (EPI_SCALE_BN_TRAIN_AVGPOOL, EPI_SCALE_BN_EVAL_AVGPOOL)
 
 STATUS = {
     0: "OK", 1: "ERR_NULL", 2: "ERR_GEOMETRY", 3: "ERR_GROUPS", 4: "ERR_ALIGNMENT",
@@ -33,7 +35,8 @@ class Geom(ctypes.Structure):
 class Epilogue(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("groups", ctypes.c_int32), ("eps", ctypes.c_float),
                 ("scale", ctypes.c_float), ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p),
-                ("stats_out", ctypes.c_void_p)]
+                ("stats_out", ctypes.c_void_p), ("momentum", ctypes.c_float),
+                ("running_mean", ctypes.c_void_p), ("running_var", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -44,7 +47,8 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("workgroups", ctypes.c_int64),
                 ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64),
                 ("phase_loop", ctypes.c_int32),
-                ("tuned", ctypes.c_int32), ("border_split", ctypes.c_int32), ("xcd_order", ctypes.c_int32)]
+                ("tuned", ctypes.c_int32), ("border_split", ctypes.c_int32), ("xcd_order", ctypes.c_int32),
+                ("softmax_pass", ctypes.c_int32), ("eval_bins", ctypes.c_int32)]
 
 
 class TuneResult(ctypes.Structure):
@@ -54,7 +58,8 @@ class TuneResult(ctypes.Structure):
 
 class Profile(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int32), ("conv_ms", ctypes.c_double), ("finalize_ms", ctypes.c_double),
-                ("normalize_ms", ctypes.c_double)]
+                ("normalize_ms", ctypes.c_double), ("reduce_ms", ctypes.c_double),
+                ("prepack_ms", ctypes.c_double)]
 
 
 class Convt3dError(RuntimeError):
@@ -86,6 +91,15 @@ def lib():
         L.convt3d_packed_weight_bytes.argtypes = [P(Geom)]
         L.convt3d_prepack_weights.restype = ctypes.c_int
         L.convt3d_prepack_weights.argtypes = [P(Geom), vp, vp, vp]
+        L.convt3d_eval_weight_bytes.restype = sz
+        L.convt3d_eval_weight_bytes.argtypes = [P(Geom)]
+        L.convt3d_prepack_eval_weights.restype = ctypes.c_int
+        L.convt3d_prepack_eval_weights.argtypes = [P(Geom), vp, vp, vp]
+        L.convt3d_epilogue_workspace_size.restype = sz
+        L.convt3d_epilogue_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P(Epilogue)]
+        L.convt3d_epilogue_only.restype = ctypes.c_int
+        L.convt3d_epilogue_only.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P(Epilogue), vp,
+                                            vp, sz, vp]
         L.convt3d_workspace_size.restype = sz
         L.convt3d_workspace_size.argtypes = [P(Geom), P(Epilogue)]
         L.convt3d_fused.restype = ctypes.c_int
@@ -103,9 +117,10 @@ def lib():
 
 
 EXPORTED = ["convt3d_status_string", "convt3d_output_dims", "convt3d_output_elems",
-            "convt3d_packed_weight_bytes", "convt3d_prepack_weights", "convt3d_workspace_size",
-            "convt3d_fused", "convt3d_autotune", "convt3d_get_plan_info", "convt3d_profile_begin",
-            "convt3d_profile_end"]
+            "convt3d_packed_weight_bytes", "convt3d_prepack_weights", "convt3d_eval_weight_bytes",
+            "convt3d_prepack_eval_weights", "convt3d_workspace_size", "convt3d_fused", "convt3d_autotune",
+            "convt3d_epilogue_workspace_size", "convt3d_epilogue_only", "convt3d_get_plan_info",
+            "convt3d_profile_begin", "convt3d_profile_end"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -130,8 +145,10 @@ def make_geom(n, cin, cout, d, h, w, k, stride=1, pad=0, out_pad=0) -> Geom:
     return Geom(n, cin, cout, d, h, w, k, stride, pad, out_pad)
 
 
-def make_epilogue(kind, groups=1, eps=1e-5, scale=1.0, gamma=None, beta=None, stats_out=None) -> Epilogue:
-    return Epilogue(kind, groups, eps, scale, _ptr(gamma), _ptr(beta), _ptr(stats_out))
+def make_epilogue(kind, groups=1, eps=1e-5, scale=1.0, gamma=None, beta=None, stats_out=None,
+                  momentum=0.1, running_mean=None, running_var=None) -> Epilogue:
+    return Epilogue(kind, groups, eps, scale, _ptr(gamma), _ptr(beta), _ptr(stats_out), momentum,
+                    _ptr(running_mean), _ptr(running_var))
 
 
 def status_string(status: int) -> str:
@@ -166,6 +183,30 @@ def convt3d_prepack_weights(geom: Geom, w, w_packed, stream=None, check=True) ->
     st = lib().convt3d_prepack_weights(ctypes.byref(geom), _ptr(w), _ptr(w_packed), _stream(stream))
     if check and st:
         raise Convt3dError(st, "convt3d_prepack_weights")
+    return st
+
+
+def convt3d_eval_weight_bytes(geom: Geom) -> int:
+    return int(lib().convt3d_eval_weight_bytes(ctypes.byref(geom)))
+
+
+def convt3d_prepack_eval_weights(geom: Geom, w, w_eval, stream=None, check=True) -> int:
+    st = lib().convt3d_prepack_eval_weights(ctypes.byref(geom), _ptr(w), _ptr(w_eval), _stream(stream))
+    if check and st:
+        raise Convt3dError(st, "convt3d_prepack_eval_weights")
+    return st
+
+
+def convt3d_epilogue_workspace_size(n: int, c: int, spatial: int, epi: Epilogue) -> int:
+    return int(lib().convt3d_epilogue_workspace_size(n, c, spatial, ctypes.byref(epi)))
+
+
+def convt3d_epilogue_only(y, n: int, c: int, spatial: int, epi: Epilogue, out, workspace, workspace_bytes: int,
+                          stream=None, check=True) -> int:
+    st = lib().convt3d_epilogue_only(_ptr(y), n, c, spatial, ctypes.byref(epi), _ptr(out), _ptr(workspace),
+                                     workspace_bytes, _stream(stream))
+    if check and st:
+        raise Convt3dError(st, "convt3d_epilogue_only")
     return st
 
 
@@ -231,21 +272,26 @@ class FusedCall:
     """
 
     def __init__(self, geom: Geom, kind: int, groups: int = 1, eps: float = 1e-5, scale: float = 1.0,
-                 device="cuda", want_stats: bool = False):
+                 device="cuda", want_stats: bool = False, momentum: float = 0.1):
         import torch
         self.geom = geom
         self.kind = kind
-        self.groups, self.eps, self.scale = groups, eps, scale
+        self.groups, self.eps, self.scale, self.momentum = groups, eps, scale, momentum
         probe = make_epilogue(kind, groups, eps, scale)
         self.out_dims = convt3d_output_dims(geom)
         self.out_elems = convt3d_output_elems(geom, probe)
         if self.out_elems < 0:
             raise Convt3dError(2, "convt3d_output_elems")
         self.ws_bytes = convt3d_workspace_size(geom, probe)
-        self.packed_bytes = convt3d_packed_weight_bytes(geom)
+        if kind == EPI_SCALE_BN_EVAL_AVGPOOL:  # tap-summed weights, no conv operand
+            self.packed_bytes = convt3d_eval_weight_bytes(geom)
+        else:
+            self.packed_bytes = convt3d_packed_weight_bytes(geom)
+        if self.packed_bytes == 0:
+            raise Convt3dError(6, "weight buffer size")
         self.w_packed = torch.empty(max(1, self.packed_bytes // 4), dtype=torch.float32, device=device)
         self.workspace = torch.empty(max(1, self.ws_bytes // 4), dtype=torch.float32, device=device)
-        if kind == EPI_SCALE_BN_TRAIN_AVGPOOL:
+        if kind in POOLED:
             self.out = torch.empty((geom.n, geom.cout, 1, 1, 1), dtype=torch.float32, device=device)
         else:
             self.out = torch.empty((geom.n, geom.cout) + tuple(self.out_dims), dtype=torch.float32,
@@ -257,15 +303,19 @@ class FusedCall:
             elif kind == EPI_SCALE_BN_TRAIN_AVGPOOL:
                 self.stats = torch.empty((geom.cout, 2), dtype=torch.float32, device=device)
 
-    def epilogue(self, gamma=None, beta=None) -> Epilogue:
-        return make_epilogue(self.kind, self.groups, self.eps, self.scale, gamma, beta, self.stats)
+    def epilogue(self, gamma=None, beta=None, running_mean=None, running_var=None) -> Epilogue:
+        return make_epilogue(self.kind, self.groups, self.eps, self.scale, gamma, beta, self.stats,
+                             self.momentum, running_mean, running_var)
 
     def prepack(self, w, stream=None):
-        convt3d_prepack_weights(self.geom, w, self.w_packed, stream)
+        if self.kind == EPI_SCALE_BN_EVAL_AVGPOOL:
+            convt3d_prepack_eval_weights(self.geom, w, self.w_packed, stream)
+        else:
+            convt3d_prepack_weights(self.geom, w, self.w_packed, stream)
 
-    def __call__(self, x, bias=None, gamma=None, beta=None, stream=None):
-        convt3d_fused(x, self.w_packed, bias, self.geom, self.epilogue(gamma, beta), self.out,
-                      self.workspace, self.ws_bytes, stream)
+    def __call__(self, x, bias=None, gamma=None, beta=None, stream=None, running_mean=None, running_var=None):
+        convt3d_fused(x, self.w_packed, bias, self.geom, self.epilogue(gamma, beta, running_mean, running_var),
+                      self.out, self.workspace, self.ws_bytes, stream)
         return self.out
 
     def autotune(self, x, bias=None, gamma=None, beta=None, stream=None) -> dict:

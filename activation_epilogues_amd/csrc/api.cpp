@@ -118,8 +118,9 @@ void store_tuned(const convt3d_geom *g, const convt3d_epilogue *e, const Plan &p
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---- optional per-kernel timing with HIP events (measurement only)
+enum TimedKind { kTimedConv = 0, kTimedFinalize = 1, kTimedNormalize = 2, kTimedReduce = 3, kTimedPrepack = 4 };
 struct Timed {
-    int kind;  // 0 conv, 1 finalize, 2 normalize
+    int kind;  // TimedKind
     hipEvent_t beg, end;
 };
 std::mutex g_prof_mu;
@@ -159,6 +160,21 @@ int timed(int kind, void *stream, F fn) {
     return rc;
 }
 
+void count_call() {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on) ++g_prof_calls;
+}
+
+// Running-statistics arguments of the BatchNorm kinds: both buffers or none,
+// and more than one value per channel (count) for the unbiased variance.
+int check_running(const convt3d_epilogue *e, double count) {
+    if (e->kind != CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) return CONVT3D_OK;
+    const bool rm = e->running_mean != nullptr, rv = e->running_var != nullptr;
+    if (rm != rv) return CONVT3D_ERR_NULL;
+    if (rm && count <= 1.0) return CONVT3D_ERR_UNSUPPORTED;
+    return CONVT3D_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,7 +208,8 @@ int convt3d_output_dims(const convt3d_geom *geom, int32_t out_dhw[3]) {
 int64_t convt3d_output_elems(const convt3d_geom *geom, const convt3d_epilogue *epi) {
     int32_t od[3];
     if (!epi || convt3d_output_dims(geom, od) != CONVT3D_OK) return -1;
-    if (epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) return (int64_t)geom->n * geom->cout;
+    if (epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL || epi->kind == CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL)
+        return (int64_t)geom->n * geom->cout;
     return (int64_t)geom->n * geom->cout * od[0] * od[1] * od[2];
 }
 
@@ -208,7 +225,26 @@ int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_pa
     Plan pl;
     const int st = make_geometry(geom, &pl);
     if (st) return st;
-    if (launch_prepack(pl, w, static_cast<float *>(w_packed), stream) != (int)hipSuccess)
+    if (timed(kTimedPrepack, stream, [&] { return launch_prepack(pl, w, static_cast<float *>(w_packed), stream); }) !=
+        (int)hipSuccess)
+        return CONVT3D_ERR_LAUNCH;
+    return CONVT3D_OK;
+}
+
+size_t convt3d_eval_weight_bytes(const convt3d_geom *geom) {
+    EvalGeom eg;
+    if (!geom || make_eval_geom(geom, &eg) != CONVT3D_OK) return 0;
+    return (size_t)geom->cin * geom->cout * eg.nbins * sizeof(float);
+}
+
+int convt3d_prepack_eval_weights(const convt3d_geom *geom, const float *w, void *w_eval, void *stream) {
+    if (!geom || !w || !w_eval) return CONVT3D_ERR_NULL;
+    if (!aligned16(w_eval)) return CONVT3D_ERR_ALIGNMENT;
+    EvalGeom eg;
+    const int st = make_eval_geom(geom, &eg);
+    if (st) return st;
+    if (timed(kTimedPrepack, stream,
+              [&] { return launch_eval_pack(eg, w, static_cast<float *>(w_eval), stream); }) != (int)hipSuccess)
         return CONVT3D_ERR_LAUNCH;
     return CONVT3D_OK;
 }
@@ -242,6 +278,8 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
     info->tuned = ent.tuned ? 1 : 0;
     info->border_split = pl.split;
     info->xcd_order = pl.order;
+    info->softmax_pass = pl.softmax_pass;
+    info->eval_bins = pl.eval ? pl.eg.nbins : 0;
     return CONVT3D_OK;
 }
 
@@ -260,13 +298,27 @@ static int check_call(const float *x, const void *w_packed, const float *bias, c
     const char *ob = reinterpret_cast<const char *>(out);
     const char *oe = ob + (size_t)convt3d_output_elems(geom, epi) * sizeof(float);
     if (ob < xe && xb < oe) return CONVT3D_ERR_ALIAS;
-    return CONVT3D_OK;
+    int32_t od[3];
+    convt3d_output_dims(geom, od);
+    return check_running(epi, (double)geom->n * od[0] * od[1] * od[2]);
 }
 
 // Enqueue the kernels of one call with plan pl (arguments already checked).
 static int run_plan(const Plan &pl, const float *x, const void *w_packed, const float *bias,
                     const convt3d_epilogue *epi, float *out, void *workspace, void *stream) {
     char *ws = static_cast<char *>(workspace);
+    count_call();
+    if (pl.eval) {
+        // eval-mode BatchNorm + pool: bin sums of x, then their contraction
+        float *R = reinterpret_cast<float *>(ws + pl.ws_bins);
+        if (timed(kTimedReduce, stream, [&] { return launch_eval_binsum(pl.eg, x, R, stream); }) != (int)hipSuccess)
+            return CONVT3D_ERR_LAUNCH;
+        if (timed(kTimedFinalize, stream, [&] {
+                return launch_eval_finalize(pl.eg, R, static_cast<const float *>(w_packed), bias, *epi, out, stream);
+            }) != (int)hipSuccess)
+            return CONVT3D_ERR_LAUNCH;
+        return CONVT3D_OK;
+    }
     const bool stats = epi->kind == CONVT3D_EPI_RELU_GROUPNORM || epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
     float *partials = stats ? reinterpret_cast<float *>(ws + pl.ws_partials) : nullptr;
 
@@ -277,24 +329,31 @@ static int run_plan(const Plan &pl, const float *x, const void *w_packed, const 
     cp.bias = bias;
     cp.out = out;
     cp.partials = partials;
-    {
-        std::lock_guard<std::mutex> lk(g_prof_mu);
-        if (g_prof_on) ++g_prof_calls;
-    }
-    if (timed(0, stream, [&] { return launch_conv(pl, cp, stream); }) != (int)hipSuccess)
+    if (timed(kTimedConv, stream, [&] { return launch_conv(pl, cp, stream); }) != (int)hipSuccess)
         return CONVT3D_ERR_LAUNCH;
 
+    const convt3d_geom &g = pl.g;
+    const int tiles = (int)pl.tiles_per_n;
     if (epi->kind == CONVT3D_EPI_RELU_GROUPNORM) {
         float *ab = reinterpret_cast<float *>(ws + pl.ws_ab);
-        if (timed(1, stream, [&] {
-                return launch_gn_finalize(pl, partials, epi->gamma, epi->beta, ab, epi->stats_out, stream);
+        const double count = (double)(g.cout / epi->groups) * (double)pl.S;
+        if (timed(kTimedFinalize, stream, [&] {
+                return launch_gn_finalize(partials, g.n, tiles, g.cout, epi->groups, count, epi->eps, epi->gamma,
+                                          epi->beta, ab, epi->stats_out, stream);
             }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
-        if (timed(2, stream, [&] { return launch_normalize(pl, out, ab, stream); }) != (int)hipSuccess)
+        if (timed(kTimedNormalize, stream, [&] {
+                return launch_normalize(out, out, ab, g.n * g.cout, pl.S, false, stream);
+            }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
     } else if (epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) {
-        if (timed(1, stream, [&] {
-                return launch_bn_finalize(pl, partials, epi->gamma, epi->beta, out, epi->stats_out, stream);
+        if (timed(kTimedFinalize, stream, [&] {
+                return launch_bn_finalize(partials, g.n, tiles, g.cout, (double)pl.S, *epi, out, stream);
+            }) != (int)hipSuccess)
+            return CONVT3D_ERR_LAUNCH;
+    } else if (pl.softmax_pass) {
+        if (timed(kTimedNormalize, stream, [&] {
+                return launch_softmax_pass(out, out, g.n, g.cout, pl.S, stream);
             }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
     }
@@ -328,6 +387,10 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     std::vector<Plan> cands;
     st = plan_candidates(geom, epi, tune_candidates(), &cands);
     if (st) return st;
+    // the timed calls leave BatchNorm running statistics alone
+    convt3d_epilogue quiet = *epi;
+    quiet.running_mean = quiet.running_var = nullptr;
+    epi = &quiet;
     hipEvent_t b = nullptr, e = nullptr;
     if (hipEventCreate(&b) != hipSuccess || hipEventCreate(&e) != hipSuccess) {
         if (b) hipEventDestroy(b);
@@ -377,6 +440,105 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     return CONVT3D_OK;
 }
 
+// ---- the epilogue alone, on a conv output in memory
+
+namespace {
+struct EpiOnlyLayout {
+    int chunks = 1;
+    size_t partials = 0, ab = 0, bytes = 0;
+};
+
+int epi_only_layout(int32_t n, int32_t c, int64_t spatial, const convt3d_epilogue *e, EpiOnlyLayout *L) {
+    if (!e) return CONVT3D_ERR_NULL;
+    if (n < 0 || c < 1 || spatial < 1) return CONVT3D_ERR_GEOMETRY;
+    if ((int64_t)n * c * spatial > (int64_t)INT32_MAX) return CONVT3D_ERR_TOO_LARGE;
+    if (e->kind < CONVT3D_EPI_RELU_GROUPNORM || e->kind > CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL)
+        return CONVT3D_ERR_UNSUPPORTED;
+    if (e->kind == CONVT3D_EPI_RELU_GROUPNORM && (e->groups < 1 || c % e->groups != 0)) return CONVT3D_ERR_GROUPS;
+    *L = EpiOnlyLayout{};
+    L->chunks = row_stat_chunks(spatial);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) & ~size_t(255);
+        return o;
+    };
+    if (e->kind != CONVT3D_EPI_SOFTMAX_SIGMOID)
+        L->partials = take((size_t)std::max(n, 1) * L->chunks * c * 2 * sizeof(float));
+    if (e->kind == CONVT3D_EPI_RELU_GROUPNORM) L->ab = take((size_t)std::max(n, 1) * c * 2 * sizeof(float));
+    L->bytes = off;
+    return CONVT3D_OK;
+}
+}  // namespace
+
+size_t convt3d_epilogue_workspace_size(int32_t n, int32_t c, int64_t spatial, const convt3d_epilogue *epi) {
+    EpiOnlyLayout L;
+    if (epi_only_layout(n, c, spatial, epi, &L) != CONVT3D_OK) return 0;
+    return L.bytes;
+}
+
+int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial, const convt3d_epilogue *epi,
+                          float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    EpiOnlyLayout L;
+    int st = epi_only_layout(n, c, spatial, epi, &L);
+    if (st) return st;
+    if (!y || !out) return CONVT3D_ERR_NULL;
+    if (!aligned16(y) || !aligned16(out)) return CONVT3D_ERR_ALIGNMENT;
+    const int kind = epi->kind;
+    const bool pooled = kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL || kind == CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL;
+    const size_t y_bytes = (size_t)n * c * spatial * sizeof(float);
+    const size_t o_bytes = (pooled ? (size_t)n * c : (size_t)n * c * spatial) * sizeof(float);
+    const char *yb = reinterpret_cast<const char *>(y), *ob = reinterpret_cast<const char *>(out);
+    const bool overlap = ob < yb + y_bytes && yb < ob + o_bytes;
+    if (overlap && (pooled || ob != yb)) return CONVT3D_ERR_ALIAS;  // only exact in-place is allowed
+    if (L.bytes > 0 && (!workspace || workspace_bytes < L.bytes || !aligned16(workspace)))
+        return CONVT3D_ERR_WORKSPACE;
+    st = check_running(epi, (double)n * (double)spatial);
+    if (st) return st;
+    if (n == 0) return CONVT3D_OK;
+
+    count_call();
+    char *ws = static_cast<char *>(workspace);
+    float *partials = reinterpret_cast<float *>(ws + L.partials);
+    const double S = (double)spatial;
+    auto ok = [](int rc) { return rc == (int)hipSuccess; };
+    switch (kind) {
+        case CONVT3D_EPI_RELU_GROUPNORM: {
+            float *ab = reinterpret_cast<float *>(ws + L.ab);
+            const double count = (double)(c / epi->groups) * S;
+            if (!ok(timed(kTimedReduce, stream,
+                          [&] { return launch_row_stats(y, n, c, spatial, true, 1.0f, partials, stream); })) ||
+                !ok(timed(kTimedFinalize, stream, [&] {
+                    return launch_gn_finalize(partials, n, L.chunks, c, epi->groups, count, epi->eps, epi->gamma,
+                                              epi->beta, ab, epi->stats_out, stream);
+                })) ||
+                !ok(timed(kTimedNormalize, stream,
+                          [&] { return launch_normalize(y, out, ab, n * c, spatial, true, stream); })))
+                return CONVT3D_ERR_LAUNCH;
+            break;
+        }
+        case CONVT3D_EPI_SOFTMAX_SIGMOID:
+            if (!ok(timed(kTimedNormalize, stream, [&] { return launch_softmax_pass(y, out, n, c, spatial, stream); })))
+                return CONVT3D_ERR_LAUNCH;
+            break;
+        case CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL:
+            if (!ok(timed(kTimedReduce, stream,
+                          [&] { return launch_row_stats(y, n, c, spatial, false, epi->scale, partials, stream); })) ||
+                !ok(timed(kTimedFinalize, stream,
+                          [&] { return launch_bn_finalize(partials, n, L.chunks, c, S, *epi, out, stream); })))
+                return CONVT3D_ERR_LAUNCH;
+            break;
+        default:  // CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL
+            if (!ok(timed(kTimedReduce, stream,
+                          [&] { return launch_row_stats(y, n, c, spatial, false, 1.0f, partials, stream); })) ||
+                !ok(timed(kTimedFinalize, stream,
+                          [&] { return launch_bn_eval_rows(partials, n, L.chunks, c, S, *epi, out, stream); })))
+                return CONVT3D_ERR_LAUNCH;
+            break;
+    }
+    return CONVT3D_OK;
+}
+
 int convt3d_profile_begin(void) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (auto &t : g_prof_used) {
@@ -402,9 +564,13 @@ int convt3d_profile_end(convt3d_profile *out) {
             status = CONVT3D_ERR_LAUNCH;
             continue;
         }
-        if (t.kind == 0) out->conv_ms += ms;
-        else if (t.kind == 1) out->finalize_ms += ms;
-        else out->normalize_ms += ms;
+        switch (t.kind) {
+            case kTimedConv: out->conv_ms += ms; break;
+            case kTimedFinalize: out->finalize_ms += ms; break;
+            case kTimedNormalize: out->normalize_ms += ms; break;
+            case kTimedReduce: out->reduce_ms += ms; break;
+            default: out->prepack_ms += ms; break;
+        }
         g_prof_pool.push_back(t.beg);
         g_prof_pool.push_back(t.end);
     }

@@ -18,6 +18,10 @@ constexpr int kBlockThreads = 256; // 4 wavefronts per workgroup
 constexpr int kMaxLdsBytes = 80 * 1024;  // at least two workgroups per CU
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs (256 CUs), one L2 each
 constexpr int64_t kL2Bytes = 4 << 20;    // L2 per XCD
+constexpr int kRowStatChunk = 8192;      // vector elements per workgroup in the statistics pass over y
+constexpr int kEvalMaxK = 31;            // eval-mode BN: kernel size limit (bins per dim <= 2k+1)
+constexpr int kEvalMaxBins = 2 * kEvalMaxK + 1;
+constexpr int kEvalTargetBlocks = 2048;  // eval-mode bin sums: workgroups to aim for
 
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
 // taps that reach it are k = r + s*j (j = 0..J-1) from input i = q + c - j.
@@ -65,6 +69,20 @@ struct ConvParams {
     int steps4[kMaxPhases];   // packed float4 groups per co-block of each phase = octets*ntaps
 };
 
+// Evaluation-mode BatchNorm + pool (no convolution).  Along dim `dim` the
+// input index range [0, in) splits into bins [cut[j], cut[j+1]), j < nb; tap t
+// reaches the output from inputs [lo[t], hi1[t]) (lo >= hi1: from none), and
+// every such range is a union of whole bins.
+struct EvalGeom {
+    int N, Cin, Cout, D, H, W, k;
+    int nb[3];
+    int nbins;                        // nb[0] * nb[1] * nb[2]
+    int cut[3][kEvalMaxBins + 1];
+    int lo[3][kEvalMaxK], hi1[3][kEvalMaxK];
+    int nchunk, dchunk;               // d-chunks per (n, cin) plane in the bin-sum kernel
+    double inv_S;                     // 1 / (Do * Ho * Wo)
+};
+
 struct Plan {
     convt3d_geom g{};
     convt3d_epilogue e{};
@@ -91,12 +109,15 @@ struct Plan {
     int co_tiles = 1, nwgroups = 1;
     int phase_loop = 0, red_off = 0;
     int split = 0;            // dims split into border / interior segments (bit 0 d, 1 h, 2 w)
+    int softmax_pass = 0;     // softmax with cout > 128: conv stores y, a second pass finishes
+    int eval = 0;             // eval-mode BatchNorm + pool: no conv (EvalGeom below)
+    EvalGeom eg{};
     int order = 0;            // workgroup order within an XCD (see ConvParams::order)
     int64_t tiles_per_n = 0;
     int64_t grid_x = 0, grid_y = 0, grid_z = 0;
     int64_t issued_macs = 0, valid_macs = 0;
     // workspace layout (bytes)
-    size_t ws_partials = 0, ws_ab = 0, ws_bytes = 0;
+    size_t ws_partials = 0, ws_ab = 0, ws_bins = 0, ws_bytes = 0;
 };
 
 // Kernel variants the library is built with.
@@ -115,14 +136,28 @@ int make_geometry(const convt3d_geom *g, Plan *pl);        // phases + packing o
 int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl);
 int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k, std::vector<Plan> *out);
 void fill_conv_params(const Plan &pl, ConvParams *cp);
+int make_eval_geom(const convt3d_geom *g, EvalGeom *eg);  // CONVT3D_ERR_UNSUPPORTED for k > kEvalMaxK
 
-// Launchers (kernels.hip).  Return a hipError_t as int.
+// Launchers (kernels.hip: pre-pack and convolution).  Return a hipError_t as int.
 int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream);
 int launch_conv(const Plan &pl, const ConvParams &cp, void *stream);
-int launch_gn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta,
-                       float *ab, float *stats_out, void *stream);
-int launch_normalize(const Plan &pl, float *out, const float *ab, void *stream);
-int launch_bn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta,
-                       float *out, float *stats_out, void *stream);
+
+// Launchers (epilogue.hip).  partials are [n][chunk or tile][C][2].
+int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, double count, float eps,
+                       const float *gamma, const float *beta, float *ab, float *stats_out, void *stream);
+int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool relu,
+                     void *stream);
+int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,
+                       float *out, void *stream);
+int row_stat_chunks(int64_t S);
+int launch_row_stats(const float *y, int N, int C, int64_t S, bool relu, float mult, float *partials,
+                     void *stream);
+int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, void *stream);
+int launch_bn_eval_rows(const float *partials, int N, int chunks, int C, double S, const convt3d_epilogue &e,
+                        float *out, void *stream);
+int launch_eval_pack(const EvalGeom &E, const float *w, float *wb, void *stream);
+int launch_eval_binsum(const EvalGeom &E, const float *x, float *R, void *stream);
+int launch_eval_finalize(const EvalGeom &E, const float *R, const float *wb, const float *bias,
+                         const convt3d_epilogue &e, float *out, void *stream);
 
 }  // namespace convt3d

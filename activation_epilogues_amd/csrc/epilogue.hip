@@ -1,0 +1,597 @@
+// HIP kernels of libconvt3d for gfx950 around the convolution kernel: the
+// statistics and normalisation passes of the fused epilogues, the standalone
+// epilogue passes over a conv output the caller holds, and the evaluation-mode
+// BatchNorm + pool path, which needs no convolution.
+//
+//  * gn_finalize_kernel   -- per (n, group) fp64 merge of statistics partials,
+//                            mean / biased variance / rstd, per-channel a, b.
+//  * normalize_kernel     -- out = a[n,c] * v + b[n,c] with v = src (or
+//                            ReLU(src)), float4, in place when src == out.
+//  * bn_finalize_kernel   -- per channel fp64 batch mean / biased variance,
+//                            the pooled output and the running statistics.
+//  * row_stats_kernel     -- per (n, c, chunk) sums of v and v^2 over a conv
+//                            output held in memory (v = ReLU(y) or scale*y).
+//  * softmax_pass_kernel  -- channel softmax then sigmoid over a conv output in
+//                            memory: one pass for the running max and sum of
+//                            exponentials, one for the result.
+//  * bn_eval_rows_kernel  -- eval-mode BatchNorm + pool from per-row sums.
+//  * eval_pack_kernel     -- tap-summed weights per input bin (eval mode).
+//  * eval_binsum_kernel   -- sums of x over the input bins of each (n, cin).
+//  * eval_finalize_kernel -- pooled conv mean = bias + bin sums . weights / S,
+//                            then BatchNorm with the running statistics.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "convt3d_internal.hpp"
+
+namespace convt3d {
+
+namespace {
+
+constexpr int kNormUnroll = 4;        // loads in flight per thread in the HBM passes
+constexpr float kLog2e = 1.4426950408889634f;
+
+// exp(x) as 2^(x log2 e) on the hardware exp2 (relative error a few ulp).
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// Sum of two values over a 256-thread workgroup, same order every run.
+// red holds 4 float2; every thread gets the result.
+__device__ __forceinline__ float2 block_sum2(float a, float b, float2 *red) {
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off);
+        b += __shfl_xor(b, off);
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(a, b);
+    __syncthreads();
+    const float2 r = make_float2((red[0].x + red[1].x) + (red[2].x + red[3].x),
+                                 (red[0].y + red[1].y) + (red[2].y + red[3].y));
+    __syncthreads();  // red may be reused
+    return r;
+}
+
+template <class V>
+__device__ __forceinline__ float *comps(V &v) { return reinterpret_cast<float *>(&v); }
+template <class V>
+constexpr int ncomp() { return (int)(sizeof(V) / sizeof(float)); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// GroupNorm statistics: one workgroup per (n, group); fp64 sums of the fp32
+// partials (layout [n][tile][C][2]) in a fixed order, then mean, biased
+// variance E[r^2] - mean^2, rstd = 1/sqrt(var + eps), and per channel
+// a = gamma*rstd, b = beta - mean*a.
+__global__ __launch_bounds__(256) void gn_finalize_kernel(const float *partials, int tiles_per_n, int C,
+                                                          int G, float eps, const float *gamma,
+                                                          const float *beta, float *ab, float *stats_out,
+                                                          double count) {
+    const int n = blockIdx.x / G, g = blockIdx.x % G;
+    const int cpg = C / G;
+    const int items = tiles_per_n * cpg;
+    double a1 = 0.0, a2 = 0.0;
+    for (int i = threadIdx.x; i < items; i += blockDim.x) {
+        const int t = i / cpg, cc = i - t * cpg;
+        const float *pp = partials + (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2;
+        a1 += (double)pp[0];
+        a2 += (double)pp[1];
+    }
+    __shared__ double r1[256], r2[256];
+    __shared__ double mean_s, rstd_s;
+    r1[threadIdx.x] = a1;
+    r2[threadIdx.x] = a2;
+    __syncthreads();
+    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) {
+            r1[threadIdx.x] += r1[threadIdx.x + off];
+            r2[threadIdx.x] += r2[threadIdx.x + off];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double mean = r1[0] / count;
+        double var = r2[0] / count - mean * mean;
+        if (var < 0.0) var = 0.0;
+        mean_s = mean;
+        rstd_s = 1.0 / sqrt(var + (double)eps);
+        if (stats_out) {
+            stats_out[((size_t)n * G + g) * 2 + 0] = (float)mean;
+            stats_out[((size_t)n * G + g) * 2 + 1] = (float)rstd_s;
+        }
+    }
+    __syncthreads();
+    for (int cc = threadIdx.x; cc < cpg; cc += blockDim.x) {
+        const int c = g * cpg + cc;
+        const double ga = gamma ? (double)gamma[c] : 1.0;
+        const double be = beta ? (double)beta[c] : 0.0;
+        const double a = ga * rstd_s;
+        ab[((size_t)n * C + c) * 2 + 0] = (float)a;
+        ab[((size_t)n * C + c) * 2 + 1] = (float)(be - mean_s * a);
+    }
+}
+
+// GroupNorm normalisation, out = a[n,c] * v + b[n,c] with v = src or
+// ReLU(src).  Block row y is one (n, c) channel (rows beyond gridDim.y are
+// taken in further passes), so (a, b) is one scalar load; each thread issues
+// kNormUnroll loads before its stores to keep enough bytes in flight for HBM.
+// src == out is the in-place form.
+template <class V, bool RELU>
+__global__ __launch_bounds__(256) void normalize_kernel(const V *src, V *out, const float2 *ab, int rows,
+                                                        int row_len) {
+    for (int row = blockIdx.y; row < rows; row += gridDim.y) {
+        const float2 p = ab[row];
+        const V *s = src + (size_t)row * row_len;
+        V *o = out + (size_t)row * row_len;
+        const int base = blockIdx.x * (256 * kNormUnroll) + threadIdx.x;
+        V v[kNormUnroll];
+#pragma unroll
+        for (int k = 0; k < kNormUnroll; ++k) {
+            const int i = base + k * 256;
+            if (i < row_len) v[k] = s[i];
+        }
+#pragma unroll
+        for (int k = 0; k < kNormUnroll; ++k) {
+            const int i = base + k * 256;
+            if (i < row_len) {
+                float *c = comps(v[k]);
+#pragma unroll
+                for (int e = 0; e < ncomp<V>(); ++e) {
+                    const float x = RELU ? fmaxf(c[e], 0.0f) : c[e];
+                    c[e] = fmaf(p.x, x, p.y);
+                }
+                o[i] = v[k];
+            }
+        }
+    }
+}
+
+// BatchNorm (training) + average pool: one workgroup per channel.  partials
+// is [n][tile][C][2] of (sum z, sum z^2) with z = scale * y.  Writes the
+// pooled [n, C] output, the batch statistics and, when both buffers are
+// given, the running statistics (unbiased variance folded in).
+__global__ __launch_bounds__(256) void bn_finalize_kernel(const float *partials, int N, int tiles_per_n, int C,
+                                                          double S, float eps, const float *gamma,
+                                                          const float *beta, float *out, float *stats_out,
+                                                          float momentum, float *rmean, float *rvar) {
+    const int c = blockIdx.x;
+    double a1 = 0.0, a2 = 0.0;
+    const int items = N * tiles_per_n;
+    for (int i = threadIdx.x; i < items; i += blockDim.x) {
+        const float *pp = partials + ((size_t)i * C + c) * 2;  // i = n*tiles_per_n + t
+        a1 += (double)pp[0];
+        a2 += (double)pp[1];
+    }
+    __shared__ double r1[256], r2[256];
+    __shared__ double mean_s, rstd_s;
+    r1[threadIdx.x] = a1;
+    r2[threadIdx.x] = a2;
+    __syncthreads();
+    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) {
+            r1[threadIdx.x] += r1[threadIdx.x + off];
+            r2[threadIdx.x] += r2[threadIdx.x + off];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double cnt = (double)N * S;
+        const double mean = r1[0] / cnt;
+        double var = r2[0] / cnt - mean * mean;
+        if (var < 0.0) var = 0.0;
+        mean_s = mean;
+        rstd_s = 1.0 / sqrt(var + (double)eps);
+        if (stats_out) {
+            stats_out[(size_t)c * 2 + 0] = (float)mean;
+            stats_out[(size_t)c * 2 + 1] = (float)var;
+        }
+        if (rmean && rvar) {  // cnt > 1 is checked on the host
+            const double m = (double)momentum;
+            rmean[c] = (float)((1.0 - m) * (double)rmean[c] + m * mean);
+            rvar[c] = (float)((1.0 - m) * (double)rvar[c] + m * var * cnt / (cnt - 1.0));
+        }
+    }
+    __syncthreads();
+    const double ga = gamma ? (double)gamma[c] : 1.0;
+    const double be = beta ? (double)beta[c] : 0.0;
+    for (int n = threadIdx.x; n < N; n += blockDim.x) {
+        double m = 0.0;
+        for (int t = 0; t < tiles_per_n; ++t) m += (double)partials[(((size_t)n * tiles_per_n + t) * C + c) * 2];
+        m /= S;
+        out[(size_t)n * C + c] = (float)((m - mean_s) * rstd_s * ga + be);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Statistics of a conv output in memory: workgroup (chunk, row) sums
+// v = ReLU(mult*y) (RELU) or mult*y over elements [chunk*chunk_len,
+// (chunk+1)*chunk_len) of row = n*C + c and writes (sum v, sum v^2) to
+// partials[n][chunk][C][2], the layout the finalize kernels read.
+template <class V, bool RELU>
+__global__ __launch_bounds__(256) void row_stats_kernel(const V *y, int rows, int row_len, int chunk_len,
+                                                        int chunks, int C, float mult, float *partials) {
+    __shared__ float2 red[4];
+    for (int row = blockIdx.y; row < rows; row += gridDim.y) {
+        const V *p = y + (size_t)row * row_len;
+        const int beg = blockIdx.x * chunk_len;
+        const int end = min(row_len, beg + chunk_len);
+        float s1 = 0.0f, s2 = 0.0f;
+        for (int i0 = beg + (int)threadIdx.x; i0 < end; i0 += 256 * kNormUnroll) {
+            V v[kNormUnroll];
+#pragma unroll
+            for (int k = 0; k < kNormUnroll; ++k)
+                if (i0 + k * 256 < end) v[k] = p[i0 + k * 256];
+#pragma unroll
+            for (int k = 0; k < kNormUnroll; ++k)
+                if (i0 + k * 256 < end) {
+                    const float *c = comps(v[k]);
+#pragma unroll
+                    for (int e = 0; e < ncomp<V>(); ++e) {
+                        float a = mult * c[e];
+                        if (RELU) a = fmaxf(a, 0.0f);
+                        s1 += a;
+                        s2 = fmaf(a, a, s2);
+                    }
+                }
+        }
+        const float2 r = block_sum2(s1, s2, red);
+        if (threadIdx.x == 0) {
+            const int n = row / C, c = row - n * C;
+            float *pp = partials + (((size_t)n * chunks + blockIdx.x) * C + c) * 2;
+            pp[0] = r.x;
+            pp[1] = r.y;
+        }
+    }
+}
+
+// Channel softmax then sigmoid of a conv output in memory, [n][C][S] with S
+// counted in V units.  Thread = (n, one V of positions).  Pass 1 keeps a
+// running max m and sum l of exp(v - m) over the channels, four channels per
+// rescale; pass 2 reads the channels again and writes 1/(1 + exp(-p)) with
+// p = exp(v - m) / l.  out may equal src.
+template <class V>
+__global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out, int N, int C, int S) {
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= S) return;
+    constexpr int NC = ncomp<V>();
+    for (int n = blockIdx.y; n < N; n += gridDim.y) {
+        const V *p = src + (size_t)n * C * S + s;
+        V *o = out + (size_t)n * C * S + s;
+        float m[NC], l[NC];
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+            m[e] = -INFINITY;
+            l[e] = 0.0f;
+        }
+        int c = 0;
+        for (; c + 4 <= C; c += 4) {
+            V v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = p[(size_t)(c + j) * S];
+#pragma unroll
+            for (int e = 0; e < NC; ++e) {
+                const float a0 = comps(v[0])[e], a1 = comps(v[1])[e], a2 = comps(v[2])[e], a3 = comps(v[3])[e];
+                const float mn = fmaxf(m[e], fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)));
+                l[e] = l[e] * fast_exp(m[e] - mn) +
+                       ((fast_exp(a0 - mn) + fast_exp(a1 - mn)) + (fast_exp(a2 - mn) + fast_exp(a3 - mn)));
+                m[e] = mn;
+            }
+        }
+        for (; c < C; ++c) {
+            V v = p[(size_t)c * S];
+#pragma unroll
+            for (int e = 0; e < NC; ++e) {
+                const float a = comps(v)[e];
+                const float mn = fmaxf(m[e], a);
+                l[e] = l[e] * fast_exp(m[e] - mn) + fast_exp(a - mn);
+                m[e] = mn;
+            }
+        }
+        float inv[NC];
+#pragma unroll
+        for (int e = 0; e < NC; ++e) inv[e] = __builtin_amdgcn_rcpf(l[e]);
+        for (c = 0; c < C; ++c) {
+            V v = p[(size_t)c * S];
+            float *a = comps(v);
+#pragma unroll
+            for (int e = 0; e < NC; ++e) {
+                const float pr = fast_exp(a[e] - m[e]) * inv[e];
+                a[e] = __builtin_amdgcn_rcpf(1.0f + fast_exp(-pr));
+            }
+            o[(size_t)c * S] = v;
+        }
+    }
+}
+
+// Eval-mode BatchNorm + pool from per-row sums (partials [n][chunk][C][2] of
+// (sum y, -)): thread per (n, c), pooled mean m = sum / S, then
+// out = (scale*m - rmean) / sqrt(rvar + eps) * gamma + beta.
+__global__ __launch_bounds__(256) void bn_eval_rows_kernel(const float *partials, int N, int chunks, int C,
+                                                           double S, float scale, float eps, const float *gamma,
+                                                           const float *beta, const float *rmean,
+                                                           const float *rvar, float *out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= N * C) return;
+    const int n = i / C, c = i - n * C;
+    double sum = 0.0;
+    for (int t = 0; t < chunks; ++t) sum += (double)partials[(((size_t)n * chunks + t) * C + c) * 2];
+    const double m = (double)scale * sum / S;
+    const double ga = gamma ? (double)gamma[c] : 1.0, be = beta ? (double)beta[c] : 0.0;
+    const double mu = rmean ? (double)rmean[c] : 0.0, var = rvar ? (double)rvar[c] : 1.0;
+    out[i] = (float)((m - mu) / sqrt(var + (double)eps) * ga + be);
+}
+
+// ---------------------------------------------------------------------------
+// Evaluation-mode BatchNorm + pool without the convolution.  Along each dim
+// the input range splits into bins [cut[j], cut[j+1]); tap t reaches the
+// output from exactly the inputs [lo[t], hi1[t]), a union of whole bins.  So
+//   sum_o y[n,co,o] = S*bias[co] + sum_ci sum_bins R[n,ci,bin] * Wb[co,ci,bin]
+// with R the sum of x over the bin box and Wb the sum of w over the taps whose
+// input range holds the bin.
+
+__device__ __forceinline__ int bin_of(const EvalGeom &E, int b, int dim) {
+    if (dim == 0) return b / (E.nb[1] * E.nb[2]);
+    if (dim == 1) return (b / E.nb[2]) % E.nb[1];
+    return b % E.nb[2];
+}
+
+// Wb[co][ci][bin]: one wave per (ci, co) weight row of k^3 taps.
+__global__ __launch_bounds__(256) void eval_pack_kernel(const EvalGeom E, const float *w, float *wb) {
+    const int pair = blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // ci*Cout + co
+    const int lane = threadIdx.x & 63;
+    if (pair >= E.Cin * E.Cout) return;
+    const int ci = pair / E.Cout, co = pair - ci * E.Cout;
+    const int k = E.k, k2 = k * k, k3 = k2 * k;
+    const float *row = w + (size_t)pair * k3;
+    for (int b = 0; b < E.nbins; ++b) {
+        const int bd = bin_of(E, b, 0), bh = bin_of(E, b, 1), bw = bin_of(E, b, 2);
+        double acc = 0.0;
+        for (int t = lane; t < k3; t += 64) {
+            const int td = t / k2, th = (t / k) % k, tw = t % k;
+            const bool in = E.lo[0][td] <= E.cut[0][bd] && E.cut[0][bd + 1] <= E.hi1[0][td] &&
+                            E.lo[1][th] <= E.cut[1][bh] && E.cut[1][bh + 1] <= E.hi1[1][th] &&
+                            E.lo[2][tw] <= E.cut[2][bw] && E.cut[2][bw + 1] <= E.hi1[2][tw];
+            if (in) acc += (double)row[t];
+        }
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        if (lane == 0) wb[((size_t)co * E.Cin + ci) * E.nbins + b] = (float)acc;
+    }
+}
+
+// Sum of x over the box [da,db) x [ha,hb) x [wa,wb) of one plane, this
+// wave's share (4 waves).  Rows are dealt to lanes so that a row of up to 64
+// vectors (VEC: float4, else float) is one coalesced wave access, and each
+// lane issues 4 row loads before it adds; wider rows loop over the lanes.
+template <bool VEC>
+__device__ float box_sum(const float *xp, int H, int W, int da, int db, int ha, int hb, int wa, int wb,
+                         int lane, int wave) {
+    constexpr int U = 4;
+    const int bh_len = hb - ha;
+    const int nrows = (db - da) * bh_len;
+    const int width = VEC ? (wb - wa) >> 2 : (wb - wa);
+    auto load = [&](const float *rowp, int i) {
+        if (VEC) {
+            const float4 v = reinterpret_cast<const float4 *>(rowp)[i];
+            return (v.x + v.y) + (v.z + v.w);
+        }
+        return rowp[i];
+    };
+    // row r of the box -> (dd, hh), advanced by `step` rows at a time
+    float acc = 0.0f;
+    if (width <= 64) {
+        const int rpi = 64 / width;            // rows per wave access
+        const int lr = lane / width, lw = lane - lr * width;
+        if (lr >= rpi) return 0.0f;
+        const int step = 4 * rpi;              // rows per workgroup step
+        const int sd = step / bh_len, sh = step - sd * bh_len;
+        int r = wave * rpi + lr;
+        int dd = r / bh_len, hh = r - dd * bh_len;
+        for (; r < nrows; r += U * step) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                v[u] = 0.0f;
+                if (r + u * step < nrows) v[u] = load(xp + ((size_t)(da + dd) * H + (ha + hh)) * W + wa, lw);
+                dd += sd;
+                hh += sh;
+                if (hh >= bh_len) {
+                    hh -= bh_len;
+                    ++dd;
+                }
+            }
+            acc += (v[0] + v[1]) + (v[2] + v[3]);
+        }
+    } else {
+        int dd = wave / bh_len, hh = wave - (wave / bh_len) * bh_len;
+        const int sd = 4 / bh_len, sh = 4 - sd * bh_len;
+        for (int r = wave; r < nrows; r += 4) {
+            const float *rowp = xp + ((size_t)(da + dd) * H + (ha + hh)) * W + wa;
+            int i = lane;
+            for (; i + (U - 1) * 64 < width; i += U * 64) {
+                float v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = load(rowp, i + u * 64);
+                acc += (v[0] + v[1]) + (v[2] + v[3]);
+            }
+            for (; i < width; i += 64) acc += load(rowp, i);
+            dd += sd;
+            hh += sh;
+            if (hh >= bh_len) {
+                hh -= bh_len;
+                ++dd;
+            }
+        }
+    }
+    return acc;
+}
+
+// R[plane][chunk][bin]: workgroup = (plane = n*Cin + ci, d-chunk).
+__global__ __launch_bounds__(256) void eval_binsum_kernel(const EvalGeom E, const float *x, float *R) {
+    const int plane = blockIdx.x / E.nchunk, chunk = blockIdx.x - plane * E.nchunk;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int d0 = chunk * E.dchunk, d1 = min(E.D, d0 + E.dchunk);
+    const float *xp = x + (size_t)plane * E.D * E.H * E.W;
+    float *Rp = R + ((size_t)plane * E.nchunk + chunk) * E.nbins;
+    __shared__ float red[4];
+    for (int b = 0; b < E.nbins; ++b) {
+        const int bd = bin_of(E, b, 0), bh = bin_of(E, b, 1), bw = bin_of(E, b, 2);
+        const int da = max(E.cut[0][bd], d0), db = min(E.cut[0][bd + 1], d1);
+        const int ha = E.cut[1][bh], hb = E.cut[1][bh + 1], wa = E.cut[2][bw], wb = E.cut[2][bw + 1];
+        float acc = 0.0f;
+        if (da < db) {
+            if (((wa | wb | E.W) & 3) == 0) acc = box_sum<true>(xp, E.H, E.W, da, db, ha, hb, wa, wb, lane, wave);
+            else acc = box_sum<false>(xp, E.H, E.W, da, db, ha, hb, wa, wb, lane, wave);
+        }
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        if (lane == 0) red[wave] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) Rp[b] = (red[0] + red[1]) + (red[2] + red[3]);
+        __syncthreads();
+    }
+}
+
+// out[n, co]: one wave per (n, co); fp64 dot product of the chunk-summed bin
+// sums with Wb, then BatchNorm with the running statistics.
+__global__ __launch_bounds__(256) void eval_finalize_kernel(const EvalGeom E, const float *R, const float *wb,
+                                                            const float *bias, float scale, float eps,
+                                                            const float *gamma, const float *beta,
+                                                            const float *rmean, const float *rvar, float *out) {
+    const int item = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (item >= E.N * E.Cout) return;
+    const int n = item / E.Cout, co = item - n * E.Cout;
+    const int K = E.Cin * E.nbins;
+    double acc = 0.0;
+    for (int j = lane; j < K; j += 64) {
+        const int ci = j / E.nbins, b = j - ci * E.nbins;
+        const float *r = R + ((size_t)(n * E.Cin + ci) * E.nchunk) * E.nbins + b;
+        double rs = 0.0;
+        for (int c = 0; c < E.nchunk; ++c) rs += (double)r[(size_t)c * E.nbins];
+        acc += rs * (double)wb[(size_t)co * K + j];
+    }
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) {
+        const double m = (bias ? (double)bias[co] : 0.0) + acc * E.inv_S;
+        const double ga = gamma ? (double)gamma[co] : 1.0, be = beta ? (double)beta[co] : 0.0;
+        const double mu = rmean ? (double)rmean[co] : 0.0, var = rvar ? (double)rvar[co] : 1.0;
+        out[item] = (float)(((double)scale * m - mu) / sqrt(var + (double)eps) * ga + be);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, double count, float eps,
+                       const float *gamma, const float *beta, float *ab, float *stats_out, void *stream) {
+    hipLaunchKernelGGL(gn_finalize_kernel, dim3(N * G), dim3(256), 0, (hipStream_t)stream, partials, tiles_per_n,
+                       C, G, eps, gamma, beta, ab, stats_out, count);
+    return (int)hipGetLastError();
+}
+
+template <class V, bool RELU>
+static void launch_normalize_t(const float *src, float *out, const float *ab, int rows, int len, void *stream) {
+    const int gx = (len + 256 * kNormUnroll - 1) / (256 * kNormUnroll);
+    const int gy = rows < 65535 ? rows : 65535;
+    hipLaunchKernelGGL((normalize_kernel<V, RELU>), dim3(gx, gy), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const V *>(src), reinterpret_cast<V *>(out),
+                       reinterpret_cast<const float2 *>(ab), rows, len);
+}
+
+int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool relu,
+                     void *stream) {
+    const bool vec = S % 4 == 0;
+    const int len = (int)(vec ? S / 4 : S);
+    if (vec) {
+        if (relu) launch_normalize_t<float4, true>(src, out, ab, rows, len, stream);
+        else launch_normalize_t<float4, false>(src, out, ab, rows, len, stream);
+    } else {
+        if (relu) launch_normalize_t<float, true>(src, out, ab, rows, len, stream);
+        else launch_normalize_t<float, false>(src, out, ab, rows, len, stream);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,
+                       float *out, void *stream) {
+    hipLaunchKernelGGL(bn_finalize_kernel, dim3(C), dim3(256), 0, (hipStream_t)stream, partials, N, tiles_per_n,
+                       C, S, e.eps, e.gamma, e.beta, out, e.stats_out, e.momentum, e.running_mean,
+                       e.running_var);
+    return (int)hipGetLastError();
+}
+
+int row_stat_chunks(int64_t S) {
+    const int64_t len = S % 4 == 0 ? S / 4 : S;          // in vector units
+    int64_t c = (len + kRowStatChunk - 1) / kRowStatChunk;
+    return (int)(c < 1 ? 1 : c);
+}
+
+template <class V, bool RELU>
+static void launch_row_stats_t(const float *y, int rows, int len, int chunks, int C, float mult, float *partials,
+                               void *stream) {
+    const int chunk_len = (len + chunks - 1) / chunks;
+    const int gy = rows < 65535 ? rows : 65535;
+    hipLaunchKernelGGL((row_stats_kernel<V, RELU>), dim3(chunks, gy), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const V *>(y), rows, len, chunk_len, chunks, C, mult, partials);
+}
+
+int launch_row_stats(const float *y, int N, int C, int64_t S, bool relu, float mult, float *partials,
+                     void *stream) {
+    const bool vec = S % 4 == 0;
+    const int len = (int)(vec ? S / 4 : S);
+    const int chunks = row_stat_chunks(S);
+    const int rows = N * C;
+    if (vec) {
+        if (relu) launch_row_stats_t<float4, true>(y, rows, len, chunks, C, mult, partials, stream);
+        else launch_row_stats_t<float4, false>(y, rows, len, chunks, C, mult, partials, stream);
+    } else {
+        if (relu) launch_row_stats_t<float, true>(y, rows, len, chunks, C, mult, partials, stream);
+        else launch_row_stats_t<float, false>(y, rows, len, chunks, C, mult, partials, stream);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, void *stream) {
+    const int gy = N < 65535 ? N : 65535;
+    if (S % 4 == 0) {
+        const int len = (int)(S / 4);
+        hipLaunchKernelGGL(softmax_pass_kernel<float4>, dim3((len + 255) / 256, gy), dim3(256), 0,
+                           (hipStream_t)stream, reinterpret_cast<const float4 *>(src),
+                           reinterpret_cast<float4 *>(out), N, C, len);
+    } else {
+        const int len = (int)S;
+        hipLaunchKernelGGL(softmax_pass_kernel<float>, dim3((len + 255) / 256, gy), dim3(256), 0,
+                           (hipStream_t)stream, src, out, N, C, len);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_bn_eval_rows(const float *partials, int N, int chunks, int C, double S, const convt3d_epilogue &e,
+                        float *out, void *stream) {
+    const int items = N * C;
+    hipLaunchKernelGGL(bn_eval_rows_kernel, dim3((items + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       partials, N, chunks, C, S, e.scale, e.eps, e.gamma, e.beta, e.running_mean, e.running_var,
+                       out);
+    return (int)hipGetLastError();
+}
+
+int launch_eval_pack(const EvalGeom &E, const float *w, float *wb, void *stream) {
+    const int64_t pairs = (int64_t)E.Cin * E.Cout;
+    hipLaunchKernelGGL(eval_pack_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, (hipStream_t)stream, E,
+                       w, wb);
+    return (int)hipGetLastError();
+}
+
+int launch_eval_binsum(const EvalGeom &E, const float *x, float *R, void *stream) {
+    const int64_t blocks = (int64_t)E.N * E.Cin * E.nchunk;
+    hipLaunchKernelGGL(eval_binsum_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, E, x, R);
+    return (int)hipGetLastError();
+}
+
+int launch_eval_finalize(const EvalGeom &E, const float *R, const float *wb, const float *bias,
+                         const convt3d_epilogue &e, float *out, void *stream) {
+    const int64_t items = (int64_t)E.N * E.Cout;
+    hipLaunchKernelGGL(eval_finalize_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, (hipStream_t)stream,
+                       E, R, wb, bias, e.scale, e.eps, e.gamma, e.beta, e.running_mean, e.running_var, out);
+    return (int)hipGetLastError();
+}
+
+}  // namespace convt3d

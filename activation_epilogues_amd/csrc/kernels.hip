@@ -9,12 +9,9 @@
 //                           bias (+ReLU) store with per-tile channel sums for
 //                           GroupNorm, in-register channel softmax + sigmoid,
 //                           or per-tile channel sums of scale*y for BatchNorm.
-//  * gn_finalize_kernel  -- per (n, group) fp64 merge of the tile partials,
-//                           mean / biased variance / rstd, per-channel a, b.
-//  * normalize_kernel    -- out = a[n,c] * out + b[n,c], in place, float4.
-//  * bn_finalize_kernel  -- per channel fp64 batch mean / biased variance and
-//                           the pooled output (mean over voxels of the
-//                           normalised values = (mean_nc - mean_c)*rstd*g + b).
+//
+// The statistics, normalisation and standalone epilogue passes that run after
+// this kernel are in epilogue.hip.
 //
 // MFMA 32x32x2 f32 operand layout (checked on the device): lane l supplies
 // A[row = l%32][k = l/32] and B[k = l/32][col = l%32]; accumulator register r
@@ -650,142 +647,6 @@ void convt3d_mfma_kernel(const ConvParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// GroupNorm statistics: one workgroup per (n, group); fp64 sums of the fp32
-// tile partials in a fixed order, then mean, biased variance E[r^2] - mean^2,
-// rstd = 1/sqrt(var + eps), and per channel a = gamma*rstd, b = beta - mean*a.
-__global__ __launch_bounds__(256) void gn_finalize_kernel(const float *partials, int tiles_per_n, int C,
-                                                          int G, float eps, const float *gamma,
-                                                          const float *beta, float *ab, float *stats_out,
-                                                          double count) {
-    const int n = blockIdx.x / G, g = blockIdx.x % G;
-    const int cpg = C / G;
-    const int items = tiles_per_n * cpg;
-    double a1 = 0.0, a2 = 0.0;
-    for (int i = threadIdx.x; i < items; i += blockDim.x) {
-        const int t = i / cpg, cc = i - t * cpg;
-        const float *pp = partials + (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2;
-        a1 += (double)pp[0];
-        a2 += (double)pp[1];
-    }
-    __shared__ double r1[256], r2[256];
-    __shared__ double mean_s, rstd_s;
-    r1[threadIdx.x] = a1;
-    r2[threadIdx.x] = a2;
-    __syncthreads();
-    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) {
-            r1[threadIdx.x] += r1[threadIdx.x + off];
-            r2[threadIdx.x] += r2[threadIdx.x + off];
-        }
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        const double mean = r1[0] / count;
-        double var = r2[0] / count - mean * mean;
-        if (var < 0.0) var = 0.0;
-        mean_s = mean;
-        rstd_s = 1.0 / sqrt(var + (double)eps);
-        if (stats_out) {
-            stats_out[((size_t)n * G + g) * 2 + 0] = (float)mean;
-            stats_out[((size_t)n * G + g) * 2 + 1] = (float)rstd_s;
-        }
-    }
-    __syncthreads();
-    for (int cc = threadIdx.x; cc < cpg; cc += blockDim.x) {
-        const int c = g * cpg + cc;
-        const double ga = gamma ? (double)gamma[c] : 1.0;
-        const double be = beta ? (double)beta[c] : 0.0;
-        const double a = ga * rstd_s;
-        ab[((size_t)n * C + c) * 2 + 0] = (float)a;
-        ab[((size_t)n * C + c) * 2 + 1] = (float)(be - mean_s * a);
-    }
-}
-
-// out = a[row] * out + b[row] for rows of S elements (S % 4 == 0: float4 path).
-// GroupNorm normalisation in place, out = a[n,c] * out + b[n,c].  Block row y
-// is one (n, c) channel (rows beyond gridDim.y are taken in further passes),
-// so (a, b) is one scalar load; each thread issues kNormUnroll loads before
-// its stores to keep enough bytes in flight for HBM.
-constexpr int kNormUnroll = 4;
-template <class V>
-__global__ __launch_bounds__(256) void normalize_kernel(V *out, const float2 *ab, int rows, int row_len) {
-    for (int row = blockIdx.y; row < rows; row += gridDim.y) {
-        const float2 p = ab[row];
-        V *o = out + (size_t)row * row_len;
-        const int base = blockIdx.x * (256 * kNormUnroll) + threadIdx.x;
-        V v[kNormUnroll];
-#pragma unroll
-        for (int k = 0; k < kNormUnroll; ++k) {
-            const int i = base + k * 256;
-            if (i < row_len) v[k] = o[i];
-        }
-#pragma unroll
-        for (int k = 0; k < kNormUnroll; ++k) {
-            const int i = base + k * 256;
-            if (i < row_len) {
-                if constexpr (sizeof(V) == 16) {
-                    float4 &x = reinterpret_cast<float4 &>(v[k]);
-                    x.x = fmaf(p.x, x.x, p.y);
-                    x.y = fmaf(p.x, x.y, p.y);
-                    x.z = fmaf(p.x, x.z, p.y);
-                    x.w = fmaf(p.x, x.w, p.y);
-                } else {
-                    reinterpret_cast<float &>(v[k]) = fmaf(p.x, reinterpret_cast<float &>(v[k]), p.y);
-                }
-                o[i] = v[k];
-            }
-        }
-    }
-}
-
-// BatchNorm (training) + average pool: one workgroup per channel.
-__global__ __launch_bounds__(256) void bn_finalize_kernel(const float *partials, int N, int tiles_per_n, int C,
-                                                          double S, float eps, const float *gamma,
-                                                          const float *beta, float *out, float *stats_out) {
-    const int c = blockIdx.x;
-    double a1 = 0.0, a2 = 0.0;
-    const int items = N * tiles_per_n;
-    for (int i = threadIdx.x; i < items; i += blockDim.x) {
-        const float *pp = partials + ((size_t)i * C + c) * 2;  // i = n*tiles_per_n + t
-        a1 += (double)pp[0];
-        a2 += (double)pp[1];
-    }
-    __shared__ double r1[256], r2[256];
-    __shared__ double mean_s, rstd_s;
-    r1[threadIdx.x] = a1;
-    r2[threadIdx.x] = a2;
-    __syncthreads();
-    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) {
-            r1[threadIdx.x] += r1[threadIdx.x + off];
-            r2[threadIdx.x] += r2[threadIdx.x + off];
-        }
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        const double cnt = (double)N * S;
-        const double mean = r1[0] / cnt;
-        double var = r2[0] / cnt - mean * mean;
-        if (var < 0.0) var = 0.0;
-        mean_s = mean;
-        rstd_s = 1.0 / sqrt(var + (double)eps);
-        if (stats_out) {
-            stats_out[(size_t)c * 2 + 0] = (float)mean;
-            stats_out[(size_t)c * 2 + 1] = (float)var;
-        }
-    }
-    __syncthreads();
-    const double ga = gamma ? (double)gamma[c] : 1.0;
-    const double be = beta ? (double)beta[c] : 0.0;
-    for (int n = threadIdx.x; n < N; n += blockDim.x) {
-        double m = 0.0;
-        for (int t = 0; t < tiles_per_n; ++t) m += (double)partials[(((size_t)n * tiles_per_n + t) * C + c) * 2];
-        m /= S;
-        out[(size_t)n * C + c] = (float)((m - mean_s) * rstd_s * ga + be);
-    }
-}
-
-// ---------------------------------------------------------------------------
 // launchers
 
 static int grid_for(int64_t items, int per_block, int cap) {
@@ -874,39 +735,6 @@ int launch_conv(const Plan &pl, const ConvParams &cp, void *stream) {
 #undef CONVT3D_VARIANT
 #undef CONVT3D_VARIANT_PL
     return (int)hipErrorInvalidValue;
-}
-
-int launch_gn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta, float *ab,
-                       float *stats_out, void *stream) {
-    const int G = pl.e.groups;
-    const double count = (double)(pl.g.cout / G) * (double)pl.S;
-    hipLaunchKernelGGL(gn_finalize_kernel, dim3(pl.g.n * G), dim3(256), 0, (hipStream_t)stream, partials,
-                       (int)pl.tiles_per_n, pl.g.cout, G, pl.e.eps, gamma, beta, ab, stats_out, count);
-    return (int)hipGetLastError();
-}
-
-int launch_normalize(const Plan &pl, float *out, const float *ab, void *stream) {
-    const int rows = pl.g.n * pl.g.cout;
-    const int gy = rows < 65535 ? rows : 65535;
-    if (pl.S % 4 == 0) {
-        const int len = (int)(pl.S / 4);
-        const int gx = (len + 256 * kNormUnroll - 1) / (256 * kNormUnroll);
-        hipLaunchKernelGGL(normalize_kernel<float4>, dim3(gx, gy), dim3(256), 0, (hipStream_t)stream,
-                           reinterpret_cast<float4 *>(out), reinterpret_cast<const float2 *>(ab), rows, len);
-    } else {
-        const int len = (int)pl.S;
-        const int gx = (len + 256 * kNormUnroll - 1) / (256 * kNormUnroll);
-        hipLaunchKernelGGL(normalize_kernel<float>, dim3(gx, gy), dim3(256), 0, (hipStream_t)stream, out,
-                           reinterpret_cast<const float2 *>(ab), rows, len);
-    }
-    return (int)hipGetLastError();
-}
-
-int launch_bn_finalize(const Plan &pl, const float *partials, const float *gamma, const float *beta, float *out,
-                       float *stats_out, void *stream) {
-    hipLaunchKernelGGL(bn_finalize_kernel, dim3(pl.g.cout), dim3(256), 0, (hipStream_t)stream, partials, pl.g.n,
-                       (int)pl.tiles_per_n, pl.g.cout, (double)pl.S, pl.e.eps, gamma, beta, out, stats_out);
-    return (int)hipGetLastError();
 }
 
 }  // namespace convt3d

@@ -124,14 +124,73 @@ static void ws_layout(Plan *pl) {
         off += (bytes + 255) & ~size_t(255);
         return o;
     };
-    pl->ws_partials = pl->ws_ab = 0;
+    pl->ws_partials = pl->ws_ab = pl->ws_bins = 0;
     const int epi = pl->e.kind;
-    if (epi == CONVT3D_EPI_RELU_GROUPNORM || epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) {
+    if (pl->eval) {
+        const EvalGeom &E = pl->eg;
+        pl->ws_bins = take((size_t)E.N * E.Cin * E.nchunk * E.nbins * sizeof(float));
+    } else if (epi == CONVT3D_EPI_RELU_GROUPNORM || epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) {
         pl->ws_partials = take((size_t)g.n * pl->tiles_per_n * g.cout * 2 * sizeof(float));
         if (epi == CONVT3D_EPI_RELU_GROUPNORM)
             pl->ws_ab = take((size_t)g.n * g.cout * 2 * sizeof(float));
     }
     pl->ws_bytes = off;
+}
+
+// Input bins of the evaluation-mode BatchNorm + pool path.  Along one dim,
+// tap t reaches output s*i - p + t in [0, out) from inputs i in
+// [ceil((p - t)/s), floor((out - 1 + p - t)/s)] clipped to [0, in); the cuts
+// are every such range's ends plus 0 and in, so each range is a union of
+// consecutive bins.
+int make_eval_geom(const convt3d_geom *g, EvalGeom *eg) {
+    const int st = validate_geom(g);
+    if (st) return st;
+    if (g->k > kEvalMaxK) return CONVT3D_ERR_UNSUPPORTED;
+    std::memset(eg, 0, sizeof(*eg));
+    eg->N = g->n; eg->Cin = g->cin; eg->Cout = g->cout;
+    eg->D = g->d; eg->H = g->h; eg->W = g->w; eg->k = g->k;
+    const int s = g->stride, p = g->pad;
+    const int ins[3] = {g->d, g->h, g->w};
+    int64_t S = 1;
+    for (int dim = 0; dim < 3; ++dim) {
+        const int in = ins[dim];
+        const int out = (int)out_dim(in, g->k, s, p, g->out_pad);
+        S *= out;
+        std::vector<int> cuts = {0, in};
+        for (int t = 0; t < g->k; ++t) {
+            // smallest i with s*i >= p - t, largest i with s*i <= out - 1 + p - t
+            const int64_t a = p - t, b = (int64_t)out - 1 + p - t;
+            int64_t lo = a <= 0 ? 0 : (a + s - 1) / s;
+            int64_t hi = b < 0 ? -1 : b / s;
+            lo = std::max<int64_t>(lo, 0);
+            hi = std::min<int64_t>(hi, in - 1);
+            if (lo > hi) {
+                eg->lo[dim][t] = 1;
+                eg->hi1[dim][t] = 0;  // reaches nothing
+                continue;
+            }
+            eg->lo[dim][t] = (int)lo;
+            eg->hi1[dim][t] = (int)hi + 1;
+            cuts.push_back((int)lo);
+            cuts.push_back((int)hi + 1);
+        }
+        std::sort(cuts.begin(), cuts.end());
+        cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+        eg->nb[dim] = (int)cuts.size() - 1;
+        for (size_t j = 0; j < cuts.size(); ++j) eg->cut[dim][j] = cuts[j];
+    }
+    eg->nbins = eg->nb[0] * eg->nb[1] * eg->nb[2];
+    eg->inv_S = 1.0 / (double)S;
+    if ((int64_t)g->cin * g->cout * eg->nbins > (int64_t)INT32_MAX / 4) return CONVT3D_ERR_TOO_LARGE;
+    // d-chunks: enough workgroups to cover the chip when n * cin is small
+    const int64_t planes = std::max<int64_t>((int64_t)g->n * g->cin, 1);
+    int64_t nchunk = (kEvalTargetBlocks + planes - 1) / planes;
+    nchunk = std::max<int64_t>(1, std::min<int64_t>(nchunk, g->d));
+    eg->dchunk = (int)((g->d + nchunk - 1) / nchunk);
+    eg->nchunk = (int)((g->d + eg->dchunk - 1) / eg->dchunk);
+    if (planes * eg->nchunk > (int64_t)INT32_MAX || planes * eg->nchunk * eg->nbins > (int64_t)INT32_MAX)
+        return CONVT3D_ERR_TOO_LARGE;
+    return CONVT3D_OK;
 }
 
 // Search of the kernel configuration: every (variant, wave grid, border split,
@@ -148,12 +207,24 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     if (st == CONVT3D_OK && pl->S * 20 >= (int64_t(1) << 32)) st = CONVT3D_ERR_TOO_LARGE;
     if (st) return st;
     pl->e = *e;
-    if (e->kind < CONVT3D_EPI_NONE || e->kind > CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL)
+    if (e->kind < CONVT3D_EPI_NONE || e->kind > CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL)
         return CONVT3D_ERR_UNSUPPORTED;
     if (e->kind == CONVT3D_EPI_RELU_GROUPNORM && (e->groups < 1 || g->cout % e->groups != 0))
         return CONVT3D_ERR_GROUPS;
-    const bool softmax = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID;
-    if (softmax && pl->cb_total > 4) return CONVT3D_ERR_UNSUPPORTED;
+    if (e->kind == CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL) {
+        // no convolution: one plan, the bin sums of x and their contraction
+        st = make_eval_geom(g, &pl->eg);
+        if (st) return st;
+        pl->eval = 1;
+        pl->valid_macs = 0;
+        ws_layout(pl);
+        out->push_back(*pl);
+        return CONVT3D_OK;
+    }
+    // the in-register softmax needs every channel in one workgroup (<= 4 blocks
+    // of 32); beyond that the conv stores y and a second pass finishes
+    const bool softmax = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID && pl->cb_total <= 4;
+    pl->softmax_pass = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID && !softmax;
 
     const int s = pl->s;
     const int ins[3] = {g->d, g->h, g->w};
@@ -529,7 +600,7 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->nxcd = kNumXcd;
     cp->order = pl.order;
     cp->phase_loop = pl.phase_loop; cp->red_off = pl.red_off;
-    cp->epi = pl.e.kind;
+    cp->epi = pl.softmax_pass ? CONVT3D_EPI_NONE : pl.e.kind;
     cp->scale = pl.e.kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL ? pl.e.scale : 1.0f;
     cp->tiles_per_n = (int)pl.tiles_per_n;
     for (int dim = 0; dim < 3; ++dim)

@@ -36,19 +36,23 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense FP32 matrix peak
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 METRIC = "ConvTranspose3d+epilogue GFLOP/s and ms/forward; % FP32 MFMA peak"
-KERNEL_SRC = os.path.join(ROOT, "activation_epilogues_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "activation_epilogues_amd", "csrc")
+# source file of each kernel a roofline line is given for
+KERNEL_SRC = {"convt3d_mfma_kernel": os.path.join(CSRC, "kernels.hip"),
+              "eval_binsum_kernel": os.path.join(CSRC, "epilogue.hip")}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_source_hash(kernel: str = "convt3d_mfma_kernel") -> str:
+    """Hash of the HIP source file `kernel` is built from."""
+    with open(KERNEL_SRC[kernel], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per conv launch from the committed rocprofv3 --pmc summary, if it
-    was taken from the current kernel source (else None)."""
-    path = os.path.join(PROFILES, f"convt3d_mfma_kernel_{workload}_traffic.txt")
+def stored_traffic(workload: str, kernel: str = "convt3d_mfma_kernel"):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
+    summary, if it was taken from the current kernel source (else None)."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -56,7 +60,7 @@ def stored_traffic(workload: str):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -80,6 +84,74 @@ def cpu_baseline(wl, inp, max_samples: int):
     return n, dt, oracle.num_threads()
 
 
+def torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, fused_ms, reps: int = 5):
+    """Context only: PyTorch-ROCm's own ConvTranspose3d followed by its
+    epilogue ops (eager), its conv alone, and its conv followed by
+    convt3d_epilogue_only; each timed with events over `reps` calls after one
+    warm-up call, plus the largest difference of the eager result from the
+    fused one."""
+    import torch
+    import torch.nn.functional as F
+    from activation_epilogues_amd import convt3d as C
+    from activation_epilogues_amd import workloads as W
+    torch.backends.cudnn.allow_tf32 = False   # keep fp32 arithmetic in the vendor conv
+    torch.backends.cuda.matmul.allow_tf32 = False
+    rm_t = None if rmean is None else rmean.clone()
+    rv_t = None if rvar is None else rvar.clone()
+
+    def conv():
+        return F.conv_transpose3d(x, w, b, stride=wl.stride, padding=wl.pad, output_padding=wl.out_pad)
+
+    def tail(y):
+        if wl.epi == W.EPI_RELU_GROUPNORM:
+            return F.group_norm(F.relu(y), wl.groups, gamma, beta, eps=wl.eps)
+        if wl.epi == W.EPI_SOFTMAX_SIGMOID:
+            return torch.sigmoid(torch.softmax(y, dim=1))
+        if wl.epi in (W.EPI_SCALE_BN_TRAIN_AVGPOOL, W.EPI_SCALE_BN_EVAL_AVGPOOL):
+            training = wl.epi == W.EPI_SCALE_BN_TRAIN_AVGPOOL
+            z = F.batch_norm(y * wl.scale, rm_t, rv_t, gamma, beta, training=training, momentum=wl.momentum,
+                             eps=wl.eps)
+            return F.adaptive_avg_pool3d(z, 1)
+        return y
+
+    S = int(call.out_dims[0] * call.out_dims[1] * call.out_dims[2])
+    epi = C.make_epilogue(wl.epi, wl.groups, wl.eps, wl.scale, gamma, beta, None, wl.momentum, None, None)
+    has_tail = wl.epi != W.EPI_NONE
+    ws_bytes = C.convt3d_epilogue_workspace_size(wl.n, wl.cout, S, epi) if has_tail else 0
+    ws = torch.empty(max(1, ws_bytes // 4), device=x.device)
+    pooled = wl.epi in (W.EPI_SCALE_BN_TRAIN_AVGPOOL, W.EPI_SCALE_BN_EVAL_AVGPOOL)
+
+    def conv_then_ours():
+        y = conv()
+        if not has_tail:
+            return y
+        out = torch.empty((wl.n, wl.cout), device=x.device) if pooled else y
+        C.convt3d_epilogue_only(y, wl.n, wl.cout, S, epi, out, ws, ws_bytes)
+        return out
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    print("[bench] timing the PyTorch comparison", file=sys.stderr, flush=True)
+    eager_ms = timed(lambda: tail(conv()))
+    conv_ms = timed(conv)
+    ours_tail_ms = timed(conv_then_ours)
+    ref = tail(conv()).reshape(call.out.shape)
+    diff = float((ref - call.out).abs().max())
+    return {"torch_eager_ms": round(eager_ms, 3), "torch_conv_ms": round(conv_ms, 3),
+            "torch_conv_plus_epilogue_only_ms": round(ours_tail_ms, 3), "fused_ms_per_step": round(fused_ms, 3),
+            "speedup_vs_torch_eager": round(eager_ms / fused_ms, 2), "max_abs_diff_vs_torch_eager": diff,
+            "reps": reps, "note": "PyTorch-ROCm (MIOpen) fp32, TF32 off; context only"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +165,9 @@ def main():
     ap.add_argument("--plan", default=None, help="force a plan (CONVT3D_PLAN string); implies --no-tune")
     ap.add_argument("--phase-loop", type=int, choices=(0, 1), default=None,
                     help="force the phase-group loop off / on (with --plan)")
+    ap.add_argument("--compare-torch", action="store_true",
+                    help="also time PyTorch's own ConvTranspose3d + epilogue ops, and its conv followed by "
+                         "convt3d_epilogue_only (context only)")
     args = ap.parse_args()
     if args.plan is not None:
         os.environ["CONVT3D_PLAN"] = args.plan
@@ -119,6 +194,10 @@ def main():
     b = None if inp.b is None else torch.from_numpy(inp.b).to(dev)
     gamma = None if inp.gamma is None else torch.from_numpy(inp.gamma).to(dev)
     beta = None if inp.beta is None else torch.from_numpy(inp.beta).to(dev)
+    # BatchNorm running statistics (training: updated every step; eval: read)
+    rmean = None if inp.rmean is None else torch.from_numpy(inp.rmean).to(dev)
+    rvar = None if inp.rvar is None else torch.from_numpy(inp.rvar).to(dev)
+    evalmode = wl.epi == W.EPI_SCALE_BN_EVAL_AVGPOOL
     stream = torch.cuda.current_stream()
     tune = None
     if not args.no_tune:
@@ -126,11 +205,15 @@ def main():
         tune = call.autotune(x, b, gamma, beta, stream)
         print(f"[bench] plan tuned: {tune}", file=sys.stderr, flush=True)
     info = call.plan_info()
-    flops = 2.0 * info["valid_macs"]
+    # the eval path runs no convolution; its throughput is quoted against the
+    # multiply-adds of the convolution it replaces (same output)
+    conv_macs = C.convt3d_get_plan_info(g, C.make_epilogue(W.EPI_NONE))["valid_macs"] if evalmode else \
+        info["valid_macs"]
+    flops = 2.0 * conv_macs
 
     def step():
         call.prepack(w, stream)
-        call(x, b, gamma, beta, stream)
+        call(x, b, gamma, beta, stream, running_mean=rmean, running_var=rvar)
 
     for _ in range(args.warmup):
         step()
@@ -149,29 +232,50 @@ def main():
     gflops = flops / (ms * 1e-3) / 1e9
     print(f"[bench] timed region done: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    conv_ms = prof["conv_ms"] / max(1, prof["calls"])
-    conv_tflops = flops / (conv_ms * 1e-3) / 1e12
-    traffic = stored_traffic(wl.name)
-    roofline = {
-        "kernel": "convt3d_mfma_kernel",
-        "bound": "mfma",
-        "achieved": round(conv_tflops, 3),
-        "peak": PEAK_FP32_MFMA_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(conv_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
-        "traffic": traffic,
-        "algorithmic_flop_per_launch": flops,
-        "avg_launch_ms": round(conv_ms, 4),
-    }
-    kernels = {
-        "conv_ms": round(conv_ms, 4),
-        "finalize_ms": round(prof["finalize_ms"] / max(1, prof["calls"]), 4),
-        "normalize_ms": round(prof["normalize_ms"] / max(1, prof["calls"]), 4),
-    }
+    calls = max(1, prof["calls"])
+    conv_ms = prof["conv_ms"] / calls
+    if evalmode:
+        # dominant kernel: the bin sums of x, HBM bound (reads x once, writes
+        # the per-chunk bin sums)
+        red_ms = prof["reduce_ms"] / calls
+        eg_bins = info["eval_bins"]
+        alg_bytes = 4.0 * (x.numel() + call.ws_bytes / 4)
+        gbps = alg_bytes / (red_ms * 1e-3) / 1e9
+        traffic = stored_traffic(wl.name, kernel="eval_binsum_kernel")
+        roofline = {
+            "kernel": "eval_binsum_kernel",
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_ms": round(red_ms, 4),
+            "bins_per_plane": eg_bins,
+        }
+    else:
+        conv_tflops = flops / (conv_ms * 1e-3) / 1e12
+        traffic = stored_traffic(wl.name)
+        roofline = {
+            "kernel": "convt3d_mfma_kernel",
+            "bound": "mfma",
+            "achieved": round(conv_tflops, 3),
+            "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(conv_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flop_per_launch": flops,
+            "avg_launch_ms": round(conv_ms, 4),
+        }
+    kernels = {k: round(prof[k] / calls, 4)
+               for k in ("conv_ms", "finalize_ms", "normalize_ms", "reduce_ms", "prepack_ms")}
     if prof["normalize_ms"] > 0:
         norm_bytes = 2.0 * 4 * call.out.numel()  # read + write of the output
         kernels["normalize_GBps"] = round(norm_bytes / (kernels["normalize_ms"] * 1e-3) / 1e9, 1)
         kernels["normalize_frac_hbm"] = round(kernels["normalize_GBps"] / PEAK_HBM_GBS, 4)
+
+    comparison = torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, ms) if args.compare_torch else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -198,13 +302,17 @@ def main():
         "config": {"workload": wl.name, "x": list(wl.x_shape), "cout": wl.cout, "k": wl.k, "stride": wl.stride,
                    "pad": wl.pad, "out_pad": wl.out_pad, "bias": wl.bias,
                    "epilogue": W.EPI_NAMES[wl.epi], "groups": wl.groups, "scale": wl.scale},
-        "pct_fp32_mfma_peak_whole_step": round(100 * gflops / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
+        "value_kind": ("conv-equivalent: 2 x the in-range multiply-adds of the ConvTranspose3d whose pooled, "
+                       "eval-mode-normalised output this path computes without running it") if evalmode else
+                      "algorithmic: 2 x in-range multiply-adds of the ConvTranspose3d run",
+        "pct_fp32_mfma_peak_whole_step": None if evalmode else round(100 * gflops / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
         "roofline": roofline,
         "kernels": kernels,
         "plan": {k: v for k, v in info.items()},
         "plan_string": C.plan_string(info),
         "tune": tune,
         "cpu_baseline": cpu,
+        "torch_comparison": comparison,
     }
     print(json.dumps(res), flush=True)
 

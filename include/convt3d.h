@@ -15,7 +15,14 @@
  *     softmax, then 1/(1+exp(-v)));
  *   - multiply by `scale`, training-mode BatchNorm3d with batch statistics
  *     over (N, D, H, W) and the biased variance, then AdaptiveAvgPool3d(1)
- *     (p77 page); only the pooled [n, cout] result is produced.
+ *     (p77 page); only the pooled [n, cout] result is produced.  The running
+ *     statistics move toward the batch ones by the momentum (p77 page, its
+ *     remark that training mode updates them), with the unbiased variance as
+ *     nn.BatchNorm3d keeps it;
+ *   - the same in evaluation mode (p77 page: the module in eval mode
+ *     normalises with its running mean and variance): the pooled result is
+ *     then an affine map of the spatial mean of y, which the p77 page reduces
+ *     to input sums times tap-summed weights; no convolution is run.
  *
  * Conventions for every entry point:
  *   - All tensors are caller-owned, contiguous, fp32, in DEVICE memory of the
@@ -53,7 +60,8 @@ enum convt3d_epi_kind {
     CONVT3D_EPI_NONE = 0,                    /* out = y                                   */
     CONVT3D_EPI_RELU_GROUPNORM = 1,          /* out = GroupNorm(ReLU(y))                  */
     CONVT3D_EPI_SOFTMAX_SIGMOID = 2,         /* out = sigmoid(softmax_channels(y))        */
-    CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL = 3   /* out[n,c] = mean_dhw BN_train(scale * y)   */
+    CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL = 3,  /* out[n,c] = mean_dhw BN_train(scale * y)   */
+    CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL = 4    /* out[n,c] = mean_dhw BN_eval(scale * y)    */
 };
 
 /* Epilogue description.
@@ -65,9 +73,19 @@ enum convt3d_epi_kind {
  *   beta      [cout] device, per-channel shift for GN/BN; NULL means 0.
  *   stats_out optional device output, NULL to skip:
  *               GroupNorm: [n, groups, 2] = (mean, 1/sqrt(var + eps)) of ReLU(y);
- *               BatchNorm: [cout, 2]      = (batch mean, biased batch variance)
- *                                           of scale*y;
- *               others: ignored. */
+ *               BatchNorm (training): [cout, 2] = (batch mean, biased batch
+ *                                                  variance) of scale*y;
+ *               others: ignored.
+ *   momentum      BatchNorm training: weight of the batch statistics in the
+ *                 running-statistics update (0.1 in nn.BatchNorm3d).
+ *   running_mean  [cout] device.  BatchNorm training: when running_mean and
+ *   running_var   running_var are both non-NULL they are updated in place,
+ *                   rm = (1 - momentum) * rm + momentum * mean,
+ *                   rv = (1 - momentum) * rv + momentum * var * M / (M - 1)
+ *                 with M = n * Do * Ho * Wo values per channel (M > 1
+ *                 required); both NULL: no update.  BatchNorm eval: read only;
+ *                 NULL means 0 (mean) / 1 (variance), a fresh module.
+ *                 Ignored by the other kinds. */
 typedef struct convt3d_epilogue {
     int32_t kind;
     int32_t groups;
@@ -76,6 +94,9 @@ typedef struct convt3d_epilogue {
     const float *gamma;
     const float *beta;
     float *stats_out;
+    float momentum;
+    float *running_mean;
+    float *running_var;
 } convt3d_epilogue;
 
 enum convt3d_status {
@@ -85,7 +106,7 @@ enum convt3d_status {
     CONVT3D_ERR_GROUPS = 3,        /* GroupNorm groups < 1 or cout % groups != 0      */
     CONVT3D_ERR_ALIGNMENT = 4,     /* a tensor pointer is not 16-byte aligned         */
     CONVT3D_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required         */
-    CONVT3D_ERR_UNSUPPORTED = 6,   /* epilogue kind unknown, or softmax with cout>128 */
+    CONVT3D_ERR_UNSUPPORTED = 6,   /* epilogue kind unknown or not valid for the call */
     CONVT3D_ERR_LAUNCH = 7,        /* HIP reported an error when launching            */
     CONVT3D_ERR_TOO_LARGE = 8,     /* a tensor exceeds 2^31 elements                  */
     CONVT3D_ERR_ALIAS = 9          /* out overlaps x                                  */
@@ -98,7 +119,7 @@ const char *convt3d_status_string(int status);
 int convt3d_output_dims(const convt3d_geom *geom, int32_t out_dhw[3]);
 
 /* Number of fp32 elements `out` must hold: n*cout*Do*Ho*Wo for NONE / GN /
- * softmax, n*cout for the pooled BatchNorm epilogue; -1 on invalid input. */
+ * softmax, n*cout for the pooled BatchNorm epilogues; -1 on invalid input. */
 int64_t convt3d_output_elems(const convt3d_geom *geom, const convt3d_epilogue *epi);
 
 /* Bytes of the pre-packed weight buffer for this geometry (0 on invalid input). */
@@ -111,6 +132,22 @@ size_t convt3d_packed_weight_bytes(const convt3d_geom *geom);
 int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_packed,
                             void *stream);
 
+/* The weight form of the evaluation-mode BatchNorm + pool epilogue, which runs
+ * no convolution (p77 page, its reduction of the pooled output to input sums
+ * times weights summed over the kernel taps).  Along each dimension the input
+ * index range splits into at most 2k+1 bins, cut where some tap starts or
+ * stops reaching the output; for every (cin, cout) pair and bin triple the
+ * weights of the taps that reach the output from that whole bin are summed.
+ * With pad 0 there is one bin (the whole input) and this is the tap sum.
+ * Bytes of that buffer (0 on invalid input or k > 31): */
+size_t convt3d_eval_weight_bytes(const convt3d_geom *geom);
+
+/* Fill w_eval (device, convt3d_eval_weight_bytes bytes) from w [cin, cout, k,
+ * k, k] (device).  Enqueued on stream.  convt3d_fused with the kind
+ * CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL takes w_eval in place of w_packed. */
+int convt3d_prepack_eval_weights(const convt3d_geom *geom, const float *w, void *w_eval,
+                                 void *stream);
+
 /* Bytes of device workspace convt3d_fused needs for (geom, epi) (statistics
  * partials and per-channel scale/shift), for every plan convt3d_autotune may
  * choose.  May be 0 (then workspace may be NULL). */
@@ -118,11 +155,14 @@ size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *
 
 /* The fused forward pass.
  *   x          [n, cin, d, h, w] device input.
- *   w_packed   output of convt3d_prepack_weights for this geometry.
+ *   w_packed   output of convt3d_prepack_weights for this geometry (for
+ *              CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL: of convt3d_prepack_eval_weights).
  *   bias       [cout] device, or NULL for no bias.
  *   out        device output, convt3d_output_elems(geom, epi) floats; must not
  *              overlap x.  For GroupNorm it is also used as the staging buffer
- *              of ReLU(y) before normalisation in place.
+ *              of ReLU(y) before normalisation in place; for softmax with
+ *              cout > 128 (more channels than one workgroup's tile holds) it
+ *              stages y, which a second pass turns into the result in place.
  *   workspace  device scratch of at least convt3d_workspace_size bytes.
  * Enqueues 1 to 3 kernels on stream and returns without waiting. */
 int convt3d_fused(const float *x, const void *w_packed, const float *bias,
@@ -137,7 +177,8 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias,
  * computes the same result up to float summation order.  Unlike
  * convt3d_fused it waits on the device (it times the candidates with HIP
  * events on `stream`).  Candidates needing more workspace than
- * workspace_bytes are skipped.  result may be NULL.  The best 12 candidates
+ * workspace_bytes are skipped.  BatchNorm running statistics are left
+ * untouched (the timed calls do not update them).  result may be NULL.  The best 12 candidates
  * are timed (environment CONVT3D_TUNE_CANDIDATES=1..64 changes that;
  * CONVT3D_TUNE_LOG prints one line per candidate to stderr). */
 typedef struct convt3d_tune_result {
@@ -151,6 +192,22 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias,
                      const convt3d_geom *geom, const convt3d_epilogue *epi, float *out,
                      void *workspace, size_t workspace_bytes, void *stream,
                      convt3d_tune_result *result);
+
+/* The epilogue alone, on a conv output the caller already holds (for
+ * instance from another convolution implementation): y is [n, c, spatial]
+ * (NCDHW with the three spatial dims flattened, spatial = Do*Ho*Wo), device,
+ * fp32.  Kinds: CONVT3D_EPI_RELU_GROUPNORM and CONVT3D_EPI_SOFTMAX_SIGMOID
+ * write out [n, c, spatial] (out == y is allowed: in place; a partial overlap
+ * is not); the two BatchNorm kinds write out [n, c] (must not overlap y), and
+ * the training one updates the running statistics as convt3d_fused does (the
+ * count M is n * spatial).  CONVT3D_EPI_NONE is rejected
+ * (CONVT3D_ERR_UNSUPPORTED).  Same numerics as the fused epilogues; y is read
+ * twice for GroupNorm and softmax (statistics, then the output pass) and once
+ * for BatchNorm.  Enqueued on stream, no waiting. */
+size_t convt3d_epilogue_workspace_size(int32_t n, int32_t c, int64_t spatial, const convt3d_epilogue *epi);
+int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
+                          const convt3d_epilogue *epi, float *out, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* Planner's choices for (geom, epi), for reporting and tests. */
 typedef struct convt3d_plan_info {
@@ -167,6 +224,8 @@ typedef struct convt3d_plan_info {
     int32_t tuned;             /* 1: chosen by convt3d_autotune                         */
     int32_t border_split;      /* dims split into border / interior tile regions (bit 0 d, 1 h, 2 w) */
     int32_t xcd_order;         /* 0: phase / channel-tile index fastest per XCD, 1: tile fastest */
+    int32_t softmax_pass;      /* 1: softmax runs as a second pass (cout > 128)         */
+    int32_t eval_bins;         /* BN eval: input bins per (n, cin) plane, else 0        */
 } convt3d_plan_info;
 
 int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
@@ -174,15 +233,18 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
 
 /* Kernel timing for measurement.  Between convt3d_profile_begin() and
  * convt3d_profile_end(), every convt3d_fused call records HIP events on its
- * stream around each kernel it launches.  convt3d_profile_end() waits for the
+ * stream around each kernel it launches (convt3d_epilogue_only and the
+ * pre-pack calls too).  convt3d_profile_end() waits for the
  * recorded events (it synchronises on them, so call it after the timed
  * region), fills `out` with the summed per-kernel durations and stops
  * recording.  Not thread-safe with respect to concurrent recording sessions. */
 typedef struct convt3d_profile {
-    int32_t calls;        /* convt3d_fused calls recorded                       */
-    double conv_ms;       /* convolution (+ fused epilogue) kernel, summed      */
-    double finalize_ms;   /* GroupNorm / BatchNorm statistics kernels, summed   */
-    double normalize_ms;  /* GroupNorm in-place normalisation kernels, summed   */
+    int32_t calls;        /* convt3d_fused / convt3d_epilogue_only calls recorded */
+    double conv_ms;       /* convolution (+ fused epilogue) kernel, summed        */
+    double finalize_ms;   /* GroupNorm / BatchNorm statistics kernels, summed     */
+    double normalize_ms;  /* output passes: GroupNorm normalisation, softmax      */
+    double reduce_ms;     /* full-tensor sums: statistics of y, eval input bins   */
+    double prepack_ms;    /* convt3d_prepack_weights / _eval_weights kernels      */
 } convt3d_profile;
 
 int convt3d_profile_begin(void);

@@ -1,0 +1,193 @@
+"""GPU parity of the epilogue paths beyond the fused conv kernels:
+BatchNorm running statistics, evaluation-mode BatchNorm + pool (no conv),
+the standalone epilogue entry point on a conv output in memory, and softmax
+over more channels than one workgroup holds.  Every case goes through the C
+ABI and is compared with the fp64 oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+from activation_epilogues_amd import convt3d as C
+from activation_epilogues_amd import workloads as W
+
+from gpu_helpers import TOL, geom_of, max_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def fused(wl, inp, with_running=True):
+    """prepack + convt3d_fused; returns (out, stats, rmean, rvar) as numpy."""
+    import torch
+    call = C.FusedCall(geom_of(wl), wl.epi, wl.groups, wl.eps, wl.scale, want_stats=True, momentum=wl.momentum)
+    call.prepack(to_dev(inp.w))
+    call.out.fill_(float("nan"))
+    rm = to_dev(inp.rmean) if with_running else None
+    rv = to_dev(inp.rvar) if with_running else None
+    out = call(to_dev(inp.x), to_dev(inp.b), to_dev(inp.gamma), to_dev(inp.beta), running_mean=rm, running_var=rv)
+    torch.cuda.synchronize()
+    host = lambda t: None if t is None else t.cpu().numpy()
+    return host(out), host(call.stats), host(rm), host(rv), call
+
+
+# ---------------------------------------------------------------- BatchNorm running statistics
+
+@pytest.mark.parametrize("geo", [(3, 12, 20, 5, 6, 7, 3, 1, 0, 0), (2, 9, 40, 4, 5, 6, 4, 2, 1, 1),
+                                 (4, 16, 33, 3, 4, 5, 5, 3, 2, 2)])
+def test_bn_training_updates_running_statistics(geo):
+    n, cin, cout, d, h, w, k, s, p, op = geo
+    wl = W.Workload("bnrun", n, cin, cout, d, h, w, k=k, stride=s, pad=p, out_pad=op, bias=True,
+                    epi=W.EPI_SCALE_BN_TRAIN_AVGPOOL, scale=-1.5, momentum=0.3, seed=4100 + k)
+    say(f"[case] bn running stats {geo}")
+    inp = W.make_inputs(wl)
+    out, st, rm, rv, _ = fused(wl, inp)
+    ref = oracle.run_workload(wl, inp)
+    assert max_err(out, ref.out.reshape(out.shape)) <= TOL
+    np.testing.assert_allclose(st, ref.stats, rtol=1e-5, atol=1e-6)
+    assert max_err(rm, ref.running[0]) <= TOL and max_err(rv, ref.running[1]) <= TOL
+    # without buffers nothing else changes
+    out2, _, _, _, _ = fused(wl, inp, with_running=False)
+    assert max_err(out2, out) <= 1e-6
+
+
+def test_autotune_leaves_running_statistics_alone():
+    import torch
+    wl = W.Workload("bntune", 2, 8, 24, 5, 5, 5, k=3, epi=W.EPI_SCALE_BN_TRAIN_AVGPOOL, scale=2.0, seed=4200)
+    inp = W.make_inputs(wl)
+    call = C.FusedCall(geom_of(wl), wl.epi, scale=wl.scale, want_stats=True)
+    call.prepack(to_dev(inp.w))
+    rm, rv = to_dev(inp.rmean), to_dev(inp.rvar)
+    epi = call.epilogue(to_dev(inp.gamma), to_dev(inp.beta), rm, rv)
+    C.convt3d_autotune(to_dev(inp.x), call.w_packed, to_dev(inp.b), call.geom, epi, call.out, call.workspace,
+                       call.ws_bytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(rm.cpu().numpy(), inp.rmean) and np.array_equal(rv.cpu().numpy(), inp.rvar)
+
+
+# ---------------------------------------------------------------- eval-mode BatchNorm + pool
+
+def eval_sweep(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        wl = W.random_geometry(rng, max_in=9, max_ch=24, epi=W.EPI_SCALE_BN_EVAL_AVGPOOL)
+        if min(oracle.out_dims(wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)) <= 0:
+            continue
+        out.append(wl.with_(name=f"eval{len(out)}"))
+    return out
+
+
+@pytest.mark.parametrize("wl", eval_sweep(16, 77) + [
+    W.Workload("eval_s4", 2, 13, 40, 5, 6, 7, k=6, stride=4, pad=1, out_pad=0, epi=W.EPI_SCALE_BN_EVAL_AVGPOOL,
+               scale=2.0, seed=4301),
+    W.Workload("eval_wide", 2, 5, 7, 3, 4, 300, k=3, stride=2, pad=1, out_pad=1,
+               epi=W.EPI_SCALE_BN_EVAL_AVGPOOL, scale=0.5, seed=4302),
+    W.Workload("eval_p77_small", 3, 64, 128, 4, 8, 8, k=5, epi=W.EPI_SCALE_BN_EVAL_AVGPOOL, scale=2.0, seed=4303),
+], ids=lambda w: w.name)
+def test_bn_eval_pool_matches_oracle(wl):
+    say(f"[case] eval {wl.name} n={wl.n} cin={wl.cin} cout={wl.cout} in={wl.d}x{wl.h}x{wl.w} "
+        f"k={wl.k} s={wl.stride} p={wl.pad} op={wl.out_pad}")
+    inp = W.make_inputs(wl)
+    out, _, _, _, call = fused(wl, inp)
+    ref = oracle.run_workload(wl, inp)
+    err = max_err(out, ref.out.reshape(out.shape))
+    assert err <= TOL, f"max|err| {err:.3e}"
+    # running statistics are inputs here: NULL means a fresh module (0, 1)
+    fresh = oracle.run_workload(wl, W.Inputs(inp.x, inp.w, inp.b, inp.gamma, inp.beta))
+    out0, _, _, _, _ = fused(wl, inp, with_running=False)
+    assert max_err(out0, fresh.out.reshape(out0.shape)) <= TOL
+
+
+def test_bn_eval_pool_full_size_sampled():
+    """The p77 shape at full size (16 x 64 x 16x32x32, k5) in eval mode; eval
+    mode has no batch statistics, so the first two samples are checked against
+    the oracle on those samples alone."""
+    wl = W.BY_NAME["k5s1_bnpool_eval"]
+    say(f"[case] eval full size {wl.name}")
+    inp = W.make_inputs(wl)
+    out, _, _, _, _ = fused(wl, inp)
+    sub = wl.with_(n=2)
+    ref = oracle.run_workload(sub, W.Inputs(inp.x[:2].copy(), inp.w, inp.b, inp.gamma, inp.beta, inp.rmean,
+                                            inp.rvar))
+    assert max_err(out[:2], ref.out.reshape(out[:2].shape)) <= TOL
+    assert np.isfinite(out).all()
+
+
+# ---------------------------------------------------------------- standalone epilogue
+
+def y_case(n, c, dims, seed):
+    rng = np.random.default_rng(seed)
+    y = (rng.standard_normal((n, c) + dims) * 0.6 + rng.standard_normal((1, c, 1, 1, 1)) * 0.3).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, c).astype(np.float32)
+    beta = rng.normal(0, 0.1, c).astype(np.float32)
+    rmean = rng.normal(0, 0.1, c).astype(np.float32)
+    rvar = rng.uniform(0.5, 1.5, c).astype(np.float32)
+    return y, gamma, beta, rmean, rvar
+
+
+EPI_ONLY_CASES = [
+    # (kind, n, c, dims, groups, in_place)
+    (W.EPI_RELU_GROUPNORM, 2, 16, (6, 10, 12), 4, False),
+    (W.EPI_RELU_GROUPNORM, 3, 12, (5, 7, 9), 3, True),          # odd spatial size: scalar path
+    (W.EPI_RELU_GROUPNORM, 1, 8, (40, 40, 40), 2, True),        # several chunks per row
+    (W.EPI_SOFTMAX_SIGMOID, 2, 64, (4, 8, 8), 1, False),
+    (W.EPI_SOFTMAX_SIGMOID, 2, 301, (3, 5, 7), 1, True),        # many channels, odd size
+    (W.EPI_SOFTMAX_SIGMOID, 1, 3, (4, 4, 4), 1, False),         # fewer than four channels
+    (W.EPI_SCALE_BN_TRAIN_AVGPOOL, 4, 10, (5, 6, 7), 1, False),
+    (W.EPI_SCALE_BN_TRAIN_AVGPOOL, 2, 6, (36, 36, 36), 1, False),
+    (W.EPI_SCALE_BN_EVAL_AVGPOOL, 3, 9, (4, 6, 8), 1, False),
+]
+
+
+@pytest.mark.parametrize("case", EPI_ONLY_CASES, ids=lambda c: f"k{c[0]}_c{c[2]}_{'x'.join(map(str, c[3]))}")
+def test_epilogue_only_matches_oracle(case):
+    import torch
+    kind, n, c, dims, groups, in_place = case
+    say(f"[case] epilogue_only kind {kind} n {n} c {c} dims {dims} in_place {in_place}")
+    y, gamma, beta, rmean, rvar = y_case(n, c, dims, 500 + kind + c)
+    S = int(np.prod(dims))
+    scale, eps, mom = -0.75, 1e-5, 0.2
+    dy = to_dev(y)
+    pooled = kind in (W.EPI_SCALE_BN_TRAIN_AVGPOOL, W.EPI_SCALE_BN_EVAL_AVGPOOL)
+    out = dy if in_place else torch.full((n, c) if pooled else y.shape, float("nan"), device="cuda:0")
+    stats = torch.empty((n, groups, 2) if kind == W.EPI_RELU_GROUPNORM else (c, 2), device="cuda:0")
+    rm, rv = to_dev(rmean), to_dev(rvar)
+    g_, b_ = to_dev(gamma), to_dev(beta)
+    epi = C.make_epilogue(kind, groups, eps, scale, g_, b_, stats, mom, rm, rv)
+    ws_bytes = C.convt3d_epilogue_workspace_size(n, c, S, epi)
+    ws = torch.empty(max(1, ws_bytes // 4), device="cuda:0")
+    C.convt3d_epilogue_only(dy, n, c, S, epi, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    y64 = y.astype(np.float64)
+    if kind == W.EPI_RELU_GROUPNORM:
+        want, st = oracle.relu_groupnorm(y64, groups, eps, gamma, beta)
+        np.testing.assert_allclose(stats.cpu().numpy(), st, rtol=1e-5, atol=1e-6)
+    elif kind == W.EPI_SOFTMAX_SIGMOID:
+        want, _ = oracle.softmax_sigmoid(y64)
+    elif kind == W.EPI_SCALE_BN_TRAIN_AVGPOOL:
+        want, st = oracle.scale_bn_avgpool(y64, scale, eps, gamma, beta)
+        np.testing.assert_allclose(stats.cpu().numpy(), st, rtol=1e-5, atol=1e-6)
+        rm_want, rv_want = oracle.bn_running_update(st, n * S, mom, rmean, rvar)
+        assert max_err(rm.cpu().numpy(), rm_want) <= TOL and max_err(rv.cpu().numpy(), rv_want) <= TOL
+    else:
+        want = oracle.scale_bn_eval_avgpool(y64, scale, eps, gamma, beta, rmean, rvar)
+    err = max_err(got, want.reshape(got.shape))
+    assert err <= TOL, f"max|err| {err:.3e}"
+
+
+# ---------------------------------------------------------------- softmax over > 128 channels
+
+@pytest.mark.parametrize("geo", [(2, 8, 160, 4, 5, 6, 3, 1, 0, 0), (2, 12, 300, 3, 4, 5, 3, 2, 1, 1),
+                                 (1, 20, 129, 5, 5, 5, 4, 2, 1, 0)])
+def test_fused_softmax_beyond_one_workgroup(geo):
+    n, cin, cout, d, h, w, k, s, p, op = geo
+    wl = W.Workload("smbig", n, cin, cout, d, h, w, k=k, stride=s, pad=p, out_pad=op, bias=True,
+                    epi=W.EPI_SOFTMAX_SIGMOID, seed=4400 + cout)
+    say(f"[case] softmax second pass {geo}")
+    info = C.convt3d_get_plan_info(geom_of(wl), C.make_epilogue(wl.epi))
+    assert info["softmax_pass"] == 1
+    inp = W.make_inputs(wl)
+    out, _, _, _, _ = fused(wl, inp, with_running=False)
+    ref = oracle.run_workload(wl, inp)
+    err = max_err(out, ref.out.reshape(out.shape))
+    assert err <= TOL, f"max|err| {err:.3e}"

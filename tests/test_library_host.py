@@ -56,7 +56,7 @@ def test_output_dims_match_oracle():
 
 def test_status_strings():
     for st in range(10):
-        assert C.status_string(st)
+        assert C.status_string(st) != "unknown status"
     assert C.status_string(123) == "unknown status"
 
 
@@ -126,9 +126,59 @@ def test_groups_and_epilogue_checks():
         assert st == 3
     st = C.convt3d_fused(FAKE, FAKE, None, g, C.make_epilogue(7), FAKE * 64, None, 0, stream=0, check=False)
     assert st == 6
-    big = C.make_geom(1, 4, 129, 3, 3, 3, 3)
-    st = C.convt3d_fused(FAKE, FAKE, None, big, C.make_epilogue(2), FAKE * 64, None, 0, stream=0, check=False)
+    st = C.convt3d_fused(FAKE, FAKE, None, g, C.make_epilogue(5), FAKE * 64, None, 0, stream=0, check=False)
     assert st == 6
+
+
+def test_softmax_beyond_one_workgroup_runs_as_a_second_pass():
+    """cout > 128 does not fit the in-register softmax: the plan stores y and
+    finishes in a separate pass; cout <= 128 keeps the fused epilogue."""
+    for cout, want in ((128, 0), (129, 1), (300, 1)):
+        info = C.convt3d_get_plan_info(C.make_geom(2, 8, cout, 5, 6, 7, 3, 2, 1, 1), C.make_epilogue(2))
+        assert info["softmax_pass"] == want
+        if want:
+            assert info["waves_co"] * info["co_blocks_per_wave"] >= 1  # a plain conv plan
+
+
+def eval_bins_brute_force(wl):
+    """Bins per dim of the eval-mode path: the input range cut wherever some
+    tap starts or stops reaching the output (counted by brute force)."""
+    od = oracle.out_dims(wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)
+    nb = []
+    for n_in, n_out in zip((wl.d, wl.h, wl.w), od):
+        cuts = {0, n_in}
+        for t in range(wl.k):
+            reach = [i for i in range(n_in) if 0 <= wl.stride * i - wl.pad + t < n_out]
+            if reach:
+                cuts.update((min(reach), max(reach) + 1))
+        nb.append(len(cuts) - 1)
+    return nb[0] * nb[1] * nb[2]
+
+
+def test_eval_mode_bins_and_weight_size():
+    rng = np.random.default_rng(5)
+    seen = set()
+    for _ in range(60):
+        wl = W.random_geometry(rng, max_in=9)
+        if min(oracle.out_dims(wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)) <= 0:
+            continue
+        g = geom_of(wl)
+        nb = eval_bins_brute_force(wl)
+        info = C.convt3d_get_plan_info(g, C.make_epilogue(4))
+        assert info["eval_bins"] == nb
+        assert info["valid_macs"] == 0  # no convolution
+        assert C.convt3d_eval_weight_bytes(g) == wl.cin * wl.cout * nb * 4
+        assert C.convt3d_workspace_size(g, C.make_epilogue(4)) > 0
+        seen.add(nb)
+    assert 1 in seen and max(seen) > 8
+    # the p77 shape (pad 0): one bin, the plain tap sum
+    wl = W.BY_NAME["k5s1_bnpool_eval"]
+    assert C.convt3d_get_plan_info(geom_of(wl), C.make_epilogue(4))["eval_bins"] == 1
+    # kernels wider than 31 taps are not supported by the eval path
+    big = C.make_geom(1, 2, 2, 3, 3, 3, 32)
+    assert C.convt3d_eval_weight_bytes(big) == 0
+    with pytest.raises(C.Convt3dError):
+        C.convt3d_get_plan_info(big, C.make_epilogue(4))
 
 
 def test_pointer_checks():
@@ -151,9 +201,52 @@ def test_pointer_checks():
     assert C.convt3d_prepack_weights(g, FAKE, FAKE + 4, stream=0, check=False) == 4
 
 
+def test_running_statistics_checks():
+    """Both running buffers or none; the unbiased update needs more than one
+    value per channel."""
+    g = C.make_geom(1, 4, 8, 3, 3, 3, 3)
+    need = C.convt3d_workspace_size(g, C.make_epilogue(3))
+    e = C.make_epilogue(3, running_mean=FAKE * 256)
+    assert C.convt3d_fused(FAKE, FAKE, None, g, e, FAKE * 64, FAKE * 128, need, stream=0, check=False) == 1
+    one = C.make_geom(1, 4, 8, 1, 1, 1, 1)  # one output voxel, one sample
+    e = C.make_epilogue(3, running_mean=FAKE * 256, running_var=FAKE * 260)
+    need = C.convt3d_workspace_size(one, e)
+    assert C.convt3d_fused(FAKE, FAKE, None, one, e, FAKE * 64, FAKE * 128, need, stream=0, check=False) == 6
+
+
+def test_epilogue_only_argument_checks():
+    n, c, S = 2, 8, 60
+    y, out, ws = FAKE, FAKE * 64, FAKE * 128
+    gn = C.make_epilogue(1, 4)
+    need = C.convt3d_epilogue_workspace_size(n, c, S, gn)
+    assert need >= n * c * 2 * 4 * 2
+    assert C.convt3d_epilogue_workspace_size(n, c, S, C.make_epilogue(2)) == 0
+    only = lambda *a: C.convt3d_epilogue_only(*a, stream=0, check=False)
+    assert only(None, n, c, S, gn, out, ws, need) == 1
+    assert only(y, n, c, S, gn, None, ws, need) == 1
+    assert only(y, n, c, S, C.make_epilogue(0), out, ws, need) == 6
+    assert only(y, n, c, S, C.make_epilogue(9), out, ws, need) == 6
+    assert only(y, n, c, S, C.make_epilogue(1, 3), out, ws, need) == 3
+    assert only(y, -1, c, S, gn, out, ws, need) == 2
+    assert only(y, n, 0, S, gn, out, ws, need) == 2
+    assert only(y, n, c, 0, gn, out, ws, need) == 2
+    assert only(y + 4, n, c, S, gn, out, ws, need) == 4
+    assert only(y, n, c, S, gn, y + 16, ws, need) == 9          # partial overlap
+    assert only(y, n, c, S, C.make_epilogue(3), y, ws, need) == 9  # pooled output over y
+    assert only(y, n, c, S, gn, out, ws, need - 1) == 5
+    assert only(y, n, c, S, gn, out, None, need) == 5
+    bn = C.make_epilogue(3, running_var=FAKE * 512)
+    assert only(y, n, c, S, bn, out, ws, need) == 1
+    bn = C.make_epilogue(3, running_mean=FAKE * 256, running_var=FAKE * 512)
+    assert only(y, 1, c, 1, bn, out, ws, need) == 6
+    assert only(y, 1 << 20, 1 << 10, 1 << 10, gn, out, ws, need) == 8
+    # an empty batch launches nothing
+    assert only(y, 0, c, S, gn, out, ws, need) == 0
+
+
 def test_empty_batch_is_a_no_op():
     g = C.make_geom(0, 4, 8, 3, 3, 3, 3)
-    for kind in (0, 1, 2, 3):
+    for kind in (0, 1, 2, 3, 4):
         e = C.make_epilogue(kind, 2)
         # null pointers are fine: nothing is launched for an empty batch
         assert C.convt3d_fused(None, None, None, g, e, None, None, 0, stream=0, check=False) == 0
