@@ -15,7 +15,7 @@ plus a tiny GroupNorm case and a stride-2, k=4 GroupNorm case at 128 channels.
 
 Input recipe (every workload): numpy ``default_rng(seed)`` draws, in this
 order and as float64, x ~ N(0,1); w ~ U(-a, a) and b ~ U(-a, a) with
-a = 1/sqrt(cin*k^3); gamma ~ U(0.5, 1.5); beta ~ N(0, 0.1); then the
+a = 1/sqrt(cin*k^3) (1/sqrt((cin/groups)*kD*kH*kW) in general); gamma ~ U(0.5, 1.5); beta ~ N(0, 0.1); then the
 BatchNorm running statistics, running mean ~ N(0, 0.1) and running variance
 ~ U(0.5, 1.5) (the state of a module some steps into training; a fresh one
 holds 0 and 1).  All seven arrays are always drawn (so the streams do not
@@ -44,9 +44,17 @@ EPI_NAMES = {
 }
 
 
+def triple(v):
+    """(d, h, w) values of an int or a 3-sequence."""
+    return tuple(int(a) for a in v) if isinstance(v, (tuple, list)) else (int(v),) * 3
+
+
 @dataclass(frozen=True)
 class Workload:
-    """One transposed-convolution + epilogue problem (NCDHW, cubic kernel)."""
+    """One transposed-convolution + epilogue problem (NCDHW).  k, stride, pad,
+    out_pad and dilation are ints (cubic) or (d, h, w) triples; conv_groups
+    splits the channels as nn.ConvTranspose3d's `groups` does (groups is the
+    GroupNorm group count)."""
 
     name: str
     n: int
@@ -55,10 +63,10 @@ class Workload:
     d: int
     h: int
     w: int
-    k: int
-    stride: int = 1
-    pad: int = 0
-    out_pad: int = 0
+    k: object
+    stride: object = 1
+    pad: object = 0
+    out_pad: object = 0
     bias: bool = True
     epi: int = EPI_RELU_GROUPNORM
     groups: int = 1
@@ -66,10 +74,22 @@ class Workload:
     scale: float = 1.0
     momentum: float = 0.1
     seed: int = 0
+    dilation: object = 1
+    conv_groups: int = 1
     note: str = field(default="", compare=False)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
+
+    @property
+    def kdims(self):
+        return triple(self.k)
+
+    @property
+    def is_cubic(self) -> bool:
+        """Cubic kernel, one stride / pad / out_pad for every dim, no dilation, one group."""
+        return (all(len(set(triple(v))) == 1 for v in (self.k, self.stride, self.pad, self.out_pad))
+                and triple(self.dilation) == (1, 1, 1) and self.conv_groups == 1)
 
     @property
     def x_shape(self):
@@ -77,7 +97,7 @@ class Workload:
 
     @property
     def w_shape(self):
-        return (self.cin, self.cout, self.k, self.k, self.k)
+        return (self.cin, self.cout // self.conv_groups) + self.kdims
 
 
 # The five workloads.  Seeds are 20260 + (position in this list, from 1).
@@ -128,7 +148,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, x_dist: str = "normal"
     Returned bias/gamma/beta are None when the workload does not use them.
     """
     rng = np.random.default_rng(wl.seed if seed is None else seed)
-    a = 1.0 / np.sqrt(wl.cin * wl.k ** 3)
+    kd, kh, kw = wl.kdims
+    a = 1.0 / np.sqrt(wl.cin // wl.conv_groups * kd * kh * kw)  # 1/sqrt(fan-in of one output)
     if x_dist == "normal":
         x = rng.standard_normal(wl.x_shape)
     elif x_dist == "uniform":
@@ -177,3 +198,28 @@ def random_geometry(rng: np.random.Generator, max_in: int = 6, max_ch: int = 7,
                     bias=bool(rng.integers(0, 2)), epi=epi, groups=groups,
                     scale=float(rng.choice([1.0, 2.0, -0.5])),
                     seed=int(rng.integers(0, 2**31)))
+
+
+def random_general_geometry(rng: np.random.Generator, max_in: int = 6, max_ch: int = 6,
+                            epi: int = EPI_NONE) -> Workload:
+    """A small random geometry with per-dim kernel sizes 1..4, strides 1..3,
+    pads, output paddings (below max(stride, dilation)), dilations 1..3 and
+    1..3 channel groups.  Some draws have an empty output; the caller decides
+    (with its own size formula) whether to keep a draw."""
+    k = tuple(int(v) for v in rng.integers(1, 5, size=3))
+    s = tuple(int(v) for v in rng.integers(1, 4, size=3))
+    dl = tuple(int(v) for v in rng.integers(1, 4, size=3))
+    p = tuple(int(rng.integers(0, dl[i] * (k[i] - 1) + 1)) for i in range(3))
+    op = tuple(int(rng.integers(0, max(s[i], dl[i]))) for i in range(3))
+    d, h, w = (int(v) for v in rng.integers(1, max_in + 1, size=3))
+    G = int(rng.integers(1, 4))
+    cin = G * int(rng.integers(1, max_ch + 1))
+    cout = G * int(rng.integers(1, max_ch + 1))
+    groups = 1
+    if epi == EPI_RELU_GROUPNORM:
+        divs = [g for g in range(1, cout + 1) if cout % g == 0]
+        groups = int(rng.choice(divs))
+    n = int(rng.integers(1, 4))
+    return Workload("rgen", n, cin, cout, d, h, w, k=k, stride=s, pad=p, out_pad=op, bias=bool(rng.integers(0, 2)),
+                    epi=epi, groups=groups, scale=float(rng.choice([1.0, 2.0, -0.5])),
+                    seed=int(rng.integers(0, 2**31)), dilation=dl, conv_groups=G)

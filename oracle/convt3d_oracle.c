@@ -100,6 +100,73 @@ void oracle_convt3d(const float *x, const float *w, const float *b,
     }
 }
 
+/*
+ * The same scatter definition for the general nn.ConvTranspose3d geometry:
+ * per-dimension kernel size k[], stride s[], padding p[], output padding op[]
+ * and dilation dl[] (index 0 = D, 1 = H, 2 = W), and `groups` channel groups.
+ * Tap t along a dimension sits dl*t from the first one, so input i reaches
+ * output s*i - p + dl*t; the output length is (in - 1)*s - 2p + dl*(k - 1) +
+ * op + 1.  With groups G, output channel co belongs to group g = co / (Cout/G)
+ * and sums only over input channels g*(Cin/G) .. (g+1)*(Cin/G) - 1; the weight
+ * is [Cin, Cout/G, kD, kH, kW] (nn.ConvTranspose3d's layout).  The pages fix
+ * groups = 1 and dilation = 1 and a cubic kernel; this is the module's own
+ * definition for the other values.
+ */
+long oracle_out_dim_general(long in, long k, long s, long p, long op, long dl)
+{
+    return (in - 1) * s - 2 * p + dl * (k - 1) + op + 1;
+}
+
+void oracle_convt3d_general(const float *x, const float *w, const float *b,
+                            int N, int Cin, int Cout, int D, int H, int W,
+                            const int *k, const int *s, const int *p, const int *op,
+                            const int *dl, int groups, double *y)
+{
+    const long Do = oracle_out_dim_general(D, k[0], s[0], p[0], op[0], dl[0]);
+    const long Ho = oracle_out_dim_general(H, k[1], s[1], p[1], op[1], dl[1]);
+    const long Wo = oracle_out_dim_general(W, k[2], s[2], p[2], op[2], dl[2]);
+    if (Do <= 0 || Ho <= 0 || Wo <= 0 || groups < 1 || Cin % groups || Cout % groups) return;
+    const long S = Do * Ho * Wo;
+    const long Sin = (long)D * H * W;
+    const long kk = (long)k[0] * k[1] * k[2];
+    const int cig = Cin / groups, cog = Cout / groups;
+
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int n = 0; n < N; ++n) {
+        for (int co = 0; co < Cout; ++co) {
+            double *yc = y + ((size_t)n * Cout + co) * (size_t)S;
+            const double init = b ? (double)b[co] : 0.0;
+            for (long i = 0; i < S; ++i) yc[i] = init;
+            const int g = co / cog, col = co % cog;
+            for (int cl = 0; cl < cig; ++cl) {
+                const int ci = g * cig + cl;
+                const float *xc = x + ((size_t)n * Cin + ci) * (size_t)Sin;
+                const float *wc = w + ((size_t)ci * cog + col) * (size_t)kk;
+                for (int kd = 0; kd < k[0]; ++kd)
+                for (int kh = 0; kh < k[1]; ++kh)
+                for (int kw = 0; kw < k[2]; ++kw) {
+                    const double wv = (double)wc[((long)kd * k[1] + kh) * k[2] + kw];
+                    for (int id = 0; id < D; ++id) {
+                        const long od = (long)s[0] * id - p[0] + (long)dl[0] * kd;
+                        if (od < 0 || od >= Do) continue;
+                        for (int ih = 0; ih < H; ++ih) {
+                            const long oh = (long)s[1] * ih - p[1] + (long)dl[1] * kh;
+                            if (oh < 0 || oh >= Ho) continue;
+                            const float *xrow = xc + ((long)id * H + ih) * W;
+                            double *yrow = yc + (od * Ho + oh) * Wo;
+                            for (int iw = 0; iw < W; ++iw) {
+                                const long ow = (long)s[2] * iw - p[2] + (long)dl[2] * kw;
+                                if (ow < 0 || ow >= Wo) continue;
+                                yrow[ow] += (double)xrow[iw] * wv;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 /* Does tap kk of an output index o come from an input index?  Gather form of
  * the same relation (p49 page): o receives tap kk iff (o + p - kk) is a
  * non-negative multiple of s, from i = (o + p - kk) / s, if i < in. */

@@ -22,7 +22,8 @@ _LIB = os.path.join(_HERE, "liboracle_convt3d.so")
 _lib = None
 
 __all__ = [
-    "build", "out_dim", "out_dims", "convt3d", "convt3d_gather", "convt3d_point",
+    "build", "out_dim", "out_dims", "out_dim_general", "convt3d", "convt3d_general", "convt3d_gather",
+    "convt3d_point",
     "relu_groupnorm", "softmax_sigmoid", "scale_bn_avgpool", "bn_running_update",
     "scale_bn_eval_avgpool", "run_workload",
     "num_threads", "OracleResult",
@@ -55,6 +56,10 @@ def _load():
         lib.oracle_convt3d_gather.argtypes = conv_args
         lib.oracle_convt3d_point.restype = d
         lib.oracle_convt3d_point.argtypes = [vp, vp, vp] + [i] * 10 + [i, i, l, l, l]
+        lib.oracle_out_dim_general.restype = l
+        lib.oracle_out_dim_general.argtypes = [l, l, l, l, l, l]
+        lib.oracle_convt3d_general.restype = None
+        lib.oracle_convt3d_general.argtypes = [vp, vp, vp] + [i] * 6 + [vp] * 5 + [i, vp]
         lib.oracle_relu_groupnorm.restype = None
         lib.oracle_relu_groupnorm.argtypes = [vp, i, i, l, i, d, vp, vp, vp, vp]
         lib.oracle_softmax_sigmoid.restype = None
@@ -89,6 +94,34 @@ def out_dim(n_in: int, k: int, s: int, p: int, op: int) -> int:
 
 def out_dims(d, h, w, k, s, p, op):
     return tuple(out_dim(v, k, s, p, op) for v in (d, h, w))
+
+
+def _triple(v):
+    return tuple(int(a) for a in v) if isinstance(v, (tuple, list)) else (int(v),) * 3
+
+
+def out_dim_general(n_in: int, k: int, s: int, p: int, op: int, dl: int = 1) -> int:
+    return int(_load().oracle_out_dim_general(n_in, k, s, p, op, dl))
+
+
+def convt3d_general(x, w, b=None, stride=1, pad=0, out_pad=0, dilation=1, groups=1) -> np.ndarray:
+    """Scatter-form transposed convolution for the general geometry: stride,
+    pad, out_pad and dilation may be ints or (d, h, w) triples; w is
+    [Cin, Cout/groups, kD, kH, kW].  fp64 result [N, Cout, Do, Ho, Wo]."""
+    x, w, b = _f32(x), _f32(w), _f32(b)
+    N, Cin, D, H, W = x.shape
+    Cin2, Cog, kd, kh, kw = w.shape
+    assert Cin == Cin2 and Cin % groups == 0
+    Cout = Cog * groups
+    k, s, p, op, dl = (kd, kh, kw), _triple(stride), _triple(pad), _triple(out_pad), _triple(dilation)
+    od = tuple(out_dim_general(n, *a) for n, a in zip((D, H, W), zip(k, s, p, op, dl)))
+    if min(od) <= 0:
+        raise ValueError("empty transposed-convolution output")
+    y = np.empty((N, Cout) + od, dtype=np.float64)
+    arr = lambda t: (ctypes.c_int * 3)(*t)
+    _load().oracle_convt3d_general(_ptr(x), _ptr(w), _ptr(b), N, Cin, Cout, D, H, W, arr(k), arr(s), arr(p),
+                                   arr(op), arr(dl), groups, _ptr(y))
+    return y
 
 
 def _conv(fn, x, w, b, s, p, op):
@@ -199,7 +232,10 @@ def run_workload(wl, inp) -> OracleResult:
     2 softmax+sigmoid, 3 scale+BatchNorm(train)+avgpool, 4 scale+BatchNorm(eval,
     running statistics)+avgpool).  For code 3 with running statistics in the
     inputs, the result also carries them after the step's update."""
-    y = convt3d(inp.x, inp.w, inp.b, wl.stride, wl.pad, wl.out_pad)
+    if wl.is_cubic:
+        y = convt3d(inp.x, inp.w, inp.b, wl.stride, wl.pad, wl.out_pad)
+    else:
+        y = convt3d_general(inp.x, inp.w, inp.b, wl.stride, wl.pad, wl.out_pad, wl.dilation, wl.conv_groups)
     if wl.epi == 0:
         return OracleResult(y, y, None)
     if wl.epi == 1:

@@ -266,6 +266,83 @@ def test_unreached_outputs_keep_only_the_bias():
         assert np.all(y[0, co][~mask] == np.float64(b[co]))
 
 
+# ---------------------------------------------------------------- general geometry pins
+
+def general_geometries(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        wl = W.random_general_geometry(rng)
+        od = [oracle.out_dim_general(n, k, s, p, op, dl) for n, k, s, p, op, dl in
+              zip((wl.d, wl.h, wl.w), wl.kdims, W.triple(wl.stride), W.triple(wl.pad), W.triple(wl.out_pad),
+                  W.triple(wl.dilation))]
+        if min(od) <= 0:
+            continue
+        out.append(wl)
+    return out
+
+
+def gen_inputs(wl, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(wl.x_shape).astype(np.float32)
+    w = rng.uniform(-1, 1, wl.w_shape).astype(np.float32)
+    b = rng.uniform(-1, 1, wl.cout).astype(np.float32) if wl.bias else None
+    return x, w, b
+
+
+@pytest.mark.parametrize("wl", general_geometries(40, 31), ids=lambda wl: f"k{wl.kdims}s{wl.stride}dl{wl.dilation}g{wl.conv_groups}")
+def test_general_geometry_matches_torch(wl):
+    """Per-dim kernel / stride / pad / output padding, dilation and groups
+    against torch conv_transpose3d in fp64 (library routine for the same op);
+    the output shape follows (in-1)*s - 2p + dl*(k-1) + op + 1."""
+    x, w, b = gen_inputs(wl, 5)
+    y = oracle.convt3d_general(x, w, b, wl.stride, wl.pad, wl.out_pad, wl.dilation, wl.conv_groups)
+    ref = F.conv_transpose3d(t64(x), t64(w), None if b is None else t64(b), stride=W.triple(wl.stride),
+                             padding=W.triple(wl.pad), output_padding=W.triple(wl.out_pad),
+                             groups=wl.conv_groups, dilation=W.triple(wl.dilation)).numpy()
+    assert y.shape == ref.shape
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("k,s,p,op", [(3, 1, 0, 0), (3, 2, 1, 1), (4, 2, 1, 0), (5, 3, 2, 2)])
+def test_general_with_cubic_values_is_the_cubic_definition(k, s, p, op):
+    rng = np.random.default_rng(k * 10 + s)
+    x, w, b = rand_case(rng, 2, 3, 4, (4, 3, 5), k, s, p, op, True)
+    np.testing.assert_allclose(oracle.convt3d_general(x, w, b, s, p, op), oracle.convt3d(x, w, b, s, p, op),
+                               rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("k,s,dl", [((3, 2, 2), (1, 2, 1), (2, 1, 3)), ((2, 3, 1), (2, 1, 3), (3, 2, 1))])
+def test_dilation_is_a_zero_inserted_kernel(k, s, dl):
+    """Dilation dl spaces the taps dl apart: the same as an undilated kernel of
+    size dl*(k-1)+1 holding the weights at every dl-th tap and zeros between."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((2, 3, 4, 5, 3)).astype(np.float32)
+    w = rng.uniform(-1, 1, (3, 4) + k).astype(np.float32)
+    keff = tuple(d * (a - 1) + 1 for a, d in zip(k, dl))
+    wz = np.zeros((3, 4) + keff, np.float32)
+    wz[:, :, ::dl[0], ::dl[1], ::dl[2]] = w
+    p, op = (1, 0, 2), (0, 1, 0)
+    got = oracle.convt3d_general(x, w, None, s, p, op, dl)
+    want = oracle.convt3d_general(x, wz, None, s, p, op, 1)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_groups_are_independent_convolutions():
+    """groups G: channel group g of the output is the ungrouped transposed
+    convolution of input channel group g with its weight slice."""
+    rng = np.random.default_rng(42)
+    G, cig, cog = 3, 2, 4
+    x = rng.standard_normal((2, G * cig, 3, 4, 5)).astype(np.float32)
+    w = rng.uniform(-1, 1, (G * cig, cog, 3, 2, 3)).astype(np.float32)
+    b = rng.uniform(-1, 1, G * cog).astype(np.float32)
+    y = oracle.convt3d_general(x, w, b, (2, 1, 2), (1, 0, 1), (1, 0, 0), 1, G)
+    for g in range(G):
+        part = oracle.convt3d_general(x[:, g * cig:(g + 1) * cig], w[g * cig:(g + 1) * cig], b[g * cog:(g + 1) * cog],
+                                      (2, 1, 2), (1, 0, 1), (1, 0, 0))
+        np.testing.assert_allclose(y[:, g * cog:(g + 1) * cog], part, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- epilogue pins
 
 def test_relu_groupnorm_matches_torch_and_invariants():
