@@ -28,8 +28,9 @@ STATUS = {
 
 
 class Geom(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_int32) for f in
-                ("n", "cin", "cout", "d", "h", "w", "k", "stride", "pad", "out_pad")]
+    _fields_ = [(f, ctypes.c_int32) for f in ("n", "cin", "cout", "d", "h", "w")] + \
+               [(f, ctypes.c_int32 * 3) for f in ("k", "stride", "pad", "out_pad", "dilation")] + \
+               [("groups", ctypes.c_int32)]
 
 
 class Epilogue(ctypes.Structure):
@@ -141,8 +142,15 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def make_geom(n, cin, cout, d, h, w, k, stride=1, pad=0, out_pad=0) -> Geom:
-    return Geom(n, cin, cout, d, h, w, k, stride, pad, out_pad)
+def _triple(v):
+    t = tuple(int(a) for a in v) if isinstance(v, (tuple, list)) else (int(v),) * 3
+    return (ctypes.c_int32 * 3)(*t)
+
+
+def make_geom(n, cin, cout, d, h, w, k, stride=1, pad=0, out_pad=0, dilation=1, groups=1) -> Geom:
+    """k, stride, pad, out_pad and dilation: an int (every dim) or a (d, h, w) triple."""
+    return Geom(n, cin, cout, d, h, w, _triple(k), _triple(stride), _triple(pad), _triple(out_pad),
+                _triple(dilation), groups)
 
 
 def make_epilogue(kind, groups=1, eps=1e-5, scale=1.0, gamma=None, beta=None, stats_out=None,

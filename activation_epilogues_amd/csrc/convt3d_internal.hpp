@@ -24,11 +24,14 @@ constexpr int kEvalMaxBins = 2 * kEvalMaxK + 1;
 constexpr int kEvalTargetBlocks = 2048;  // eval-mode bin sums: workgroups to aim for
 
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
-// taps that reach it are k = r + s*j (j = 0..J-1) from input i = q + c - j.
+// taps that reach it are t = r + ts*j (j = 0..J-1) from input i = q + c - e*j,
+// where with dilation dl and g = gcd(dl, s): ts = s/g, e = dl/g, r is the
+// smallest tap with dl*r = rho + pad (mod s) and c = (rho + pad - dl*r) / s.
+// Without dilation: ts = s, e = 1, r = (rho + pad) mod s, c = (rho + pad) div s.
 struct DimPhase {
-    int r;   // first kernel tap of the phase: (rho + pad) mod s
-    int c;   // carry: (rho + pad) div s
-    int J;   // number of taps: ceil((k - r) / s), 0 if r >= k
+    int r;   // first kernel tap of the phase
+    int c;   // input offset of tap r (may be negative with dilation)
+    int J;   // number of taps (0: no tap reaches this phase)
     int nq;  // number of q with s*q + rho < Out
 };
 
@@ -39,8 +42,11 @@ struct ConvParams {
     const float *bias;    // may be null
     float *out;
     float *partials;      // [n][tiles_per_n][cout][2] or null
-    int N, Cin, Cout, D, H, W, Do, Ho, Wo;
-    int s;
+    int N, Cin, Cout, D, H, W, Do, Ho, Wo;  // Cin, Cout: of one channel group
+    int Cout_total;       // output channels of the whole conv (row stride of out and partials)
+    int x_nstride;        // floats per sample of x (all groups' channels)
+    int s3[3];            // stride per dim
+    int pe[3];            // input step per tap index j, per dim (dilation / gcd)
     int Qd, Qh, Qw;
     // Tiling regions.  rg[r] = {start d,h,w; end d,h,w; box d,h,w; tiles d,h,w}
     // in stride-phase coordinates q; workgroup x-index b belongs to region r when
@@ -74,7 +80,9 @@ struct ConvParams {
 // reaches the output from inputs [lo[t], hi1[t]) (lo >= hi1: from none), and
 // every such range is a union of whole bins.
 struct EvalGeom {
-    int N, Cin, Cout, D, H, W, k;
+    int N, Cin, Cout, D, H, W;
+    int cig, cog;                     // channels per group (input, output)
+    int k3[3];
     int nb[3];
     int nbins;                        // nb[0] * nb[1] * nb[2]
     int cut[3][kEvalMaxBins + 1];
@@ -88,14 +96,18 @@ struct Plan {
     convt3d_epilogue e{};
     int Do = 0, Ho = 0, Wo = 0;
     int64_t S = 0;            // output voxels per channel
-    int s = 1;
+    int s3[3] = {1, 1, 1};    // stride per dim
+    int ts[3] = {1, 1, 1};    // tap step per dim within a phase
+    int pe[3] = {1, 1, 1};    // input step per dim per tap index
+    int nph = 1;              // s3[0] * s3[1] * s3[2]
+    int G = 1, cig = 1, cog = 1;  // channel groups, input / output channels per group
     int Q[3] = {0, 0, 0};     // ceil(Out / s)
     DimPhase ph[3][kMaxStride]{};
     int ntaps[kMaxPhases]{};
     int64_t wp_off[kMaxPhases]{};
     int steps4[kMaxPhases]{};
-    int cb_total = 0, octets = 0;
-    int64_t packed_floats = 0;
+    int cb_total = 0, octets = 0;  // of one channel group
+    int64_t packed_floats = 0;       // one group's packed weights (floats)
     // kernel choice
     int variant = -1;
     int CBW = 1, NPH = 1, PBW = 1, WCO = 1, WPOS = 1;
@@ -130,7 +142,7 @@ struct Variant {
 extern const Variant kVariants[];
 extern const int kNumVariants;
 
-int64_t out_dim(int64_t in, int64_t k, int64_t s, int64_t p, int64_t op);
+int64_t out_dim(int64_t in, int64_t k, int64_t s, int64_t p, int64_t op, int64_t dl);
 int validate_geom(const convt3d_geom *g);
 int make_geometry(const convt3d_geom *g, Plan *pl);        // phases + packing only
 int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl);
@@ -139,6 +151,7 @@ void fill_conv_params(const Plan &pl, ConvParams *cp);
 int make_eval_geom(const convt3d_geom *g, EvalGeom *eg);  // CONVT3D_ERR_UNSUPPORTED for k > kEvalMaxK
 
 // Launchers (kernels.hip: pre-pack and convolution).  Return a hipError_t as int.
+// launch_prepack packs one channel group: w points at its [cig, cog, k...] slice.
 int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream);
 int launch_conv(const Plan &pl, const ConvParams &cp, void *stream);
 

@@ -334,26 +334,28 @@ __device__ __forceinline__ int bin_of(const EvalGeom &E, int b, int dim) {
     return b % E.nb[2];
 }
 
-// Wb[co][ci][bin]: one wave per (ci, co) weight row of k^3 taps.
+// Wb[co][ci_local][bin] (ci_local: input channel within co's group): one
+// wave per weight row [ci][co_local] of kD*kH*kW taps.
 __global__ __launch_bounds__(256) void eval_pack_kernel(const EvalGeom E, const float *w, float *wb) {
-    const int pair = blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // ci*Cout + co
+    const int pair = blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // ci*cog + co_local
     const int lane = threadIdx.x & 63;
-    if (pair >= E.Cin * E.Cout) return;
-    const int ci = pair / E.Cout, co = pair - ci * E.Cout;
-    const int k = E.k, k2 = k * k, k3 = k2 * k;
-    const float *row = w + (size_t)pair * k3;
+    if (pair >= E.Cin * E.cog) return;
+    const int ci = pair / E.cog, col = pair - ci * E.cog;
+    const int grp = ci / E.cig, cil = ci - grp * E.cig, co = grp * E.cog + col;
+    const int kh_ = E.k3[1], kw_ = E.k3[2], khw = kh_ * kw_, kk = E.k3[0] * khw;
+    const float *row = w + (size_t)pair * kk;
     for (int b = 0; b < E.nbins; ++b) {
         const int bd = bin_of(E, b, 0), bh = bin_of(E, b, 1), bw = bin_of(E, b, 2);
         double acc = 0.0;
-        for (int t = lane; t < k3; t += 64) {
-            const int td = t / k2, th = (t / k) % k, tw = t % k;
+        for (int t = lane; t < kk; t += 64) {
+            const int td = t / khw, th = (t / kw_) % kh_, tw = t % kw_;
             const bool in = E.lo[0][td] <= E.cut[0][bd] && E.cut[0][bd + 1] <= E.hi1[0][td] &&
                             E.lo[1][th] <= E.cut[1][bh] && E.cut[1][bh + 1] <= E.hi1[1][th] &&
                             E.lo[2][tw] <= E.cut[2][bw] && E.cut[2][bw + 1] <= E.hi1[2][tw];
             if (in) acc += (double)row[t];
         }
         for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (lane == 0) wb[((size_t)co * E.Cin + ci) * E.nbins + b] = (float)acc;
+        if (lane == 0) wb[((size_t)co * E.cig + cil) * E.nbins + b] = (float)acc;
     }
 }
 
@@ -459,10 +461,11 @@ __global__ __launch_bounds__(256) void eval_finalize_kernel(const EvalGeom E, co
     const int lane = threadIdx.x & 63;
     if (item >= E.N * E.Cout) return;
     const int n = item / E.Cout, co = item - n * E.Cout;
-    const int K = E.Cin * E.nbins;
+    const int K = E.cig * E.nbins;           // input channels of co's group x bins
+    const int ci0 = (co / E.cog) * E.cig;
     double acc = 0.0;
     for (int j = lane; j < K; j += 64) {
-        const int ci = j / E.nbins, b = j - ci * E.nbins;
+        const int ci = ci0 + j / E.nbins, b = j % E.nbins;
         const float *r = R + ((size_t)(n * E.Cin + ci) * E.nchunk) * E.nbins + b;
         double rs = 0.0;
         for (int c = 0; c < E.nchunk; ++c) rs += (double)r[(size_t)c * E.nbins];
@@ -574,7 +577,7 @@ int launch_bn_eval_rows(const float *partials, int N, int chunks, int C, double 
 }
 
 int launch_eval_pack(const EvalGeom &E, const float *w, float *wb, void *stream) {
-    const int64_t pairs = (int64_t)E.Cin * E.Cout;
+    const int64_t pairs = (int64_t)E.Cin * E.cog;
     hipLaunchKernelGGL(eval_pack_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, (hipStream_t)stream, E,
                        w, wb);
     return (int)hipGetLastError();

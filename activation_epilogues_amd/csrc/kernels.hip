@@ -27,20 +27,29 @@ namespace convt3d {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// floor / ceil of a / b for b > 0 and any sign of a (tap ranges with dilation;
+// b is wave-uniform and 1 without dilation)
+__device__ __forceinline__ int floor_div_any(int a, int b) {
+    if (b == 1) return a;
+    return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+__device__ __forceinline__ int ceil_div_any(int a, int b) { return -floor_div_any(-a, b); }
+
 __device__ __forceinline__ v16f mfma32x32x2(float a, float b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// Weight pre-pack.  Packed order per phase: [co_block][octet][tap][lane][4]
-// (as float4 groups [co_block][octet*ntaps + tap][lane]); element e of lane l
-// of group (octet, tap) is w[ci = 8*octet + 2*e + l/32][co = 32*co_block + l%32]
-// at kernel tap (r_d + s*j_d, r_h + s*j_h, r_w + s*j_w), zero outside
-// [0, Cin) x [0, Cout).
+// Weight pre-pack of one channel group.  Packed order per phase:
+// [co_block][octet][tap][lane][4] (as float4 groups [co_block][octet*ntaps +
+// tap][lane]); element e of lane l of group (octet, tap) is
+// w[ci = 8*octet + 2*e + l/32][co = 32*co_block + l%32] at kernel tap
+// (r_d + ts_d*j_d, r_h + ts_h*j_h, r_w + ts_w*j_w), zero outside [0, Cin) x [0, Cout).
 struct PackParams {
     const float *w;
     float *wp;
-    int Cin, Cout, k, s, cb_total, nph;
+    int Cin, Cout, cb_total, nph;
+    int k3[3], s3[3], ts[3];
     int pr[3][kMaxStride], pJ[3][kMaxStride];
     int ntaps[kMaxPhases], steps4[kMaxPhases], wp_off[kMaxPhases];
     int total4;
@@ -63,19 +72,18 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
         const int cb = t / steps4;
         const int ntp = P.ntaps[ph];
         const int octet = G / ntp, tap = G % ntp;
-        const int s = P.s;
-        const int rd = ph / (s * s), rh = (ph / s) % s, rw = ph % s;
+        const int sh = P.s3[1], sw = P.s3[2];
+        const int rd = ph / (sh * sw), rh = (ph / sw) % sh, rw = ph % sw;
         const int Jh = P.pJ[1][rh], Jw = P.pJ[2][rw];
         const int jw = tap % Jw, jh = (tap / Jw) % Jh, jd = tap / (Jw * Jh);
-        const int kd = P.pr[0][rd] + s * jd, kh = P.pr[1][rh] + s * jh, kw = P.pr[2][rw] + s * jw;
+        const int kd = P.pr[0][rd] + P.ts[0] * jd, kh = P.pr[1][rh] + P.ts[1] * jh, kw = P.pr[2][rw] + P.ts[2] * jw;
         const int co = cb * 32 + (lane & 31);
-        const int k = P.k;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int ci = octet * 8 + 2 * e + (lane >> 5);
             v[e] = (ci < P.Cin && co < P.Cout)
-                       ? P.w[((((size_t)ci * P.Cout + co) * k + kd) * k + kh) * k + kw]
+                       ? P.w[((((size_t)ci * P.Cout + co) * P.k3[0] + kd) * P.k3[1] + kh) * P.k3[2] + kw]
                        : 0.0f;
         }
         *reinterpret_cast<float4 *>(P.wp + f) = make_float4(v[0], v[1], v[2], v[3]);
@@ -145,7 +153,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
     by /= P.co_tiles;
     const int wgrp = by % P.nwgroups;
     by /= P.nwgroups;
-    const int s = P.s;
+    const int sd = P.s3[0], sh = P.s3[1], sw = P.s3[2];
+    const int ed = P.pe[0], eh = P.pe[1], ew = P.pe[2];  // input step per tap index
 
     const int TQd = RG[6], TQh = RG[7], TQw = RG[8];
     const int q0d = RG[0] + td_i * TQd, q0h = RG[1] + th_i * TQh, q0w = RG[2] + tw_i * TQw;
@@ -153,19 +162,19 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int TQd_e = min(TQd, RG[3] - q0d), TQh_e = min(TQh, RG[4] - q0h), TQw_e = min(TQw, RG[5] - q0w);
 
     // (rho_d, rho_h) phase groups of this workgroup: one (from the grid), or all
-    // s*s of them over one staged halo when the whole channel range fits in
+    // sd*sh of them over one staged halo when the whole channel range fits in
     // one LDS chunk.  The staged box is the union of the groups' footprints.
     constexpr bool ploop = PL;  // == (P.phase_loop != 0): the launcher picks the instantiation
-    const int npg = ploop ? s * s : 1;
+    const int npg = ploop ? sd * sh : 1;
     const int pg0 = ploop ? 0 : by;
     int lo_d_rel = 0, lo_h_rel = 0, HD = TQd, HH = TQh;
     {
         int dlo = INT_MAX, dhi = INT_MIN, hlo = INT_MAX, hhi = INT_MIN;
         for (int g = pg0; g < pg0 + npg; ++g) {
-            const int rd = g / s, rh = g % s;
+            const int rd = g / sh, rh = g % sh;
             const int Jd_ = P.pJ[0][rd], cd_ = P.pc[0][rd], Jh_ = P.pJ[1][rh], ch_ = P.pc[1][rh];
-            if (Jd_ > 0) { dlo = min(dlo, cd_ - Jd_ + 1); dhi = max(dhi, TQd - 1 + cd_); }
-            if (Jh_ > 0) { hlo = min(hlo, ch_ - Jh_ + 1); hhi = max(hhi, TQh - 1 + ch_); }
+            if (Jd_ > 0) { dlo = min(dlo, cd_ - ed * (Jd_ - 1)); dhi = max(dhi, TQd - 1 + cd_); }
+            if (Jh_ > 0) { hlo = min(hlo, ch_ - eh * (Jh_ - 1)); hhi = max(hhi, TQh - 1 + ch_); }
         }
         if (dlo <= dhi) { lo_d_rel = dlo; HD = dhi - dlo + 1; }
         if (hlo <= hhi) { lo_h_rel = hlo; HH = hhi - hlo + 1; }
@@ -178,7 +187,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
         Jw[p] = P.pJ[2][rw[p]];
         cw[p] = P.pc[2][rw[p]];
         if (Jw[p] > 0) {
-            lo_w_rel = min(lo_w_rel, cw[p] - Jw[p] + 1);
+            lo_w_rel = min(lo_w_rel, cw[p] - ew * (Jw[p] - 1));
             hi_w_rel = max(hi_w_rel, TQw - 1 + cw[p]);
         }
     }
@@ -192,8 +201,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
     int jw_lo[NPH], jw_hi[NPH];
 #pragma unroll
     for (int p = 0; p < NPH; ++p) {
-        jw_lo[p] = max(0, q0w + cw[p] - (P.W - 1));
-        jw_hi[p] = min(Jw[p] - 1, q0w + TQw_e - 1 + cw[p]);
+        jw_lo[p] = max(0, ceil_div_any(q0w + cw[p] - (P.W - 1), ew));
+        jw_hi[p] = min(Jw[p] - 1, floor_div_any(q0w + TQw_e - 1 + cw[p], ew));
     }
 
     // ---- LDS layout of a staged chunk: float4 [octet][k-row h][d][h][w].  The
@@ -231,7 +240,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const float4 *wp4 = reinterpret_cast<const float4 *>(P.wp);
     const int G4 = P.CI_T >> 3;
     const int DHWin = P.D * P.H * P.W;
-    const float *xn = P.x + (size_t)n * P.Cin * DHWin;
+    const float *xn = P.x + (size_t)n * P.x_nstride;
 
     // ---- halo staging.  Thread t takes halo positions t, t + 256, ...; for each
     // position inside the input it loads the 8 channels of every octet of the
@@ -289,13 +298,15 @@ void convt3d_mfma_kernel(const ConvParams P) {
 
   for (int pgi = 0; pgi < npg; ++pgi) {
     const int pg = pg0 + pgi;
-    const int rho_h = pg % s;
-    const int rho_d = pg / s;
+    const int rho_h = pg % sh;
+    const int rho_d = pg / sh;
     const int Jd = P.pJ[0][rho_d], cd = P.pc[0][rho_d];
     const int Jh = P.pJ[1][rho_h], ch = P.pc[1][rho_h];
     // ---- taps that touch the input for this box (border tiles skip the rest)
-    const int jd_lo = max(0, q0d + cd - (P.D - 1)), jd_hi = min(Jd - 1, q0d + TQd_e - 1 + cd);
-    const int jh_lo = max(0, q0h + ch - (P.H - 1)), jh_hi = min(Jh - 1, q0h + TQh_e - 1 + ch);
+    const int jd_lo = max(0, ceil_div_any(q0d + cd - (P.D - 1), ed));
+    const int jd_hi = min(Jd - 1, floor_div_any(q0d + TQd_e - 1 + cd, ed));
+    const int jh_lo = max(0, ceil_div_any(q0h + ch - (P.H - 1), eh));
+    const int jh_hi = min(Jh - 1, floor_div_any(q0h + TQh_e - 1 + ch, eh));
 
     v16f acc[NPH][CBW][PBW];
 #pragma unroll
@@ -326,7 +337,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
             for (int p = 0; p < NPH; ++p) {
                 if (!wave_live || Jw[p] == 0 || jw_lo[p] > jw_hi[p]) continue;
-                const int ph = (rho_d * s + rho_h) * s + rw[p];
+                const int ph = (rho_d * sh + rho_h) * sw + rw[p];
                 const int ntp = P.ntaps[ph];
                 const int jwl = jw_lo[p], jwh = jw_hi[p], jwn = Jw[p], cwp = cw[p];
                 const float4 *wb[CBW];
@@ -342,8 +353,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 int jd = jd_lo, jh = jh_lo, jw = jwl, g4 = 0;
                 auto next_group = [&](int &gi, int &bo) {
                     gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
-                    bo = ((cd - jd - lo_d_rel) * HH + (ch - jh - lo_h_rel)) * HW + (cwp - jw - lo_w_rel) +
-                         2 * g4 * SLAB;
+                    bo = ((cd - ed * jd - lo_d_rel) * HH + (ch - eh * jh - lo_h_rel)) * HW +
+                         (cwp - ew * jw - lo_w_rel) + 2 * g4 * SLAB;
                     if (++g4 == G4) {
                         g4 = 0;
                         if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } }
@@ -456,11 +467,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
     for (int pb = 0; pb < PBW; ++pb) {
         int td, th, tw;
         const bool pos_ok = decode_pos(pb, td, th, tw);
-        const int od = s * (q0d + td) + rho_d;
-        const int oh = s * (q0h + th) + rho_h;
+        const int od = sd * (q0d + td) + rho_d;
+        const int oh = sh * (q0h + th) + rho_h;
 #pragma unroll
         for (int p = 0; p < NPH; ++p) {
-            const int ow = s * (q0w + tw) + rw[p];
+            const int ow = sw * (q0w + tw) + rw[p];
             ok[p][pb] = pos_ok && od < Do && oh < Ho && ow < Wo;
             vofs[p][pb] = (unsigned)(4 * half * S + (od * Ho + oh) * Wo + ow) * 4u;
         }
@@ -480,7 +491,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
     int row0 = cb0 * 32;
     if constexpr (PL) asm volatile("" : "+s"(row0));
     const bool rows_full = row0 + CBW * 32 <= Cout;  // every accumulator row is a channel
-    char *outb = reinterpret_cast<char *>(P.out + (size_t)n * Cout * S);
+    char *outb = reinterpret_cast<char *>(P.out + (size_t)n * P.Cout_total * S);
     auto row_u = [&](int c, int r) { return row0 + c * 32 + 8 * (r >> 2) + (r & 3); };
     auto row_ok = [&](int c, int r) { return rows_full || row_u(c, r) + 4 * half < Cout; };
     auto rowp = [&](int c, int r) { return outb + (size_t)row_u(c, r) * S * 4; };
@@ -628,7 +639,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
             }
         if (gn || bn) {
             __syncthreads();
-            const int tile = ((rho_d * s + rho_h) * P.nwgroups + wgrp) * P.tiles_total + bx;
+            const int tile = ((rho_d * sh + rho_h) * P.nwgroups + wgrp) * P.tiles_total + bx;
             for (int row = tid; row < CO32; row += blockDim.x) {
                 const int co = co_tile * CO32 + row;
                 if (co >= Cout) continue;
@@ -637,7 +648,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     t1 += red[(w * CO32 + row) * 2 + 0];
                     t2 += red[(w * CO32 + row) * 2 + 1];
                 }
-                float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * Cout + co) * 2;
+                float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * P.Cout_total + co) * 2;
                 pp[0] = t1;
                 pp[1] = t2;
             }
@@ -660,12 +671,15 @@ int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream) {
     PackParams P{};
     P.w = w;
     P.wp = wp;
-    P.Cin = pl.g.cin;
-    P.Cout = pl.g.cout;
-    P.k = pl.g.k;
-    P.s = pl.s;
+    P.Cin = pl.cig;
+    P.Cout = pl.cog;
+    for (int d = 0; d < 3; ++d) {
+        P.k3[d] = pl.g.k[d];
+        P.s3[d] = pl.s3[d];
+        P.ts[d] = pl.ts[d];
+    }
     P.cb_total = pl.cb_total;
-    P.nph = pl.s * pl.s * pl.s;
+    P.nph = pl.nph;
     for (int d = 0; d < 3; ++d)
         for (int r = 0; r < kMaxStride; ++r) {
             P.pr[d][r] = pl.ph[d][r].r;

@@ -7,7 +7,11 @@
 // r = (rho + pad) mod s, from input i = q + c - j with c = (rho + pad) div s,
 // j = 0 .. J-1, J = ceil((k - r)/s).  Each phase (rho_d, rho_h, rho_w) is a
 // dense correlation over q with a J_d x J_h x J_w sub-kernel, so no tap that
-// can never be valid is ever multiplied.
+// can never be valid is ever multiplied.  With dilation dl the taps sit dl
+// apart: o receives tap t iff s divides (o + pad - dl*t); with g = gcd(dl, s)
+// the taps of a phase are t = r + (s/g)*j and their inputs q + c - (dl/g)*j.
+// Strides, kernel sizes, pads and dilations are per dimension; channel groups
+// are independent convolutions run one after another.
 #include <algorithm>
 #include <climits>
 #include <cmath>
@@ -40,27 +44,47 @@ const Variant kVariants[] = {
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int64_t out_dim(int64_t in, int64_t k, int64_t s, int64_t p, int64_t op) {
-    return (in - 1) * s - 2 * p + k + op;
+int64_t out_dim(int64_t in, int64_t k, int64_t s, int64_t p, int64_t op, int64_t dl) {
+    return (in - 1) * s - 2 * p + dl * (k - 1) + op + 1;
 }
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// floor / ceil of a / b for b > 0 and any sign of a
+static int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+static int64_t ceil_div_any(int64_t a, int64_t b) { return -floor_div(-a, b); }
+static int gcd_int(int a, int b) { while (b) { const int t = a % b; a = b; b = t; } return a; }
+
+// Tap index range [lo, hi] of a phase (input offset c, step e, J taps) that
+// reaches the input [0, in) from some q of [q0, q0 + te - 1]: inputs are
+// q + c - e*j.
+static void live_taps(int q0, int te, int c, int e, int J, int in, int *lo, int *hi) {
+    *lo = (int)std::max<int64_t>(0, ceil_div_any((int64_t)q0 + c - (in - 1), e));
+    *hi = (int)std::min<int64_t>(J - 1, floor_div((int64_t)q0 + te - 1 + c, e));
+}
 
 int validate_geom(const convt3d_geom *g) {
     if (!g) return CONVT3D_ERR_NULL;
-    if (g->n < 0 || g->cin < 1 || g->cout < 1 || g->d < 1 || g->h < 1 || g->w < 1 || g->k < 1 ||
-        g->stride < 1 || g->stride > kMaxStride || g->pad < 0 || g->out_pad < 0 ||
-        g->out_pad >= g->stride)
+    if (g->n < 0 || g->cin < 1 || g->cout < 1 || g->d < 1 || g->h < 1 || g->w < 1 || g->groups < 1 ||
+        g->cin % g->groups != 0 || g->cout % g->groups != 0)
         return CONVT3D_ERR_GEOMETRY;
-    const int64_t Do = out_dim(g->d, g->k, g->stride, g->pad, g->out_pad);
-    const int64_t Ho = out_dim(g->h, g->k, g->stride, g->pad, g->out_pad);
-    const int64_t Wo = out_dim(g->w, g->k, g->stride, g->pad, g->out_pad);
-    if (Do < 1 || Ho < 1 || Wo < 1) return CONVT3D_ERR_GEOMETRY;
+    const int ins[3] = {g->d, g->h, g->w};
     const int64_t lim = (int64_t)INT32_MAX;
-    const int64_t S = Do * Ho * Wo;
+    int64_t S = 1, K = 1;
+    for (int i = 0; i < 3; ++i) {
+        if (g->k[i] < 1 || g->stride[i] < 1 || g->stride[i] > kMaxStride || g->pad[i] < 0 || g->dilation[i] < 1 ||
+            g->out_pad[i] < 0 || g->out_pad[i] >= std::max(g->stride[i], g->dilation[i]))
+            return CONVT3D_ERR_GEOMETRY;
+        if (g->k[i] > 4096 || g->dilation[i] > 4096 || g->pad[i] > lim / 8 || g->out_pad[i] > 4096)
+            return CONVT3D_ERR_TOO_LARGE;
+        const int64_t o = out_dim(ins[i], g->k[i], g->stride[i], g->pad[i], g->out_pad[i], g->dilation[i]);
+        if (o < 1) return CONVT3D_ERR_GEOMETRY;
+        if (o > lim / 8) return CONVT3D_ERR_TOO_LARGE;
+        S *= o;
+        K *= g->k[i];
+        if (S > lim || K > lim) return CONVT3D_ERR_TOO_LARGE;
+    }
     if ((int64_t)g->n * g->cout * S > lim || (int64_t)g->n * g->cin * g->d * g->h * g->w > lim ||
-        (int64_t)g->cin * g->cout * g->k * g->k * g->k > lim / 4 || Do > lim / 8 || Ho > lim / 8 ||
-        Wo > lim / 8)
+        (int64_t)g->cin * (g->cout / g->groups) * K > lim / 4)
         return CONVT3D_ERR_TOO_LARGE;
     return CONVT3D_OK;
 }
@@ -69,32 +93,49 @@ int make_geometry(const convt3d_geom *g, Plan *pl) {
     int st = validate_geom(g);
     if (st) return st;
     pl->g = *g;
-    pl->s = g->stride;
-    pl->Do = (int)out_dim(g->d, g->k, g->stride, g->pad, g->out_pad);
-    pl->Ho = (int)out_dim(g->h, g->k, g->stride, g->pad, g->out_pad);
-    pl->Wo = (int)out_dim(g->w, g->k, g->stride, g->pad, g->out_pad);
-    pl->S = (int64_t)pl->Do * pl->Ho * pl->Wo;
-    const int s = pl->s;
-    const int outs[3] = {pl->Do, pl->Ho, pl->Wo};
+    const int ins[3] = {g->d, g->h, g->w};
+    int outs[3];
     for (int dim = 0; dim < 3; ++dim) {
+        outs[dim] = (int)out_dim(ins[dim], g->k[dim], g->stride[dim], g->pad[dim], g->out_pad[dim], g->dilation[dim]);
+        const int s = g->stride[dim], dl = g->dilation[dim], k = g->k[dim], p = g->pad[dim];
+        const int gc = gcd_int(dl, s);
+        pl->s3[dim] = s;
+        pl->ts[dim] = s / gc;
+        pl->pe[dim] = dl / gc;
         pl->Q[dim] = (int)ceil_div(outs[dim], s);
         for (int rho = 0; rho < kMaxStride; ++rho) {
             DimPhase &d = pl->ph[dim][rho];
-            if (rho >= s) { d = DimPhase{0, 0, 0, 0}; continue; }
-            d.r = (rho + g->pad) % s;
-            d.c = (rho + g->pad) / s;
-            d.J = d.r < g->k ? (int)ceil_div(g->k - d.r, s) : 0;
+            d = DimPhase{0, 0, 0, 0};
+            if (rho >= s) continue;
             d.nq = outs[dim] > rho ? (int)ceil_div(outs[dim] - rho, s) : 0;
+            // smallest tap r (< s/g) with dl*r = rho + p (mod s)
+            int r = -1;
+            for (int t = 0; t < pl->ts[dim] && r < 0; ++t)
+                if (((int64_t)dl * t - rho - p) % s == 0) r = t;
+            if (r < 0 || r >= k) continue;  // no tap reaches this phase
+            d.r = r;
+            d.c = (int)floor_div((int64_t)rho + p - (int64_t)dl * r, s);  // exact
+            d.J = (int)ceil_div(k - r, pl->ts[dim]);
         }
     }
-    pl->cb_total = (int)ceil_div(g->cout, 32);
-    pl->octets = (int)ceil_div(g->cin, kOctet);
-    // Packed weights: for each phase, for each 32-channel output block, the
-    // float4 groups ordered (input-channel octet, tap); one group holds, for
-    // each of the 64 lanes, the A operands of 4 consecutive MFMA k-steps.
+    pl->Do = outs[0];
+    pl->Ho = outs[1];
+    pl->Wo = outs[2];
+    pl->S = (int64_t)pl->Do * pl->Ho * pl->Wo;
+    pl->nph = pl->s3[0] * pl->s3[1] * pl->s3[2];
+    pl->G = g->groups;
+    pl->cig = g->cin / g->groups;
+    pl->cog = g->cout / g->groups;
+    pl->cb_total = (int)ceil_div(pl->cog, 32);
+    pl->octets = (int)ceil_div(pl->cig, kOctet);
+    // Packed weights of one group: for each phase, for each 32-channel output
+    // block, the float4 groups ordered (input-channel octet, tap); one group
+    // holds, for each of the 64 lanes, the A operands of 4 consecutive MFMA
+    // k-steps.  Groups follow one another.
     int64_t off = 0;
-    for (int ph = 0; ph < s * s * s; ++ph) {
-        const int rd = ph / (s * s), rh = (ph / s) % s, rw = ph % s;
+    const int sh = pl->s3[1], sw = pl->s3[2];
+    for (int ph = 0; ph < pl->nph; ++ph) {
+        const int rd = ph / (sh * sw), rh = (ph / sw) % sh, rw = ph % sw;
         const int nt = pl->ph[0][rd].J * pl->ph[1][rh].J * pl->ph[2][rw].J;
         pl->ntaps[ph] = nt;
         pl->steps4[ph] = pl->octets * nt;
@@ -102,15 +143,15 @@ int make_geometry(const convt3d_geom *g, Plan *pl) {
         off += (int64_t)pl->cb_total * pl->steps4[ph] * 64 * 4;
     }
     pl->packed_floats = off;
-    if (off > (int64_t)INT32_MAX) return CONVT3D_ERR_TOO_LARGE;
+    if (off * pl->G > (int64_t)INT32_MAX) return CONVT3D_ERR_TOO_LARGE;
     return CONVT3D_OK;
 }
 
-static int64_t valid_taps_dim(int out, int in, int k, int s, int p) {
+static int64_t valid_taps_dim(int out, int in, int k, int s, int p, int dl) {
     int64_t t = 0;
     for (int o = 0; o < out; ++o)
         for (int kk = 0; kk < k; ++kk) {
-            const int v = o + p - kk;
+            const int64_t v = (int64_t)o + p - (int64_t)dl * kk;
             if (v >= 0 && v % s == 0 && v / s < in) ++t;
         }
     return t;
@@ -138,32 +179,30 @@ static void ws_layout(Plan *pl) {
 }
 
 // Input bins of the evaluation-mode BatchNorm + pool path.  Along one dim,
-// tap t reaches output s*i - p + t in [0, out) from inputs i in
-// [ceil((p - t)/s), floor((out - 1 + p - t)/s)] clipped to [0, in); the cuts
-// are every such range's ends plus 0 and in, so each range is a union of
+// tap t reaches output s*i - p + dl*t in [0, out) from inputs i in
+// [ceil((p - dl*t)/s), floor((out - 1 + p - dl*t)/s)] clipped to [0, in); the
+// cuts are every such range's ends plus 0 and in, so each range is a union of
 // consecutive bins.
 int make_eval_geom(const convt3d_geom *g, EvalGeom *eg) {
     const int st = validate_geom(g);
     if (st) return st;
-    if (g->k > kEvalMaxK) return CONVT3D_ERR_UNSUPPORTED;
+    if (g->k[0] > kEvalMaxK || g->k[1] > kEvalMaxK || g->k[2] > kEvalMaxK) return CONVT3D_ERR_UNSUPPORTED;
     std::memset(eg, 0, sizeof(*eg));
     eg->N = g->n; eg->Cin = g->cin; eg->Cout = g->cout;
-    eg->D = g->d; eg->H = g->h; eg->W = g->w; eg->k = g->k;
-    const int s = g->stride, p = g->pad;
+    eg->cig = g->cin / g->groups; eg->cog = g->cout / g->groups;
+    eg->D = g->d; eg->H = g->h; eg->W = g->w;
     const int ins[3] = {g->d, g->h, g->w};
     int64_t S = 1;
     for (int dim = 0; dim < 3; ++dim) {
-        const int in = ins[dim];
-        const int out = (int)out_dim(in, g->k, s, p, g->out_pad);
+        const int in = ins[dim], k = g->k[dim], s = g->stride[dim], p = g->pad[dim], dl = g->dilation[dim];
+        eg->k3[dim] = k;
+        const int out = (int)out_dim(in, k, s, p, g->out_pad[dim], dl);
         S *= out;
         std::vector<int> cuts = {0, in};
-        for (int t = 0; t < g->k; ++t) {
-            // smallest i with s*i >= p - t, largest i with s*i <= out - 1 + p - t
-            const int64_t a = p - t, b = (int64_t)out - 1 + p - t;
-            int64_t lo = a <= 0 ? 0 : (a + s - 1) / s;
-            int64_t hi = b < 0 ? -1 : b / s;
-            lo = std::max<int64_t>(lo, 0);
-            hi = std::min<int64_t>(hi, in - 1);
+        for (int t = 0; t < k; ++t) {
+            const int64_t a = (int64_t)p - (int64_t)dl * t, b = (int64_t)out - 1 + p - (int64_t)dl * t;
+            const int64_t lo = std::max<int64_t>(ceil_div_any(a, s), 0);
+            const int64_t hi = std::min<int64_t>(floor_div(b, s), in - 1);
             if (lo > hi) {
                 eg->lo[dim][t] = 1;
                 eg->hi1[dim][t] = 0;  // reaches nothing
@@ -181,7 +220,7 @@ int make_eval_geom(const convt3d_geom *g, EvalGeom *eg) {
     }
     eg->nbins = eg->nb[0] * eg->nb[1] * eg->nb[2];
     eg->inv_S = 1.0 / (double)S;
-    if ((int64_t)g->cin * g->cout * eg->nbins > (int64_t)INT32_MAX / 4) return CONVT3D_ERR_TOO_LARGE;
+    if ((int64_t)eg->cig * g->cout * eg->nbins > (int64_t)INT32_MAX / 4) return CONVT3D_ERR_TOO_LARGE;
     // d-chunks: enough workgroups to cover the chip when n * cin is small
     const int64_t planes = std::max<int64_t>((int64_t)g->n * g->cin, 1);
     int64_t nchunk = (kEvalTargetBlocks + planes - 1) / planes;
@@ -222,16 +261,18 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         return CONVT3D_OK;
     }
     // the in-register softmax needs every channel in one workgroup (<= 4 blocks
-    // of 32); beyond that the conv stores y and a second pass finishes
-    const bool softmax = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID && pl->cb_total <= 4;
+    // of 32, one channel group); beyond that the conv stores y and a second
+    // pass finishes
+    const bool softmax = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID && pl->cb_total <= 4 && pl->G == 1;
     pl->softmax_pass = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID && !softmax;
 
-    const int s = pl->s;
+    const int sd = pl->s3[0], sh = pl->s3[1], sw = pl->s3[2];
     const int ins[3] = {g->d, g->h, g->w};
-    pl->valid_macs = (int64_t)g->n * g->cin * g->cout *
-                     valid_taps_dim(pl->Do, g->d, g->k, s, g->pad) *
-                     valid_taps_dim(pl->Ho, g->h, g->k, s, g->pad) *
-                     valid_taps_dim(pl->Wo, g->w, g->k, s, g->pad);
+    // every output channel sums over the cig input channels of its group
+    pl->valid_macs = (int64_t)g->n * pl->cig * g->cout *
+                     valid_taps_dim(pl->Do, g->d, g->k[0], sd, g->pad[0], g->dilation[0]) *
+                     valid_taps_dim(pl->Ho, g->h, g->k[1], sh, g->pad[1], g->dilation[1]) *
+                     valid_taps_dim(pl->Wo, g->w, g->k[2], sw, g->pad[2], g->dilation[2]);
 
     // ---- tiling regions.  Along each dim, positions q whose every phase has all
     // of its taps on the input form the interior [lo, hi); the borders around it
@@ -242,10 +283,10 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     int nseg_split[3];
     for (int dim = 0; dim < 3; ++dim) {
         int lo = 0, hi = pl->Q[dim];
-        for (int rho = 0; rho < s; ++rho) {
+        for (int rho = 0; rho < pl->s3[dim]; ++rho) {
             const DimPhase &d = pl->ph[dim][rho];
             if (d.J == 0) continue;
-            lo = std::max(lo, d.J - 1 - d.c);
+            lo = std::max(lo, pl->pe[dim] * (d.J - 1) - d.c);
             hi = std::min(hi, ins[dim] - d.c);
         }
         lo = std::min(std::max(lo, 0), pl->Q[dim]);
@@ -264,8 +305,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         int64_t t = 0;
         for (int q0 = sg.a; q0 < sg.b; q0 += tq) {
             const int te = std::min(tq, sg.b - q0);
-            const int lo = std::max(0, q0 + d.c - (ins[dim] - 1));
-            const int hi = std::min(d.J - 1, q0 + te - 1 + d.c);
+            int lo, hi;
+            live_taps(q0, te, d.c, pl->pe[dim], d.J, ins[dim], &lo, &hi);
             if (hi >= lo) t += hi - lo + 1;
         }
         return t;
@@ -279,8 +320,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         int64_t t = 0;
         for (int q0 = sg.a; q0 < sg.b; q0 += tq) {
             const int te = std::min(tq, sg.b - q0);
-            const int lo = std::max(0, q0 + d.c - (ins[0] - 1));
-            const int hi = std::min(d.J - 1, q0 + te - 1 + d.c);
+            int lo, hi;
+            live_taps(q0, te, d.c, pl->pe[0], d.J, ins[0], &lo, &hi);
             const int64_t cols = std::min<int64_t>(pt, ceil_div((int64_t)te * plane, wave_cols) * wave_cols);
             if (hi >= lo) t += (hi - lo + 1) * cols;
         }
@@ -312,7 +353,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     bool found = false, too_large = false;
     for (int vi = 0; vi < kNumVariants; ++vi) {
         const Variant v = kVariants[vi];
-        if (s % v.NPH != 0) continue;
+        if (sw % v.NPH != 0) continue;
         if (forced && vi != force[0]) continue;
         if (v.softmax != softmax) continue;
         if (softmax && v.CBW < pl->cb_total) continue;
@@ -324,11 +365,10 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
           for (int split = 0; split < 8; ++split) {
            // ploop: one workgroup loops over every (rho_d, rho_h) group on one staged
            // halo (needs the whole channel range in one LDS chunk)
-           for (int ploop = 0; ploop < (s > 1 ? 2 : 1); ++ploop) {
+           for (int ploop = 0; ploop < (sd * sh > 1 ? 2 : 1); ++ploop) {
             if (forced && force[6] >= 0 && split != force[6]) continue;
             if (ploop_only >= 0 && ploop != ploop_only) continue;
             if (ploop && !v.phase_loop) continue;
-            const int npg = ploop ? s * s : 1;
             Seg segs[3][3];
             int nseg[3];
             bool redundant = false;
@@ -344,18 +384,20 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
             if (CO_T > pl->cb_total && WCO > 1) continue;  // do not waste whole waves on padding
             const int co_tiles = (int)ceil_div(pl->cb_total, CO_T);
             const int PT = WPOS * v.PBW * 32;
-            const int nwg = s / v.NPH;
-            // halo width along w of a box for each w-phase group
-            auto halo_w = [&](int TQw, int wg) {
+            const int nwg = sw / v.NPH;
+            // halo length along a dim of a box for the phases [rho0, rho0 + nr):
+            // inputs q + c - e*j of every phase's taps
+            auto halo_len = [&](int dim, int TQ, int rho0, int nr) {
                 int lo = INT_MAX, hi = INT_MIN;
-                for (int p = 0; p < v.NPH; ++p) {
-                    const DimPhase &d = pl->ph[2][wg * v.NPH + p];
+                for (int rho = rho0; rho < rho0 + nr; ++rho) {
+                    const DimPhase &d = pl->ph[dim][rho];
                     if (d.J == 0) continue;
-                    lo = std::min(lo, d.c - d.J + 1);
-                    hi = std::max(hi, TQw - 1 + d.c);
+                    lo = std::min(lo, d.c - pl->pe[dim] * (d.J - 1));
+                    hi = std::max(hi, TQ - 1 + d.c);
                 }
                 return lo <= hi ? hi - lo + 1 : 0;
             };
+            auto halo_w = [&](int TQw, int wg) { return halo_len(2, TQw, wg * v.NPH, v.NPH); };
             // largest region (the one a forced box applies to)
             int big = 0, big_vol = -1, ri = 0;
             for (int i0 = 0; i0 < nseg[0]; ++i0)
@@ -373,8 +415,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
             for (int i0 = 0; i0 < nseg[0] && ok_all; ++i0)
                 for (int i1 = 0; i1 < nseg[1] && ok_all; ++i1)
                     for (int i2 = 0; i2 < nseg[2] && ok_all; ++i2) {
-                        const Seg sd = segs[0][i0], sh = segs[1][i1], sw = segs[2][i2];
-                        const int ext[3] = {sd.b - sd.a, sh.b - sh.a, sw.b - sw.a};
+                        const Seg sgd = segs[0][i0], sgh = segs[1][i1], sgw = segs[2][i2];
+                        const int ext[3] = {sgd.b - sgd.a, sgh.b - sgh.a, sgw.b - sgw.a};
                         RChoice bestr{};
                         bestr.cost = 1e300;
                         // rows of at least 16 positions keep LDS reads and stores contiguous
@@ -392,19 +434,15 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                                         continue;
                                     int HD = 1, HH = 1, HW = TQw;
                                     if (ploop) {  // union of the groups' footprints
-                                        int dlo = INT_MAX, dhi = INT_MIN, hlo = INT_MAX, hhi = INT_MIN;
-                                        for (int rho = 0; rho < s; ++rho) {
-                                            const DimPhase &a = pl->ph[0][rho], &b = pl->ph[1][rho];
-                                            if (a.J) { dlo = std::min(dlo, a.c - a.J + 1); dhi = std::max(dhi, TQd - 1 + a.c); }
-                                            if (b.J) { hlo = std::min(hlo, b.c - b.J + 1); hhi = std::max(hhi, TQh - 1 + b.c); }
-                                        }
-                                        HD = dlo <= dhi ? dhi - dlo + 1 : TQd;
-                                        HH = hlo <= hhi ? hhi - hlo + 1 : TQh;
+                                        HD = halo_len(0, TQd, 0, sd);
+                                        HH = halo_len(1, TQh, 0, sh);
+                                        if (HD == 0) HD = TQd;
+                                        if (HH == 0) HH = TQh;
                                     } else {
-                                        for (int rho = 0; rho < s; ++rho) {
-                                            HD = std::max(HD, TQd + std::max(pl->ph[0][rho].J, 1) - 1);
-                                            HH = std::max(HH, TQh + std::max(pl->ph[1][rho].J, 1) - 1);
-                                        }
+                                        for (int rho = 0; rho < sd; ++rho) HD = std::max(HD, halo_len(0, TQd, rho, 1));
+                                        for (int rho = 0; rho < sh; ++rho) HH = std::max(HH, halo_len(1, TQh, rho, 1));
+                                        HD = std::max(HD, TQd);
+                                        HH = std::max(HH, TQh);
                                     }
                                     for (int wg = 0; wg < nwg; ++wg) HW = std::max(HW, halo_w(TQw, wg));
                                     const int slab = HD * HH * HW;
@@ -413,17 +451,17 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                                                        (int)ceil_div(ext[2], TQw)};
                                     const int64_t tiles = (int64_t)nt[0] * nt[1] * nt[2];
                                     int64_t taps = 0, halo = 0;
-                                    for (int rd = 0; rd < s; ++rd) {
-                                        const int64_t ld = seg_live_cols(rd, sd, TQd, TQh * TQw, v.PBW * 32, PT);
-                                        for (int rh = 0; rh < s; ++rh) {
-                                            const int64_t lh = seg_live(1, rh, sh, TQh);
+                                    for (int rd = 0; rd < sd; ++rd) {
+                                        const int64_t ld = seg_live_cols(rd, sgd, TQd, TQh * TQw, v.PBW * 32, PT);
+                                        for (int rh = 0; rh < sh; ++rh) {
+                                            const int64_t lh = seg_live(1, rh, sgh, TQh);
                                             int64_t lw = 0;
-                                            for (int rw = 0; rw < s; ++rw) lw += seg_live(2, rw, sw, TQw);
+                                            for (int rw = 0; rw < sw; ++rw) lw += seg_live(2, rw, sgw, TQw);
                                             taps += ld * lh * lw;
                                             if (ploop || pl->ph[0][rd].J == 0 || pl->ph[1][rh].J == 0) continue;
                                             for (int wg = 0; wg < nwg; ++wg)
-                                                halo += (int64_t)(TQd + pl->ph[0][rd].J - 1) *
-                                                        (TQh + pl->ph[1][rh].J - 1) * halo_w(TQw, wg);
+                                                halo += (int64_t)halo_len(0, TQd, rd, 1) * halo_len(1, TQh, rh, 1) *
+                                                        halo_w(TQw, wg);
                                         }
                                     }
                                     // taps already carries the live output columns of each tile
@@ -431,7 +469,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                                     const int64_t staged = nn * co_tiles * tiles * CI_pad * halo;
                                     if (ploop)
                                         for (int wg = 0; wg < nwg; ++wg) halo += (int64_t)HD * HH * halo_w(TQw, wg);
-                                    const int64_t wgs = nn * co_tiles * s * s * nwg * tiles;
+                                    const int64_t wgs = nn * co_tiles * sd * sh * nwg * tiles;
                                     // MAC-equivalents: issued MFMA work, ~24 per staged element
                                     // (address arithmetic, load, LDS store), ~64 per output of
                                     // the epilogue
@@ -489,7 +527,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
             }
             if (CI_T == 0) continue;
             const int nchunks = (int)ceil_div(CI_pad, CI_T);
-            const int64_t grid = nn * co_tiles * (s * s / npg) * nwg * tiles_total;
+            const int64_t grid = nn * co_tiles * (ploop ? 1 : sd * sh) * nwg * tiles_total;
             // whole rounds of workgroups over the CUs; workgroups per CU from the
             // variant's register occupancy and the LDS size
             const int lds_wg = (int)lds_of(CI_T);
@@ -540,11 +578,11 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                 c.red_off = halo_floats(CI_T);
                 c.lds_bytes = lds_wg;
                 c.co_tiles = co_tiles; c.nwgroups = nwg;
-                c.tiles_per_n = (int64_t)s * s * nwg * tiles_total;
+                c.tiles_per_n = (int64_t)sd * sh * nwg * tiles_total;
                 c.grid_x = tiles_total;
-                c.grid_y = (int64_t)co_tiles * (s * s / npg) * nwg;
+                c.grid_y = (int64_t)co_tiles * (ploop ? 1 : sd * sh) * nwg;
                 c.grid_z = g->n;
-                c.issued_macs = issued / nn * g->n;
+                c.issued_macs = issued / nn * g->n * pl->G;  // every channel group
                 // packed weights that do not fit in half an L2: keep each XCD on
                 // one (co tile, phase) group at a time (CONVT3D_ORDER overrides)
                 c.order = (c.grid_y > 1 && pl->packed_floats * 4 > kL2Bytes / 2) ? 1 : 0;
@@ -582,10 +620,15 @@ int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
 void fill_conv_params(const Plan &pl, ConvParams *cp) {
     std::memset(cp, 0, sizeof(*cp));
     const convt3d_geom &g = pl.g;
-    cp->N = g.n; cp->Cin = g.cin; cp->Cout = g.cout;
+    cp->N = g.n; cp->Cin = pl.cig; cp->Cout = pl.cog;
+    cp->Cout_total = g.cout;
+    cp->x_nstride = g.cin * g.d * g.h * g.w;
     cp->D = g.d; cp->H = g.h; cp->W = g.w;
     cp->Do = pl.Do; cp->Ho = pl.Ho; cp->Wo = pl.Wo;
-    cp->s = pl.s;
+    for (int dim = 0; dim < 3; ++dim) {
+        cp->s3[dim] = pl.s3[dim];
+        cp->pe[dim] = pl.pe[dim];
+    }
     cp->Qd = pl.Q[0]; cp->Qh = pl.Q[1]; cp->Qw = pl.Q[2];
     cp->nreg = pl.nreg;
     for (int r = 0; r < kMaxRegions; ++r)

@@ -146,10 +146,22 @@ def torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, fused_ms, reps
     ours_tail_ms = timed(conv_then_ours)
     ref = tail(conv()).reshape(call.out.shape)
     diff = float((ref - call.out).abs().max())
-    return {"torch_eager_ms": round(eager_ms, 3), "torch_conv_ms": round(conv_ms, 3),
-            "torch_conv_plus_epilogue_only_ms": round(ours_tail_ms, 3), "fused_ms_per_step": round(fused_ms, 3),
-            "speedup_vs_torch_eager": round(eager_ms / fused_ms, 2), "max_abs_diff_vs_torch_eager": diff,
-            "reps": reps, "note": "PyTorch-ROCm (MIOpen) fp32, TF32 off; context only"}
+    res = {"torch_eager_ms": round(eager_ms, 3), "torch_conv_ms": round(conv_ms, 3),
+           "torch_conv_plus_epilogue_only_ms": round(ours_tail_ms, 3), "fused_ms_per_step": round(fused_ms, 3),
+           "speedup_vs_torch_eager": round(eager_ms / fused_ms, 2), "max_abs_diff_vs_torch_eager": diff,
+           "reps": reps, "note": "PyTorch-ROCm (MIOpen) fp32, TF32 off; context only"}
+    if has_tail:
+        # convt3d_epilogue_only alone on a resident y: its passes move
+        # (reads, writes) x |y| bytes: GN (2, 1), softmax (2, 1), BN (1, 0)
+        y = conv()
+        out = torch.empty((wl.n, wl.cout), device=x.device) if pooled else torch.empty_like(y)
+        ep_ms = timed(lambda: C.convt3d_epilogue_only(y, wl.n, wl.cout, S, epi, out, ws, ws_bytes))
+        passes = 1 if pooled else 3
+        gbps = passes * 4.0 * y.numel() / (ep_ms * 1e-3) / 1e9
+        res.update({"epilogue_only_ms": round(ep_ms, 4), "epilogue_only_GBps": round(gbps, 1),
+                    "epilogue_only_frac_hbm": round(gbps / PEAK_HBM_GBS, 4),
+                    "epilogue_only_y_passes": passes})
+    return res
 
 
 def main():
@@ -187,7 +199,8 @@ def main():
     wl = W.BY_NAME[args.workload]
     inp = W.make_inputs(wl)
     dev = torch.device("cuda:0")
-    g = C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)
+    g = C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad,
+                    wl.dilation, wl.conv_groups)
     call = C.FusedCall(g, wl.epi, wl.groups, wl.eps, wl.scale, device=dev)
     x = torch.from_numpy(inp.x).to(dev)
     w = torch.from_numpy(inp.w).to(dev)

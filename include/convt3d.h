@@ -7,7 +7,12 @@
  * over every (input voxel i, kernel tap) pair with o = stride*i - pad + tap in
  * each spatial dimension (p49 page, its scatter statement of the transposed
  * convolution; p77 page and p49 page, the output size
- * (in - 1)*stride - 2*pad + k + out_pad), followed by one epilogue:
+ * (in - 1)*stride - 2*pad + k + out_pad), and its general nn.ConvTranspose3d
+ * form: per-dimension kernel size, stride, padding and output padding,
+ * dilation dl (tap t sits dl*t from the first: o = stride*i - pad + dl*t,
+ * output size (in - 1)*stride - 2*pad + dl*(k - 1) + out_pad + 1) and channel
+ * groups (output channel co sums over the input channels of its group only);
+ * the pages use groups 1, dilation 1 and cubic kernels.  Then one epilogue:
  *   - ReLU then GroupNorm (p61 page's statement of GroupNorm: per (n, group)
  *     mean and biased variance over channels of the group and all voxels, eps
  *     inside the square root, per-channel gamma/beta);
@@ -46,14 +51,16 @@
 extern "C" {
 #endif
 
-/* Geometry.  Input x is [n, cin, d, h, w]; weight is [cin, cout, k, k, k] (the
- * layout nn.ConvTranspose3d stores); cubic kernel, same stride / pad /
- * out_pad in all three dims, dilation 1, groups 1.  Limits: n >= 0 (n == 0 is
- * an empty batch: nothing is launched), every other size >= 1, 1 <= stride
- * <= 4, 0 <= pad, 0 <= out_pad < stride, and each output dim >= 1. */
+/* Geometry.  Input x is [n, cin, d, h, w]; weight is [cin, cout/groups, k[0],
+ * k[1], k[2]] (the layout nn.ConvTranspose3d stores).  Arrays are indexed
+ * (0 = d, 1 = h, 2 = w).  Limits: n >= 0 (n == 0 is an empty batch: nothing is
+ * launched), every other size >= 1, 1 <= stride <= 4, 0 <= pad,
+ * 0 <= out_pad < max(stride, dilation) (nn.ConvTranspose3d's rule), groups
+ * divides cin and cout, and each output dim >= 1. */
 typedef struct convt3d_geom {
     int32_t n, cin, cout, d, h, w;
-    int32_t k, stride, pad, out_pad;
+    int32_t k[3], stride[3], pad[3], out_pad[3], dilation[3];
+    int32_t groups;
 } convt3d_geom;
 
 enum convt3d_epi_kind {
@@ -125,10 +132,11 @@ int64_t convt3d_output_elems(const convt3d_geom *geom, const convt3d_epilogue *e
 /* Bytes of the pre-packed weight buffer for this geometry (0 on invalid input). */
 size_t convt3d_packed_weight_bytes(const convt3d_geom *geom);
 
-/* Re-lay the nn.ConvTranspose3d weight w [cin, cout, k, k, k] (device) into the
- * per-stride-phase, matrix-core operand order the convolution kernel reads
- * (w_packed, device, convt3d_packed_weight_bytes bytes).  Enqueued on stream;
- * w_packed depends only on the geometry's cin, cout, k, stride and pad. */
+/* Re-lay the nn.ConvTranspose3d weight w [cin, cout/groups, k...] (device) into
+ * the per-group, per-stride-phase, matrix-core operand order the convolution
+ * kernel reads (w_packed, device, convt3d_packed_weight_bytes bytes).  Enqueued
+ * on stream; w_packed depends only on the geometry's channels, kernel size,
+ * stride, pad, dilation and groups. */
 int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_packed,
                             void *stream);
 
@@ -139,12 +147,12 @@ int convt3d_prepack_weights(const convt3d_geom *geom, const float *w, void *w_pa
  * stops reaching the output; for every (cin, cout) pair and bin triple the
  * weights of the taps that reach the output from that whole bin are summed.
  * With pad 0 there is one bin (the whole input) and this is the tap sum.
- * Bytes of that buffer (0 on invalid input or k > 31): */
+ * Bytes of that buffer (0 on invalid input or a kernel size above 31): */
 size_t convt3d_eval_weight_bytes(const convt3d_geom *geom);
 
-/* Fill w_eval (device, convt3d_eval_weight_bytes bytes) from w [cin, cout, k,
- * k, k] (device).  Enqueued on stream.  convt3d_fused with the kind
- * CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL takes w_eval in place of w_packed. */
+/* Fill w_eval (device, convt3d_eval_weight_bytes bytes) from w [cin,
+ * cout/groups, k...] (device).  Enqueued on stream.  convt3d_fused with the
+ * kind CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL takes w_eval in place of w_packed. */
 int convt3d_prepack_eval_weights(const convt3d_geom *geom, const float *w, void *w_eval,
                                  void *stream);
 
@@ -160,9 +168,11 @@ size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *
  *   bias       [cout] device, or NULL for no bias.
  *   out        device output, convt3d_output_elems(geom, epi) floats; must not
  *              overlap x.  For GroupNorm it is also used as the staging buffer
- *              of ReLU(y) before normalisation in place; for softmax with
- *              cout > 128 (more channels than one workgroup's tile holds) it
- *              stages y, which a second pass turns into the result in place.
+ *              of ReLU(y) before normalisation in place; for softmax with more
+ *              than 128 channels or with groups > 1 (then one workgroup's tile
+ *              does not hold every channel) it stages y, which a second pass
+ *              turns into the result in place.
+ * With groups > 1 the convolution kernel runs once per group.
  *   workspace  device scratch of at least convt3d_workspace_size bytes.
  * Enqueues 1 to 3 kernels on stream and returns without waiting. */
 int convt3d_fused(const float *x, const void *w_packed, const float *bias,
@@ -178,9 +188,11 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias,
  * convt3d_fused it waits on the device (it times the candidates with HIP
  * events on `stream`).  Candidates needing more workspace than
  * workspace_bytes are skipped.  BatchNorm running statistics are left
- * untouched (the timed calls do not update them).  result may be NULL.  The best 12 candidates
- * are timed (environment CONVT3D_TUNE_CANDIDATES=1..64 changes that;
- * CONVT3D_TUNE_LOG prints one line per candidate to stderr). */
+ * untouched (the timed calls do not update them).  result may be NULL.  The
+ * best 12 candidates are timed (environment CONVT3D_TUNE_CANDIDATES=1..64
+ * changes that; CONVT3D_TUNE_LOG prints one line per candidate to stderr):
+ * after about 20 ms of warm-up calls, each in three rounds of repeated calls
+ * (about 2 ms of work per round), its fastest round counting. */
 typedef struct convt3d_tune_result {
     int32_t candidates;      /* plans timed                                      */
     int32_t chosen;          /* rank of the chosen plan in cost-model order (0 = the model's pick) */
@@ -224,7 +236,7 @@ typedef struct convt3d_plan_info {
     int32_t tuned;             /* 1: chosen by convt3d_autotune                         */
     int32_t border_split;      /* dims split into border / interior tile regions (bit 0 d, 1 h, 2 w) */
     int32_t xcd_order;         /* 0: phase / channel-tile index fastest per XCD, 1: tile fastest */
-    int32_t softmax_pass;      /* 1: softmax runs as a second pass (cout > 128)         */
+    int32_t softmax_pass;      /* 1: softmax runs as a second pass (cout > 128, groups) */
     int32_t eval_bins;         /* BN eval: input bins per (n, cin) plane, else 0        */
 } convt3d_plan_info;
 

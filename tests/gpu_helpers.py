@@ -16,7 +16,8 @@ def say(*a):
 
 
 def geom_of(wl):
-    return C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad)
+    return C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad,
+                       wl.dilation, wl.conv_groups)
 
 
 def to_dev(a):

@@ -1,0 +1,115 @@
+"""GPU parity for the general nn.ConvTranspose3d geometry: per-dimension
+kernel size, stride, padding and output padding, dilation and channel groups,
+with every epilogue, against the fp64 oracle (its general scatter definition)
+on the same seeded inputs; also every compiled kernel variant forced on one
+dilated, grouped, anisotropic geometry."""
+import numpy as np
+import pytest
+
+import oracle
+from activation_epilogues_amd import convt3d as C
+from activation_epilogues_amd import workloads as W
+
+from gpu_helpers import TOL, geom_of, max_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [W.EPI_NONE, W.EPI_RELU_GROUPNORM, W.EPI_SOFTMAX_SIGMOID, W.EPI_SCALE_BN_TRAIN_AVGPOOL,
+         W.EPI_SCALE_BN_EVAL_AVGPOOL]
+
+
+def out_dims(wl):
+    return [oracle.out_dim_general(n, *a) for n, a in
+            zip((wl.d, wl.h, wl.w), zip(wl.kdims, W.triple(wl.stride), W.triple(wl.pad), W.triple(wl.out_pad),
+                                         W.triple(wl.dilation)))]
+
+
+def general_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        kind = KINDS[len(out) % len(KINDS)]
+        wl = W.random_general_geometry(rng, max_in=8, max_ch=12, epi=kind)
+        if min(out_dims(wl)) <= 0:
+            continue
+        out.append(wl.with_(name=f"gen{len(out)}"))
+    return out
+
+
+def run_and_check(wl, inp=None):
+    import torch
+    inp = W.make_inputs(wl) if inp is None else inp
+    call = C.FusedCall(geom_of(wl), wl.epi, wl.groups, wl.eps, wl.scale, want_stats=True, momentum=wl.momentum)
+    call.prepack(to_dev(inp.w))
+    call.out.fill_(float("nan"))
+    rm, rv = to_dev(inp.rmean), to_dev(inp.rvar)
+    out = call(to_dev(inp.x), to_dev(inp.b), to_dev(inp.gamma), to_dev(inp.beta), running_mean=rm, running_var=rv)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref = oracle.run_workload(wl, inp)
+    err = max_err(out, ref.out.reshape(out.shape))
+    assert np.isfinite(out).all()
+    assert err <= TOL, f"max|err| {err:.3e}"
+    if call.stats is not None:
+        st = call.stats.cpu().numpy()
+        np.testing.assert_allclose(st, ref.stats.reshape(st.shape), rtol=1e-5, atol=1e-6)
+    if ref.running is not None:
+        assert max_err(rm.cpu().numpy(), ref.running[0]) <= TOL
+        assert max_err(rv.cpu().numpy(), ref.running[1]) <= TOL
+    return call
+
+
+def describe(wl):
+    return (f"{wl.name} {W.EPI_NAMES[wl.epi]} n={wl.n} cin={wl.cin} cout={wl.cout} in={wl.d}x{wl.h}x{wl.w} "
+            f"k={wl.k} s={wl.stride} p={wl.pad} op={wl.out_pad} dl={wl.dilation} G={wl.conv_groups} seed={wl.seed}")
+
+
+@pytest.mark.parametrize("wl", general_cases(40, 606), ids=lambda w: w.name)
+def test_random_general_geometry(wl):
+    say(f"[case] {describe(wl)}")
+    run_and_check(wl)
+
+
+NAMED = [
+    # anisotropic strides / kernels with dilation, larger channel counts
+    W.Workload("aniso", 2, 24, 40, 6, 7, 9, k=(3, 4, 2), stride=(2, 1, 2), pad=(1, 2, 0), out_pad=(1, 0, 1),
+               dilation=(1, 2, 3), epi=W.EPI_RELU_GROUPNORM, groups=5, seed=6101),
+    # grouped softmax: the softmax runs as a second pass over all channels
+    W.Workload("grp_softmax", 2, 16, 48, 5, 6, 7, k=3, stride=2, pad=1, out_pad=1, conv_groups=4,
+               epi=W.EPI_SOFTMAX_SIGMOID, seed=6102),
+    # depthwise: one input and one output channel per group
+    W.Workload("depthwise", 2, 8, 8, 5, 5, 6, k=3, stride=(1, 2, 2), pad=1, out_pad=(0, 1, 1), conv_groups=8,
+               epi=W.EPI_NONE, seed=6103),
+    # dilation sharing a factor with the stride (taps split unevenly over phases)
+    W.Workload("dl2s2", 2, 12, 36, 6, 6, 6, k=(3, 3, 3), stride=(2, 2, 4), pad=(2, 1, 3), out_pad=(1, 1, 1),
+               dilation=(2, 2, 2), epi=W.EPI_SCALE_BN_TRAIN_AVGPOOL, scale=2.0, seed=6104),
+    W.Workload("eval_general", 3, 18, 30, 5, 6, 7, k=(2, 3, 4), stride=(3, 1, 2), pad=(1, 2, 1), out_pad=(2, 0, 1),
+               dilation=(2, 1, 2), conv_groups=3, epi=W.EPI_SCALE_BN_EVAL_AVGPOOL, scale=-1.5, seed=6105),
+]
+
+
+@pytest.mark.parametrize("wl", NAMED, ids=lambda w: w.name)
+def test_named_general_geometry(wl):
+    say(f"[case] {describe(wl)}")
+    call = run_and_check(wl)
+    info = call.plan_info()
+    if wl.epi == W.EPI_SOFTMAX_SIGMOID:
+        assert info["softmax_pass"] == 1
+
+
+# every compiled variant on one dilated, grouped geometry (w-stride 2 so the
+# two-w-phase variants apply; d/h strides > 1 so the phase-group loop applies)
+VARIANTS = [(0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (1, 1), (3, 1), (4, 1)]
+
+
+@pytest.mark.parametrize("vi,ploop", VARIANTS, ids=[f"v{v}-pl{p}" for v, p in VARIANTS])
+def test_forced_variants_general(vi, ploop, monkeypatch):
+    wl = W.Workload(f"gv{vi}", 2, 20, 44, 6, 7, 8, k=(3, 2, 4), stride=(2, 3, 2), pad=(1, 0, 2), out_pad=(1, 2, 1),
+                    dilation=(2, 1, 1), conv_groups=2, epi=[W.EPI_NONE, W.EPI_RELU_GROUPNORM][vi % 2],
+                    groups=2, seed=6200 + vi)
+    monkeypatch.setenv("CONVT3D_PLAN", f"{vi},-1,-1,-1,-1,-1")
+    monkeypatch.setenv("CONVT3D_PHASE_LOOP", str(ploop))
+    say(f"[case] variant {vi} phase_loop {ploop} {describe(wl)}")
+    info = C.convt3d_get_plan_info(geom_of(wl), C.make_epilogue(wl.epi, wl.groups))
+    assert info["variant"] == vi and info["phase_loop"] == ploop
+    run_and_check(wl)

@@ -27,7 +27,7 @@ def header_functions():
 
 def geom_of(wl, n=None):
     return C.make_geom(wl.n if n is None else n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride,
-                       wl.pad, wl.out_pad)
+                       wl.pad, wl.out_pad, wl.dilation, wl.conv_groups)
 
 
 def test_library_exports_every_declared_function():
@@ -37,6 +37,32 @@ def test_library_exports_every_declared_function():
     for nm in names:
         assert hasattr(L, nm), nm
     assert sorted(C.EXPORTED) == names
+
+
+def test_general_geometry_dims_and_macs_match_brute_force():
+    """Per-dim kernel / stride / pad / output padding, dilation and groups: the
+    output size and the in-range multiply-add count the planner reports."""
+    rng = np.random.default_rng(3)
+    done = 0
+    while done < 60:
+        wl = W.random_general_geometry(rng, max_in=7)
+        ks, ss, ps, ops, dls = (W.triple(v) for v in (wl.k, wl.stride, wl.pad, wl.out_pad, wl.dilation))
+        od = [oracle.out_dim_general(n, *a) for n, a in zip((wl.d, wl.h, wl.w), zip(ks, ss, ps, ops, dls))]
+        if min(od) <= 0:
+            with pytest.raises(C.Convt3dError):
+                C.convt3d_output_dims(geom_of(wl))
+            continue
+        assert C.convt3d_output_dims(geom_of(wl)) == tuple(od)
+        per_dim = []
+        for n_in, n_out, k, s, p, dl in zip((wl.d, wl.h, wl.w), od, ks, ss, ps, dls):
+            per_dim.append(sum(0 <= s * i - p + dl * t < n_out for i in range(n_in) for t in range(k)))
+        want = wl.n * (wl.cin // wl.conv_groups) * wl.cout * per_dim[0] * per_dim[1] * per_dim[2]
+        info = C.convt3d_get_plan_info(geom_of(wl), C.make_epilogue(0))
+        assert info["valid_macs"] == want
+        assert info["issued_macs"] >= want
+        assert C.convt3d_packed_weight_bytes(geom_of(wl)) >= 4 * wl.cin * (wl.cout // wl.conv_groups) * \
+            ks[0] * ks[1] * ks[2]
+        done += 1
 
 
 def test_output_dims_match_oracle():
@@ -101,11 +127,16 @@ FAKE = 0x100000  # never dereferenced: every case below fails its checks before 
 
 @pytest.mark.parametrize("field,value,code", [
     ("n", -1, 2), ("cin", 0, 2), ("cout", 0, 2), ("d", 0, 2), ("k", 0, 2), ("stride", 0, 2),
-    ("stride", 5, 2), ("pad", -1, 2), ("out_pad", 1, 2),
+    ("stride", 5, 2), ("pad", -1, 2), ("out_pad", 1, 2), ("dilation", 0, 2), ("groups", 0, 2),
+    ("groups", 3, 2),
 ])
 def test_bad_geometry_is_rejected(field, value, code):
+    """Bad values, per-dim ones set along h only."""
     g = C.make_geom(1, 4, 8, 3, 3, 3, 3)
-    setattr(g, field, value)
+    if field in ("k", "stride", "pad", "out_pad", "dilation"):
+        getattr(g, field)[1] = value
+    else:
+        setattr(g, field, value)
     e = C.make_epilogue(0)
     st = C.convt3d_fused(FAKE, FAKE, None, g, e, FAKE + (1 << 30), None, 0, stream=0, check=False)
     assert st == code
@@ -113,7 +144,7 @@ def test_bad_geometry_is_rejected(field, value, code):
 
 
 def test_empty_output_is_rejected():
-    g = C.make_geom(1, 2, 2, 1, 1, 1, 3, 1, 2, 0)  # (1-1)*1 - 4 + 3 = -1
+    g = C.make_geom(1, 2, 2, 1, 1, 1, 3, 1, 2, 0)  # (1-1)*1 - 4 + 2 + 0 + 1 = -1
     st = C.convt3d_fused(FAKE, FAKE, None, g, C.make_epilogue(0), FAKE * 4, None, 0, stream=0, check=False)
     assert st == 2
 
