@@ -13,7 +13,9 @@
 //                            output held in memory (v = ReLU(y) or scale*y).
 //  * softmax_pass_kernel  -- channel softmax then sigmoid over a conv output in
 //                            memory: one pass for the running max and sum of
-//                            exponentials, one for the result.
+//                            exponentials, one for the result (more than 64
+//                            channels); softmax_regs_kernel holds up to 64
+//                            channels of a position in registers (one read).
 //  * bn_eval_rows_kernel  -- eval-mode BatchNorm + pool from per-row sums.
 //  * eval_pack_kernel     -- tap-summed weights per input bin (eval mode).
 //  * eval_binsum_kernel   -- sums of x over the input bins of each (n, cin).
@@ -302,6 +304,35 @@ __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out,
     }
 }
 
+// The same for C <= CR channels with one read: thread = (n, one position),
+// its C values held in registers (CR of them, unused ones at -inf), then max,
+// exponentials, sum and the result.  out may equal src.
+template <int CR>
+__global__ __launch_bounds__(256) void softmax_regs_kernel(const float *src, float *out, int N, int C, int S) {
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= S) return;
+    for (int n = blockIdx.y; n < N; n += gridDim.y) {
+        const float *p = src + (size_t)n * C * S + s;
+        float *o = out + (size_t)n * C * S + s;
+        float v[CR];
+#pragma unroll
+        for (int c = 0; c < CR; ++c) v[c] = c < C ? p[(size_t)c * S] : -INFINITY;
+        float m = v[0];
+#pragma unroll
+        for (int c = 1; c < CR; ++c) m = fmaxf(m, v[c]);
+        float l = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CR; ++c) {
+            v[c] = fast_exp(v[c] - m);  // 0 for the unused (-inf) entries
+            l += v[c];
+        }
+        const float inv = __builtin_amdgcn_rcpf(l);
+#pragma unroll
+        for (int c = 0; c < CR; ++c)
+            if (c < C) o[(size_t)c * S] = __builtin_amdgcn_rcpf(1.0f + fast_exp(-v[c] * inv));
+    }
+}
+
 // Eval-mode BatchNorm + pool from per-row sums (partials [n][chunk][C][2] of
 // (sum y, -)): thread per (n, c), pooled mean m = sum / S, then
 // out = (scale*m - rmean) / sqrt(rvar + eps) * gamma + beta.
@@ -554,6 +585,17 @@ int launch_row_stats(const float *y, int N, int C, int64_t S, bool relu, float m
 
 int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, void *stream) {
     const int gy = N < 65535 ? N : 65535;
+    if (C <= 64) {  // every channel of a position in registers: one read of y
+        const int len = (int)S;
+        const dim3 grid((len + 255) / 256, gy);
+        if (C <= 16)
+            hipLaunchKernelGGL(softmax_regs_kernel<16>, grid, dim3(256), 0, (hipStream_t)stream, src, out, N, C, len);
+        else if (C <= 32)
+            hipLaunchKernelGGL(softmax_regs_kernel<32>, grid, dim3(256), 0, (hipStream_t)stream, src, out, N, C, len);
+        else
+            hipLaunchKernelGGL(softmax_regs_kernel<64>, grid, dim3(256), 0, (hipStream_t)stream, src, out, N, C, len);
+        return (int)hipGetLastError();
+    }
     if (S % 4 == 0) {
         const int len = (int)(S / 4);
         hipLaunchKernelGGL(softmax_pass_kernel<float4>, dim3((len + 255) / 256, gy), dim3(256), 0,

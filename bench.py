@@ -152,11 +152,17 @@ def torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, fused_ms, reps
            "reps": reps, "note": "PyTorch-ROCm (MIOpen) fp32, TF32 off; context only"}
     if has_tail:
         # convt3d_epilogue_only alone on a resident y: its passes move
-        # (reads, writes) x |y| bytes: GN (2, 1), softmax (2, 1), BN (1, 0)
+        # (reads, writes) x |y| bytes: GN (2, 1), softmax (1, 1) up to 64
+        # channels (held in registers) else (2, 1), BN (1, 0)
         y = conv()
         out = torch.empty((wl.n, wl.cout), device=x.device) if pooled else torch.empty_like(y)
         ep_ms = timed(lambda: C.convt3d_epilogue_only(y, wl.n, wl.cout, S, epi, out, ws, ws_bytes))
-        passes = 1 if pooled else 3
+        if pooled:
+            passes = 1
+        elif wl.epi == W.EPI_SOFTMAX_SIGMOID and wl.cout <= 64:
+            passes = 2
+        else:
+            passes = 3
         gbps = passes * 4.0 * y.numel() / (ep_ms * 1e-3) / 1e9
         res.update({"epilogue_only_ms": round(ep_ms, 4), "epilogue_only_GBps": round(gbps, 1),
                     "epilogue_only_frac_hbm": round(gbps / PEAK_HBM_GBS, 4),
