@@ -84,6 +84,18 @@ def cpu_baseline(wl, inp, max_samples: int):
     return n, dt, oracle.num_threads()
 
 
+def dense_equivalent(wl, call, ms: float) -> dict:
+    """The pages' way of counting the work, for context only: every output
+    voxel times every input channel (of its group) times every kernel tap,
+    as a direct convolution over a zero-inserted, zero-padded input would
+    multiply (the p77 page's 424 G multiply-adds for its k5 layer)."""
+    kd, kh, kw = wl.kdims
+    S = call.out_dims[0] * call.out_dims[1] * call.out_dims[2]
+    macs = wl.n * wl.cout * S * (wl.cin // wl.conv_groups) * kd * kh * kw
+    return {"gmac_per_step": round(macs / 1e9, 3), "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
+            "note": "context only: counts zero-inserted and padding taps, not work done"}
+
+
 def torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, fused_ms, reps: int = 5):
     """Context only: PyTorch-ROCm's own ConvTranspose3d followed by its
     epilogue ops (eager), its conv alone, and its conv followed by
@@ -325,6 +337,7 @@ def main():
                        "eval-mode-normalised output this path computes without running it") if evalmode else
                       "algorithmic: 2 x in-range multiply-adds of the ConvTranspose3d run",
         "pct_fp32_mfma_peak_whole_step": None if evalmode else round(100 * gflops / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
+        "dense_equivalent": dense_equivalent(wl, call, ms),
         "roofline": roofline,
         "kernels": kernels,
         "plan": {k: v for k, v in info.items()},
