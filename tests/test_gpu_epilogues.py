@@ -175,6 +175,42 @@ def test_epilogue_only_matches_oracle(case):
     assert err <= TOL, f"max|err| {err:.3e}"
 
 
+# ---------------------------------------------------------------- softmax arithmetic bound
+
+@pytest.mark.parametrize("c", [64, 100])
+def test_softmax_arithmetic_error_bound(c):
+    """With y given exactly, the softmax + sigmoid result differs from fp64 only
+    by the hardware exp2 / reciprocal (a few ulp) and the final rounding: a
+    bound of 1e-6, far tighter than the 1e-4 output tolerance.  64 channels
+    take the register-held kernel, 100 the two-read one."""
+    import torch
+    rng = np.random.default_rng(800 + c)
+    y = (rng.standard_normal((2, c, 5, 6, 7)) * 3.0).astype(np.float32)
+    dy = to_dev(y)
+    out = torch.empty_like(dy)
+    epi = C.make_epilogue(W.EPI_SOFTMAX_SIGMOID)
+    C.convt3d_epilogue_only(dy, 2, c, 5 * 6 * 7, epi, out, None, 0)
+    torch.cuda.synchronize()
+    want, _ = oracle.softmax_sigmoid(y.astype(np.float64))
+    err = max_err(out.cpu().numpy(), want)
+    say(f"[case] softmax arithmetic c={c}: max|err| {err:.2e}")
+    assert err <= 1e-6, f"max|err| {err:.3e}"
+
+
+def test_fused_softmax_arithmetic_error_bound():
+    """The in-register softmax of the conv kernel behind a k=1 convolution of 8
+    channels (its rounding is a few ulp): the polynomial sigmoid (error 7.4e-8)
+    and hardware exp2 / reciprocal keep the result within 1e-6 of fp64."""
+    wl = W.Workload("smtight", 2, 8, 64, 6, 7, 9, k=1, bias=True, epi=W.EPI_SOFTMAX_SIGMOID, seed=4500)
+    inp = W.make_inputs(wl)
+    inp = W.Inputs(inp.x * 4.0, inp.w * 8.0, inp.b, None, None)  # logits spread over several units
+    out, _, _, _, _ = fused(wl, inp, with_running=False)
+    ref = oracle.run_workload(wl, inp)
+    err = max_err(out, ref.out.reshape(out.shape))
+    say(f"[case] fused softmax arithmetic: max|err| {err:.2e}")
+    assert err <= 1e-6, f"max|err| {err:.3e}"
+
+
 # ---------------------------------------------------------------- softmax over > 128 channels
 
 @pytest.mark.parametrize("geo", [(2, 8, 160, 4, 5, 6, 3, 1, 0, 0), (2, 12, 300, 3, 4, 5, 3, 2, 1, 1),

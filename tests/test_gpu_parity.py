@@ -89,6 +89,16 @@ def test_workload_reduced_batch_final_and_raw(name):
     check(wl, W.EPI_NONE, inp, tag="reduced-raw")
 
 
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_workload_uniform_inputs(name):
+    """The same shapes with x ~ U[0, 1) (the input distribution the pages'
+    harness most likely used): every conv output has a large common offset,
+    which stresses the statistics and the softmax shift."""
+    wl = W.BY_NAME[name].with_(n=REDUCED[name])
+    inp = W.make_inputs(wl, x_dist="uniform")
+    check(wl, wl.epi, inp, tag="uniform")
+
+
 def test_run_twice_is_bitwise_identical():
     wl = W.BY_NAME["k3s1_gn"].with_(n=1, d=12, h=10, w=9)
     inp = W.make_inputs(wl)
