@@ -275,6 +275,26 @@ def test_epilogue_only_argument_checks():
     assert only(y, 0, c, S, gn, out, ws, need) == 0
 
 
+def test_size_limits():
+    """Sizes past the 32-bit offsets the kernels use are refused with
+    CONVT3D_ERR_TOO_LARGE before anything runs; just inside, a plan exists."""
+    def status(g, kind=0):
+        try:
+            C.convt3d_get_plan_info(g, C.make_epilogue(kind))
+            return 0
+        except C.Convt3dError as ex:
+            return ex.status
+    # per-channel output size: the conv kernel's row byte offsets reach 20 * S
+    assert status(C.make_geom(1, 2, 2, 590, 590, 590, 3, 1, 1, 0)) == 0      # S = 590^3, 20 S < 2^32
+    assert status(C.make_geom(1, 2, 2, 600, 600, 600, 3, 1, 1, 0)) == 8      # S = 600^3, 20 S > 2^32
+    # whole output and whole input beyond 2^31 elements
+    assert status(C.make_geom(11, 1, 1, 590, 590, 590, 1)) == 8              # 11 * 590^3 > 2^31
+    assert status(C.make_geom(1, 11, 1, 590, 590, 590, 1)) == 8
+    # packed weights
+    assert status(C.make_geom(1, 1024, 1024, 2, 2, 2, 16)) == 8
+    assert C.convt3d_packed_weight_bytes(C.make_geom(1, 1024, 1024, 2, 2, 2, 16)) == 0
+
+
 def test_empty_batch_is_a_no_op():
     g = C.make_geom(0, 4, 8, 3, 3, 3, 3)
     for kind in (0, 1, 2, 3, 4):
