@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--plan", default=None, help="force a plan (CONVT3D_PLAN string); implies --no-tune")
     ap.add_argument("--phase-loop", type=int, choices=(0, 1), default=None,
                     help="force the phase-group loop off / on (with --plan)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (context; value stays eager)")
     ap.add_argument("--compare-torch", action="store_true",
                     help="also time PyTorch's own ConvTranspose3d + epilogue ops, and its conv followed by "
                          "convt3d_epilogue_only (context only)")
@@ -308,6 +310,27 @@ def main():
 
     comparison = torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, ms) if args.compare_torch else None
 
+    graph_ms = None
+    if args.graph:
+        # the same step captured once on a side stream and replayed: no host
+        # launch cost per kernel (the library enqueues kernels only)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g_step = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g_step, stream=side):
+                call.prepack(w, side)
+                call(x, b, gamma, beta, side, running_mean=rmean, running_var=rvar)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g_step.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g_step.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
@@ -345,6 +368,7 @@ def main():
         "tune": tune,
         "cpu_baseline": cpu,
         "torch_comparison": comparison,
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
     }
     print(json.dumps(res), flush=True)
 
