@@ -49,7 +49,8 @@ class PlanInfo(ctypes.Structure):
                 ("issued_macs", ctypes.c_int64), ("valid_macs", ctypes.c_int64),
                 ("phase_loop", ctypes.c_int32),
                 ("tuned", ctypes.c_int32), ("border_split", ctypes.c_int32), ("xcd_order", ctypes.c_int32),
-                ("softmax_pass", ctypes.c_int32), ("eval_bins", ctypes.c_int32)]
+                ("softmax_pass", ctypes.c_int32), ("eval_bins", ctypes.c_int32),
+                ("conv_launches", ctypes.c_int32)]
 
 
 class TuneResult(ctypes.Structure):

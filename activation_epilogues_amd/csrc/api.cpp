@@ -286,6 +286,7 @@ int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,
     info->xcd_order = pl.order;
     info->softmax_pass = pl.softmax_pass;
     info->eval_bins = pl.eval ? pl.eg.nbins : 0;
+    info->conv_launches = pl.eval ? 0 : pl.group_launch ? 1 : pl.G;
     return CONVT3D_OK;
 }
 
@@ -332,7 +333,10 @@ static int run_plan(const Plan &pl, const float *x, const void *w_packed, const 
     ConvParams cp;
     fill_conv_params(pl, &cp);
     const bool pooled = epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;  // the kernel never writes out
-    for (int gi = 0; gi < pl.G; ++gi) {  // channel groups: independent convolutions
+    // channel groups are independent convolutions: one launch covers them all
+    // (the kernel offsets by its group), or one launch per group
+    const int launches = pl.group_launch ? 1 : pl.G;
+    for (int gi = 0; gi < launches; ++gi) {
         cp.x = x + (size_t)gi * pl.cig * g.d * g.h * g.w;
         cp.wp = static_cast<const float *>(w_packed) + (size_t)gi * pl.packed_floats;
         cp.bias = bias ? bias + (size_t)gi * pl.cog : nullptr;

@@ -45,6 +45,10 @@ struct ConvParams {
     int N, Cin, Cout, D, H, W, Do, Ho, Wo;  // Cin, Cout: of one channel group
     int Cout_total;       // output channels of the whole conv (row stride of out and partials)
     int x_nstride;        // floats per sample of x (all groups' channels)
+    int G;                // channel groups in this launch (grid z = sample * G + group); 1 when
+                          // the host launches once per group with offset pointers
+    int xg;               // floats from one group's first input channel to the next (cig * D*H*W)
+    int wpg;              // floats from one group's packed weights to the next
     int s3[3];            // stride per dim
     int pe[3];            // input step per tap index j, per dim (dilation / gcd)
     int Qd, Qh, Qw;
@@ -127,6 +131,7 @@ struct Plan {
     int order = 0;            // workgroup order within an XCD (see ConvParams::order)
     int64_t tiles_per_n = 0;
     int64_t grid_x = 0, grid_y = 0, grid_z = 0;
+    int group_launch = 1;     // 1: one launch covers every channel group (grid z = n * G)
     int64_t issued_macs = 0, valid_macs = 0;
     // workspace layout (bytes)
     size_t ws_partials = 0, ws_ab = 0, ws_bins = 0, ws_bytes = 0;

@@ -94,12 +94,16 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // Transposed convolution on FP32 MFMA.
 //
 // Workgroup = 4 waves = WCO (co direction) x WPOS (position direction).  It
-// owns: one sample n, one (rho_d, rho_h) phase pair, NPH consecutive w-phases,
-// a box of TQd x TQh x TQw stride-phase positions q, and WCO*CBW blocks of 32
-// output channels.  Each wave owns CBW co-blocks x PBW blocks of 32 positions
-// for each of its NPH w-phases.  Input channels are consumed in chunks of CI_T:
-// the input halo of the box for those channels is staged in LDS, then every
-// live tap of every phase runs 4 MFMA k-steps per 8 input channels.
+// owns: one sample n, one (rho_d, rho_h) phase pair (every pair with the
+// phase-group loop), NPH consecutive w-phases, a box of TQd x TQh x TQw
+// stride-phase positions q, and WCO*CBW blocks of 32 output channels.  Each
+// wave owns CBW co-blocks x PBW blocks of 32 positions for each of its NPH
+// w-phases.  Input channels are consumed in chunks of CI_T: the input halo of
+// the box for those channels is staged in LDS, then every live tap of every
+// phase runs 4 MFMA k-steps per 8 input channels.  With channel groups, grid z
+// is sample * G + group and x, w, bias, out and partials are offset to the
+// group's channels (Cout_total is the row stride); when that grid would be too
+// tall the host launches once per group with offset pointers and G = 1.
 template <int CBW, int NPH, int PBW, bool SM, bool PL>
 __global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
                                           : (CBW * NPH * PBW <= 2) ? 6
@@ -141,6 +145,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
         }
         n = lin / (gx * gy);
     }
+    // channel group of this workgroup (grid z = sample * G + group)
+    const int grp = n % P.G;
+    n /= P.G;
     // ---- tile: find the region, then the tile inside it
     int reg = 0;
     while (reg + 1 < P.nreg && bx >= P.rg_off[reg + 1]) ++reg;
@@ -237,10 +244,10 @@ void convt3d_mfma_kernel(const ConvParams P) {
 
     const int CO_T = P.WCO * CBW;                   // co blocks per workgroup
     const int cb0 = co_tile * CO_T + wco * CBW;     // first co block of this wave
-    const float4 *wp4 = reinterpret_cast<const float4 *>(P.wp);
+    const float4 *wp4 = reinterpret_cast<const float4 *>(P.wp + (size_t)grp * P.wpg);
     const int G4 = P.CI_T >> 3;
     const int DHWin = P.D * P.H * P.W;
-    const float *xn = P.x + (size_t)n * P.x_nstride;
+    const float *xn = P.x + (size_t)n * P.x_nstride + (size_t)grp * P.xg;
 
     // ---- halo staging.  Thread t takes halo positions t, t + 256, ...; for each
     // position inside the input it loads the 8 channels of every octet of the
@@ -491,12 +498,12 @@ void convt3d_mfma_kernel(const ConvParams P) {
     int row0 = cb0 * 32;
     if constexpr (PL) asm volatile("" : "+s"(row0));
     const bool rows_full = row0 + CBW * 32 <= Cout;  // every accumulator row is a channel
-    char *outb = reinterpret_cast<char *>(P.out + (size_t)n * P.Cout_total * S);
+    char *outb = reinterpret_cast<char *>(P.out + ((size_t)n * P.Cout_total + (size_t)grp * Cout) * S);
     auto row_u = [&](int c, int r) { return row0 + c * 32 + 8 * (r >> 2) + (r & 3); };
     auto row_ok = [&](int c, int r) { return rows_full || row_u(c, r) + 4 * half < Cout; };
     auto rowp = [&](int c, int r) { return outb + (size_t)row_u(c, r) * S * 4; };
     auto bias_of = [&](int c, int r, float dflt) {  // bias of the lane's row c, r (dflt: no bias)
-        return P.bias ? P.bias[row_u(c, r) + 4 * half] : dflt;
+        return P.bias ? P.bias[grp * Cout + row_u(c, r) + 4 * half] : dflt;
     };
     // the stores of one accumulator row (c, r) of position block pb
     auto store_row = [&](char *rp, int pb, const float (&v)[NPH]) {
@@ -648,7 +655,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     t1 += red[(w * CO32 + row) * 2 + 0];
                     t2 += red[(w * CO32 + row) * 2 + 1];
                 }
-                float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * P.Cout_total + co) * 2;
+                float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * P.Cout_total + grp * Cout + co) * 2;
                 pp[0] = t1;
                 pp[1] = t2;
             }

@@ -346,7 +346,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     // CONVT3D_PHASE_LOOP=0|1 restricts the phase-group loop choice (tests, sweeps)
     int ploop_only = -1;
     if (const char *env = std::getenv("CONVT3D_PHASE_LOOP")) ploop_only = std::atoi(env) ? 1 : 0;
-    const int64_t nn = std::max(g->n, 1);  // plan an empty batch like n = 1
+    // workgroups are planned for every (sample, channel group); an empty batch like n = 1
+    const int64_t nn = (int64_t)std::max(g->n, 1) * pl->G;
     const int CI_pad = pl->octets * kOctet;
 
     std::vector<std::pair<double, Plan>> top;  // cheapest first, at most max_k
@@ -581,7 +582,10 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                 c.tiles_per_n = (int64_t)sd * sh * nwg * tiles_total;
                 c.grid_x = tiles_total;
                 c.grid_y = (int64_t)co_tiles * (ploop ? 1 : sd * sh) * nwg;
-                c.grid_z = g->n;
+                // one launch for every (sample, group) unless that passes the
+                // grid's z limit: then one launch per group
+                c.group_launch = (int64_t)g->n * pl->G <= 65535 ? 1 : 0;
+                c.grid_z = c.group_launch ? (int64_t)g->n * pl->G : g->n;
                 c.issued_macs = issued / nn * g->n * pl->G;  // every channel group
                 // packed weights that do not fit in half an L2: keep each XCD on
                 // one (co tile, phase) group at a time (CONVT3D_ORDER overrides)
@@ -623,6 +627,9 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->N = g.n; cp->Cin = pl.cig; cp->Cout = pl.cog;
     cp->Cout_total = g.cout;
     cp->x_nstride = g.cin * g.d * g.h * g.w;
+    cp->G = pl.group_launch ? pl.G : 1;
+    cp->xg = pl.cig * g.d * g.h * g.w;
+    cp->wpg = (int)pl.packed_floats;
     cp->D = g.d; cp->H = g.h; cp->W = g.w;
     cp->Do = pl.Do; cp->Ho = pl.Ho; cp->Wo = pl.Wo;
     for (int dim = 0; dim < 3; ++dim) {

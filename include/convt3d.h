@@ -238,6 +238,8 @@ typedef struct convt3d_plan_info {
     int32_t xcd_order;         /* 0: phase / channel-tile index fastest per XCD, 1: tile fastest */
     int32_t softmax_pass;      /* 1: softmax runs as a second pass (cout > 128, groups) */
     int32_t eval_bins;         /* BN eval: input bins per (n, cin) plane, else 0        */
+    int32_t conv_launches;     /* conv kernel launches per call: 1, or one per channel group
+                                  when n * groups exceeds the grid's z limit (0: no conv) */
 } convt3d_plan_info;
 
 int convt3d_get_plan_info(const convt3d_geom *geom, const convt3d_epilogue *epi,

@@ -85,6 +85,10 @@ NAMED = [
                dilation=(2, 2, 2), epi=W.EPI_SCALE_BN_TRAIN_AVGPOOL, scale=2.0, seed=6104),
     W.Workload("eval_general", 3, 18, 30, 5, 6, 7, k=(2, 3, 4), stride=(3, 1, 2), pad=(1, 2, 1), out_pad=(2, 0, 1),
                dilation=(2, 1, 2), conv_groups=3, epi=W.EPI_SCALE_BN_EVAL_AVGPOOL, scale=-1.5, seed=6105),
+    # more (sample, group) pairs than the grid's z dimension holds: one conv
+    # launch per group instead of one for all
+    W.Workload("many_groups", 1000, 66, 66, 2, 2, 2, k=2, stride=1, conv_groups=66, epi=W.EPI_RELU_GROUPNORM,
+               groups=6, seed=6106),
 ]
 
 
@@ -95,6 +99,9 @@ def test_named_general_geometry(wl):
     info = call.plan_info()
     if wl.epi == W.EPI_SOFTMAX_SIGMOID:
         assert info["softmax_pass"] == 1
+    if wl.epi != W.EPI_SCALE_BN_EVAL_AVGPOOL:
+        want = 1 if wl.n * wl.conv_groups <= 65535 else wl.conv_groups
+        assert info["conv_launches"] == want
 
 
 # every compiled variant on one dilated, grouped geometry (w-stride 2 so the
