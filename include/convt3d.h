@@ -172,7 +172,8 @@ size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *
  *              than 128 channels or with groups > 1 (then one workgroup's tile
  *              does not hold every channel) it stages y, which a second pass
  *              turns into the result in place.
- * With groups > 1 the convolution kernel runs once per group.
+ * With groups > 1 one convolution launch covers every (sample, group) pair
+ * (one launch per group when n * groups exceeds 65535).
  *   workspace  device scratch of at least convt3d_workspace_size bytes.
  * Enqueues 1 to 3 kernels on stream and returns without waiting. */
 int convt3d_fused(const float *x, const void *w_packed, const float *bias,
