@@ -119,12 +119,21 @@ WORKLOADS = [
              note="stride-2 k4 GroupNorm(16) case at 128 channels"),
 ]
 
-# Further cases beyond the five: the p77 shape with BatchNorm in evaluation
-# mode (running statistics), seeded like the p77 case.
+# Further cases beyond the five, each on one of the pages' shapes: the p77
+# layer with BatchNorm in evaluation mode (running statistics); the p61 layer
+# with 4 channel groups and dilation 2 (nn.ConvTranspose3d's general form);
+# the p49 layer with 256 output channels (more than one workgroup's softmax
+# tile, so the softmax runs as a second pass).
 EXTRA_WORKLOADS = [
     Workload("k5s1_bnpool_eval", 16, 64, 128, 16, 32, 32, k=5, stride=1, pad=0, bias=True,
              epi=EPI_SCALE_BN_EVAL_AVGPOOL, scale=2.0, seed=20264,
              note="p77 page shape with BatchNorm3d in eval mode (running statistics)"),
+    Workload("k3s1_gn_g4_dl2", 16, 64, 128, 32, 32, 32, k=3, stride=1, pad=0, bias=False,
+             epi=EPI_RELU_GROUPNORM, groups=8, seed=20266, dilation=2, conv_groups=4,
+             note="p61 page shape with groups=4 and dilation=2"),
+    Workload("k3s2_softmax_c256", 16, 32, 256, 16, 32, 32, k=3, stride=2, pad=1, out_pad=1, bias=True,
+             epi=EPI_SOFTMAX_SIGMOID, seed=20267,
+             note="p49 page shape with 256 output channels (softmax as a second pass)"),
 ]
 
 BY_NAME = {wl.name: wl for wl in WORKLOADS + EXTRA_WORKLOADS}

@@ -112,7 +112,9 @@ def torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, fused_ms, reps
     rv_t = None if rvar is None else rvar.clone()
 
     def conv():
-        return F.conv_transpose3d(x, w, b, stride=wl.stride, padding=wl.pad, output_padding=wl.out_pad)
+        return F.conv_transpose3d(x, w, b, stride=W.triple(wl.stride), padding=W.triple(wl.pad),
+                                  output_padding=W.triple(wl.out_pad), groups=wl.conv_groups,
+                                  dilation=W.triple(wl.dilation))
 
     def tail(y):
         if wl.epi == W.EPI_RELU_GROUPNORM:
