@@ -16,7 +16,9 @@ from gpu_helpers import TOL, max_err, run_gpu, say
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-NAMES = ["k3s1_gn", "k3s2_softmax", "k5s1_bnpool", "k4s2_gn"]
+# the four conv workloads, then the two general-geometry ones (the p61 layer
+# with 4 groups and dilation 2; the p49 layer with 256 channels)
+NAMES = ["k3s1_gn", "k3s2_softmax", "k5s1_bnpool", "k4s2_gn", "k3s1_gn_g4_dl2", "k3s2_softmax_c256"]
 
 
 def load_golden(name):
