@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const V *y, int rows, in
 // running max m and sum l of exp(v - m) over the channels, four channels per
 // rescale; pass 2 reads the channels again and writes 1/(1 + exp(-p)) with
 // p = exp(v - m) / l.  out may equal src.
-template <class V>
+template <class V, bool NT>
 __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out, int N, int C, int S) {
     const int s = blockIdx.x * 256 + threadIdx.x;
     if (s >= S) return;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out,
         for (; c + 4 <= C; c += 4) {
             V v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = p[(size_t)(c + j) * S];
+            for (int j = 0; j < 4; ++j) v[j] = load_stream<NT>(p + (size_t)(c + j) * S);
 #pragma unroll
             for (int e = 0; e < NC; ++e) {
                 const float a0 = comps(v[0])[e], a1 = comps(v[1])[e], a2 = comps(v[2])[e], a3 = comps(v[3])[e];
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out,
             }
         }
         for (; c < C; ++c) {
-            V v = p[(size_t)c * S];
+            V v = load_stream<NT>(p + (size_t)c * S);
 #pragma unroll
             for (int e = 0; e < NC; ++e) {
                 const float a = comps(v)[e];
@@ -321,14 +321,14 @@ __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out,
 #pragma unroll
         for (int e = 0; e < NC; ++e) inv[e] = __builtin_amdgcn_rcpf(l[e]);
         for (c = 0; c < C; ++c) {
-            V v = p[(size_t)c * S];
+            V v = load_stream<NT>(p + (size_t)c * S);
             float *a = comps(v);
 #pragma unroll
             for (int e = 0; e < NC; ++e) {
                 const float pr = fast_exp(a[e] - m[e]) * inv[e];
                 a[e] = __builtin_amdgcn_rcpf(1.0f + fast_exp(-pr));
             }
-            o[(size_t)c * S] = v;
+            store_stream<NT>(o + (size_t)c * S, v);
         }
     }
 }
@@ -635,15 +635,27 @@ int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, v
             hipLaunchKernelGGL(softmax_regs_kernel<64>, grid, dim3(256), 0, (hipStream_t)stream, src, out, N, C, len);
         return (int)hipGetLastError();
     }
+    const bool nt = (double)N * C * (double)S * sizeof(float) > (double)kStreamBytes;
     if (S % 4 == 0) {
         const int len = (int)(S / 4);
-        hipLaunchKernelGGL(softmax_pass_kernel<float4>, dim3((len + 255) / 256, gy), dim3(256), 0,
-                           (hipStream_t)stream, reinterpret_cast<const float4 *>(src),
-                           reinterpret_cast<float4 *>(out), N, C, len);
+        const dim3 grid((len + 255) / 256, gy);
+        const float4 *s4 = reinterpret_cast<const float4 *>(src);
+        float4 *o4 = reinterpret_cast<float4 *>(out);
+        if (nt)
+            hipLaunchKernelGGL((softmax_pass_kernel<float4, true>), grid, dim3(256), 0, (hipStream_t)stream, s4, o4, N,
+                               C, len);
+        else
+            hipLaunchKernelGGL((softmax_pass_kernel<float4, false>), grid, dim3(256), 0, (hipStream_t)stream, s4, o4,
+                               N, C, len);
     } else {
         const int len = (int)S;
-        hipLaunchKernelGGL(softmax_pass_kernel<float>, dim3((len + 255) / 256, gy), dim3(256), 0,
-                           (hipStream_t)stream, src, out, N, C, len);
+        const dim3 grid((len + 255) / 256, gy);
+        if (nt)
+            hipLaunchKernelGGL((softmax_pass_kernel<float, true>), grid, dim3(256), 0, (hipStream_t)stream, src, out,
+                               N, C, len);
+        else
+            hipLaunchKernelGGL((softmax_pass_kernel<float, false>), grid, dim3(256), 0, (hipStream_t)stream, src, out,
+                               N, C, len);
     }
     return (int)hipGetLastError();
 }
