@@ -255,15 +255,22 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
 
+    # per-step events on the launch stream give the median step time
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     C.convt3d_profile_begin()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     prof = C.convt3d_profile_end()
     ms = (t1 - t0) * 1e3 / args.steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     gflops = flops / (ms * 1e-3) / 1e9
     print(f"[bench] timed region done: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
@@ -306,9 +313,14 @@ def main():
     kernels = {k: round(prof[k] / calls, 4)
                for k in ("conv_ms", "finalize_ms", "normalize_ms", "reduce_ms", "prepack_ms")}
     if prof["normalize_ms"] > 0:
-        norm_bytes = 2.0 * 4 * call.out.numel()  # read + write of the output
+        # the output pass moves |y| per read and per write: GroupNorm's
+        # normalise and the register-held softmax read once and write once;
+        # the softmax over more than 64 channels reads twice
+        passes = 3 if (wl.epi == W.EPI_SOFTMAX_SIGMOID and wl.cout > 64) else 2
+        norm_bytes = passes * 4.0 * call.out.numel()
         kernels["normalize_GBps"] = round(norm_bytes / (kernels["normalize_ms"] * 1e-3) / 1e9, 1)
         kernels["normalize_frac_hbm"] = round(kernels["normalize_GBps"] / PEAK_HBM_GBS, 4)
+        kernels["normalize_y_passes"] = passes
 
     comparison = torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, ms) if args.compare_torch else None
 
@@ -350,6 +362,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(ms_median, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
