@@ -150,12 +150,17 @@ int timed(int kind, void *stream, F fn) {
         on = g_prof_on;
         if (on) { b = prof_event(); e = prof_event(); }
     }
-    if (on && b && e) hipEventRecord(b, (hipStream_t)stream);
+    // a failed record only loses this timing entry (measurement, not results)
+    const bool rec = on && b && e && hipEventRecord(b, (hipStream_t)stream) == hipSuccess;
     const int rc = fn();
     if (on && b && e) {
-        hipEventRecord(e, (hipStream_t)stream);
         std::lock_guard<std::mutex> lk(g_prof_mu);
-        g_prof_used.push_back(Timed{kind, b, e});
+        if (rec && hipEventRecord(e, (hipStream_t)stream) == hipSuccess) {
+            g_prof_used.push_back(Timed{kind, b, e});
+        } else {
+            g_prof_pool.push_back(b);
+            g_prof_pool.push_back(e);
+        }
     }
     return rc;
 }
@@ -406,7 +411,7 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     epi = &quiet;
     hipEvent_t b = nullptr, e = nullptr;
     if (hipEventCreate(&b) != hipSuccess || hipEventCreate(&e) != hipSuccess) {
-        if (b) hipEventDestroy(b);
+        if (b) (void)hipEventDestroy(b);  // cleanup on an error path
         return CONVT3D_ERR_LAUNCH;
     }
     // Clocks ramp up under load and single timings jitter by a few per cent,
@@ -417,13 +422,13 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     constexpr int kRounds = 3;
     const bool log = std::getenv("CONVT3D_TUNE_LOG") != nullptr;  // one stderr line per candidate
     auto time_calls = [&](Plan &pl, int calls, float *ms) {
-        hipEventRecord(b, (hipStream_t)stream);
+        if (hipEventRecord(b, (hipStream_t)stream) != hipSuccess) return (int)CONVT3D_ERR_LAUNCH;
         for (int r = 0; r < calls; ++r) {
             const int rc = run_plan(pl, x, w_packed, bias, epi, out, workspace, stream);
             if (rc) return rc;
         }
-        hipEventRecord(e, (hipStream_t)stream);
-        if (hipEventSynchronize(e) != hipSuccess || hipEventElapsedTime(ms, b, e) != hipSuccess)
+        if (hipEventRecord(e, (hipStream_t)stream) != hipSuccess || hipEventSynchronize(e) != hipSuccess ||
+            hipEventElapsedTime(ms, b, e) != hipSuccess)
             return (int)CONVT3D_ERR_LAUNCH;
         *ms /= calls;
         return (int)CONVT3D_OK;
@@ -435,8 +440,8 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
             fit.push_back((int)i);  // else it needs more workspace than the caller gave
     }
     if (fit.empty()) {
-        hipEventDestroy(b);
-        hipEventDestroy(e);
+        (void)hipEventDestroy(b);  // cleanup; the status reports the real problem
+        (void)hipEventDestroy(e);
         return CONVT3D_ERR_WORKSPACE;
     }
     float est = 0.0f;
@@ -468,8 +473,8 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     }
     const int timed_n = (int)fit.size();
     const float best_ms = best_of[best], first_ms = best_of[fit[0]];
-    hipEventDestroy(b);
-    hipEventDestroy(e);
+    (void)hipEventDestroy(b);  // cleanup: a failure here does not change the result
+    (void)hipEventDestroy(e);
     if (st) return st;
     if (best < 0) return CONVT3D_ERR_WORKSPACE;  // no candidate fits the workspace
     store_tuned(geom, epi, cands[best]);

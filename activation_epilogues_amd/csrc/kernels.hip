@@ -19,7 +19,9 @@
 // output channels, columns are output voxels, k runs over (input channel, tap).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
+#include <cstdint>
 
 #include "convt3d_internal.hpp"
 
@@ -707,11 +709,18 @@ int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream) {
 template <int CBW, int NPH, int PBW, bool SM, bool PL>
 static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
     auto fn = convt3d_mfma_kernel<CBW, NPH, PBW, SM, PL>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kMaxLdsBytes);
-        attr_set = true;
+    // the dynamic-LDS limit is a per-device attribute of the function: set it
+    // once on every device the kernel runs on (bit d: done on device d)
+    static std::atomic<uint64_t> attr_done{0};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return (int)err;
+    const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+    if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kMaxLdsBytes);
+        if (err != hipSuccess) return (int)err;
+        attr_done.fetch_or(bit, std::memory_order_acq_rel);
     }
     hipLaunchKernelGGL(fn, dim3((unsigned)pl.grid_x, (unsigned)pl.grid_y, (unsigned)pl.grid_z),
                        dim3(kBlockThreads), pl.lds_bytes, (hipStream_t)stream, cp);
