@@ -395,8 +395,20 @@ __device__ __forceinline__ int bin_of(const EvalGeom &E, int b, int dim) {
 }
 
 // Wb[co][ci_local][bin] (ci_local: input channel within co's group): one
-// wave per weight row [ci][co_local] of kD*kH*kW taps.
+// wave per weight row [ci][co_local] of kD*kH*kW taps.  The workgroup first
+// turns the bin tables into one bit mask per (dim, tap) in LDS: bit j set when
+// bin j of that dim lies in the tap's input range.
 __global__ __launch_bounds__(256) void eval_pack_kernel(const EvalGeom E, const float *w, float *wb) {
+    __shared__ unsigned long long mask[3][kEvalMaxK];
+    for (int i = threadIdx.x; i < 3 * kEvalMaxK; i += blockDim.x) {
+        const int d = i / kEvalMaxK, t = i - d * kEvalMaxK;
+        unsigned long long m = 0;
+        if (t < E.k3[d])
+            for (int j = 0; j < E.nb[d]; ++j)
+                if (E.lo[d][t] <= E.cut[d][j] && E.cut[d][j + 1] <= E.hi1[d][t]) m |= 1ull << j;
+        mask[d][t] = m;
+    }
+    __syncthreads();
     const int pair = blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // ci*cog + co_local
     const int lane = threadIdx.x & 63;
     if (pair >= E.Cin * E.cog) return;
@@ -409,10 +421,7 @@ __global__ __launch_bounds__(256) void eval_pack_kernel(const EvalGeom E, const 
         double acc = 0.0;
         for (int t = lane; t < kk; t += 64) {
             const int td = t / khw, th = (t / kw_) % kh_, tw = t % kw_;
-            const bool in = E.lo[0][td] <= E.cut[0][bd] && E.cut[0][bd + 1] <= E.hi1[0][td] &&
-                            E.lo[1][th] <= E.cut[1][bh] && E.cut[1][bh + 1] <= E.hi1[1][th] &&
-                            E.lo[2][tw] <= E.cut[2][bw] && E.cut[2][bw + 1] <= E.hi1[2][tw];
-            if (in) acc += (double)row[t];
+            if ((mask[0][td] >> bd) & (mask[1][th] >> bh) & (mask[2][tw] >> bw) & 1ull) acc += (double)row[t];
         }
         for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
         if (lane == 0) wb[((size_t)co * E.cig + cil) * E.nbins + b] = (float)acc;
