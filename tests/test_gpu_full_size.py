@@ -1,5 +1,7 @@
-"""GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (same geometry -> same plan).  Expected values were written by
+"""GPU parity at the full workload sizes: with the cost model's first plan
+(what convt3d_fused runs before any tuning) and with the plan convt3d_autotune
+picks on the full-size buffers (the launch configuration the benchmark times,
+since bench.py tunes before its warm-up).  Expected values were written by
 tests/golden/make_full_size_golden.py, which runs only the fp64 oracle:
 sampled voxels of the raw convolution and of the final output, the exported
 statistics, and for the pooled BatchNorm path the whole [n, cout] output.
@@ -82,3 +84,50 @@ def test_full_size_raw_convolution(name):
     raw, _, _ = run_gpu(wl.with_(epi=W.EPI_NONE), inp, kind=W.EPI_NONE, want_stats=False)
     idx = g["sample_index"]
     assert max_err(raw[tuple(idx.T)], g["raw_at_samples"]) <= TOL
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_tuned_plan(name):
+    """The plan the benchmark times: convt3d_autotune on the full-size buffers
+    (as bench.py calls it before its warm-up), then one fused call, checked at
+    the golden's sampled voxels (gathered on the device) and on its statistics.
+    Runs after the default-plan tests above: the tuned plan is kept for the
+    rest of the process."""
+    import torch
+    from activation_epilogues_amd import convt3d as C
+    from gpu_helpers import geom_of, to_dev
+    wl = W.BY_NAME[name]
+    g = load_golden(name)
+    inp = W.make_inputs(wl)
+    check_inputs(g, inp)
+    say(f"[case] full-size tuned plan {name} x={wl.x_shape}")
+    call = C.FusedCall(geom_of(wl), wl.epi, wl.groups, wl.eps, wl.scale, want_stats=True)
+    x, w, b = to_dev(inp.x), to_dev(inp.w), to_dev(inp.b)
+    gamma, beta = to_dev(inp.gamma), to_dev(inp.beta)
+    call.prepack(w)
+    res = call.autotune(x, b, gamma, beta)
+    info = call.plan_info()
+    say(f"  tuned: chosen {res['chosen']} of {res['candidates']}, plan {C.plan_string(info)} "
+        f"phase_loop {info['phase_loop']}")
+    assert info["tuned"] == 1
+    call.out.fill_(float("nan"))
+    if call.stats is not None:
+        call.stats.fill_(float("nan"))
+    out = call(x, b, gamma, beta)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    st = None if call.stats is None else call.stats.cpu().numpy()
+    if wl.epi == W.EPI_SCALE_BN_TRAIN_AVGPOOL:
+        o2 = out.reshape(wl.n, wl.cout).cpu().numpy()
+        assert max_err(o2, g["out"]) <= TOL
+        np.testing.assert_allclose(st[:, 0], g["stats"][:, 0], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(st[:, 1], g["stats"][:, 1], rtol=1e-5, atol=1e-6)
+        return
+    idx = torch.from_numpy(np.ascontiguousarray(g["sample_index"])).to(out.device, torch.long)
+    got = out[tuple(idx[:, i] for i in range(idx.shape[1]))].cpu().numpy()
+    assert max_err(got, g["out_at_samples"]) <= TOL
+    if wl.epi == W.EPI_RELU_GROUPNORM:
+        np.testing.assert_allclose(st[..., 0], g["stats"][..., 0], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(st[..., 1], g["stats"][..., 1], rtol=1e-5, atol=1e-6)
+    if wl.epi == W.EPI_SOFTMAX_SIGMOID:
+        assert float(out.min()) > 0.5 and float(out.max()) <= 1.0 / (1.0 + np.exp(-1.0)) + 1e-6
