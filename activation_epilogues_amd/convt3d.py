@@ -112,6 +112,8 @@ def lib():
         L.convt3d_get_plan_info.argtypes = [P(Geom), P(Epilogue), P(PlanInfo)]
         L.convt3d_profile_begin.restype = ctypes.c_int
         L.convt3d_profile_begin.argtypes = []
+        L.convt3d_profile_begin_kinds.restype = ctypes.c_int
+        L.convt3d_profile_begin_kinds.argtypes = [ctypes.c_uint32]
         L.convt3d_profile_end.restype = ctypes.c_int
         L.convt3d_profile_end.argtypes = [P(Profile)]
         _lib = L
@@ -122,7 +124,7 @@ EXPORTED = ["convt3d_status_string", "convt3d_output_dims", "convt3d_output_elem
             "convt3d_packed_weight_bytes", "convt3d_prepack_weights", "convt3d_eval_weight_bytes",
             "convt3d_prepack_eval_weights", "convt3d_workspace_size", "convt3d_fused", "convt3d_autotune",
             "convt3d_epilogue_workspace_size", "convt3d_epilogue_only", "convt3d_get_plan_info",
-            "convt3d_profile_begin", "convt3d_profile_end"]
+            "convt3d_profile_begin", "convt3d_profile_begin_kinds", "convt3d_profile_end"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -260,6 +262,16 @@ def convt3d_profile_begin() -> None:
     st = lib().convt3d_profile_begin()
     if st:
         raise Convt3dError(st, "convt3d_profile_begin")
+
+
+PROFILE_CONV, PROFILE_FINALIZE, PROFILE_NORMALIZE, PROFILE_REDUCE, PROFILE_PREPACK = 0x1, 0x2, 0x4, 0x8, 0x10
+PROFILE_ALL = 0x1F
+
+
+def convt3d_profile_begin_kinds(kinds: int) -> None:
+    st = lib().convt3d_profile_begin_kinds(kinds)
+    if st:
+        raise Convt3dError(st, "convt3d_profile_begin_kinds")
 
 
 def convt3d_profile_end() -> dict:

@@ -125,6 +125,7 @@ struct Timed {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+uint32_t g_prof_kinds = CONVT3D_PROFILE_ALL;  // bit k: record TimedKind k
 int g_prof_calls = 0;
 std::vector<Timed> g_prof_used;
 std::vector<hipEvent_t> g_prof_pool;
@@ -147,7 +148,7 @@ int timed(int kind, void *stream, F fn) {
     bool on;
     {
         std::lock_guard<std::mutex> lk(g_prof_mu);
-        on = g_prof_on;
+        on = g_prof_on && ((g_prof_kinds >> kind) & 1u);
         if (on) { b = prof_event(); e = prof_event(); }
     }
     // a failed record only loses this timing entry (measurement, not results)
@@ -586,8 +587,16 @@ int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
     return CONVT3D_OK;
 }
 
-int convt3d_profile_begin(void) {
+int convt3d_profile_begin(void) { return convt3d_profile_begin_kinds(CONVT3D_PROFILE_ALL); }
+
+int convt3d_profile_begin_kinds(uint32_t kinds) {
+    if (kinds == 0 || (kinds & ~CONVT3D_PROFILE_ALL) != 0) return CONVT3D_ERR_UNSUPPORTED;
+    static_assert(CONVT3D_PROFILE_CONV == 1u << kTimedConv && CONVT3D_PROFILE_FINALIZE == 1u << kTimedFinalize &&
+                      CONVT3D_PROFILE_NORMALIZE == 1u << kTimedNormalize &&
+                      CONVT3D_PROFILE_REDUCE == 1u << kTimedReduce && CONVT3D_PROFILE_PREPACK == 1u << kTimedPrepack,
+                  "profile mask bits follow the timed kinds");
     std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_kinds = kinds;
     for (auto &t : g_prof_used) {
         g_prof_pool.push_back(t.beg);
         g_prof_pool.push_back(t.end);

@@ -262,7 +262,23 @@ typedef struct convt3d_profile {
     double prepack_ms;    /* convt3d_prepack_weights / _eval_weights kernels      */
 } convt3d_profile;
 
+/* Kernel kinds convt3d_profile_begin_kinds records (bit mask); the fields of
+ * convt3d_profile in the same order. */
+#define CONVT3D_PROFILE_CONV 0x1u      /* conv_ms      */
+#define CONVT3D_PROFILE_FINALIZE 0x2u  /* finalize_ms  */
+#define CONVT3D_PROFILE_NORMALIZE 0x4u /* normalize_ms */
+#define CONVT3D_PROFILE_REDUCE 0x8u    /* reduce_ms    */
+#define CONVT3D_PROFILE_PREPACK 0x10u  /* prepack_ms   */
+#define CONVT3D_PROFILE_ALL 0x1Fu
+
+/* convt3d_profile_begin() records every kernel kind.  An event pair in the
+ * stream costs a few microseconds per kernel, so a timed region that wants its
+ * step time undisturbed records only the kind it needs:
+ * convt3d_profile_begin_kinds(mask) records the kernels of the kinds in `mask`
+ * (a nonzero subset of CONVT3D_PROFILE_ALL, else CONVT3D_ERR_UNSUPPORTED and
+ * nothing changes); the fields of the other kinds stay 0. */
 int convt3d_profile_begin(void);
+int convt3d_profile_begin_kinds(uint32_t kinds);
 int convt3d_profile_end(convt3d_profile *out);
 
 #ifdef __cplusplus

@@ -374,3 +374,18 @@ def test_plan_cache_keys_on_every_override(monkeypatch):
     assert C.convt3d_get_plan_info(g, e)["xcd_order"] == 0
     monkeypatch.setenv("CONVT3D_ORDER", "1")
     assert C.convt3d_get_plan_info(g, e)["xcd_order"] == 1
+
+def test_profile_kind_mask_is_checked():
+    """convt3d_profile_begin_kinds takes a nonzero subset of the kernel kinds;
+    a session with nothing recorded ends with every duration 0."""
+    lib = C.lib()
+    assert lib.convt3d_profile_begin_kinds(0) == 6
+    assert lib.convt3d_profile_begin_kinds(0x20) == 6
+    assert lib.convt3d_profile_begin_kinds(0xFFFFFFFF) == 6
+    for mask in (C.PROFILE_CONV, C.PROFILE_REDUCE | C.PROFILE_PREPACK, C.PROFILE_ALL):
+        C.convt3d_profile_begin_kinds(mask)
+        prof = C.convt3d_profile_end()
+        assert prof["calls"] == 0
+        assert all(prof[k] == 0.0 for k in ("conv_ms", "finalize_ms", "normalize_ms", "reduce_ms", "prepack_ms"))
+    assert lib.convt3d_profile_begin() == 0
+    assert C.convt3d_profile_end()["calls"] == 0
