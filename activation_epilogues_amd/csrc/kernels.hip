@@ -107,9 +107,12 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // group's channels (Cout_total is the row stride); when that grid would be too
 // tall the host launches once per group with offset pointers and G = 1.
 template <int CBW, int NPH, int PBW, bool SM, bool PL>
+// Minimum waves per SIMD: the register budget of each variant.  Four position
+// blocks of one co block (64 accumulators, 16 B registers) take 134 VGPRs, so
+// that variant runs three waves per SIMD: held to four it spilled in its chunk
+// prologue and ran 1.5-2 % slower.
 __global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
                                           : (CBW * NPH * PBW <= 2) ? 6
-                                          : (CBW * NPH * PBW == 4 && PBW == 4) ? 4
                                           : (CBW * NPH * PBW <= 4) ? 3
                                           : (CBW * NPH * PBW <= 8) ? 2 : 1)
 void convt3d_mfma_kernel(const ConvParams P) {
