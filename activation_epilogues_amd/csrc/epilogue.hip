@@ -32,6 +32,11 @@ namespace convt3d {
 namespace {
 
 constexpr int kNormUnroll = 4;        // loads in flight per thread in the HBM passes
+// Statistics merges: one workgroup per (n, group) or per channel reads all of
+// its partial sums.  Few workgroups, so each needs many bytes in flight:
+// 1024 threads with 8 partial-sum pairs in flight each.
+constexpr int kStatThreads = 1024;
+constexpr int kStatUnroll = 8;
 constexpr int64_t kStreamBytes = int64_t(512) << 20;  // above this a pass streams past the 256 MB cache
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -65,7 +70,7 @@ constexpr int ncomp() { return (int)(sizeof(V) / sizeof(float)); }
 // partials (layout [n][tile][C][2]) in a fixed order, then mean, biased
 // variance E[r^2] - mean^2, rstd = 1/sqrt(var + eps), and per channel
 // a = gamma*rstd, b = beta - mean*a.
-__global__ __launch_bounds__(256) void gn_finalize_kernel(const float *partials, int tiles_per_n, int C,
+__global__ __launch_bounds__(kStatThreads) void gn_finalize_kernel(const float *partials, int tiles_per_n, int C,
                                                           int G, float eps, const float *gamma,
                                                           const float *beta, float *ab, float *stats_out,
                                                           double count) {
@@ -73,13 +78,25 @@ __global__ __launch_bounds__(256) void gn_finalize_kernel(const float *partials,
     const int cpg = C / G;
     const int items = tiles_per_n * cpg;
     double a1 = 0.0, a2 = 0.0;
-    for (int i = threadIdx.x; i < items; i += blockDim.x) {
-        const int t = i / cpg, cc = i - t * cpg;
-        const float *pp = partials + (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2;
-        a1 += (double)pp[0];
-        a2 += (double)pp[1];
+    for (int i0 = threadIdx.x; i0 < items; i0 += blockDim.x * kStatUnroll) {
+        float2 v[kStatUnroll];
+#pragma unroll
+        for (int u = 0; u < kStatUnroll; ++u) {
+            const int i = i0 + u * (int)blockDim.x;
+            v[u] = make_float2(0.0f, 0.0f);
+            if (i < items) {
+                const int t = i / cpg, cc = i - t * cpg;
+                v[u] = *reinterpret_cast<const float2 *>(partials +
+                                                          (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kStatUnroll; ++u) {
+            a1 += (double)v[u].x;
+            a2 += (double)v[u].y;
+        }
     }
-    __shared__ double r1[256], r2[256];
+    __shared__ double r1[kStatThreads], r2[kStatThreads];
     __shared__ double mean_s, rstd_s;
     r1[threadIdx.x] = a1;
     r2[threadIdx.x] = a2;
@@ -180,19 +197,28 @@ __global__ __launch_bounds__(256) void normalize_kernel(const V *src, V *out, co
 // is [n][tile][C][2] of (sum z, sum z^2) with z = scale * y.  Writes the
 // pooled [n, C] output, the batch statistics and, when both buffers are
 // given, the running statistics (unbiased variance folded in).
-__global__ __launch_bounds__(256) void bn_finalize_kernel(const float *partials, int N, int tiles_per_n, int C,
+__global__ __launch_bounds__(kStatThreads) void bn_finalize_kernel(const float *partials, int N, int tiles_per_n, int C,
                                                           double S, float eps, const float *gamma,
                                                           const float *beta, float *out, float *stats_out,
                                                           float momentum, float *rmean, float *rvar) {
     const int c = blockIdx.x;
     double a1 = 0.0, a2 = 0.0;
     const int items = N * tiles_per_n;
-    for (int i = threadIdx.x; i < items; i += blockDim.x) {
-        const float *pp = partials + ((size_t)i * C + c) * 2;  // i = n*tiles_per_n + t
-        a1 += (double)pp[0];
-        a2 += (double)pp[1];
+    for (int i0 = threadIdx.x; i0 < items; i0 += blockDim.x * kStatUnroll) {
+        float2 v[kStatUnroll];
+#pragma unroll
+        for (int u = 0; u < kStatUnroll; ++u) {
+            const int i = i0 + u * (int)blockDim.x;  // i = n*tiles_per_n + t
+            v[u] = i < items ? *reinterpret_cast<const float2 *>(partials + ((size_t)i * C + c) * 2)
+                             : make_float2(0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < kStatUnroll; ++u) {
+            a1 += (double)v[u].x;
+            a2 += (double)v[u].y;
+        }
     }
-    __shared__ double r1[256], r2[256];
+    __shared__ double r1[kStatThreads], r2[kStatThreads];
     __shared__ double mean_s, rstd_s;
     r1[threadIdx.x] = a1;
     r2[threadIdx.x] = a2;
@@ -224,11 +250,17 @@ __global__ __launch_bounds__(256) void bn_finalize_kernel(const float *partials,
     __syncthreads();
     const double ga = gamma ? (double)gamma[c] : 1.0;
     const double be = beta ? (double)beta[c] : 0.0;
-    for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    // pooled output: one wave per sample sums that sample's tile partials
+    // (lane l takes tiles l, l + 64, ...; then a fixed xor-shuffle tree)
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int n0 = 0; n0 < N; n0 += (int)blockDim.x >> 6) {
+        const int n = n0 + wave;  // uniform within the wave
         double m = 0.0;
-        for (int t = 0; t < tiles_per_n; ++t) m += (double)partials[(((size_t)n * tiles_per_n + t) * C + c) * 2];
-        m /= S;
-        out[(size_t)n * C + c] = (float)((m - mean_s) * rstd_s * ga + be);
+        if (n < N)
+            for (int t = lane; t < tiles_per_n; t += 64)
+                m += (double)partials[(((size_t)n * tiles_per_n + t) * C + c) * 2];
+        for (int off = 32; off > 0; off >>= 1) m += __shfl_xor(m, off);
+        if (n < N && lane == 0) out[(size_t)n * C + c] = (float)((m / S - mean_s) * rstd_s * ga + be);
     }
 }
 
@@ -554,8 +586,8 @@ __global__ __launch_bounds__(256) void eval_finalize_kernel(const EvalGeom E, co
 
 int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, double count, float eps,
                        const float *gamma, const float *beta, float *ab, float *stats_out, void *stream) {
-    hipLaunchKernelGGL(gn_finalize_kernel, dim3(N * G), dim3(256), 0, (hipStream_t)stream, partials, tiles_per_n,
-                       C, G, eps, gamma, beta, ab, stats_out, count);
+    hipLaunchKernelGGL(gn_finalize_kernel, dim3(N * G), dim3(kStatThreads), 0, (hipStream_t)stream, partials,
+                       tiles_per_n, C, G, eps, gamma, beta, ab, stats_out, count);
     return (int)hipGetLastError();
 }
 
@@ -594,8 +626,8 @@ int launch_normalize(const float *src, float *out, const float *ab, int rows, in
 
 int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,
                        float *out, void *stream) {
-    hipLaunchKernelGGL(bn_finalize_kernel, dim3(C), dim3(256), 0, (hipStream_t)stream, partials, N, tiles_per_n,
-                       C, S, e.eps, e.gamma, e.beta, out, e.stats_out, e.momentum, e.running_mean,
+    hipLaunchKernelGGL(bn_finalize_kernel, dim3(C), dim3(kStatThreads), 0, (hipStream_t)stream, partials, N,
+                       tiles_per_n, C, S, e.eps, e.gamma, e.beta, out, e.stats_out, e.momentum, e.running_mean,
                        e.running_var);
     return (int)hipGetLastError();
 }
