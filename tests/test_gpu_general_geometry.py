@@ -120,3 +120,26 @@ def test_forced_variants_general(vi, ploop, monkeypatch):
     info = C.convt3d_get_plan_info(geom_of(wl), C.make_epilogue(wl.epi, wl.groups))
     assert info["variant"] == vi and info["phase_loop"] == ploop
     run_and_check(wl)
+
+
+def test_random_general_geometry_sweep():
+    """600 more random geometries (every epilogue, up to 48 channels and 16
+    voxels per side), run in one test; every failing case is listed."""
+    plan = [(200, 9101, 8, 12), (200, 9102, 12, 24), (200, 9103, 16, 48)]
+    fails = []
+    for count, seed, max_in, max_ch in plan:
+        rng = np.random.default_rng(seed)
+        done = 0
+        while done < count:
+            kind = KINDS[done % len(KINDS)]
+            wl = W.random_general_geometry(rng, max_in=max_in, max_ch=max_ch, epi=kind)
+            if min(out_dims(wl)) <= 0:
+                continue
+            wl = wl.with_(name=f"sweep{seed}_{done}")
+            done += 1
+            try:
+                run_and_check(wl)
+            except AssertionError as e:
+                fails.append(f"{describe(wl)}: {str(e)[:200]}")
+        say(f"[case] sweep seed {seed}: {count} geometries, {len(fails)} failures so far")
+    assert not fails, "\n".join(fails)
