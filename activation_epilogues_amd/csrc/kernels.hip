@@ -515,17 +515,28 @@ void convt3d_mfma_kernel(const ConvParams P) {
     auto bias_of = [&](int c, int r, float dflt) {  // bias of the lane's row c, r (dflt: no bias)
         return P.bias ? P.bias[grp * Cout + row_u(c, r) + 4 * half] : dflt;
     };
-    // the stores of one accumulator row (c, r) of position block pb
+    // the stores of one accumulator row (c, r) of position block pb.  The
+    // softmax kernels write the final output, which nothing here reads again:
+    // non-temporal stores (2 % faster on the 64-channel stride-2 layer); the
+    // other kernels' y is read back by the normalise pass and stays cached.
     auto store_row = [&](char *rp, int pb, const float (&v)[NPH]) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
         if constexpr (NPH == 2) {
             if (pair_ok[pb]) {
-                *reinterpret_cast<float2 *>(rp + vofs[0][pb]) = make_float2(v[0], v[1]);
+                f2 *dst = reinterpret_cast<f2 *>(rp + vofs[0][pb]);
+                const f2 val = {v[0], v[1]};
+                if constexpr (SM) __builtin_nontemporal_store(val, dst);
+                else *dst = val;
                 return;
             }
         }
 #pragma unroll
         for (int p = 0; p < NPH; ++p)
-            if (ok[p][pb]) *reinterpret_cast<float *>(rp + vofs[p][pb]) = v[p];
+            if (ok[p][pb]) {
+                float *dst = reinterpret_cast<float *>(rp + vofs[p][pb]);
+                if constexpr (SM) __builtin_nontemporal_store(v[p], dst);
+                else *dst = v[p];
+            }
     };
 
     if constexpr (SM) {
