@@ -223,6 +223,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
     // with one 16-byte LDS read, and the 32 lanes of a k-row read consecutive
     // float4s along w (no bank conflicts).
     const int SLAB = HD * HH * HW;  // halo positions per octet
+    const int slab2 = __builtin_amdgcn_readfirstlane(2 * SLAB);  // B offset per octet pair, scalar
     const int vol = TQd * TQh * TQw;
     const int plane = TQh * TQw;
     // The tile position of a lane's column in position block pb; decoded again
@@ -356,11 +357,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 const int ph = (rho_d * sh + rho_h) * sw + rw[p];
                 const int ntp = P.ntaps[ph];
                 const int jwl = jw_lo[p], jwh = jw_hi[p], jwn = Jw[p], cwp = cw[p];
+                // uniform base of each co block's packed weights: the group's A
+                // operands are (base + group)[lane], a scalar base plus a fixed
+                // per-lane offset
                 const float4 *wb[CBW];
 #pragma unroll
                 for (int c = 0; c < CBW; ++c) {
                     const int cb = min(cb0 + c, P.cb_total - 1);
-                    wb[c] = wp4 + (P.wp_off[ph] >> 2) + (size_t)cb * P.steps4[ph] * 64 + lane;
+                    wb[c] = wp4 + (P.wp_off[ph] >> 2) + (size_t)cb * P.steps4[ph] * 64;
                 }
                 const int n_it = (jd_hi - jd_lo + 1) * (jh_hi - jh_lo + 1) * (jwh - jwl + 1) * G4;
                 // Iteration state (jd, jh, jw, g4) of the next group to load; every
@@ -370,7 +374,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 auto next_group = [&](int &gi, int &bo) {
                     gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
                     bo = ((cd - ed * jd - lo_d_rel) * HH + (ch - eh * jh - lo_h_rel)) * HW +
-                         (cwp - ew * jw - lo_w_rel) + 2 * g4 * SLAB;
+                         (cwp - ew * jw - lo_w_rel) + g4 * slab2;
                     if (++g4 == G4) {
                         g4 = 0;
                         if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } }
@@ -384,7 +388,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 int giA, boA, giB, boB;
                 next_group(giA, boA);
 #pragma unroll
-                for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                for (int c = 0; c < CBW; ++c) aA[c] = (wb[c] + giA)[lane];
                 if constexpr (PBW >= 4) {
                     // One B register set: a position block's registers are refilled
                     // with the next group's B right after their last MFMA (k-step 3);
@@ -417,14 +421,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     for (int it = 0; it < n_it; it += 2) {
                         if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
+                        for (int c = 0; c < CBW; ++c) aB[c] = (wb[c] + giB)[lane];
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aA, boB);
                         __builtin_amdgcn_sched_barrier(0);
                         if (it + 1 >= n_it) break;
                         if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                        for (int c = 0; c < CBW; ++c) aA[c] = (wb[c] + giA)[lane];
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aB, boA);
                         __builtin_amdgcn_sched_barrier(0);
@@ -450,7 +454,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     for (int it = 0; it < n_it; it += 2) {
                         if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aB[c] = wb[c][giB];
+                        for (int c = 0; c < CBW; ++c) aB[c] = (wb[c] + giB)[lane];
                         read_b(bB, boB);
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aA, bA);
@@ -458,7 +462,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         if (it + 1 >= n_it) break;
                         if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aA[c] = wb[c][giA];
+                        for (int c = 0; c < CBW; ++c) aA[c] = (wb[c] + giA)[lane];
                         read_b(bA, boA);
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aB, bB);
