@@ -106,11 +106,12 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // is sample * G + group and x, w, bias, out and partials are offset to the
 // group's channels (Cout_total is the row stride); when that grid would be too
 // tall the host launches once per group with offset pointers and G = 1.
+// Minimum waves per SIMD, i.e. the register budget of each variant.  Four
+// position blocks of one co block (64 accumulators, 16 B registers) may use up
+// to 170 VGPRs (three waves) rather than being held to 128 (four), where an
+// earlier form spilled in its chunk prologue; it now needs about 125 and runs
+// four waves per SIMD.
 template <int CBW, int NPH, int PBW, bool SM, bool PL>
-// Minimum waves per SIMD: the register budget of each variant.  Four position
-// blocks of one co block (64 accumulators, 16 B registers) take 134 VGPRs, so
-// that variant runs three waves per SIMD: held to four it spilled in its chunk
-// prologue and ran 1.5-2 % slower.
 __global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
                                           : (CBW * NPH * PBW <= 2) ? 6
                                           : (CBW * NPH * PBW <= 4) ? 3
@@ -357,15 +358,24 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 const int ph = (rho_d * sh + rho_h) * sw + rw[p];
                 const int ntp = P.ntaps[ph];
                 const int jwl = jw_lo[p], jwh = jw_hi[p], jwn = Jw[p], cwp = cw[p];
-                // uniform base of each co block's packed weights: the group's A
-                // operands are (base + group)[lane], a scalar base plus a fixed
-                // per-lane offset
-                const float4 *wb[CBW];
+                // A operands of a group: 16 bytes per lane at (co block base +
+                // group) of the packed weights, read as a raw buffer (stride 0,
+                // no range limit, 32-bit data format) with the group offset in a
+                // scalar register and the lane offset in a fixed vector register:
+                // no vector address arithmetic per group
+                __amdgpu_buffer_rsrc_t wr[CBW];
 #pragma unroll
                 for (int c = 0; c < CBW; ++c) {
                     const int cb = min(cb0 + c, P.cb_total - 1);
-                    wb[c] = wp4 + (P.wp_off[ph] >> 2) + (size_t)cb * P.steps4[ph] * 64;
+                    const float4 *base = wp4 + (P.wp_off[ph] >> 2) + (size_t)cb * P.steps4[ph] * 64;
+                    wr[c] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFF0, 0x00020000);
                 }
+                const int lane16 = lane * 16;
+                typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+                auto aload = [&](int c, int gi) -> float4 {
+                    const u4v v = __builtin_amdgcn_raw_buffer_load_b128(wr[c], lane16, gi * 16, 0);
+                    return *reinterpret_cast<const float4 *>(&v);
+                };
                 const int n_it = (jd_hi - jd_lo + 1) * (jh_hi - jh_lo + 1) * (jwh - jwl + 1) * G4;
                 // Iteration state (jd, jh, jw, g4) of the next group to load; every
                 // group is 4 MFMA k-steps = 8 input channels of one tap.  gi: float4
@@ -388,7 +398,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 int giA, boA, giB, boB;
                 next_group(giA, boA);
 #pragma unroll
-                for (int c = 0; c < CBW; ++c) aA[c] = (wb[c] + giA)[lane];
+                for (int c = 0; c < CBW; ++c) aA[c] = aload(c, giA);
                 if constexpr (PBW >= 4) {
                     // One B register set: a position block's registers are refilled
                     // with the next group's B right after their last MFMA (k-step 3);
@@ -421,14 +431,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     for (int it = 0; it < n_it; it += 2) {
                         if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aB[c] = (wb[c] + giB)[lane];
+                        for (int c = 0; c < CBW; ++c) aB[c] = aload(c, giB);
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aA, boB);
                         __builtin_amdgcn_sched_barrier(0);
                         if (it + 1 >= n_it) break;
                         if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aA[c] = (wb[c] + giA)[lane];
+                        for (int c = 0; c < CBW; ++c) aA[c] = aload(c, giA);
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aB, boA);
                         __builtin_amdgcn_sched_barrier(0);
@@ -454,7 +464,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     for (int it = 0; it < n_it; it += 2) {
                         if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aB[c] = (wb[c] + giB)[lane];
+                        for (int c = 0; c < CBW; ++c) aB[c] = aload(c, giB);
                         read_b(bB, boB);
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aA, bA);
@@ -462,7 +472,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         if (it + 1 >= n_it) break;
                         if (it + 2 < n_it) next_group(giA, boA); else { giA = giB; boA = boB; }
 #pragma unroll
-                        for (int c = 0; c < CBW; ++c) aA[c] = (wb[c] + giA)[lane];
+                        for (int c = 0; c < CBW; ++c) aA[c] = aload(c, giA);
                         read_b(bA, boA);
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aB, bB);

@@ -35,9 +35,9 @@ constexpr double kStageWaitMacs = 250e3;
 // (used only by the cost model; the phase-loop build of a variant has the
 // same occupancy as the plain one).
 const Variant kVariants[] = {
-    {1, 1, 8, false, 2, false}, {1, 1, 4, false, 3, true},  {1, 1, 2, false, 6, false},
+    {1, 1, 8, false, 2, false}, {1, 1, 4, false, 4, true},  {1, 1, 2, false, 6, false},
     {1, 2, 4, false, 2, true},  {1, 2, 2, false, 4, true},
-    {1, 1, 4, true, 3, false},  {1, 1, 2, true, 6, true},   {1, 2, 2, true, 4, true},
+    {1, 1, 4, true, 4, false},  {1, 1, 2, true, 6, true},   {1, 2, 2, true, 4, true},
     {2, 1, 4, true, 2, false},  {2, 2, 2, true, 2, true},   {2, 1, 2, true, 3, true},
     {2, 2, 1, true, 3, true},
     {4, 1, 2, true, 1, false},  {4, 2, 1, true, 1, true},   {4, 1, 1, true, 3, true},
