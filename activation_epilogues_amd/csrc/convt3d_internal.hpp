@@ -71,6 +71,7 @@ struct ConvParams {
     int phase_loop;       // 1: each workgroup loops over all (rho_d, rho_h) groups
     int red_off;          // LDS float offset of the epilogue's reduction scratch
     int epi;
+    int gn_block8;        // GroupNorm whose groups are whole 8-channel blocks: tile sums per block
     float scale;
     int tiles_per_n;
     int pr[3][kMaxStride], pc[3][kMaxStride], pJ[3][kMaxStride];

@@ -644,6 +644,48 @@ void convt3d_mfma_kernel(const ConvParams P) {
         const int CO32 = CO_T * 32;
         float *red = lds + P.red_off;  // [WPOS][CO_T*32][2], after the halo
         if (gn || bn) __syncthreads();  // the previous phase group's readers are done
+        const bool blk8 = gn && P.gn_block8;
+        if (blk8) {
+            // GroupNorm over groups of whole 8-channel blocks: a lane's four rows
+            // of block q (channels 8q + r%4 + 4*half) are summed first, then the
+            // block sum over all 64 lanes; one (sum, sum of squares) per
+            // (tile, block), kept at the block's first channel
+#pragma unroll
+            for (int c = 0; c < CBW; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bool bok = row_ok(c, 4 * q);  // whole block in range (Cout % 8 == 0)
+                    float b1 = 0.0f, b2 = 0.0f;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int r = 4 * q + rr;
+                        const float bco = bok ? bias_of(c, r, 0.0f) : 0.0f;
+                        char *rp = rowp(c, r);
+#pragma unroll
+                        for (int pb = 0; pb < PBW; ++pb) {
+                            float v[NPH];
+#pragma unroll
+                            for (int p = 0; p < NPH; ++p) {
+                                v[p] = fmaxf(acc[p][c][pb][r] + bco, 0.0f);
+                                const float vm = ok[p][pb] ? v[p] : 0.0f;
+                                b1 += vm;
+                                b2 = fmaf(vm, vm, b2);
+                            }
+                            if (bok) store_row(rp, pb, v);
+                        }
+                    }
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) {
+                        b1 += __shfl_xor(b1, off);
+                        b2 += __shfl_xor(b2, off);
+                    }
+                    if (lane == 0 && bok) {
+                        const int row = (wco * CBW + c) * 32 + 8 * q;
+                        red[(wpos * CO32 + row) * 2 + 0] = b1;
+                        red[(wpos * CO32 + row) * 2 + 1] = b2;
+                    }
+                }
+        } else
 #pragma unroll
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
@@ -686,10 +728,11 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 const int co = co_tile * CO32 + row;
                 if (co >= Cout) continue;
                 float t1 = 0.0f, t2 = 0.0f;
-                for (int w = 0; w < P.WPOS; ++w) {
-                    t1 += red[(w * CO32 + row) * 2 + 0];
-                    t2 += red[(w * CO32 + row) * 2 + 1];
-                }
+                if (!blk8 || (row & 7) == 0)  // block sums sit at each block's first channel
+                    for (int w = 0; w < P.WPOS; ++w) {
+                        t1 += red[(w * CO32 + row) * 2 + 0];
+                        t2 += red[(w * CO32 + row) * 2 + 1];
+                    }
                 float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * P.Cout_total + grp * Cout + co) * 2;
                 pp[0] = t1;
                 pp[1] = t2;

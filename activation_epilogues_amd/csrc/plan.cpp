@@ -651,6 +651,11 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->order = pl.order;
     cp->phase_loop = pl.phase_loop; cp->red_off = pl.red_off;
     cp->epi = pl.softmax_pass ? CONVT3D_EPI_NONE : pl.e.kind;
+    // GroupNorm needs only per-group sums: when every group is a run of whole
+    // 8-channel blocks (and no block straddles a channel-group boundary), the
+    // conv epilogue sums each block before the cross-lane reduction
+    cp->gn_block8 = pl.e.kind == CONVT3D_EPI_RELU_GROUPNORM && pl.e.groups > 0 &&
+                    (pl.g.cout / pl.e.groups) % 8 == 0 && pl.cog % 8 == 0;
     cp->scale = pl.e.kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL ? pl.e.scale : 1.0f;
     cp->tiles_per_n = (int)pl.tiles_per_n;
     for (int dim = 0; dim < 3; ++dim)
