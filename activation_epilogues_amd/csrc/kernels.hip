@@ -636,8 +636,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
             }
     } else {
         // bias (+ReLU) and store, or scale; per-channel sums over the tile: the
-        // lane's columns, then the 32 columns of each half (xor shuffles), then
-        // the waves (LDS), one (sum, sum of squares) per (tile, channel).
+        // lane's columns, then the 32 columns of each half (xor-shuffle
+        // butterfly, or per 8-channel block for GroupNorm), then the waves
+        // (LDS), one (sum, sum of squares) per (tile, channel).
         const bool gn = P.epi == CONVT3D_EPI_RELU_GROUPNORM;
         const bool bn = P.epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
         const float scale = P.scale;
@@ -687,7 +688,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 }
         } else
 #pragma unroll
-        for (int c = 0; c < CBW; ++c)
+        for (int c = 0; c < CBW; ++c) {
+            // per-row sums x[r] (sum) and x[16 + r] (sum of squares) of the lane
+            float x[32];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const bool cok = row_ok(c, r);
@@ -708,19 +711,29 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     }
                     if (cok && !bn) store_row(rp, pb, v);
                 }
-                if (gn || bn) {
+                x[r] = a1;
+                x[16 + r] = a2;
+            }
+            if (gn || bn) {
+                // butterfly reduce-scatter over the 32 lanes of a half: at each
+                // step a lane keeps one half of its values, sends the other half
+                // to lane ^ m and adds what it receives; afterwards lane col holds
+                // the half's total of value col (row col % 16, sum or square sum)
 #pragma unroll
-                    for (int off = 16; off >= 1; off >>= 1) {
-                        a1 += __shfl_xor(a1, off);
-                        a2 += __shfl_xor(a2, off);
-                    }
-                    if (col == 0 && cok) {
-                        const int row = (wco * CBW + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                        red[(wpos * CO32 + row) * 2 + 0] = a1;
-                        red[(wpos * CO32 + row) * 2 + 1] = a2;
+                for (int m = 16, k = 16; m >= 1; m >>= 1, k >>= 1) {
+                    const bool up = (col & m) != 0;
+#pragma unroll
+                    for (int j = 0; j < k; ++j) {
+                        const float keep = up ? x[j + k] : x[j];
+                        const float send = up ? x[j] : x[j + k];
+                        x[j] = keep + __shfl_xor(send, m);
                     }
                 }
+                const int r = col & 15;
+                const int row = (wco * CBW + c) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (row_ok(c, r)) red[(wpos * CO32 + row) * 2 + (col >> 4)] = x[0];
             }
+        }
         if (gn || bn) {
             __syncthreads();
             const int tile = ((rho_d * sh + rho_h) * P.nwgroups + wgrp) * P.tiles_total + bx;
