@@ -357,8 +357,8 @@ static int run_plan(const Plan &pl, const float *x, const void *w_packed, const 
         float *ab = reinterpret_cast<float *>(ws + pl.ws_ab);
         const double count = (double)(g.cout / epi->groups) * (double)pl.S;
         if (timed(kTimedFinalize, stream, [&] {
-                return launch_gn_finalize(partials, g.n, tiles, g.cout, epi->groups, count, epi->eps, epi->gamma,
-                                          epi->beta, ab, epi->stats_out, stream);
+                return launch_gn_finalize(partials, g.n, tiles, g.cout, epi->groups, cp.gn_block8 ? 8 : 1, count,
+                                          epi->eps, epi->gamma, epi->beta, ab, epi->stats_out, stream);
             }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
         if (timed(kTimedNormalize, stream, [&] {
@@ -557,8 +557,8 @@ int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
             if (!ok(timed(kTimedReduce, stream,
                           [&] { return launch_row_stats(y, n, c, spatial, true, 1.0f, partials, stream); })) ||
                 !ok(timed(kTimedFinalize, stream, [&] {
-                    return launch_gn_finalize(partials, n, L.chunks, c, epi->groups, count, epi->eps, epi->gamma,
-                                              epi->beta, ab, epi->stats_out, stream);
+                    return launch_gn_finalize(partials, n, L.chunks, c, epi->groups, 1, count, epi->eps,
+                                              epi->gamma, epi->beta, ab, epi->stats_out, stream);
                 })) ||
                 !ok(timed(kTimedNormalize, stream,
                           [&] { return launch_normalize(y, out, ab, n * c, spatial, true, stream); })))

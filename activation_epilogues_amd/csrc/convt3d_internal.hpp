@@ -161,9 +161,11 @@ int make_eval_geom(const convt3d_geom *g, EvalGeom *eg);  // CONVT3D_ERR_UNSUPPO
 int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream);
 int launch_conv(const Plan &pl, const ConvParams &cp, void *stream);
 
-// Launchers (epilogue.hip).  partials are [n][chunk or tile][C][2].
-int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, double count, float eps,
-                       const float *gamma, const float *beta, float *ab, float *stats_out, void *stream);
+// Launchers (epilogue.hip).  partials are [n][chunk or tile][C][2]; the GroupNorm
+// merge reads every chan_step-th channel (8 when the conv kept one sum per
+// 8-channel block, at the block's first channel; else 1).
+int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, int chan_step, double count,
+                       float eps, const float *gamma, const float *beta, float *ab, float *stats_out, void *stream);
 int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool relu,
                      void *stream);
 int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,

@@ -71,12 +71,13 @@ constexpr int ncomp() { return (int)(sizeof(V) / sizeof(float)); }
 // variance E[r^2] - mean^2, rstd = 1/sqrt(var + eps), and per channel
 // a = gamma*rstd, b = beta - mean*a.
 __global__ __launch_bounds__(kStatThreads) void gn_finalize_kernel(const float *partials, int tiles_per_n, int C,
-                                                          int G, float eps, const float *gamma,
+                                                          int G, int chan_step, float eps, const float *gamma,
                                                           const float *beta, float *ab, float *stats_out,
                                                           double count) {
     const int n = blockIdx.x / G, g = blockIdx.x % G;
     const int cpg = C / G;
-    const int items = tiles_per_n * cpg;
+    const int cps = cpg / chan_step;  // channels of the group that hold sums
+    const int items = tiles_per_n * cps;
     double a1 = 0.0, a2 = 0.0;
     for (int i0 = threadIdx.x; i0 < items; i0 += blockDim.x * kStatUnroll) {
         float2 v[kStatUnroll];
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kStatThreads) void gn_finalize_kernel(const float *
             const int i = i0 + u * (int)blockDim.x;
             v[u] = make_float2(0.0f, 0.0f);
             if (i < items) {
-                const int t = i / cpg, cc = i - t * cpg;
+                const int t = i / cps, cc = (i - t * cps) * chan_step;
                 v[u] = *reinterpret_cast<const float2 *>(partials +
                                                           (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2);
             }
@@ -584,10 +585,10 @@ __global__ __launch_bounds__(256) void eval_finalize_kernel(const EvalGeom E, co
 // ---------------------------------------------------------------------------
 // launchers
 
-int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, double count, float eps,
-                       const float *gamma, const float *beta, float *ab, float *stats_out, void *stream) {
+int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, int chan_step, double count,
+                       float eps, const float *gamma, const float *beta, float *ab, float *stats_out, void *stream) {
     hipLaunchKernelGGL(gn_finalize_kernel, dim3(N * G), dim3(kStatThreads), 0, (hipStream_t)stream, partials,
-                       tiles_per_n, C, G, eps, gamma, beta, ab, stats_out, count);
+                       tiles_per_n, C, G, chan_step, eps, gamma, beta, ab, stats_out, count);
     return (int)hipGetLastError();
 }
 

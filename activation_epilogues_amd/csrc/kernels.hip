@@ -650,7 +650,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
             // GroupNorm over groups of whole 8-channel blocks: a lane's four rows
             // of block q (channels 8q + r%4 + 4*half) are summed first, then the
             // block sum over all 64 lanes; one (sum, sum of squares) per
-            // (tile, block), kept at the block's first channel
+            // (tile, block), kept at the block's first channel (the other seven
+            // channels' partials are not written)
 #pragma unroll
             for (int c = 0; c < CBW; ++c)
 #pragma unroll
@@ -740,12 +741,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
             for (int row = tid; row < CO32; row += blockDim.x) {
                 const int co = co_tile * CO32 + row;
                 if (co >= Cout) continue;
+                // block sums sit at each block's first channel, and the merge
+                // reads only those
+                if (blk8 && (row & 7) != 0) continue;
                 float t1 = 0.0f, t2 = 0.0f;
-                if (!blk8 || (row & 7) == 0)  // block sums sit at each block's first channel
-                    for (int w = 0; w < P.WPOS; ++w) {
-                        t1 += red[(w * CO32 + row) * 2 + 0];
-                        t2 += red[(w * CO32 + row) * 2 + 1];
-                    }
+                for (int w = 0; w < P.WPOS; ++w) {
+                    t1 += red[(w * CO32 + row) * 2 + 0];
+                    t2 += red[(w * CO32 + row) * 2 + 1];
+                }
                 float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * P.Cout_total + grp * Cout + co) * 2;
                 pp[0] = t1;
                 pp[1] = t2;
