@@ -125,7 +125,8 @@ struct Plan {
     int lds_bytes = 0;
     int co_tiles = 1, nwgroups = 1;
     int phase_loop = 0, red_off = 0;
-    int split = 0;            // dims split into border / interior segments (bit 0 d, 1 h, 2 w)
+    int split = 0;            // dims split into border / interior segments (bit 0 d, 1 h, 2 w);
+                              // bit 3 + d (6 + d): only the low (high) border of dim d on its own
     int softmax_pass = 0;     // softmax with cout > 128: conv stores y, a second pass finishes
     int eval = 0;             // eval-mode BatchNorm + pool: no conv (EvalGeom below)
     EvalGeom eg{};

@@ -280,6 +280,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     // box lets border tiles skip the taps that cannot reach the input.
     struct Seg { int a, b; };
     Seg segs_split[3][3], segs_whole[3][1];
+    Seg segs_lowonly[3][2], segs_highonly[3][2];  // one border on its own, the other in the interior
     int nseg_split[3];
     for (int dim = 0; dim < 3; ++dim) {
         int lo = 0, hi = pl->Q[dim];
@@ -297,6 +298,10 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         if (hi > lo) segs_split[dim][ns++] = {lo, hi};
         if (pl->Q[dim] > hi) segs_split[dim][ns++] = {hi, pl->Q[dim]};
         segs_whole[dim][0] = {0, pl->Q[dim]};
+        segs_lowonly[dim][0] = {0, lo};
+        segs_lowonly[dim][1] = {lo, pl->Q[dim]};
+        segs_highonly[dim][0] = {0, hi};
+        segs_highonly[dim][1] = {hi, pl->Q[dim]};
     }
     // live taps summed over the tiles of a segment for a tile length
     auto seg_live = [&](int dim, int rho, const Seg &sg, int tq) {
@@ -331,8 +336,9 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     // Optional override for tile sweeps:
     // CONVT3D_PLAN="variant,WCO,TQd,TQh,TQw,CI_T[,split]" restricts the search
     // to that variant / wave grid / chunk, with that box in the largest region
-    // and (bit 0 d, 1 h, 2 w) those dims split into border / interior segments
-    // (ignored if it does not fit).  A negative field leaves that choice free
+    // and (bit 0 d, 1 h, 2 w) those dims split into border / interior segments,
+    // with bit 3 + d (6 + d) set when only the low (high) border of dim d is a
+    // segment of its own (ignored if it does not fit).  A negative field leaves that choice free
     // (the box needs all three of TQd, TQh, TQw to be fixed).
     int force[7] = {-1, -1, -1, -1, -1, -1, -1};
     if (const char *env = std::getenv("CONVT3D_PLAN")) {
@@ -362,8 +368,19 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         for (int WCO = 1; WCO <= 4; WCO *= 2) {
           const int WPOS = 4 / WCO;
           if (forced && force[1] >= 0 && WCO != force[1]) continue;
-          // which dims are split into border / interior segments
-          for (int split = 0; split < 8; ++split) {
+          // segments per dim: mode 0 whole, 1 low border / interior / high border,
+          // 2 low border / interior + high border, 3 low border + interior / high
+          // border (a border's dead taps can cost less than the padding of an
+          // interior whose length the box does not divide).  Reported as bit d
+          // (dim split), bit 3 + d (mode 2) and bit 6 + d (mode 3).
+          for (int modes = 0; modes < 64; ++modes) {
+           int split = 0;
+           for (int dim = 0; dim < 3; ++dim) {
+               const int m = (modes >> (2 * dim)) & 3;
+               if (m) split |= 1 << dim;
+               if (m == 2) split |= 1 << (3 + dim);
+               if (m == 3) split |= 1 << (6 + dim);
+           }
            // ploop: one workgroup loops over every (rho_d, rho_h) group on one staged
            // halo (needs the whole channel range in one LDS chunk)
            for (int ploop = 0; ploop < (sd * sh > 1 ? 2 : 1); ++ploop) {
@@ -374,10 +391,13 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
             int nseg[3];
             bool redundant = false;
             for (int dim = 0; dim < 3; ++dim) {
-                const bool sp = (split >> dim) & 1;
-                if (sp && nseg_split[dim] == 1) redundant = true;  // same as unsplit
-                nseg[dim] = sp ? nseg_split[dim] : 1;
-                for (int i = 0; i < nseg[dim]; ++i) segs[dim][i] = sp ? segs_split[dim][i] : segs_whole[dim][0];
+                const int m = (modes >> (2 * dim)) & 3;
+                if (m == 1 && nseg_split[dim] == 1) redundant = true;  // same as unsplit
+                if (m >= 2 && nseg_split[dim] < 3) redundant = true;   // same as split or unsplit
+                const Seg *src = m == 0 ? segs_whole[dim] : m == 1 ? segs_split[dim]
+                                 : m == 2 ? segs_lowonly[dim] : segs_highonly[dim];
+                nseg[dim] = m == 0 ? 1 : m == 1 ? nseg_split[dim] : 2;
+                for (int i = 0; i < nseg[dim]; ++i) segs[dim][i] = src[i];
             }
             if (redundant) continue;
             if (softmax && WCO != 1) continue;

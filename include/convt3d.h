@@ -235,7 +235,9 @@ typedef struct convt3d_plan_info {
     int64_t valid_macs;        /* multiply-adds whose input voxel is in range          */
     int32_t phase_loop;        /* 1: a workgroup covers every (d, h) stride phase       */
     int32_t tuned;             /* 1: chosen by convt3d_autotune                         */
-    int32_t border_split;      /* dims split into border / interior tile regions (bit 0 d, 1 h, 2 w) */
+    int32_t border_split;      /* dims split into border / interior tile regions (bit 0 d, 1 h, 2 w);
+                                  bit 3 + d (6 + d): only the low (high) border of dim d is a region
+                                  of its own, the other border is tiled with the interior */
     int32_t xcd_order;         /* 0: phase / channel-tile index fastest per XCD, 1: tile fastest */
     int32_t softmax_pass;      /* 1: softmax runs as a second pass (cout > 128, groups) */
     int32_t eval_bins;         /* BN eval: input bins per (n, cin) plane, else 0        */
