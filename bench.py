@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -50,22 +51,27 @@ def kernel_source_hash(kernel: str = "convt3d_mfma_kernel") -> str:
 
 
 def stored_traffic(workload: str, kernel: str = "convt3d_mfma_kernel"):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
-    summary, if it was taken from the current kernel source (else None)."""
+    """(HBM bytes per launch, plan string) of `kernel` from the committed
+    rocprofv3 --pmc summary, if it was taken from the current kernel source
+    (else (None, None)).  The plan is the one the counters were read on (the
+    --plan of the profiled command; None when it ran untuned)."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
-        return None
-    kv = {}
+        return None, None
+    kv, plan = {}, None
     for line in open(path):
+        m = re.search(r"--plan (\S+)", line)
+        if m and plan is None:
+            plan = m.group(1)
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
-        return None
+        return None, None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_launch"]), plan
     except (KeyError, ValueError):
-        return None
+        return None, None
 
 
 def cpu_baseline(wl, inp, max_samples: int):
@@ -294,7 +300,7 @@ def main():
         eg_bins = info["eval_bins"]
         alg_bytes = 4.0 * (x.numel() + call.ws_bytes / 4)
         gbps = alg_bytes / (red_ms * 1e-3) / 1e9
-        traffic = stored_traffic(wl.name, kernel="eval_binsum_kernel")
+        traffic, _ = stored_traffic(wl.name, kernel="eval_binsum_kernel")
         roofline = {
             "kernel": "eval_binsum_kernel",
             "bound": "hbm",
@@ -309,7 +315,7 @@ def main():
         }
     else:
         conv_tflops = flops / (conv_ms * 1e-3) / 1e12
-        traffic = stored_traffic(wl.name)
+        traffic, traffic_plan = stored_traffic(wl.name)
         roofline = {
             "kernel": "convt3d_mfma_kernel",
             "bound": "mfma",
@@ -318,6 +324,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(conv_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
             "traffic": traffic,
+            # plan the traffic counters were read on (this run's plan_string may
+            # differ when autotuning picks another candidate within noise)
+            "traffic_plan": traffic_plan,
             "algorithmic_flop_per_launch": flops,
             "avg_launch_ms": round(conv_ms, 4),
         }
