@@ -34,6 +34,14 @@ def run_gpu(wl, inp, kind=None, want_stats=True, stream=None):
     x, w, b = to_dev(inp.x), to_dev(inp.w), to_dev(inp.b)
     gamma, beta = to_dev(inp.gamma), to_dev(inp.beta)
     call.prepack(w, stream)
+    # every output, exported statistic and workspace word starts as NaN: an
+    # output the kernels leave unwritten, or a partial sum read without having
+    # been written, shows up in the comparison
+    call.out.fill_(float("nan"))
+    call.workspace.fill_(float("nan"))
+    if call.stats is not None:
+        call.stats.fill_(float("nan"))
+    torch.cuda.synchronize()
     out = call(x, b, gamma, beta, stream)
     torch.cuda.synchronize()
     st = None if call.stats is None else call.stats.cpu().numpy()
