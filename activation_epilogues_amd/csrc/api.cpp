@@ -455,24 +455,64 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
         reps = (int)std::min(50.0f, std::max(3.0f, std::ceil(2.0f / std::max(est, 1e-3f))));
     }
     std::vector<float> best_of(cands.size(), 0.0f);
-    for (int round = 0; round < kRounds && st == CONVT3D_OK; ++round)
-        for (int i : fit) {
-            float ms = 0.0f;
-            st = run_plan(cands[i], x, w_packed, bias, epi, out, workspace, stream);  // untimed
-            if (st == CONVT3D_OK) st = time_calls(cands[i], reps, &ms);
-            if (st) break;
-            if (round == 0 || ms < best_of[i]) best_of[i] = ms;
-        }
-    int best = -1;
-    for (int i : fit) {
+    // time cands[i] for i in `which`, kRounds rounds, keeping each one's best round
+    auto time_all = [&](const std::vector<int> &which) {
+        for (int round = 0; round < kRounds && st == CONVT3D_OK; ++round)
+            for (int i : which) {
+                float ms = 0.0f;
+                st = run_plan(cands[i], x, w_packed, bias, epi, out, workspace, stream);  // untimed
+                if (st == CONVT3D_OK) st = time_calls(cands[i], reps, &ms);
+                if (st) break;
+                if (round == 0 || ms < best_of[i]) best_of[i] = ms;
+            }
+    };
+    auto log_plan = [&](int i) {
         const Plan &pl = cands[i];
         if (log && st == CONVT3D_OK)
             std::fprintf(stderr, "convt3d_autotune: rank %d plan %d,%d,%d,%d,%d,%d,%d phase_loop %d order %d: %.4f ms\n",
                          i, pl.variant, pl.WCO, pl.TQ[0], pl.TQ[1], pl.TQ[2], pl.CI_T, pl.split, pl.phase_loop,
                          pl.order, best_of[i]);
+    };
+    time_all(fit);
+    int best = -1;
+    for (int i : fit) {
+        log_plan(i);
         if (best < 0 || best_of[i] < best_of[best]) best = i;
     }
-    const int timed_n = (int)fit.size();
+    int timed_n = (int)fit.size();
+    // Second stage: the fastest configuration's other border segmentations
+    // (their times differ by up to a few per cent, more than the cost model
+    // resolves).  Ranks past the first list number these.
+    if (st == CONVT3D_OK && best >= 0) {
+        std::vector<Plan> alt;
+        if (plan_candidates(geom, epi, 8, &alt, &cands[best]) == CONVT3D_OK) {
+            std::vector<int> more;
+            for (Plan &pl : alt) {
+                bool seen = false;
+                for (const Plan &c : cands)
+                    seen = seen || (c.variant == pl.variant && c.WCO == pl.WCO && c.CI_T == pl.CI_T &&
+                                    c.phase_loop == pl.phase_loop && c.split == pl.split && c.TQ[0] == pl.TQ[0] &&
+                                    c.TQ[1] == pl.TQ[1] && c.TQ[2] == pl.TQ[2]);
+                if (seen) continue;
+                pl.e = *epi;
+                if (pl.ws_bytes != 0 && !(workspace && workspace_bytes >= pl.ws_bytes && aligned16(workspace)))
+                    continue;
+                more.push_back((int)cands.size());
+                cands.push_back(pl);
+                best_of.push_back(0.0f);
+            }
+            time_all(more);
+            for (int i : more) {
+                log_plan(i);
+                if (best_of[i] < best_of[best]) best = i;
+            }
+            timed_n += (int)more.size();
+            fit.insert(fit.end(), more.begin(), more.end());
+        }
+    }
+    // rank among the timed plans
+    int chosen = 0;
+    while (chosen < (int)fit.size() && fit[chosen] != best) ++chosen;
     const float best_ms = best_of[best], first_ms = best_of[fit[0]];
     (void)hipEventDestroy(b);  // cleanup: a failure here does not change the result
     (void)hipEventDestroy(e);
@@ -481,7 +521,7 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     store_tuned(geom, epi, cands[best]);
     if (result) {
         result->candidates = timed_n;
-        result->chosen = best;
+        result->chosen = chosen;
         result->chosen_ms = best_ms;
         result->model_choice_ms = first_ms;
     }

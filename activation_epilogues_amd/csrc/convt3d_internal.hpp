@@ -153,7 +153,11 @@ int64_t out_dim(int64_t in, int64_t k, int64_t s, int64_t p, int64_t op, int64_t
 int validate_geom(const convt3d_geom *g);
 int make_geometry(const convt3d_geom *g, Plan *pl);        // phases + packing only
 int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl);
-int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k, std::vector<Plan> *out);
+// The max_k cheapest plans by the cost model, one per kernel configuration
+// (variant, wave grid, box, chunk, phase loop); with `like`, only plans of that
+// plan's configuration, one per border segmentation.
+int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k, std::vector<Plan> *out,
+                    const Plan *like = nullptr);
 void fill_conv_params(const Plan &pl, ConvParams *cp);
 int make_eval_geom(const convt3d_geom *g, EvalGeom *eg);  // CONVT3D_ERR_UNSUPPORTED for k > kEvalMaxK
 

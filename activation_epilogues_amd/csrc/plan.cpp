@@ -235,7 +235,8 @@ int make_eval_geom(const convt3d_geom *g, EvalGeom *eg) {
 // Search of the kernel configuration: every (variant, wave grid, border split,
 // phase loop, halo buffers) with its best box per region and channel chunk,
 // ranked by the cost model.  Returns the best max_k plans, cheapest first.
-int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k, std::vector<Plan> *out) {
+int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k, std::vector<Plan> *out,
+                    const Plan *like) {
     if (!g || !e || !out) return CONVT3D_ERR_NULL;
     out->clear();
     if (max_k < 1) max_k = 1;
@@ -346,12 +347,19 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                                     &force[4], &force[5], &force[6]);
         if (got < 6) force[0] = -1;
     }
+    // `like`: only that plan's configuration, every border segmentation
+    if (like) {
+        force[0] = like->variant; force[1] = like->WCO;
+        force[2] = like->TQ[0]; force[3] = like->TQ[1]; force[4] = like->TQ[2];
+        force[5] = like->CI_T; force[6] = -1;
+    }
     const bool forced = force[0] >= 0;
     int order_env = -1;
     if (const char *env = std::getenv("CONVT3D_ORDER")) order_env = std::atoi(env) ? 1 : 0;
     // CONVT3D_PHASE_LOOP=0|1 restricts the phase-group loop choice (tests, sweeps)
     int ploop_only = -1;
     if (const char *env = std::getenv("CONVT3D_PHASE_LOOP")) ploop_only = std::atoi(env) ? 1 : 0;
+    if (like) ploop_only = like->phase_loop;
     // workgroups are planned for every (sample, channel group); an empty batch like n = 1
     const int64_t nn = (int64_t)std::max(g->n, 1) * pl->G;
     const int CI_pad = pl->octets * kOctet;
@@ -618,6 +626,22 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                     continue;
                 }
                 ws_layout(&c);
+                // one entry per kernel configuration (variant, wave grid, box,
+                // chunk, phase loop): plans that differ only in how the borders
+                // are segmented run within noise of each other, so the timed
+                // candidates should spread over configurations instead
+                bool dominated = false;
+                for (auto it = top.begin(); it != top.end() && !like; ++it) {
+                    const Plan &o = it->second;
+                    if (o.variant != c.variant || o.WCO != c.WCO || o.CI_T != c.CI_T ||
+                        o.phase_loop != c.phase_loop || o.TQ[0] != c.TQ[0] || o.TQ[1] != c.TQ[1] ||
+                        o.TQ[2] != c.TQ[2])
+                        continue;
+                    if (it->first <= cost) dominated = true;
+                    else top.erase(it);
+                    break;
+                }
+                if (dominated) continue;
                 auto at = top.begin();
                 while (at != top.end() && at->first <= cost) ++at;
                 top.insert(at, std::make_pair(cost, c));

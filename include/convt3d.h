@@ -190,13 +190,17 @@ int convt3d_fused(const float *x, const void *w_packed, const float *bias,
  * events on `stream`).  Candidates needing more workspace than
  * workspace_bytes are skipped.  BatchNorm running statistics are left
  * untouched (the timed calls do not update them).  result may be NULL.  The
- * best 12 candidates are timed (environment CONVT3D_TUNE_CANDIDATES=1..64
- * changes that; CONVT3D_TUNE_LOG prints one line per candidate to stderr):
- * after about 20 ms of warm-up calls, each in three rounds of repeated calls
- * (about 2 ms of work per round), its fastest round counting. */
+ * best 12 configurations are timed, one plan each (environment
+ * CONVT3D_TUNE_CANDIDATES=1..64 changes that; CONVT3D_TUNE_LOG prints one
+ * line per candidate to stderr), then up to 8 other border segmentations of
+ * the fastest one: after about 20 ms of warm-up calls, each in three rounds
+ * of repeated calls (about 2 ms of work per round), its fastest round
+ * counting. */
 typedef struct convt3d_tune_result {
     int32_t candidates;      /* plans timed                                      */
-    int32_t chosen;          /* rank of the chosen plan in cost-model order (0 = the model's pick) */
+    int32_t chosen;          /* rank of the chosen plan in cost-model order (0 = the model's pick;
+                                ranks past the first list are the fastest configuration's other
+                                border segmentations, timed in a second stage) */
     float chosen_ms;         /* time per call of the chosen plan                 */
     float model_choice_ms;   /* time per call of the cost model's pick           */
 } convt3d_tune_result;

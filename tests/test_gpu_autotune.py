@@ -32,7 +32,8 @@ def test_autotuned_plan_matches_oracle(name, monkeypatch):
     res = call.autotune(x, b, gamma, beta)
     say(f"  tuned: {res}")
     # the workspace convt3d_workspace_size reports fits every candidate
-    assert 1 <= res["candidates"] <= 12
+    # 12 configurations, then up to 8 border segmentations of the fastest
+    assert 1 <= res["candidates"] <= 12 + 8
     assert 0 <= res["chosen"] < res["candidates"]
     assert res["chosen_ms"] > 0 and res["chosen_ms"] <= res["model_choice_ms"]
     info = call.plan_info()
