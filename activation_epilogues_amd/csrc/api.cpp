@@ -85,7 +85,14 @@ int cached_entry(const convt3d_geom *g, const convt3d_epilogue *e, CacheEntry *o
     const int st = plan_candidates(g, e, tune_candidates(), &cands);
     if (st) return st;
     CacheEntry ent{cands[0], 0, false};
-    for (const Plan &c : cands) ent.ws_max = std::max(ent.ws_max, c.ws_bytes);
+    // every plan convt3d_autotune may time: the candidates and the other border
+    // segmentations of each (its second stage takes those of the fastest)
+    for (const Plan &c : cands) {
+        ent.ws_max = std::max(ent.ws_max, c.ws_bytes);
+        std::vector<Plan> alt;
+        if (plan_candidates(g, e, 8, &alt, &c) == CONVT3D_OK)
+            for (const Plan &a : alt) ent.ws_max = std::max(ent.ws_max, a.ws_bytes);
+    }
     {
         std::lock_guard<std::mutex> lk(g_mu);
         g_cache.emplace_front(key, ent);
