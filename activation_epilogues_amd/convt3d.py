@@ -73,14 +73,35 @@ class Convt3dError(RuntimeError):
 _lib = None
 
 
+def _hip_runtimes():
+    """Paths of the HIP runtime libraries mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln})
+    except OSError:
+        return []
+
+
 def lib():
-    """Load libconvt3d.so (built in-tree by activation_epilogues_amd.build)."""
+    """Load libconvt3d.so (built in-tree by activation_epilogues_amd.build).
+
+    torch is imported first: its ROCm build carries its own HIP runtime, and
+    the library must bind to that one (the runtime that owns the caller's
+    device memory and streams).  Loaded before torch, the library would pull
+    in the system HIP runtime and torch would then load its own beside it:
+    two runtimes in one process, with torch's stream handles handed to the
+    other one.  That state is refused here."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libconvt3d is not built ({LIB_PATH} missing); run "
                                "python -m activation_epilogues_amd.build")
+        import torch  # noqa: F401  (binds the process to torch's HIP runtime first)
         L = ctypes.CDLL(LIB_PATH)
+        rts = _hip_runtimes()
+        if len(rts) > 1:
+            raise RuntimeError("more than one HIP runtime is loaded in this process (" + ", ".join(rts) +
+                               "); load libconvt3d through this module, after torch")
         P = ctypes.POINTER
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.convt3d_status_string.restype = ctypes.c_char_p

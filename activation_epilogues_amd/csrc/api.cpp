@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -37,7 +38,7 @@ int tune_candidates() {
         const int k = std::atoi(env);
         if (k >= 1 && k <= 64) return k;
     }
-    return 12;
+    return kTuneCandidates;
 }
 
 struct CacheEntry {
@@ -90,7 +91,7 @@ int cached_entry(const convt3d_geom *g, const convt3d_epilogue *e, CacheEntry *o
     for (const Plan &c : cands) {
         ent.ws_max = std::max(ent.ws_max, c.ws_bytes);
         std::vector<Plan> alt;
-        if (plan_candidates(g, e, 8, &alt, &c) == CONVT3D_OK)
+        if (plan_candidates(g, e, kTuneBorderAlternatives, &alt, &c) == CONVT3D_OK)
             for (const Plan &a : alt) ent.ws_max = std::max(ent.ws_max, a.ws_bytes);
     }
     {
@@ -492,7 +493,7 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
     // resolves).  Ranks past the first list number these.
     if (st == CONVT3D_OK && best >= 0) {
         std::vector<Plan> alt;
-        if (plan_candidates(geom, epi, 8, &alt, &cands[best]) == CONVT3D_OK) {
+        if (plan_candidates(geom, epi, kTuneBorderAlternatives, &alt, &cands[best]) == CONVT3D_OK) {
             std::vector<int> more;
             for (Plan &pl : alt) {
                 bool seen = false;

@@ -22,6 +22,10 @@ constexpr int kRowStatChunk = 8192;      // vector elements per workgroup in the
 constexpr int kEvalMaxK = 31;            // eval-mode BN: kernel size limit (bins per dim <= 2k+1)
 constexpr int kEvalMaxBins = 2 * kEvalMaxK + 1;
 constexpr int kEvalTargetBlocks = 2048;  // eval-mode bin sums: workgroups to aim for
+// convt3d_autotune: kernel configurations timed (the cost model's best), then
+// border segmentations of the fastest one; the workspace bound covers both
+constexpr int kTuneCandidates = 12;
+constexpr int kTuneBorderAlternatives = 8;
 
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
 // taps that reach it are t = r + ts*j (j = 0..J-1) from input i = q + c - e*j,

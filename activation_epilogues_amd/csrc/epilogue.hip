@@ -633,12 +633,6 @@ int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, dou
     return (int)hipGetLastError();
 }
 
-int row_stat_chunks(int64_t S) {
-    const int64_t len = S % 4 == 0 ? S / 4 : S;          // in vector units
-    int64_t c = (len + kRowStatChunk - 1) / kRowStatChunk;
-    return (int)(c < 1 ? 1 : c);
-}
-
 template <class V, bool RELU>
 static void launch_row_stats_t(const float *y, int rows, int len, int chunks, int C, float mult, float *partials,
                                void *stream) {

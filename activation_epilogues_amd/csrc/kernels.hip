@@ -23,19 +23,12 @@
 #include <climits>
 #include <cstdint>
 
+#include "conv_index.hpp"
 #include "convt3d_internal.hpp"
 
 namespace convt3d {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
-
-// floor / ceil of a / b for b > 0 and any sign of a (tap ranges with dilation;
-// b is wave-uniform and 1 without dilation)
-__device__ __forceinline__ int floor_div_any(int a, int b) {
-    if (b == 1) return a;
-    return a >= 0 ? a / b : -((-a + b - 1) / b);
-}
-__device__ __forceinline__ int ceil_div_any(int a, int b) { return -floor_div_any(-a, b); }
 
 __device__ __forceinline__ v16f mfma32x32x2(float a, float b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -126,97 +119,45 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int wco = wave % P.WCO;
     const int wpos = wave / P.WCO;
 
-    // ---- workgroup -> work item.  Workgroups are handed to the XCDs round-robin
-    // (dispatch index i runs on XCD i % nxcd), each XCD with its own L2.  The
-    // dispatch index is mapped to a linear work index so that every XCD gets
-    // one contiguous range; the halo overlap of neighbouring tiles then hits in
-    // one L2.  Within it either the (co tile, phase) index varies fastest
-    // (those workgroups read the same input box; order 0) or the tile does
-    // (an XCD keeps to one phase's weights when all of them do not fit in its
-    // L2; order 1); n varies slowest.
-    int bx, by, n;
-    {
-        const int gx = gridDim.x, gy = gridDim.y;
-        const int total = gx * gy * gridDim.z;
-        const int bid = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
-        const int nx = P.nxcd, q = total / nx, r = total % nx;
-        const int xcd = bid % nx, idx = bid / nx;
-        const int lin = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
-        if (P.order == 0) {
-            by = lin % gy;
-            bx = (lin / gy) % gx;
-        } else {
-            bx = lin % gx;
-            by = (lin / gx) % gy;
-        }
-        n = lin / (gx * gy);
-    }
-    // channel group of this workgroup (grid z = sample * G + group)
-    const int grp = n % P.G;
-    n /= P.G;
-    // ---- tile: find the region, then the tile inside it
-    int reg = 0;
-    while (reg + 1 < P.nreg && bx >= P.rg_off[reg + 1]) ++reg;
-    const int *RG = P.rg[reg];
-    const int local = bx - P.rg_off[reg];
-    const int tw_i = local % RG[11];
-    const int th_i = (local / RG[11]) % RG[10];
-    const int td_i = local / (RG[11] * RG[10]);
-    const int co_tile = by % P.co_tiles;
-    by /= P.co_tiles;
-    const int wgrp = by % P.nwgroups;
-    by /= P.nwgroups;
+    // ---- workgroup -> work item (XCD-contiguous order), then its tile
+    const ix::WorkItem wi =
+        ix::work_item(P, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gridDim.x, gridDim.y,
+                      gridDim.z);
+    const int bx = wi.bx, n = wi.n, grp = wi.grp, co_tile = wi.co_tile, wgrp = wi.wgrp;
+    const ix::TileBox tb = ix::tile_box(P, bx);
     const int sd = P.s3[0], sh = P.s3[1], sw = P.s3[2];
     const int ed = P.pe[0], eh = P.pe[1], ew = P.pe[2];  // input step per tap index
 
-    const int TQd = RG[6], TQh = RG[7], TQw = RG[8];
-    const int q0d = RG[0] + td_i * TQd, q0h = RG[1] + th_i * TQh, q0w = RG[2] + tw_i * TQw;
+    const int TQd = tb.TQd, TQh = tb.TQh, TQw = tb.TQw;
+    const int q0d = tb.q0d, q0h = tb.q0h, q0w = tb.q0w;
     // extent of this tile inside its region (the box may overhang the region end)
-    const int TQd_e = min(TQd, RG[3] - q0d), TQh_e = min(TQh, RG[4] - q0h), TQw_e = min(TQw, RG[5] - q0w);
+    const int TQd_e = tb.TQd_e, TQh_e = tb.TQh_e, TQw_e = tb.TQw_e;
 
     // (rho_d, rho_h) phase groups of this workgroup: one (from the grid), or all
     // sd*sh of them over one staged halo when the whole channel range fits in
     // one LDS chunk.  The staged box is the union of the groups' footprints.
     constexpr bool ploop = PL;  // == (P.phase_loop != 0): the launcher picks the instantiation
     const int npg = ploop ? sd * sh : 1;
-    const int pg0 = ploop ? 0 : by;
-    int lo_d_rel = 0, lo_h_rel = 0, HD = TQd, HH = TQh;
-    {
-        int dlo = INT_MAX, dhi = INT_MIN, hlo = INT_MAX, hhi = INT_MIN;
-        for (int g = pg0; g < pg0 + npg; ++g) {
-            const int rd = g / sh, rh = g % sh;
-            const int Jd_ = P.pJ[0][rd], cd_ = P.pc[0][rd], Jh_ = P.pJ[1][rh], ch_ = P.pc[1][rh];
-            if (Jd_ > 0) { dlo = min(dlo, cd_ - ed * (Jd_ - 1)); dhi = max(dhi, TQd - 1 + cd_); }
-            if (Jh_ > 0) { hlo = min(hlo, ch_ - eh * (Jh_ - 1)); hhi = max(hhi, TQh - 1 + ch_); }
-        }
-        if (dlo <= dhi) { lo_d_rel = dlo; HD = dhi - dlo + 1; }
-        if (hlo <= hhi) { lo_h_rel = hlo; HH = hhi - hlo + 1; }
-    }
+    const int pg0 = ploop ? 0 : wi.pg;
+    int lo_d_rel, lo_h_rel, HD, HH;
+    ix::halo_dh(P, pg0, npg, TQd, TQh, lo_d_rel, HD, lo_h_rel, HH);
     int Jw[NPH], cw[NPH], rw[NPH];
     int lo_w_rel = INT_MAX, hi_w_rel = INT_MIN;
 #pragma unroll
     for (int p = 0; p < NPH; ++p) {
         rw[p] = wgrp * NPH + p;
-        Jw[p] = P.pJ[2][rw[p]];
-        cw[p] = P.pc[2][rw[p]];
-        if (Jw[p] > 0) {
-            lo_w_rel = min(lo_w_rel, cw[p] - ew * (Jw[p] - 1));
-            hi_w_rel = max(hi_w_rel, TQw - 1 + cw[p]);
-        }
+        ix::w_phase(P, rw[p], TQw, Jw[p], cw[p], lo_w_rel, hi_w_rel);
     }
-    const bool w_taps = lo_w_rel <= hi_w_rel;
+    const bool w_taps = ix::w_halo_close(TQw, lo_w_rel, hi_w_rel);
 
     // ---- halo box in input coordinates
-    const int HW = w_taps ? hi_w_rel - lo_w_rel + 1 : TQw;
+    const int HW = hi_w_rel - lo_w_rel + 1;
     const int lo_d = q0d + lo_d_rel;
     const int lo_h = q0h + lo_h_rel;
     const int lo_w = q0w + lo_w_rel;
     int jw_lo[NPH], jw_hi[NPH];
 #pragma unroll
-    for (int p = 0; p < NPH; ++p) {
-        jw_lo[p] = max(0, ceil_div_any(q0w + cw[p] - (P.W - 1), ew));
-        jw_hi[p] = min(Jw[p] - 1, floor_div_any(q0w + TQw_e - 1 + cw[p], ew));
-    }
+    for (int p = 0; p < NPH; ++p) ix::tap_range(q0w, TQw_e, cw[p], ew, Jw[p], P.W, jw_lo[p], jw_hi[p]);
 
     // ---- LDS layout of a staged chunk: float4 [octet][k-row h][d][h][w].  The
     // lanes that feed MFMA k-row h (h = lane/32) need channels h, h+2, h+4, h+6
@@ -233,20 +174,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
     auto decode_pos = [&](int pb, int &td, int &th, int &tw) -> bool {
         int c = col;
         asm volatile("" : "+v"(c));
-        const int pidx = (wpos * PBW + pb) * 32 + c;
-        const int pi = pidx < vol ? pidx : 0;
-        td = pi / plane;
-        const int rem = pi - td * plane;
-        th = rem / TQw;
-        tw = rem - th * TQw;
-        return pidx < vol && td < TQd_e && th < TQh_e && tw < TQw_e;
+        return ix::pos_decode(wpos * PBW + pb, c, vol, plane, TQw, TQd_e, TQh_e, TQw_e, td, th, tw);
     };
     int lane_off[PBW];  // float4 index of the lane's B reads at tap offset 0
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
         int td, th, tw;
         decode_pos(pb, td, th, tw);
-        lane_off[pb] = half * SLAB + (td * HH + th) * HW + tw;
+        lane_off[pb] = ix::b_lane_off(half, SLAB, td, th, tw, HH, HW);
     }
 
     const int CO_T = P.WCO * CBW;                   // co blocks per workgroup
@@ -291,9 +226,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                         for (int c = 0; c < 8; ++c) v[c] = ci0 + c < P.Cin ? src[(size_t)c * DHWin] : 0.0f;
                     }
-                    float4 *dst = reinterpret_cast<float4 *>(lds) + (2 * g * SLAB + pos);
-                    dst[0] = make_float4(v[0], v[2], v[4], v[6]);
-                    dst[SLAB] = make_float4(v[1], v[3], v[5], v[7]);
+                    float4 *l4 = reinterpret_cast<float4 *>(lds);
+                    l4[ix::stage_lds_index(g, SLAB, pos, 0)] = make_float4(v[0], v[2], v[4], v[6]);
+                    l4[ix::stage_lds_index(g, SLAB, pos, 1)] = make_float4(v[1], v[3], v[5], v[7]);
                 }
             }
             w += inc_w;
@@ -317,10 +252,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const int Jd = P.pJ[0][rho_d], cd = P.pc[0][rho_d];
     const int Jh = P.pJ[1][rho_h], ch = P.pc[1][rho_h];
     // ---- taps that touch the input for this box (border tiles skip the rest)
-    const int jd_lo = max(0, ceil_div_any(q0d + cd - (P.D - 1), ed));
-    const int jd_hi = min(Jd - 1, floor_div_any(q0d + TQd_e - 1 + cd, ed));
-    const int jh_lo = max(0, ceil_div_any(q0h + ch - (P.H - 1), eh));
-    const int jh_hi = min(Jh - 1, floor_div_any(q0h + TQh_e - 1 + ch, eh));
+    int jd_lo, jd_hi, jh_lo, jh_hi;
+    ix::tap_range(q0d, TQd_e, cd, ed, Jd, P.D, jd_lo, jd_hi);
+    ix::tap_range(q0h, TQh_e, ch, eh, Jh, P.H, jh_lo, jh_hi);
 
     v16f acc[NPH][CBW][PBW];
 #pragma unroll
@@ -367,7 +301,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                 for (int c = 0; c < CBW; ++c) {
                     const int cb = min(cb0 + c, P.cb_total - 1);
-                    const float4 *base = wp4 + (P.wp_off[ph] >> 2) + (size_t)cb * P.steps4[ph] * 64;
+                    const float4 *base = wp4 + ix::a_block_base(P, ph, cb);
                     wr[c] = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, 0x7FFFFFF0, 0x00020000);
                 }
                 const int lane16 = lane * 16;
@@ -382,9 +316,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 // index of its A operands; bo: float4 offset of its B operands.
                 int jd = jd_lo, jh = jh_lo, jw = jwl, g4 = 0;
                 auto next_group = [&](int &gi, int &bo) {
-                    gi = ((chunk * G4 + g4) * ntp + (jd * Jh + jh) * jwn + jw) * 64;
-                    bo = ((cd - ed * jd - lo_d_rel) * HH + (ch - eh * jh - lo_h_rel)) * HW +
-                         (cwp - ew * jw - lo_w_rel) + g4 * slab2;
+                    gi = ix::a_group_index(chunk, G4, g4, ntp, jd, Jh, jh, jwn, jw);
+                    bo = ix::b_group_off(cd, ed, jd, lo_d_rel, ch, eh, jh, lo_h_rel, cwp, ew, jw, lo_w_rel, HH, HW,
+                                         g4, slab2);
                     if (++g4 == G4) {
                         g4 = 0;
                         if (++jw > jwh) { jw = jwl; if (++jh > jh_hi) { jh = jh_lo; ++jd; } }
@@ -504,7 +438,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
         for (int p = 0; p < NPH; ++p) {
             const int ow = sw * (q0w + tw) + rw[p];
             ok[p][pb] = pos_ok && od < Do && oh < Ho && ow < Wo;
-            vofs[p][pb] = (unsigned)(4 * half * S + (od * Ho + oh) * Wo + ow) * 4u;
+            vofs[p][pb] = (unsigned)ix::out_voxel_off(half, S, od, Ho, oh, Wo, ow) * 4u;
         }
     }
     // both w-phases of a lane land in one aligned float pair (w even, w + 1)
@@ -523,7 +457,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
     if constexpr (PL) asm volatile("" : "+s"(row0));
     const bool rows_full = row0 + CBW * 32 <= Cout;  // every accumulator row is a channel
     char *outb = reinterpret_cast<char *>(P.out + ((size_t)n * P.Cout_total + (size_t)grp * Cout) * S);
-    auto row_u = [&](int c, int r) { return row0 + c * 32 + 8 * (r >> 2) + (r & 3); };
+    auto row_u = [&](int c, int r) { return ix::acc_row(row0, c, r); };
     auto row_ok = [&](int c, int r) { return rows_full || row_u(c, r) + 4 * half < Cout; };
     auto rowp = [&](int c, int r) { return outb + (size_t)row_u(c, r) * S * 4; };
     auto bias_of = [&](int c, int r, float dflt) {  // bias of the lane's row c, r (dflt: no bias)
@@ -737,7 +671,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
         }
         if (gn || bn) {
             __syncthreads();
-            const int tile = ((rho_d * sh + rho_h) * P.nwgroups + wgrp) * P.tiles_total + bx;
+            const int tile = ix::partial_tile(P, rho_d, rho_h, wgrp, bx);
             for (int row = tid; row < CO32; row += blockDim.x) {
                 const int co = co_tile * CO32 + row;
                 if (co >= Cout) continue;

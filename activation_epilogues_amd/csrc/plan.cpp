@@ -657,6 +657,15 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     return CONVT3D_OK;
 }
 
+// Chunks per row of the statistics pass over a conv output in memory (each
+// workgroup sums kRowStatChunk vectors of a row: float4 when the row length
+// is a multiple of 4, else float).
+int row_stat_chunks(int64_t S) {
+    const int64_t len = S % 4 == 0 ? S / 4 : S;
+    const int64_t c = (len + kRowStatChunk - 1) / kRowStatChunk;
+    return (int)(c < 1 ? 1 : c);
+}
+
 int make_plan(const convt3d_geom *g, const convt3d_epilogue *e, Plan *pl) {
     std::vector<Plan> c;
     const int st = plan_candidates(g, e, 1, &c);

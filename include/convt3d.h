@@ -40,6 +40,11 @@
  *     leave every output untouched.
  *   - Calls that share a workspace on overlapping streams race; give each
  *     concurrent call its own workspace.
+ *   - The library links the HIP runtime by its soname (libamdhip64.so.7) and
+ *     must share the runtime that owns the caller's memory and streams: load
+ *     it after that runtime (with PyTorch, after importing torch, which
+ *     carries its own copy).  Loaded first, it would pull in the system
+ *     runtime and the caller's would be loaded beside it.
  */
 #ifndef CONVT3D_H
 #define CONVT3D_H

@@ -95,18 +95,20 @@ def test_large_strides(stride, k, pad, out_pad, epi):
 SPLITS = [0, 7, 63, 455, 143, 103, 1, 260]
 
 
-@pytest.mark.skip(reason="the one run of these forced cases ended with the test process in a segmentation "
-                         "fault while pytest formatted an error raised inside a library call; the cause is "
-                         "not found yet (every forced plan's regions tile the output exactly, its LDS and "
-                         "workspace fit, checked on the host), so the cases stay off the GPU until it is")
+def border_workload(k, stride, split):
+    """Geometry on which every dim has both borders and an interior, with the
+    epilogue cycling over GroupNorm, BatchNorm and none."""
+    epi = [W.EPI_RELU_GROUPNORM, W.EPI_SCALE_BN_TRAIN_AVGPOOL, W.EPI_NONE][SPLITS.index(split) % 3]
+    return W.Workload(f"seg{split}k{k}s{stride}", 2, 16, 64, 10, 12, 14, k=k, stride=stride, pad=0, out_pad=0,
+                      bias=True, epi=epi, groups=8 if epi == W.EPI_RELU_GROUPNORM else 1, scale=2.0,
+                      seed=9100 + split + 10 * k)
+
+
 @pytest.mark.parametrize("k,stride", [(3, 1), (4, 2), (5, 1)])
 @pytest.mark.parametrize("split", SPLITS)
 def test_forced_border_segmentation_matches_oracle(k, stride, split, monkeypatch):
     from activation_epilogues_amd import convt3d as C
-    epi = [W.EPI_RELU_GROUPNORM, W.EPI_SCALE_BN_TRAIN_AVGPOOL, W.EPI_NONE][SPLITS.index(split) % 3]
-    wl = W.Workload(f"seg{split}k{k}s{stride}", 2, 16, 64, 10, 12, 14, k=k, stride=stride, pad=0, out_pad=0,
-                    bias=True, epi=epi, groups=8 if epi == W.EPI_RELU_GROUPNORM else 1, scale=2.0,
-                    seed=9100 + split + 10 * k)
+    wl = border_workload(k, stride, split)
     e = C.make_epilogue(wl.epi, wl.groups)
     base = C.convt3d_get_plan_info(geom_of(wl), e)
     monkeypatch.setenv("CONVT3D_PLAN", f"{base['variant']},{base['waves_co']},-1,-1,-1,-1,{split}")

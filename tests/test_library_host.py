@@ -411,3 +411,21 @@ def test_profile_kind_mask_is_checked():
         assert all(prof[k] == 0.0 for k in ("conv_ms", "finalize_ms", "normalize_ms", "reduce_ms", "prepack_ms"))
     assert lib.convt3d_profile_begin() == 0
     assert C.convt3d_profile_end()["calls"] == 0
+
+
+def test_library_binds_to_the_hip_runtime_torch_loads():
+    """Loading the library first must not leave two HIP runtimes in the process:
+    the binding imports torch before the library, so the library binds to
+    torch's runtime (which owns the caller's memory and streams)."""
+    import subprocess
+    import sys
+    code = ("from activation_epilogues_amd import convt3d as C\n"
+            "C.lib()\n"
+            "import torch\n"
+            "print('|'.join(C._hip_runtimes()))\n")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rts = res.stdout.strip().splitlines()[-1].split("|")
+    assert len(rts) == 1, rts
+    import torch
+    assert os.path.dirname(rts[0]) == os.path.join(os.path.dirname(torch.__file__), "lib"), rts
