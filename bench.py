@@ -6,8 +6,13 @@
 A step is one pass of the whole path over one batch of synthetic input that
 is already resident in HBM: re-lay the weights for the matrix cores
 (convt3d_prepack_weights), then convt3d_fused (convolution with the fused
-epilogue, statistics, normalisation).  The default workload is the
-[16,64,32,32,32] -> ConvTranspose3d(64->128, k3) -> ReLU -> GroupNorm(8) case.
+epilogue, statistics, normalisation).  The headline workload is the largest
+of the five configurations, x [8,128,32,32,32] -> ConvTranspose3d(128->128,
+k4, s2, p1) -> ReLU -> GroupNorm(16) (the largest tensors; the k5 BatchNorm
+layer has 2 % more multiply-adds and is reported beside it).  Every one of
+the five configurations is measured the same way in the same run and
+reported in ``all_configs``, each with the largest |error| of its output
+against the fp64 oracle on the same inputs.
 
 Before the warm-up the plan is chosen once by timing (convt3d_autotune, as a
 caller would do once per geometry); ``--no-tune`` keeps the cost model's
@@ -19,7 +24,8 @@ Prints ONE JSON line.  ``value`` is algorithmic GFLOP/s = 2 * (multiply-adds
 whose input voxel is in range) / time per step.  ``roofline`` describes the
 dominant kernel (the convolution kernel, FP32 MFMA bound): its duration comes
 from HIP events the library records on the launch stream over the timed
-region.  ``cpu_baseline`` times the fp64 CPU oracle on the host cores.
+region.  ``cpu_baseline`` times the fp64 CPU oracle on the host cores; the
+same oracle run gives ``max_abs_err`` of the timed plan's output.
 """
 from __future__ import annotations
 
@@ -74,29 +80,13 @@ def stored_traffic(workload: str, kernel: str = "convt3d_mfma_kernel"):
         return None, None
 
 
-def cpu_baseline(wl, inp, max_samples: int):
-    """The oracle (fp64, OpenMP) on the first samples of the same workload."""
-    import numpy as np
-    import oracle
-    from activation_epilogues_amd import workloads as W
-    n = min(wl.n, max_samples)
-    sub = wl.with_(n=n)
-    sub_inp = W.Inputs(x=np.ascontiguousarray(inp.x[:n]), w=inp.w, b=inp.b, gamma=inp.gamma, beta=inp.beta,
-                       rmean=inp.rmean, rvar=inp.rvar)
-    oracle.build()
-    t0 = time.perf_counter()
-    oracle.run_workload(sub, sub_inp)
-    dt = time.perf_counter() - t0
-    return n, dt, oracle.num_threads()
-
-
-def dense_equivalent(wl, call, ms: float) -> dict:
+def dense_equivalent(wl, out_dims, ms: float) -> dict:
     """The pages' way of counting the work, for context only: every output
     voxel times every input channel (of its group) times every kernel tap,
     as a direct convolution over a zero-inserted, zero-padded input would
     multiply (the p77 page's 424 G multiply-adds for its k5 layer)."""
     kd, kh, kw = wl.kdims
-    S = call.out_dims[0] * call.out_dims[1] * call.out_dims[2]
+    S = out_dims[0] * out_dims[1] * out_dims[2]
     macs = wl.n * wl.cout * S * (wl.cin // wl.conv_groups) * kd * kh * kw
     return {"gmac_per_step": round(macs / 1e9, 3), "gflops": round(2 * macs / (ms * 1e-3) / 1e9, 1),
             "note": "context only: counts zero-inserted and padding taps, not work done"}
@@ -190,41 +180,17 @@ def torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, fused_ms, reps
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="k3s1_gn")
-    ap.add_argument("--cpu-samples", type=int, default=16,
-                    help="batch samples the CPU oracle baseline runs (bounded)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-tune", action="store_true", help="keep the cost model's plan")
-    ap.add_argument("--plan", default=None, help="force a plan (CONVT3D_PLAN string); implies --no-tune")
-    ap.add_argument("--phase-loop", type=int, choices=(0, 1), default=None,
-                    help="force the phase-group loop off / on (with --plan)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step replayed from a captured HIP graph (context; value stays eager)")
-    ap.add_argument("--compare-torch", action="store_true",
-                    help="also time PyTorch's own ConvTranspose3d + epilogue ops, and its conv followed by "
-                         "convt3d_epilogue_only (context only)")
-    args = ap.parse_args()
-    if args.plan is not None:
-        os.environ["CONVT3D_PLAN"] = args.plan
-        args.no_tune = True
-    if args.phase_loop is not None:
-        os.environ["CONVT3D_PHASE_LOOP"] = str(args.phase_loop)
+HEADLINE = "k4s2_gn"
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
 
+def measure(wl, args, log=print):
+    """Tune, warm up and time one workload; returns its result dict (the
+    fields of the JSON line, without the top-level metric fields)."""
+    import numpy as np
     import torch
     from activation_epilogues_amd import convt3d as C
     from activation_epilogues_amd import workloads as W
 
-    wl = W.BY_NAME[args.workload]
     inp = W.make_inputs(wl)
     dev = torch.device("cuda:0")
     g = C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad,
@@ -244,7 +210,7 @@ def main():
     if not args.no_tune:
         call.prepack(w, stream)
         tune = call.autotune(x, b, gamma, beta, stream)
-        print(f"[bench] plan tuned: {tune}", file=sys.stderr, flush=True)
+        log(f"[bench] {wl.name}: plan tuned: {tune}")
     info = call.plan_info()
     # the eval path runs no convolution; its throughput is quoted against the
     # multiply-adds of the convolution it replaces (same output)
@@ -259,7 +225,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps), timing {args.steps} steps", file=sys.stderr, flush=True)
+    log(f"[bench] {wl.name}: warmup done ({args.warmup} steps), timing {args.steps} steps")
 
     # per-step events on the launch stream give the median step time; the
     # library brackets only the dominant kernel (the roofline's) with HIP
@@ -281,7 +247,10 @@ def main():
     ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
         step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     gflops = flops / (ms * 1e-3) / 1e9
-    print(f"[bench] timed region done: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    log(f"[bench] {wl.name}: timed region done: {ms:.3f} ms/step")
+    # the output of the last timed step (every step computes the same output
+    # from the same inputs; BatchNorm's running statistics do not enter it)
+    out_gpu = call.out.detach().cpu().numpy().astype(np.float64)
 
     # per-kernel breakdown (context): the same steps again after the timed
     # region, every kernel bracketed
@@ -367,37 +336,41 @@ def main():
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        n_cpu, dt, cores = cpu_baseline(wl, inp, args.cpu_samples)
-        cpu_flops = flops * n_cpu / wl.n
-        cpu = {"value": round(cpu_flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
-               "sample": f"{n_cpu} of {wl.n} samples of {wl.name}, whole path (conv + epilogue), fp64",
-               "seconds": round(dt, 2)}
+    del call, x, w, b, gamma, beta, rmean, rvar
+    torch.cuda.empty_cache()
 
-    res = {
-        "metric": METRIC,
+    # the fp64 oracle on the same inputs (the whole batch): CPU baseline time
+    # and the largest |error| of the timed plan's output
+    cpu = None
+    max_abs_err = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] {wl.name}: running the CPU oracle on the same inputs")
+        import oracle
+        oracle.build()
+        t0 = time.perf_counter()
+        ref = oracle.run_workload(wl, inp)
+        dt = time.perf_counter() - t0
+        max_abs_err = float(np.abs(out_gpu - ref.out.reshape(out_gpu.shape)).max())
+        del ref
+        cpu = {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"all {wl.n} samples of {wl.name}, whole path (conv + epilogue), fp64",
+               "seconds": round(dt, 3)}
+
+    return {
         "value": round(gflops, 2),
-        "unit": "GFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "ms_per_step_median": round(ms_median, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded N(0,1) input, U(+-1/sqrt(cin*k^3)) weights)",
         "config": {"workload": wl.name, "x": list(wl.x_shape), "cout": wl.cout, "k": wl.k, "stride": wl.stride,
-                   "pad": wl.pad, "out_pad": wl.out_pad, "bias": wl.bias,
-                   "epilogue": W.EPI_NAMES[wl.epi], "groups": wl.groups, "scale": wl.scale},
+                   "pad": wl.pad, "out_pad": wl.out_pad, "bias": wl.bias, "dilation": wl.dilation,
+                   "conv_groups": wl.conv_groups, "epilogue": W.EPI_NAMES[wl.epi], "groups": wl.groups,
+                   "scale": wl.scale},
         "value_kind": ("conv-equivalent: 2 x the in-range multiply-adds of the ConvTranspose3d whose pooled, "
                        "eval-mode-normalised output this path computes without running it") if evalmode else
                       "algorithmic: 2 x in-range multiply-adds of the ConvTranspose3d run",
         "pct_fp32_mfma_peak_whole_step": None if evalmode else round(100 * gflops / 1e3 / PEAK_FP32_MFMA_TFLOPS, 2),
-        "dense_equivalent": dense_equivalent(wl, call, ms),
+        "max_abs_err": max_abs_err,
+        "tolerance": 1e-4,
+        "dense_equivalent": dense_equivalent(wl, info_dims(wl), ms),
         "roofline": roofline,
         "kernels": kernels,
         "plan": {k: v for k, v in info.items()},
@@ -407,6 +380,89 @@ def main():
         "torch_comparison": comparison,
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
     }
+
+
+def info_dims(wl):
+    """Output dims of a workload (for the dense-equivalent count)."""
+    from activation_epilogues_amd import convt3d as C
+    g = C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad,
+                    wl.dilation, wl.conv_groups)
+    return C.convt3d_output_dims(g)
+
+
+def summary(r):
+    """One config's line in all_configs."""
+    k = r["kernels"]
+    return {"ms_per_step": r["ms_per_step"], "gflops": r["value"],
+            "conv_frac_fp32_mfma": None if r["roofline"]["bound"] != "mfma" else r["roofline"]["frac"],
+            "conv_ms": r["roofline"]["avg_launch_ms"],
+            "normalize_frac_hbm": k.get("normalize_frac_hbm"), "normalize_ms": k["normalize_ms"] or None,
+            "max_abs_err": r["max_abs_err"],
+            "oracle_s": None if r["cpu_baseline"] is None else r["cpu_baseline"]["seconds"],
+            "plan_string": r["plan_string"], "workload": r["config"]["workload"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, help="the workload of the JSON line's headline fields")
+    ap.add_argument("--only", action="store_true",
+                    help="measure only --workload (default: also every one of the five configurations)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle (no CPU time, no max_abs_err)")
+    ap.add_argument("--no-tune", action="store_true", help="keep the cost model's plan")
+    ap.add_argument("--plan", default=None, help="force a plan (CONVT3D_PLAN string); implies --no-tune, --only")
+    ap.add_argument("--phase-loop", type=int, choices=(0, 1), default=None,
+                    help="force the phase-group loop off / on (with --plan)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (context; value stays eager)")
+    ap.add_argument("--compare-torch", action="store_true",
+                    help="also time PyTorch's own ConvTranspose3d + epilogue ops, and its conv followed by "
+                         "convt3d_epilogue_only (context only)")
+    args = ap.parse_args()
+    if args.plan is not None:
+        os.environ["CONVT3D_PLAN"] = args.plan
+        args.no_tune = True
+        args.only = True
+    if args.phase_loop is not None:
+        os.environ["CONVT3D_PHASE_LOOP"] = str(args.phase_loop)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch  # noqa: F401  (loads torch's HIP runtime before the library)
+    from activation_epilogues_amd import workloads as W
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    head = measure(W.BY_NAME[args.workload], args, log)
+    all_configs = None
+    if not args.only:
+        all_configs = {}
+        for wl in W.WORKLOADS:
+            r = head if wl.name == args.workload else measure(wl, args, log)
+            all_configs[wl.name] = summary(r)
+    res = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "ms_per_step_median": head["ms_per_step_median"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) input, U(+-1/sqrt(cin*k^3)) weights)",
+    }
+    res.update({k: v for k, v in head.items() if k not in res})
+    res["all_configs"] = all_configs
     print(json.dumps(res), flush=True)
 
 
