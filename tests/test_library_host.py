@@ -33,7 +33,7 @@ def geom_of(wl, n=None):
 def test_library_exports_every_declared_function():
     names = header_functions()
     assert len(names) >= 8, names
-    L = ctypes.CDLL(C.LIB_PATH)
+    L = C.lib()  # through the binding: after torch's HIP runtime
     for nm in names:
         assert hasattr(L, nm), nm
     assert sorted(C.EXPORTED) == names
