@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libconvt3d.so")
-SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "epilogue.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "kernels.hip", "epilogue.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -24,7 +24,9 @@ POOLED = (EPI_SCALE_BN_TRAIN_AVGPOOL, EPI_SCALE_BN_EVAL_AVGPOOL)
 STATUS = {
     0: "OK", 1: "ERR_NULL", 2: "ERR_GEOMETRY", 3: "ERR_GROUPS", 4: "ERR_ALIGNMENT",
     5: "ERR_WORKSPACE", 6: "ERR_UNSUPPORTED", 7: "ERR_LAUNCH", 8: "ERR_TOO_LARGE", 9: "ERR_ALIAS",
+    10: "ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 32 << 20  # CONVT3D_NOALLOC_SCRATCH_BYTES
 
 
 class Geom(ctypes.Structure):
@@ -127,6 +129,8 @@ def lib():
         L.convt3d_workspace_size.argtypes = [P(Geom), P(Epilogue)]
         L.convt3d_fused.restype = ctypes.c_int
         L.convt3d_fused.argtypes = [vp, vp, vp, P(Geom), P(Epilogue), vp, vp, sz, vp]
+        L.convt3d_fused_noalloc.restype = ctypes.c_int
+        L.convt3d_fused_noalloc.argtypes = [vp, vp, vp, P(Geom), P(Epilogue), vp, vp]
         L.convt3d_autotune.restype = ctypes.c_int
         L.convt3d_autotune.argtypes = [vp, vp, vp, P(Geom), P(Epilogue), vp, vp, sz, vp, P(TuneResult)]
         L.convt3d_get_plan_info.restype = ctypes.c_int
@@ -143,7 +147,8 @@ def lib():
 
 EXPORTED = ["convt3d_status_string", "convt3d_output_dims", "convt3d_output_elems",
             "convt3d_packed_weight_bytes", "convt3d_prepack_weights", "convt3d_eval_weight_bytes",
-            "convt3d_prepack_eval_weights", "convt3d_workspace_size", "convt3d_fused", "convt3d_autotune",
+            "convt3d_prepack_eval_weights", "convt3d_workspace_size", "convt3d_fused", "convt3d_fused_noalloc",
+            "convt3d_autotune",
             "convt3d_epilogue_workspace_size", "convt3d_epilogue_only", "convt3d_get_plan_info",
             "convt3d_profile_begin", "convt3d_profile_begin_kinds", "convt3d_profile_end"]
 
@@ -248,6 +253,14 @@ def convt3d_fused(x, w_packed, bias, geom: Geom, epi: Epilogue, out, workspace, 
                              _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream))
     if check and st:
         raise Convt3dError(st, "convt3d_fused")
+    return st
+
+
+def convt3d_fused_noalloc(x, w_packed, bias, geom: Geom, epi: Epilogue, out, stream=None, check=True) -> int:
+    st = lib().convt3d_fused_noalloc(_ptr(x), _ptr(w_packed), _ptr(bias), ctypes.byref(geom), ctypes.byref(epi),
+                                     _ptr(out), _stream(stream))
+    if check and st:
+        raise Convt3dError(st, "convt3d_fused_noalloc")
     return st
 
 

@@ -123,6 +123,19 @@ void store_tuned(const convt3d_geom *g, const convt3d_epilogue *e, const Plan &p
         }
 }
 
+}  // namespace
+
+int convt3d::current_plan_workspace(const convt3d_geom *g, const convt3d_epilogue *e, size_t *bytes) {
+    if (!bytes) return CONVT3D_ERR_NULL;
+    Plan pl;
+    const int st = cached_plan(g, e, &pl);
+    if (st) return st;
+    *bytes = pl.ws_bytes;
+    return CONVT3D_OK;
+}
+
+namespace {
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---- optional per-kernel timing with HIP events (measurement only)
@@ -205,6 +218,7 @@ const char *convt3d_status_string(int status) {
         case CONVT3D_ERR_LAUNCH: return "HIP kernel launch failed";
         case CONVT3D_ERR_TOO_LARGE: return "tensor too large (more than 2^31 elements)";
         case CONVT3D_ERR_ALIAS: return "out overlaps x";
+        case CONVT3D_ERR_SCRATCH: return "the plan needs more workspace than the static scratch of convt3d_fused_noalloc";
         default: return "unknown status";
     }
 }

@@ -164,6 +164,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                     const Plan *like = nullptr);
 void fill_conv_params(const Plan &pl, ConvParams *cp);
 int make_eval_geom(const convt3d_geom *g, EvalGeom *eg);  // CONVT3D_ERR_UNSUPPORTED for k > kEvalMaxK
+// Workspace bytes of the plan convt3d_fused runs for (g, e) now (api.cpp).
+int current_plan_workspace(const convt3d_geom *g, const convt3d_epilogue *e, size_t *bytes);
 
 // Launchers (kernels.hip: pre-pack and convolution).  Return a hipError_t as int.
 // launch_prepack packs one channel group: w points at its [cig, cog, k...] slice.

@@ -121,7 +121,9 @@ enum convt3d_status {
     CONVT3D_ERR_UNSUPPORTED = 6,   /* epilogue kind unknown or not valid for the call */
     CONVT3D_ERR_LAUNCH = 7,        /* HIP reported an error when launching            */
     CONVT3D_ERR_TOO_LARGE = 8,     /* a tensor exceeds 2^31 elements                  */
-    CONVT3D_ERR_ALIAS = 9          /* out overlaps x                                  */
+    CONVT3D_ERR_ALIAS = 9,         /* out overlaps x                                  */
+    CONVT3D_ERR_SCRATCH = 10       /* convt3d_fused_noalloc: the plan needs more workspace than the
+                                      library's static scratch (CONVT3D_NOALLOC_SCRATCH_BYTES) */
 };
 
 /* Human-readable text for a status code (static storage). */
@@ -184,6 +186,27 @@ size_t convt3d_workspace_size(const convt3d_geom *geom, const convt3d_epilogue *
 int convt3d_fused(const float *x, const void *w_packed, const float *bias,
                   const convt3d_geom *geom, const convt3d_epilogue *epi, float *out,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* The fused forward pass for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): convt3d_fused with the library's own static device scratch as
+ * the workspace, so no workspace argument.  Same arguments otherwise, same
+ * plan (the tuned one after convt3d_autotune), same kernels and results.
+ * It allocates no device memory: the scratch is a device array of
+ * CONVT3D_NOALLOC_SCRATCH_BYTES (32 MiB) that each device the library runs
+ * on holds until the process ends; its address is looked up once per device
+ * at that device's first call (the first call for a new geometry also plans
+ * it on the host, as convt3d_fused does).  A plan needing more workspace than
+ * the scratch returns CONVT3D_ERR_SCRATCH before anything is launched (use
+ * convt3d_fused with a workspace of convt3d_workspace_size bytes instead).
+ * Every call on one device shares that device's scratch: calls that overlap
+ * on one device (different streams, or host threads) race.  Each call writes
+ * every scratch word it reads before reading it, so the previous call's
+ * contents are never cleared. */
+#define CONVT3D_NOALLOC_SCRATCH_BYTES (32u << 20)
+int convt3d_fused_noalloc(const float *x, const void *w_packed, const float *bias,
+                          const convt3d_geom *geom, const convt3d_epilogue *epi, float *out,
+                          void *stream);
 
 /* Plan selection by timing.  The cost model ranks the kernel configurations
  * for (geom, epi); this runs the best few of them on the caller's buffers

@@ -81,7 +81,7 @@ def test_output_dims_match_oracle():
 
 
 def test_status_strings():
-    for st in range(10):
+    for st in range(11):
         assert C.status_string(st) != "unknown status"
     assert C.status_string(123) == "unknown status"
 
