@@ -623,7 +623,7 @@ int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
                                               epi->gamma, epi->beta, ab, epi->stats_out, stream);
                 })) ||
                 !ok(timed(kTimedNormalize, stream,
-                          [&] { return launch_normalize(y, out, ab, n * c, spatial, true, stream); })))
+                          [&] { return launch_normalize(y, out, ab, n * c, spatial, true, stream, true); })))
                 return CONVT3D_ERR_LAUNCH;
             break;
         }

@@ -27,6 +27,12 @@ constexpr int kEvalTargetBlocks = 2048;  // eval-mode bin sums: workgroups to ai
 constexpr int kTuneCandidates = 12;
 constexpr int kTuneBorderAlternatives = 8;
 
+// sigmoid(p) for a softmax probability p in [0, 1]: the degree-6 Chebyshev
+// interpolant of sigmoid on [0, 1] in the monomial basis, float32 (Horner's
+// rule; |error| < 1e-7; sigmoid_poly.py beside the kernels prints them).
+constexpr float kSigmoidPoly[7] = {5.000000000e-01f,  2.500010431e-01f, -1.699157474e-05f, -2.072521672e-02f,
+                                   -3.389832564e-04f, 2.655707300e-03f, -5.169519573e-04f};
+
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
 // taps that reach it are t = r + ts*j (j = 0..J-1) from input i = q + c - e*j,
 // where with dilation dl and g = gcd(dl, s): ts = s/g, e = dl/g, r is the
@@ -178,7 +184,7 @@ int launch_conv(const Plan &pl, const ConvParams &cp, void *stream);
 int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, int chan_step, double count,
                        float eps, const float *gamma, const float *beta, float *ab, float *stats_out, void *stream);
 int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool relu,
-                     void *stream);
+                     void *stream, bool stream_out = false);
 int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,
                        float *out, void *stream);
 int row_stat_chunks(int64_t S);

@@ -11,11 +11,12 @@
 //                            the pooled output and the running statistics.
 //  * row_stats_kernel     -- per (n, c, chunk) sums of v and v^2 over a conv
 //                            output held in memory (v = ReLU(y) or scale*y).
-//  * softmax_pass_kernel  -- channel softmax then sigmoid over a conv output in
-//                            memory: one pass for the running max and sum of
-//                            exponentials, one for the result (more than 64
-//                            channels); softmax_regs_kernel holds up to 64
-//                            channels of a position in registers (one read).
+//  * softmax_rows_kernel  -- channel softmax then sigmoid over a conv output in
+//                            memory, one read and one write: the channels of a
+//                            position in the registers of one or more waves
+//                            (up to 1024 channels); softmax_pass_kernel, for
+//                            more, reads twice (running max and sum of
+//                            exponentials, then the result).
 //  * bn_eval_rows_kernel  -- eval-mode BatchNorm + pool from per-row sums.
 //  * eval_pack_kernel     -- tap-summed weights per input bin (eval mode).
 //  * eval_binsum_kernel   -- sums of x over the input bins of each (n, cin).
@@ -54,6 +55,25 @@ __device__ __forceinline__ float2 block_sum2(float a, float b, float2 *red) {
     __syncthreads();
     const float2 r = make_float2((red[0].x + red[1].x) + (red[2].x + red[3].x),
                                  (red[0].y + red[1].y) + (red[2].y + red[3].y));
+    __syncthreads();  // red may be reused
+    return r;
+}
+
+// Sum of two doubles over a kStatThreads workgroup in a fixed order: a 64-lane
+// xor-shuffle tree per wave, then the wave totals in wave order.  red holds
+// kStatThreads / 64 double2; every thread gets the result.
+__device__ __forceinline__ double2 block_sum2_f64(double a, double b, double2 *red) {
+    for (int off = 32; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off);
+        b += __shfl_xor(b, off);
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_double2(a, b);
+    __syncthreads();
+    double2 r = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) {
+        r.x += red[w].x;
+        r.y += red[w].y;
+    }
     __syncthreads();  // red may be reused
     return r;
 }
@@ -97,21 +117,12 @@ __global__ __launch_bounds__(kStatThreads) void gn_finalize_kernel(const float *
             a2 += (double)v[u].y;
         }
     }
-    __shared__ double r1[kStatThreads], r2[kStatThreads];
+    __shared__ double2 red[kStatThreads / 64];
     __shared__ double mean_s, rstd_s;
-    r1[threadIdx.x] = a1;
-    r2[threadIdx.x] = a2;
-    __syncthreads();
-    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) {
-            r1[threadIdx.x] += r1[threadIdx.x + off];
-            r2[threadIdx.x] += r2[threadIdx.x + off];
-        }
-        __syncthreads();
-    }
+    const double2 tot = block_sum2_f64(a1, a2, red);
     if (threadIdx.x == 0) {
-        const double mean = r1[0] / count;
-        double var = r2[0] / count - mean * mean;
+        const double mean = tot.x / count;
+        double var = tot.y / count - mean * mean;
         if (var < 0.0) var = 0.0;
         mean_s = mean;
         rstd_s = 1.0 / sqrt(var + (double)eps);
@@ -161,10 +172,11 @@ __device__ __forceinline__ void store_stream(V *p, const V &v) {
 // ReLU(src).  Block row y is one (n, c) channel (rows beyond gridDim.y are
 // taken in further passes), so (a, b) is one scalar load; each thread issues
 // kNormUnroll loads before its stores to keep enough bytes in flight for HBM.
-// src == out is the in-place form.  NT: non-temporal loads and stores, for
-// tensors well past the 256 MB last-level cache (a tensor the conv has just
-// written and that still partly sits in that cache reads faster without).
-template <class V, bool RELU, bool NT>
+// src == out is the in-place form.  NT: non-temporal loads, for tensors well
+// past the 256 MB last-level cache (a tensor the conv has just written and
+// that still partly sits in that cache reads faster without); NTS:
+// non-temporal stores.
+template <class V, bool RELU, bool NT, bool NTS>
 __global__ __launch_bounds__(256) void normalize_kernel(const V *src, V *out, const float2 *ab, int rows,
                                                         int row_len) {
     for (int row = blockIdx.y; row < rows; row += gridDim.y) {
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(const V *src, V *out, co
                     const float x = RELU ? fmaxf(c[e], 0.0f) : c[e];
                     c[e] = fmaf(p.x, x, p.y);
                 }
-                store_stream<NT>(o + i, v[k]);
+                store_stream<NTS>(o + i, v[k]);
             }
         }
     }
@@ -219,22 +231,13 @@ __global__ __launch_bounds__(kStatThreads) void bn_finalize_kernel(const float *
             a2 += (double)v[u].y;
         }
     }
-    __shared__ double r1[kStatThreads], r2[kStatThreads];
+    __shared__ double2 red[kStatThreads / 64];
     __shared__ double mean_s, rstd_s;
-    r1[threadIdx.x] = a1;
-    r2[threadIdx.x] = a2;
-    __syncthreads();
-    for (int off = blockDim.x / 2; off > 0; off >>= 1) {
-        if ((int)threadIdx.x < off) {
-            r1[threadIdx.x] += r1[threadIdx.x + off];
-            r2[threadIdx.x] += r2[threadIdx.x + off];
-        }
-        __syncthreads();
-    }
+    const double2 tot = block_sum2_f64(a1, a2, red);
     if (threadIdx.x == 0) {
         const double cnt = (double)N * S;
-        const double mean = r1[0] / cnt;
-        double var = r2[0] / cnt - mean * mean;
+        const double mean = tot.x / cnt;
+        double var = tot.y / cnt - mean * mean;
         if (var < 0.0) var = 0.0;
         mean_s = mean;
         rstd_s = 1.0 / sqrt(var + (double)eps);
@@ -366,32 +369,106 @@ __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out,
     }
 }
 
-// The same for C <= CR channels with one read: thread = (n, one position),
-// its C values held in registers (CR of them, unused ones at -inf), then max,
-// exponentials, sum and the result.  out may equal src.
-template <int CR>
-__global__ __launch_bounds__(256) void softmax_regs_kernel(const float *src, float *out, int N, int C, int S) {
-    const int s = blockIdx.x * 256 + threadIdx.x;
-    if (s >= S) return;
+// Channel softmax then sigmoid of a conv output in memory, [n][C][S], with
+// one read and one write.  A position group is WPP waves (WPP = ceil(C / CR))
+// covering 64*VEC positions: lane l of the group's wave w holds channels
+// [w*CR, (w+1)*CR) of positions s0 + VEC*l .. + VEC-1 in registers, so every
+// channel row of the group is one coalesced access of 256*VEC bytes.  The
+// waves combine their maxima and sums of exponentials through LDS in a fixed
+// order.  A workgroup holds blockDim / (64*WPP) position groups.  sigmoid of
+// the probability e/sum is the polynomial of kSigmoidPoly, evaluated in e with
+// coefficients scaled by powers of 1/sum.  out may equal src (each thread
+// writes only what it read).  NT: non-temporal loads (tensors past the
+// last-level cache); the output, which nothing here reads again, is stored
+// non-temporally.  S is counted in VEC-vectors.
+template <int CR, int VEC, bool NT>
+__global__ __launch_bounds__(1024) void softmax_rows_kernel(const float *src, float *out, int N, int C, int S,
+                                                            int WPP) {
+    typedef float vec_t __attribute__((ext_vector_type(VEC)));
+    __shared__ float red[1024 * VEC];  // [wave][lane][VEC]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int grp = wave / WPP, wq = wave - grp * WPP;
+    const int groups = (int)blockDim.x / (64 * WPP);
+    const int s = (blockIdx.x * groups + grp) * 64 + lane;  // in vectors
+    const bool live = s < S;
+    const int c0 = wq * CR;
+    const int nc = min(CR, C - c0);                          // channels of this wave (the last may hold fewer)
+    const int gw0 = (grp * WPP * 64 + lane) * VEC;           // LDS slot of this lane in the group's first wave
     for (int n = blockIdx.y; n < N; n += gridDim.y) {
-        const float *p = src + (size_t)n * C * S + s;
-        float *o = out + (size_t)n * C * S + s;
-        float v[CR];
-#pragma unroll
-        for (int c = 0; c < CR; ++c) v[c] = c < C ? p[(size_t)c * S] : -INFINITY;
-        float m = v[0];
-#pragma unroll
-        for (int c = 1; c < CR; ++c) m = fmaxf(m, v[c]);
-        float l = 0.0f;
+        const vec_t *p = reinterpret_cast<const vec_t *>(src) + ((size_t)n * C + c0) * S + s;
+        vec_t v[CR];
 #pragma unroll
         for (int c = 0; c < CR; ++c) {
-            v[c] = fast_exp(v[c] - m);  // 0 for the unused (-inf) entries
-            l += v[c];
+            v[c] = -INFINITY;
+            if (live && c < nc) {
+                if constexpr (NT) v[c] = __builtin_nontemporal_load(p + (size_t)c * S);
+                else v[c] = p[(size_t)c * S];
+            }
         }
-        const float inv = __builtin_amdgcn_rcpf(l);
+        float m[VEC], l[VEC], d[VEC][7];
 #pragma unroll
-        for (int c = 0; c < CR; ++c)
-            if (c < C) o[(size_t)c * S] = __builtin_amdgcn_rcpf(1.0f + fast_exp(-v[c] * inv));
+        for (int e = 0; e < VEC; ++e) {
+            m[e] = v[0][e];
+#pragma unroll
+            for (int c = 1; c < CR; ++c) m[e] = fmaxf(m[e], v[c][e]);
+        }
+        if (WPP > 1) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) red[threadIdx.x * VEC + e] = m[e];
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                m[e] = red[gw0 + e];
+                for (int j = 1; j < WPP; ++j) m[e] = fmaxf(m[e], red[gw0 + 64 * VEC * j + e]);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float ml = m[e] * kLog2e;
+            l[e] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CR; ++c) {
+                v[c][e] = __builtin_amdgcn_exp2f(fmaf(v[c][e], kLog2e, -ml));  // 0 for unused (-inf) entries
+                l[e] += v[c][e];
+            }
+        }
+        if (WPP > 1) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) red[threadIdx.x * VEC + e] = l[e];
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                l[e] = red[gw0 + e];
+                for (int j = 1; j < WPP; ++j) l[e] += red[gw0 + 64 * VEC * j + e];
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float inv = __builtin_amdgcn_rcpf(l[e]);
+            d[e][0] = kSigmoidPoly[0];
+            float ik = inv;
+#pragma unroll
+            for (int k = 1; k < 7; ++k) {
+                d[e][k] = kSigmoidPoly[k] * ik;
+                ik *= inv;
+            }
+        }
+        vec_t *o = reinterpret_cast<vec_t *>(out) + ((size_t)n * C + c0) * S + s;
+#pragma unroll
+        for (int c = 0; c < CR; ++c) {
+            if (!live || c >= nc) continue;
+            vec_t y;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float t = d[e][6];
+#pragma unroll
+                for (int k = 5; k >= 0; --k) t = fmaf(t, v[c][e], d[e][k]);
+                y[e] = t;
+            }
+            __builtin_nontemporal_store(y, o + (size_t)c * S);
+        }
     }
 }
 
@@ -592,35 +669,40 @@ int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int
     return (int)hipGetLastError();
 }
 
-template <class V, bool RELU, bool NT>
+template <class V, bool RELU, bool NT, bool NTS>
 static void launch_normalize_t(const float *src, float *out, const float *ab, int rows, int len, void *stream) {
     const int gx = (len + 256 * kNormUnroll - 1) / (256 * kNormUnroll);
     const int gy = rows < 65535 ? rows : 65535;
-    hipLaunchKernelGGL((normalize_kernel<V, RELU, NT>), dim3(gx, gy), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL((normalize_kernel<V, RELU, NT, NTS>), dim3(gx, gy), dim3(256), 0, (hipStream_t)stream,
                        reinterpret_cast<const V *>(src), reinterpret_cast<V *>(out),
                        reinterpret_cast<const float2 *>(ab), rows, len);
 }
 
 template <class V, bool RELU>
 static void launch_normalize_nt(const float *src, float *out, const float *ab, int rows, int len, bool nt,
-                                void *stream) {
-    if (nt) launch_normalize_t<V, RELU, true>(src, out, ab, rows, len, stream);
-    else launch_normalize_t<V, RELU, false>(src, out, ab, rows, len, stream);
+                                bool nts, void *stream) {
+    if (nt && nts) launch_normalize_t<V, RELU, true, true>(src, out, ab, rows, len, stream);
+    else if (nt) launch_normalize_t<V, RELU, true, false>(src, out, ab, rows, len, stream);
+    else if (nts) launch_normalize_t<V, RELU, false, true>(src, out, ab, rows, len, stream);
+    else launch_normalize_t<V, RELU, false, false>(src, out, ab, rows, len, stream);
 }
 
+// stream_out: the output is not read again soon (a standalone epilogue's
+// result): store it non-temporally whatever its size
 int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool relu,
-                     void *stream) {
+                     void *stream, bool stream_out) {
     const bool vec = S % 4 == 0;
     const int len = (int)(vec ? S / 4 : S);
     // measured: non-temporal access pays for a 1.07 GB tensor (+5 %) and
     // costs for a 0.32 GB one just written by the conv (-4 %)
     const bool nt = (double)rows * (double)S * sizeof(float) > (double)kStreamBytes;
+    const bool nts = nt || stream_out;
     if (vec) {
-        if (relu) launch_normalize_nt<float4, true>(src, out, ab, rows, len, nt, stream);
-        else launch_normalize_nt<float4, false>(src, out, ab, rows, len, nt, stream);
+        if (relu) launch_normalize_nt<float4, true>(src, out, ab, rows, len, nt, nts, stream);
+        else launch_normalize_nt<float4, false>(src, out, ab, rows, len, nt, nts, stream);
     } else {
-        if (relu) launch_normalize_nt<float, true>(src, out, ab, rows, len, nt, stream);
-        else launch_normalize_nt<float, false>(src, out, ab, rows, len, nt, stream);
+        if (relu) launch_normalize_nt<float, true>(src, out, ab, rows, len, nt, nts, stream);
+        else launch_normalize_nt<float, false>(src, out, ab, rows, len, nt, nts, stream);
     }
     return (int)hipGetLastError();
 }
@@ -660,18 +742,35 @@ int launch_row_stats(const float *y, int N, int C, int64_t S, bool relu, float m
 
 int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, void *stream) {
     const int gy = N < 65535 ? N : 65535;
-    if (C <= 64) {  // every channel of a position in registers: one read of y
-        const int len = (int)S;
-        const dim3 grid((len + 255) / 256, gy);
-        if (C <= 16)
-            hipLaunchKernelGGL(softmax_regs_kernel<16>, grid, dim3(256), 0, (hipStream_t)stream, src, out, N, C, len);
-        else if (C <= 32)
-            hipLaunchKernelGGL(softmax_regs_kernel<32>, grid, dim3(256), 0, (hipStream_t)stream, src, out, N, C, len);
-        else
-            hipLaunchKernelGGL(softmax_regs_kernel<64>, grid, dim3(256), 0, (hipStream_t)stream, src, out, N, C, len);
-        return (int)hipGetLastError();
-    }
     const bool nt = (double)N * C * (double)S * sizeof(float) > (double)kStreamBytes;
+    if (C <= 1024) {  // every channel of a position in registers: one read of y
+        // lanes hold CR channels x VEC positions (CR * VEC <= 64 registers);
+        // measured on the 64- and 256-channel layers' y: two positions per lane
+        // move 5.4 TB/s (the rate of a plain device copy), one 4.6-5.4, four 4.9-5.1
+        int vec = 2;
+        while (vec > 1 && (S % vec != 0 || C * vec > 1024)) vec /= 2;  // at most 16 waves per group
+        const int cr_max = 64 / vec;
+        const int CR = C <= cr_max / 4 ? cr_max / 4 : C <= cr_max / 2 ? cr_max / 2 : cr_max;
+        const int wpp = (C + CR - 1) / CR;             // waves per position group (<= 16)
+        {
+            const int groups = wpp <= 4 ? 4 / wpp : 1;  // position groups per workgroup
+            const int len = (int)(S / vec);
+            const dim3 grid((len + 64 * groups - 1) / (64 * groups), gy), block(64 * wpp * groups);
+            auto go = [&](auto kern) {
+                hipLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)stream, src, out, N, C, len, wpp);
+            };
+#define CONVT3D_SM(cr, v)                                                                        \
+            if (CR == cr && vec == v) {                                                          \
+                nt ? go(softmax_rows_kernel<cr, v, true>) : go(softmax_rows_kernel<cr, v, false>); \
+                return (int)hipGetLastError();                                                   \
+            }
+            CONVT3D_SM(16, 1) CONVT3D_SM(32, 1) CONVT3D_SM(64, 1)
+            CONVT3D_SM(8, 2) CONVT3D_SM(16, 2) CONVT3D_SM(32, 2)
+            CONVT3D_SM(4, 4) CONVT3D_SM(8, 4) CONVT3D_SM(16, 4)
+#undef CONVT3D_SM
+            return (int)hipErrorInvalidValue;
+        }
+    }
     if (S % 4 == 0) {
         const int len = (int)(S / 4);
         const dim3 grid((len + 255) / 256, gy);

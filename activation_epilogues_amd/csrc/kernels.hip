@@ -531,15 +531,12 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 // coefficients are printed by sigmoid_poly.py beside this file),
                 // sum_k c_k q^k = sum_k (c_k / sum^k) e^k by Horner's rule in e.
                 const float inv = __builtin_amdgcn_rcpf(sum);
-                constexpr float kSig[7] = {5.000000000e-01f,  2.500010431e-01f, -1.699157474e-05f,
-                                           -2.072521672e-02f, -3.389832564e-04f, 2.655707300e-03f,
-                                           -5.169519573e-04f};
                 float d[7];
-                d[0] = kSig[0];
+                d[0] = kSigmoidPoly[0];
                 float ik = inv;
 #pragma unroll
                 for (int k = 1; k < 7; ++k) {
-                    d[k] = kSig[k] * ik;
+                    d[k] = kSigmoidPoly[k] * ik;
                     ik *= inv;
                 }
 #pragma unroll

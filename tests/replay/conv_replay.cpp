@@ -430,7 +430,7 @@ int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int
     return 0;
 }
 
-int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool, void *) {
+int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool, void *, bool) {
     in_buf(find_buf(src), src, 0, (int64_t)rows * S, "normalise read");
     in_buf(find_buf(out), out, 0, (int64_t)rows * S, "normalise write");
     in_buf(find_buf(ab), ab, 0, (int64_t)rows * 2, "normalise scale/shift read");

@@ -132,6 +132,9 @@ EPI_ONLY_CASES = [
     (W.EPI_SOFTMAX_SIGMOID, 2, 64, (4, 8, 8), 1, False),
     (W.EPI_SOFTMAX_SIGMOID, 2, 301, (3, 5, 7), 1, True),        # many channels, odd size
     (W.EPI_SOFTMAX_SIGMOID, 1, 3, (4, 4, 4), 1, False),         # fewer than four channels
+    (W.EPI_SOFTMAX_SIGMOID, 2, 129, (3, 9, 11), 1, False),      # three waves per position group
+    (W.EPI_SOFTMAX_SIGMOID, 1, 700, (2, 5, 9), 1, True),        # eleven waves per position group
+    (W.EPI_SOFTMAX_SIGMOID, 1, 1100, (2, 3, 11), 1, False),     # past 1024 channels: two reads
     (W.EPI_SCALE_BN_TRAIN_AVGPOOL, 4, 10, (5, 6, 7), 1, False),
     (W.EPI_SCALE_BN_TRAIN_AVGPOOL, 2, 6, (36, 36, 36), 1, False),
     (W.EPI_SCALE_BN_EVAL_AVGPOOL, 3, 9, (4, 6, 8), 1, False),
@@ -177,12 +180,13 @@ def test_epilogue_only_matches_oracle(case):
 
 # ---------------------------------------------------------------- softmax arithmetic bound
 
-@pytest.mark.parametrize("c", [64, 100])
+@pytest.mark.parametrize("c", [64, 100, 300, 1100])
 def test_softmax_arithmetic_error_bound(c):
     """With y given exactly, the softmax + sigmoid result differs from fp64 only
-    by the hardware exp2 / reciprocal (a few ulp) and the final rounding: a
-    bound of 1e-6, far tighter than the 1e-4 output tolerance.  64 channels
-    take the register-held kernel, 100 the two-read one."""
+    by the hardware exp2 / reciprocal (a few ulp), the sigmoid polynomial
+    (7.4e-8) and the final rounding: a bound of 1e-6, far tighter than the 1e-4
+    output tolerance.  64 channels are held by one wave per position, 100 and
+    300 by several, 1100 take the two-read kernel."""
     import torch
     rng = np.random.default_rng(800 + c)
     y = (rng.standard_normal((2, c, 5, 6, 7)) * 3.0).astype(np.float32)
