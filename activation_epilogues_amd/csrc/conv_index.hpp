@@ -207,6 +207,16 @@ CONVT3D_IX int out_voxel_off(int half, int S, int od, int Ho, int oh, int Wo, in
 // accumulator row of co block c, register r: output channel row0 + this (+ 4*half)
 CONVT3D_IX int acc_row(int row0, int c, int r) { return row0 + c * 32 + 8 * (r >> 2) + (r & 3); }
 
+// bytes from the base of accumulator row `row` (channel row; its upper
+// k-row half writes the channel 4 further, at 4*S floats) that belong to
+// existing channels: both rows, the lower one only, or none.  A buffer
+// descriptor of this range drops the stores of the other lanes.
+CONVT3D_IX unsigned row_pair_bytes(int row, int Cout, int S) {
+    return row + 4 < Cout ? 20u * (unsigned)S : row < Cout ? 4u * (unsigned)S : 0u;
+}
+// byte offset a lane gives a store that must not happen: past every range
+constexpr unsigned kDropOffset = 0xFFFFFFF8u;
+
 // ---- statistics partials [n][tile][Cout_total][2]: tile index of a work item
 CONVT3D_IX int partial_tile(const ConvParams &P, int rho_d, int rho_h, int wgrp, int bx) {
     return ((rho_d * P.s3[1] + rho_h) * P.nwgroups + wgrp) * P.tiles_total + bx;

@@ -550,19 +550,45 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         acc[p][c][pb][r] = y;
                     }
             }
-        // stores: with two w-phases the lane holds outputs at w and w+1
+        // stores: bounds-checked non-temporal buffer stores, one descriptor per
+        // accumulator row covering the bytes of its existing channels.  A lane
+        // whose output does not exist gets an offset past that range and the
+        // hardware drops its store: no per-lane branches.  With two w-phases a
+        // lane holds outputs at w and w+1, stored as one float pair; lanes
+        // where only one of them exists store singly, in a second sequence a
+        // wave runs only when it has such a lane.
+        typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+        unsigned so[NPH][PBW], po[PBW];
+        bool singles = false;
+#pragma unroll
+        for (int pb = 0; pb < PBW; ++pb) {
+            po[pb] = ix::kDropOffset;
+            if constexpr (NPH == 2) po[pb] = pair_ok[pb] ? vofs[0][pb] : ix::kDropOffset;
+#pragma unroll
+            for (int p = 0; p < NPH; ++p) {
+                const bool single = ok[p][pb] && (NPH == 1 || !pair_ok[pb]);
+                so[p][pb] = single ? vofs[p][pb] : ix::kDropOffset;
+                singles = singles || (NPH == 2 && single);
+            }
+        }
+        const bool any_single = NPH == 1 || __any(singles);
 #pragma unroll
         for (int c = 0; c < CBW; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                if (!row_ok(c, r)) continue;
-                char *rp = rowp(c, r);
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    rowp(c, r), (short)0, (int)ix::row_pair_bytes(row_u(c, r), Cout, S), 0x00020000);
 #pragma unroll
                 for (int pb = 0; pb < PBW; ++pb) {
-                    float v[NPH];
+                    if constexpr (NPH == 2) {
+                        const float2 pv = make_float2(acc[0][c][pb][r], acc[1][c][pb][r]);
+                        __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u2v *>(&pv), rs, po[pb], 0, 2);
+                    }
+                    if (any_single)
 #pragma unroll
-                    for (int p = 0; p < NPH; ++p) v[p] = acc[p][c][pb][r];
-                    store_row(rp, pb, v);
+                        for (int p = 0; p < NPH; ++p)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[p][c][pb][r]), rs, so[p][pb], 0,
+                                                                  2);
                 }
             }
     } else {

@@ -344,13 +344,20 @@ int replay_conv(const Plan &pl, const ConvParams &P) {
                         if (!g_full && !(lane == 0 || lane == 31 || lane == 32 || lane == 63)) continue;
                         for (int c = 0; c < CBW; ++c)
                             for (int r = 0; r < 16; ++r) {
-                                const bool cok = blk8 ? row_ok(c, 4 * (r >> 2)) : row_ok(c, r);
-                                if (!cok) continue;
                                 const int row = ix::acc_row(row0, c, r);
-                                if (P.bias) in_buf(bb, P.bias, (int64_t)grp * Cout + row + 4 * half, 1, "bias read");
+                                // the softmax kernels store through a buffer descriptor per row that
+                                // drops stores past the row pair's existing channels; the others branch
+                                const bool cok = SM ? true : blk8 ? row_ok(c, 4 * (r >> 2)) : row_ok(c, r);
+                                if (!cok) continue;
+                                if (P.bias && row_ok(c, r))
+                                    in_buf(bb, P.bias, (int64_t)grp * Cout + row + 4 * half, 1, "bias read");
                                 const int64_t base = (rowbase + row) * S;
                                 for (int p = 0; p < NPH; ++p)
                                     if (okp[p]) {
+                                        // a float pair is one store at the first phase's offset
+                                        const uint64_t end = pair ? (uint64_t)vofs[0] * 4 + 8 : (uint64_t)vofs[p] * 4 + 4;
+                                        if (SM && end > ix::row_pair_bytes(row, Cout, S))
+                                            continue;  // dropped by the descriptor's range
                                         if (g_full) mark_write(bo, P.out, base + vofs[p], "output store");
                                         else in_buf(bo, P.out, base + vofs[p], 1, "output store");
                                     }

@@ -131,3 +131,24 @@ def test_full_size_tuned_plan(name):
         np.testing.assert_allclose(st[..., 1], g["stats"][..., 1], rtol=1e-5, atol=1e-6)
     if wl.epi == W.EPI_SOFTMAX_SIGMOID:
         assert float(out.min()) > 0.5 and float(out.max()) <= 1.0 / (1.0 + np.exp(-1.0)) + 1e-6
+
+
+@pytest.mark.parametrize("name", [wl.name for wl in W.WORKLOADS] + ["k3s1_gn_g4_dl2", "k3s2_softmax_c256"])
+def test_full_size_every_element_against_the_oracle(name):
+    """Every element of the full-size output, and of the raw convolution, of
+    every sample (so the per-sample offsets of all n samples are exercised),
+    against the fp64 oracle on the same inputs: the plan the benchmark times
+    (tuned above for these workloads; the tiny case runs its model plan)."""
+    import oracle
+    wl = W.BY_NAME[name]
+    inp = W.make_inputs(wl)
+    say(f"[case] full-size every element {name} x={wl.x_shape}")
+    out, st, _ = run_gpu(wl, inp)
+    raw, _, _ = run_gpu(wl.with_(epi=W.EPI_NONE), inp, kind=W.EPI_NONE, want_stats=False)
+    ref = oracle.run_workload(wl, inp)
+    err_out = max_err(out, ref.out.reshape(out.shape))
+    err_raw = max_err(raw, ref.y.reshape(raw.shape))
+    say(f"  max|err| final {err_out:.2e}, raw conv {err_raw:.2e}")
+    assert err_out <= TOL and err_raw <= TOL
+    if st is not None:
+        np.testing.assert_allclose(st, ref.stats.reshape(st.shape), rtol=1e-5, atol=1e-6)
