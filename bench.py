@@ -382,6 +382,74 @@ def measure(wl, args, log=print):
     }
 
 
+def measure_epilogue_only(wl, args, log=print):
+    """The standalone epilogue (convt3d_epilogue_only) on a conv output of the
+    workload's shape already in HBM (the fused path's own NONE output, so the
+    values are the real y), written to a separate buffer; repeated calls."""
+    import torch
+    from activation_epilogues_amd import convt3d as C
+    from activation_epilogues_amd import workloads as W
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    g = C.make_geom(wl.n, wl.cin, wl.cout, wl.d, wl.h, wl.w, wl.k, wl.stride, wl.pad, wl.out_pad,
+                    wl.dilation, wl.conv_groups)
+    conv = C.FusedCall(g, W.EPI_NONE, device=dev)
+    conv.prepack(torch.from_numpy(inp.w).to(dev))
+    y = conv(torch.from_numpy(inp.x).to(dev), None if inp.b is None else torch.from_numpy(inp.b).to(dev))
+    torch.cuda.synchronize()
+    del conv
+    S = int(y[0, 0].numel())
+    pooled = wl.epi in (W.EPI_SCALE_BN_TRAIN_AVGPOOL, W.EPI_SCALE_BN_EVAL_AVGPOOL)
+    out = torch.empty((wl.n, wl.cout), device=dev) if pooled else torch.empty_like(y)
+    gamma = None if inp.gamma is None else torch.from_numpy(inp.gamma).to(dev)
+    beta = None if inp.beta is None else torch.from_numpy(inp.beta).to(dev)
+    rmean = None if inp.rmean is None else torch.from_numpy(inp.rmean).to(dev)
+    rvar = None if inp.rvar is None else torch.from_numpy(inp.rvar).to(dev)
+    epi = C.make_epilogue(wl.epi, wl.groups, wl.eps, wl.scale, gamma, beta, None, wl.momentum, rmean, rvar)
+    ws_bytes = C.convt3d_epilogue_workspace_size(wl.n, wl.cout, S, epi)
+    ws = torch.empty(max(1, ws_bytes // 4), device=dev)
+
+    def call():
+        C.convt3d_epilogue_only(y, wl.n, wl.cout, S, epi, out, ws, ws_bytes)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    C.convt3d_profile_begin()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    prof = C.convt3d_profile_end()
+    # bytes the passes move, in units of |y|: GroupNorm reads y twice and
+    # writes once; the softmax (up to 1024 channels) reads once and writes
+    # once; the BatchNorm kinds read once
+    if wl.epi == W.EPI_RELU_GROUPNORM:
+        passes = 3
+    elif wl.epi == W.EPI_SOFTMAX_SIGMOID:
+        passes = 2 if wl.cout <= 1024 else 3
+    else:
+        passes = 1
+    nbytes = passes * 4.0 * y.numel()
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    kern = {k: round(prof[k] / args.steps, 4) for k in ("reduce_ms", "finalize_ms", "normalize_ms")}
+    log(f"[bench] {wl.name} epilogue only: {ms:.4f} ms/call, {gbps:.0f} GB/s")
+    return {
+        "metric": "convt3d_epilogue_only HBM rate on a resident conv output",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_call": round(ms, 4), "higher_is_better": True, "frac_hbm": round(gbps / PEAK_HBM_GBS, 4),
+        "y_passes": passes, "bytes_per_call": nbytes, "kernels_ms": kern,
+        "config": {"workload": wl.name, "y": list(y.shape), "epilogue": W.EPI_NAMES[wl.epi], "out": "separate buffer"},
+        "dtype": "f32", "data": "the workload's own conv output (synthetic seeded inputs)",
+    }
+
+
 def info_dims(wl):
     """Output dims of a workload (for the dense-equivalent count)."""
     from activation_epilogues_amd import convt3d as C
@@ -420,6 +488,8 @@ def main():
     ap.add_argument("--compare-torch", action="store_true",
                     help="also time PyTorch's own ConvTranspose3d + epilogue ops, and its conv followed by "
                          "convt3d_epilogue_only (context only)")
+    ap.add_argument("--epilogue-only", action="store_true",
+                    help="time convt3d_epilogue_only on the workload's conv output instead (its own JSON line)")
     args = ap.parse_args()
     if args.plan is not None:
         os.environ["CONVT3D_PLAN"] = args.plan
@@ -439,6 +509,9 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    if args.epilogue_only:
+        print(json.dumps(measure_epilogue_only(W.BY_NAME[args.workload], args, log)), flush=True)
+        return
     head = measure(W.BY_NAME[args.workload], args, log)
     all_configs = None
     if not args.only:
