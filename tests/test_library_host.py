@@ -362,17 +362,18 @@ def test_one_border_tiled_with_the_interior_cuts_padding(monkeypatch, name):
 
 
 def test_sigmoid_polynomial_matches_its_generator():
-    """The softmax epilogue's sigmoid coefficients are the ones sigmoid_poly.py
-    derives, and their float32 Horner evaluation stays within 1e-7 of the
-    definition on [0, 1]."""
+    """The softmax epilogues' sigmoid coefficients (one table, shared by the
+    fused and the standalone kernels) are the ones sigmoid_poly.py derives, and
+    their float32 Horner evaluation stays within 1e-7 of the definition on
+    [0, 1]."""
     import importlib.util
     csrc = os.path.join(ROOT, "activation_epilogues_amd", "csrc")
     spec = importlib.util.spec_from_file_location("sigmoid_poly", os.path.join(csrc, "sigmoid_poly.py"))
     sp = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(sp)
     want = sp.coefficients()
-    src = open(os.path.join(csrc, "kernels.hip")).read()
-    m = re.search(r"kSig\[7\]\s*=\s*\{([^}]*)\}", src)
+    src = open(os.path.join(csrc, "convt3d_internal.hpp")).read()
+    m = re.search(r"kSigmoidPoly\[7\]\s*=\s*\{([^}]*)\}", src)
     assert m
     got = np.array([float(t.strip().rstrip("f")) for t in m.group(1).split(",")], dtype=np.float32)
     assert np.array_equal(got, want)
