@@ -380,7 +380,8 @@ static int run_plan(const Plan &pl, const float *x, const void *w_packed, const 
         const double count = (double)(g.cout / epi->groups) * (double)pl.S;
         if (timed(kTimedFinalize, stream, [&] {
                 return launch_gn_finalize(partials, g.n, tiles, g.cout, epi->groups, cp.gn_block8 ? 8 : 1, count,
-                                          epi->eps, epi->gamma, epi->beta, ab, epi->stats_out, stream);
+                                          epi->eps, epi->gamma, epi->beta, ab, epi->stats_out, nullptr, bias,
+                                          (double)pl.S, stream);
             }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
         if (timed(kTimedNormalize, stream, [&] {
@@ -389,7 +390,7 @@ static int run_plan(const Plan &pl, const float *x, const void *w_packed, const 
             return CONVT3D_ERR_LAUNCH;
     } else if (epi->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL) {
         if (timed(kTimedFinalize, stream, [&] {
-                return launch_bn_finalize(partials, g.n, tiles, g.cout, (double)pl.S, *epi, out, stream);
+                return launch_bn_finalize(partials, g.n, tiles, g.cout, (double)pl.S, *epi, out, nullptr, bias, stream);
             }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
     } else if (pl.softmax_pass) {
@@ -555,7 +556,7 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias, co
 namespace {
 struct EpiOnlyLayout {
     int chunks = 1;
-    size_t partials = 0, ab = 0, bytes = 0;
+    size_t partials = 0, ab = 0, pivots = 0, bytes = 0;  // pivots: one per (n, c) row of y
 };
 
 int epi_only_layout(int32_t n, int32_t c, int64_t spatial, const convt3d_epilogue *e, EpiOnlyLayout *L) {
@@ -573,8 +574,10 @@ int epi_only_layout(int32_t n, int32_t c, int64_t spatial, const convt3d_epilogu
         off += (bytes + 255) & ~size_t(255);
         return o;
     };
-    if (e->kind != CONVT3D_EPI_SOFTMAX_SIGMOID)
+    if (e->kind != CONVT3D_EPI_SOFTMAX_SIGMOID) {
         L->partials = take((size_t)std::max(n, 1) * L->chunks * c * 2 * sizeof(float));
+        L->pivots = take((size_t)std::max(n, 1) * c * sizeof(float));
+    }
     if (e->kind == CONVT3D_EPI_RELU_GROUPNORM) L->ab = take((size_t)std::max(n, 1) * c * 2 * sizeof(float));
     L->bytes = off;
     return CONVT3D_OK;
@@ -610,6 +613,7 @@ int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
     count_call();
     char *ws = static_cast<char *>(workspace);
     float *partials = reinterpret_cast<float *>(ws + L.partials);
+    float *pivots = reinterpret_cast<float *>(ws + L.pivots);
     const double S = (double)spatial;
     auto ok = [](int rc) { return rc == (int)hipSuccess; };
     switch (kind) {
@@ -617,10 +621,10 @@ int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
             float *ab = reinterpret_cast<float *>(ws + L.ab);
             const double count = (double)(c / epi->groups) * S;
             if (!ok(timed(kTimedReduce, stream,
-                          [&] { return launch_row_stats(y, n, c, spatial, true, 1.0f, partials, stream); })) ||
+                          [&] { return launch_row_stats(y, n, c, spatial, true, 1.0f, partials, pivots, stream); })) ||
                 !ok(timed(kTimedFinalize, stream, [&] {
                     return launch_gn_finalize(partials, n, L.chunks, c, epi->groups, 1, count, epi->eps,
-                                              epi->gamma, epi->beta, ab, epi->stats_out, stream);
+                                              epi->gamma, epi->beta, ab, epi->stats_out, pivots, nullptr, S, stream);
                 })) ||
                 !ok(timed(kTimedNormalize, stream,
                           [&] { return launch_normalize(y, out, ab, n * c, spatial, true, stream, true); })))
@@ -633,16 +637,19 @@ int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
             break;
         case CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL:
             if (!ok(timed(kTimedReduce, stream,
-                          [&] { return launch_row_stats(y, n, c, spatial, false, epi->scale, partials, stream); })) ||
-                !ok(timed(kTimedFinalize, stream,
-                          [&] { return launch_bn_finalize(partials, n, L.chunks, c, S, *epi, out, stream); })))
+                          [&] {
+                              return launch_row_stats(y, n, c, spatial, false, epi->scale, partials, pivots, stream);
+                          })) ||
+                !ok(timed(kTimedFinalize, stream, [&] {
+                    return launch_bn_finalize(partials, n, L.chunks, c, S, *epi, out, pivots, nullptr, stream);
+                })))
                 return CONVT3D_ERR_LAUNCH;
             break;
         default:  // CONVT3D_EPI_SCALE_BN_EVAL_AVGPOOL
             if (!ok(timed(kTimedReduce, stream,
-                          [&] { return launch_row_stats(y, n, c, spatial, false, 1.0f, partials, stream); })) ||
+                          [&] { return launch_row_stats(y, n, c, spatial, false, 1.0f, partials, pivots, stream); })) ||
                 !ok(timed(kTimedFinalize, stream,
-                          [&] { return launch_bn_eval_rows(partials, n, L.chunks, c, S, *epi, out, stream); })))
+                          [&] { return launch_bn_eval_rows(partials, n, L.chunks, c, S, *epi, out, pivots, stream); })))
                 return CONVT3D_ERR_LAUNCH;
             break;
     }

@@ -181,18 +181,22 @@ int launch_conv(const Plan &pl, const ConvParams &cp, void *stream);
 // Launchers (epilogue.hip).  partials are [n][chunk or tile][C][2]; the GroupNorm
 // merge reads every chan_step-th channel (8 when the conv kept one sum per
 // 8-channel block, at the block's first channel; else 1).
+// Statistics partials are sums of v - pivot(n, c): the pivot is prow[n*C + c]
+// when prow is given (the statistics pass over y writes it), else relu(bias)
+// (GroupNorm) or scale*bias (BatchNorm) of pbias, else 0.
 int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, int chan_step, double count,
-                       float eps, const float *gamma, const float *beta, float *ab, float *stats_out, void *stream);
+                       float eps, const float *gamma, const float *beta, float *ab, float *stats_out,
+                       const float *prow, const float *pbias, double S, void *stream);
 int launch_normalize(const float *src, float *out, const float *ab, int rows, int64_t S, bool relu,
                      void *stream, bool stream_out = false);
 int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,
-                       float *out, void *stream);
+                       float *out, const float *prow, const float *pbias, void *stream);
 int row_stat_chunks(int64_t S);
 int launch_row_stats(const float *y, int N, int C, int64_t S, bool relu, float mult, float *partials,
-                     void *stream);
+                     float *pivots, void *stream);
 int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, void *stream);
 int launch_bn_eval_rows(const float *partials, int N, int chunks, int C, double S, const convt3d_epilogue &e,
-                        float *out, void *stream);
+                        float *out, const float *pivots, void *stream);
 int launch_eval_pack(const EvalGeom &E, const float *w, float *wb, void *stream);
 int launch_eval_binsum(const EvalGeom &E, const float *x, float *R, void *stream);
 int launch_eval_finalize(const EvalGeom &E, const float *R, const float *wb, const float *bias,

@@ -3,8 +3,9 @@
 // epilogue passes over a conv output the caller holds, and the evaluation-mode
 // BatchNorm + pool path, which needs no convolution.
 //
-//  * gn_finalize_kernel   -- per (n, group) fp64 merge of statistics partials,
-//                            mean / biased variance / rstd, per-channel a, b.
+//  * gn_finalize_kernel   -- per (n, group) fp64 merge of statistics partials
+//                            (sums around per-channel pivots), mean / biased
+//                            variance / rstd, per-channel a, b.
 //  * normalize_kernel     -- out = a[n,c] * v + b[n,c] with v = src (or
 //                            ReLU(src)), float4, in place when src == out.
 //  * bn_finalize_kernel   -- per channel fp64 batch mean / biased variance,
@@ -86,14 +87,30 @@ constexpr int ncomp() { return (int)(sizeof(V) / sizeof(float)); }
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// Pivot of the statistics partials of (n, c): the partial sums are of
+// v - pivot.  prow (one per (n, c) row, written by the statistics pass over y)
+// takes precedence; else from the conv bias: relu(bias) for GroupNorm, scale *
+// bias for BatchNorm; else 0.
+__device__ __forceinline__ double stat_pivot(const float *prow, const float *pbias, bool relu, float scale, int n,
+                                             int C, int c) {
+    if (prow) return (double)prow[(size_t)n * C + c];
+    if (!pbias) return 0.0;
+    return relu ? (double)fmaxf(pbias[c], 0.0f) : (double)scale * (double)pbias[c];
+}
+
 // GroupNorm statistics: one workgroup per (n, group); fp64 sums of the fp32
-// partials (layout [n][tile][C][2]) in a fixed order, then mean, biased
-// variance E[r^2] - mean^2, rstd = 1/sqrt(var + eps), and per channel
-// a = gamma*rstd, b = beta - mean*a.
+// partials (layout [n][tile][C][2], sums of v - pivot(n, c)) in a fixed order,
+// the pivots added back (sum v = sum d + cnt*p, sum v^2 = sum (d^2 + 2 p d) +
+// cnt*p^2 per summed channel), then mean, biased variance E[v^2] - mean^2 (in
+// fp64: the pivots keep the fp32 sums free of the mean's magnitude), rstd =
+// 1/sqrt(var + eps), and per channel a = gamma*rstd, b = beta - mean*a.
+// chan_step: every chan_step-th channel holds a sum (of chan_step channels
+// around that channel's pivot).
 __global__ __launch_bounds__(kStatThreads) void gn_finalize_kernel(const float *partials, int tiles_per_n, int C,
                                                           int G, int chan_step, float eps, const float *gamma,
                                                           const float *beta, float *ab, float *stats_out,
-                                                          double count) {
+                                                          double count, const float *prow, const float *pbias,
+                                                          double chan_count) {
     const int n = blockIdx.x / G, g = blockIdx.x % G;
     const int cpg = C / G;
     const int cps = cpg / chan_step;  // channels of the group that hold sums
@@ -101,28 +118,37 @@ __global__ __launch_bounds__(kStatThreads) void gn_finalize_kernel(const float *
     double a1 = 0.0, a2 = 0.0;
     for (int i0 = threadIdx.x; i0 < items; i0 += blockDim.x * kStatUnroll) {
         float2 v[kStatUnroll];
+        double pv[kStatUnroll];
 #pragma unroll
         for (int u = 0; u < kStatUnroll; ++u) {
             const int i = i0 + u * (int)blockDim.x;
             v[u] = make_float2(0.0f, 0.0f);
+            pv[u] = 0.0;
             if (i < items) {
                 const int t = i / cps, cc = (i - t * cps) * chan_step;
                 v[u] = *reinterpret_cast<const float2 *>(partials +
                                                           (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2);
+                pv[u] = stat_pivot(prow, pbias, true, 1.0f, n, C, g * cpg + cc);
             }
         }
 #pragma unroll
         for (int u = 0; u < kStatUnroll; ++u) {
             a1 += (double)v[u].x;
-            a2 += (double)v[u].y;
+            a2 += (double)v[u].y + 2.0 * pv[u] * (double)v[u].x;
         }
     }
     __shared__ double2 red[kStatThreads / 64];
     __shared__ double mean_s, rstd_s;
     const double2 tot = block_sum2_f64(a1, a2, red);
     if (threadIdx.x == 0) {
-        const double mean = tot.x / count;
-        double var = tot.y / count - mean * mean;
+        double s1 = tot.x, s2 = tot.y;
+        for (int cc = 0; cc < cpg; cc += chan_step) {  // each summed channel's pivot, over its values
+            const double p = stat_pivot(prow, pbias, true, 1.0f, n, C, g * cpg + cc);
+            s1 += chan_count * p;
+            s2 += chan_count * p * p;
+        }
+        const double mean = s1 / count;
+        double var = s2 / count - mean * mean;
         if (var < 0.0) var = 0.0;
         mean_s = mean;
         rstd_s = 1.0 / sqrt(var + (double)eps);
@@ -207,37 +233,50 @@ __global__ __launch_bounds__(256) void normalize_kernel(const V *src, V *out, co
 }
 
 // BatchNorm (training) + average pool: one workgroup per channel.  partials
-// is [n][tile][C][2] of (sum z, sum z^2) with z = scale * y.  Writes the
+// is [n][tile][C][2] of sums of z - pivot(n, c) and their squares, z = scale
+// * y (the pivot added back in fp64 as in the GroupNorm merge).  Writes the
 // pooled [n, C] output, the batch statistics and, when both buffers are
 // given, the running statistics (unbiased variance folded in).
 __global__ __launch_bounds__(kStatThreads) void bn_finalize_kernel(const float *partials, int N, int tiles_per_n, int C,
                                                           double S, float eps, const float *gamma,
                                                           const float *beta, float *out, float *stats_out,
-                                                          float momentum, float *rmean, float *rvar) {
+                                                          float momentum, float *rmean, float *rvar,
+                                                          const float *prow, const float *pbias, float pscale) {
     const int c = blockIdx.x;
     double a1 = 0.0, a2 = 0.0;
     const int items = N * tiles_per_n;
+    // a per-sample pivot (from the statistics pass over y) enters each item's
+    // cross term 2*p*sum; a per-channel one (from the bias) is added once below
+    const double pc = prow ? 0.0 : stat_pivot(nullptr, pbias, false, pscale, 0, C, c);
     for (int i0 = threadIdx.x; i0 < items; i0 += blockDim.x * kStatUnroll) {
         float2 v[kStatUnroll];
+        double pv[kStatUnroll];
 #pragma unroll
         for (int u = 0; u < kStatUnroll; ++u) {
             const int i = i0 + u * (int)blockDim.x;  // i = n*tiles_per_n + t
             v[u] = i < items ? *reinterpret_cast<const float2 *>(partials + ((size_t)i * C + c) * 2)
                              : make_float2(0.0f, 0.0f);
+            pv[u] = prow && i < items ? (double)prow[(size_t)(i / tiles_per_n) * C + c] : 0.0;
         }
 #pragma unroll
         for (int u = 0; u < kStatUnroll; ++u) {
             a1 += (double)v[u].x;
-            a2 += (double)v[u].y;
+            a2 += (double)v[u].y + 2.0 * pv[u] * (double)v[u].x;
         }
     }
     __shared__ double2 red[kStatThreads / 64];
     __shared__ double mean_s, rstd_s;
     const double2 tot = block_sum2_f64(a1, a2, red);
     if (threadIdx.x == 0) {
+        double s1 = tot.x, s2 = tot.y + 2.0 * pc * tot.x;
+        for (int n = 0; n < N; ++n) {  // each sample's pivot, over its S values
+            const double p = stat_pivot(prow, pbias, false, pscale, n, C, c);
+            s1 += S * p;
+            s2 += S * p * p;
+        }
         const double cnt = (double)N * S;
-        const double mean = tot.x / cnt;
-        double var = tot.y / cnt - mean * mean;
+        const double mean = s1 / cnt;
+        double var = s2 / cnt - mean * mean;
         if (var < 0.0) var = 0.0;
         mean_s = mean;
         rstd_s = 1.0 / sqrt(var + (double)eps);
@@ -264,21 +303,31 @@ __global__ __launch_bounds__(kStatThreads) void bn_finalize_kernel(const float *
             for (int t = lane; t < tiles_per_n; t += 64)
                 m += (double)partials[(((size_t)n * tiles_per_n + t) * C + c) * 2];
         for (int off = 32; off > 0; off >>= 1) m += __shfl_xor(m, off);
-        if (n < N && lane == 0) out[(size_t)n * C + c] = (float)((m / S - mean_s) * rstd_s * ga + be);
+        if (n < N && lane == 0) {
+            const double zbar = m / S + stat_pivot(prow, pbias, false, pscale, n, C, c);
+            out[(size_t)n * C + c] = (float)((zbar - mean_s) * rstd_s * ga + be);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Statistics of a conv output in memory: workgroup (chunk, row) sums
-// v = ReLU(mult*y) (RELU) or mult*y over elements [chunk*chunk_len,
-// (chunk+1)*chunk_len) of row = n*C + c and writes (sum v, sum v^2) to
-// partials[n][chunk][C][2], the layout the finalize kernels read.
+// d = v - p over elements [chunk*chunk_len, (chunk+1)*chunk_len) of row =
+// n*C + c, with v = ReLU(mult*y) (RELU) or mult*y and the row's pivot p = v
+// of the row's first element (every workgroup of the row reads it; the first
+// chunk's writes it to pivots[row]); writes (sum d, sum d^2) to
+// partials[n][chunk][C][2], the layout the finalize kernels read.  The pivot
+// is a value of the row, so a large common offset does not cancel in the fp32
+// sum of squares.
 template <class V, bool RELU>
 __global__ __launch_bounds__(256) void row_stats_kernel(const V *y, int rows, int row_len, int chunk_len,
-                                                        int chunks, int C, float mult, float *partials) {
+                                                        int chunks, int C, float mult, float *partials,
+                                                        float *pivots) {
     __shared__ float2 red[4];
     for (int row = blockIdx.y; row < rows; row += gridDim.y) {
         const V *p = y + (size_t)row * row_len;
+        float pv = mult * reinterpret_cast<const float *>(p)[0];
+        if (RELU) pv = fmaxf(pv, 0.0f);
         const int beg = blockIdx.x * chunk_len;
         const int end = min(row_len, beg + chunk_len);
         float s1 = 0.0f, s2 = 0.0f;
@@ -295,6 +344,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const V *y, int rows, in
                     for (int e = 0; e < ncomp<V>(); ++e) {
                         float a = mult * c[e];
                         if (RELU) a = fmaxf(a, 0.0f);
+                        a -= pv;
                         s1 += a;
                         s2 = fmaf(a, a, s2);
                     }
@@ -306,6 +356,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const V *y, int rows, in
             float *pp = partials + (((size_t)n * chunks + blockIdx.x) * C + c) * 2;
             pp[0] = r.x;
             pp[1] = r.y;
+            if (blockIdx.x == 0) pivots[row] = pv;
         }
     }
 }
@@ -473,18 +524,19 @@ __global__ __launch_bounds__(1024) void softmax_rows_kernel(const float *src, fl
 }
 
 // Eval-mode BatchNorm + pool from per-row sums (partials [n][chunk][C][2] of
-// (sum y, -)): thread per (n, c), pooled mean m = sum / S, then
+// (sum (y - pivot), -), pivots [n][C]): thread per (n, c), pooled mean
+// m = scale * (sum / S + pivot), then
 // out = (scale*m - rmean) / sqrt(rvar + eps) * gamma + beta.
 __global__ __launch_bounds__(256) void bn_eval_rows_kernel(const float *partials, int N, int chunks, int C,
                                                            double S, float scale, float eps, const float *gamma,
                                                            const float *beta, const float *rmean,
-                                                           const float *rvar, float *out) {
+                                                           const float *rvar, float *out, const float *pivots) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= N * C) return;
     const int n = i / C, c = i - n * C;
     double sum = 0.0;
     for (int t = 0; t < chunks; ++t) sum += (double)partials[(((size_t)n * chunks + t) * C + c) * 2];
-    const double m = (double)scale * sum / S;
+    const double m = (double)scale * (sum / S + (double)pivots[i]);
     const double ga = gamma ? (double)gamma[c] : 1.0, be = beta ? (double)beta[c] : 0.0;
     const double mu = rmean ? (double)rmean[c] : 0.0, var = rvar ? (double)rvar[c] : 1.0;
     out[i] = (float)((m - mu) / sqrt(var + (double)eps) * ga + be);
@@ -663,9 +715,11 @@ __global__ __launch_bounds__(256) void eval_finalize_kernel(const EvalGeom E, co
 // launchers
 
 int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, int chan_step, double count,
-                       float eps, const float *gamma, const float *beta, float *ab, float *stats_out, void *stream) {
+                       float eps, const float *gamma, const float *beta, float *ab, float *stats_out,
+                       const float *prow, const float *pbias, double S, void *stream) {
     hipLaunchKernelGGL(gn_finalize_kernel, dim3(N * G), dim3(kStatThreads), 0, (hipStream_t)stream, partials,
-                       tiles_per_n, C, G, chan_step, eps, gamma, beta, ab, stats_out, count);
+                       tiles_per_n, C, G, chan_step, eps, gamma, beta, ab, stats_out, count, prow, pbias,
+                       (double)chan_step * S);
     return (int)hipGetLastError();
 }
 
@@ -708,34 +762,34 @@ int launch_normalize(const float *src, float *out, const float *ab, int rows, in
 }
 
 int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,
-                       float *out, void *stream) {
+                       float *out, const float *prow, const float *pbias, void *stream) {
     hipLaunchKernelGGL(bn_finalize_kernel, dim3(C), dim3(kStatThreads), 0, (hipStream_t)stream, partials, N,
                        tiles_per_n, C, S, e.eps, e.gamma, e.beta, out, e.stats_out, e.momentum, e.running_mean,
-                       e.running_var);
+                       e.running_var, prow, pbias, e.scale);
     return (int)hipGetLastError();
 }
 
 template <class V, bool RELU>
 static void launch_row_stats_t(const float *y, int rows, int len, int chunks, int C, float mult, float *partials,
-                               void *stream) {
+                               float *pivots, void *stream) {
     const int chunk_len = (len + chunks - 1) / chunks;
     const int gy = rows < 65535 ? rows : 65535;
     hipLaunchKernelGGL((row_stats_kernel<V, RELU>), dim3(chunks, gy), dim3(256), 0, (hipStream_t)stream,
-                       reinterpret_cast<const V *>(y), rows, len, chunk_len, chunks, C, mult, partials);
+                       reinterpret_cast<const V *>(y), rows, len, chunk_len, chunks, C, mult, partials, pivots);
 }
 
 int launch_row_stats(const float *y, int N, int C, int64_t S, bool relu, float mult, float *partials,
-                     void *stream) {
+                     float *pivots, void *stream) {
     const bool vec = S % 4 == 0;
     const int len = (int)(vec ? S / 4 : S);
     const int chunks = row_stat_chunks(S);
     const int rows = N * C;
     if (vec) {
-        if (relu) launch_row_stats_t<float4, true>(y, rows, len, chunks, C, mult, partials, stream);
-        else launch_row_stats_t<float4, false>(y, rows, len, chunks, C, mult, partials, stream);
+        if (relu) launch_row_stats_t<float4, true>(y, rows, len, chunks, C, mult, partials, pivots, stream);
+        else launch_row_stats_t<float4, false>(y, rows, len, chunks, C, mult, partials, pivots, stream);
     } else {
-        if (relu) launch_row_stats_t<float, true>(y, rows, len, chunks, C, mult, partials, stream);
-        else launch_row_stats_t<float, false>(y, rows, len, chunks, C, mult, partials, stream);
+        if (relu) launch_row_stats_t<float, true>(y, rows, len, chunks, C, mult, partials, pivots, stream);
+        else launch_row_stats_t<float, false>(y, rows, len, chunks, C, mult, partials, pivots, stream);
     }
     return (int)hipGetLastError();
 }
@@ -796,11 +850,11 @@ int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, v
 }
 
 int launch_bn_eval_rows(const float *partials, int N, int chunks, int C, double S, const convt3d_epilogue &e,
-                        float *out, void *stream) {
+                        float *out, const float *pivots, void *stream) {
     const int items = N * C;
     hipLaunchKernelGGL(bn_eval_rows_kernel, dim3((items + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                        partials, N, chunks, C, S, e.scale, e.eps, e.gamma, e.beta, e.running_mean, e.running_var,
-                       out);
+                       out, pivots);
     return (int)hipGetLastError();
 }
 

@@ -595,7 +595,12 @@ void convt3d_mfma_kernel(const ConvParams P) {
         // bias (+ReLU) and store, or scale; per-channel sums over the tile: the
         // lane's columns, then the 32 columns of each half (xor-shuffle
         // butterfly, or per 8-channel block for GroupNorm), then the waves
-        // (LDS), one (sum, sum of squares) per (tile, channel).
+        // (LDS), one (sum, sum of squares) per (tile, channel).  The sums are
+        // of v - pivot with a per-channel pivot near the channel's values, so
+        // a large common offset does not cancel in the fp32 sum of squares:
+        // GroupNorm relu(bias) (of the block's first channel for block sums),
+        // BatchNorm scale*bias (the sums are then of scale*acc); the statistics
+        // merge adds the pivots back in fp64.
         const bool gn = P.epi == CONVT3D_EPI_RELU_GROUPNORM;
         const bool bn = P.epi == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
         const float scale = P.scale;
@@ -614,6 +619,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const bool bok = row_ok(c, 4 * q);  // whole block in range (Cout % 8 == 0)
+                    // the block's pivot: relu(bias) of its first channel (wave-uniform)
+                    const float pvt = bok && P.bias ? fmaxf(P.bias[grp * Cout + row0 + c * 32 + 8 * q], 0.0f) : 0.0f;
                     float b1 = 0.0f, b2 = 0.0f;
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
@@ -626,7 +633,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                             for (int p = 0; p < NPH; ++p) {
                                 v[p] = fmaxf(acc[p][c][pb][r] + bco, 0.0f);
-                                const float vm = ok[p][pb] ? v[p] : 0.0f;
+                                const float vm = ok[p][pb] ? v[p] - pvt : 0.0f;
                                 b1 += vm;
                                 b2 = fmaf(vm, vm, b2);
                             }
@@ -652,7 +659,9 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const bool cok = row_ok(c, r);
-                const float bco = cok ? bias_of(c, r, 0.0f) : 0.0f;
+                // BatchNorm sums z - scale*bias = scale*acc: its bias stays out;
+                // GroupNorm sums relu(acc + bias) - relu(bias)
+                const float bco = cok && !bn ? bias_of(c, r, 0.0f) : 0.0f;
                 float a1 = 0.0f, a2 = 0.0f;
                 char *rp = rowp(c, r);
 #pragma unroll
@@ -662,8 +671,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     for (int p = 0; p < NPH; ++p) {
                         v[p] = acc[p][c][pb][r] + bco;
                         if (gn) v[p] = fmaxf(v[p], 0.0f);
-                        if (bn) v[p] = scale * v[p];
-                        const float vm = ok[p][pb] ? v[p] : 0.0f;
+                        const float d = fmaf(v[p], bn ? scale : 1.0f, gn ? -fmaxf(bco, 0.0f) : 0.0f);
+                        const float vm = ok[p][pb] ? d : 0.0f;
                         a1 += vm;
                         a2 = fmaf(vm, vm, a2);
                     }

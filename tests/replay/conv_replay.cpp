@@ -418,7 +418,10 @@ int launch_prepack(const Plan &pl, const float *w, float *wp, void *) {
 int launch_conv(const Plan &pl, const ConvParams &cp, void *) { return replay_conv(pl, cp); }
 
 int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, int chan_step, double,
-                       float, const float *gamma, const float *beta, float *ab, float *stats_out, void *) {
+                       float, const float *gamma, const float *beta, float *ab, float *stats_out, const float *prow,
+                       const float *pbias, double, void *) {
+    if (prow) in_buf(find_buf(prow), prow, 0, (int64_t)N * C, "pivot read");
+    if (pbias) in_buf(find_buf(pbias), pbias, 0, C, "bias pivot read");
     Buf *bp = find_buf(partials), *ba = find_buf(ab);
     const int cpg = C / G;
     if (cpg % chan_step) fail("channel step %d does not divide %d channels per group", chan_step, cpg);
@@ -447,7 +450,9 @@ int launch_normalize(const float *src, float *out, const float *ab, int rows, in
 }
 
 int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double, const convt3d_epilogue &e,
-                       float *out, void *) {
+                       float *out, const float *prow, const float *pbias, void *) {
+    if (prow) in_buf(find_buf(prow), prow, 0, (int64_t)N * C, "pivot read");
+    if (pbias) in_buf(find_buf(pbias), pbias, 0, C, "bias pivot read");
     Buf *bp = find_buf(partials);
     for (int64_t i = 0; i < (int64_t)N * tiles_per_n; ++i)
         for (int c = 0; c < C; ++c) {
@@ -461,7 +466,8 @@ int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, dou
     return 0;
 }
 
-int launch_row_stats(const float *y, int N, int C, int64_t S, bool, float, float *partials, void *) {
+int launch_row_stats(const float *y, int N, int C, int64_t S, bool, float, float *partials, float *pivots, void *) {
+    in_buf(find_buf(pivots), pivots, 0, (int64_t)N * C, "pivot write");
     in_buf(find_buf(y), y, 0, (int64_t)N * C * S, "statistics pass read");
     in_buf(find_buf(partials), partials, 0, (int64_t)N * row_stat_chunks(S) * C * 2, "statistics pass write");
     return 0;
@@ -474,7 +480,8 @@ int launch_softmax_pass(const float *src, float *out, int N, int C, int64_t S, v
 }
 
 int launch_bn_eval_rows(const float *partials, int N, int chunks, int C, double, const convt3d_epilogue &,
-                        float *out, void *) {
+                        float *out, const float *pivots, void *) {
+    in_buf(find_buf(pivots), pivots, 0, (int64_t)N * C, "pivot read");
     in_buf(find_buf(partials), partials, 0, (int64_t)N * chunks * C * 2, "eval rows read");
     in_buf(find_buf(out), out, 0, (int64_t)N * C, "eval rows write");
     return 0;
@@ -641,10 +648,12 @@ int main(int argc, char **argv) {
                 if (epi_kind == CONVT3D_EPI_RELU_GROUPNORM)
                     launch_gn_finalize(reinterpret_cast<float *>(wsb->base + pl.ws_partials), g.n, (int)pl.tiles_per_n,
                                        g.cout, gn_groups, cp.gn_block8 ? 8 : 1, 1.0, 1e-5f, e.gamma, e.beta,
-                                       reinterpret_cast<float *>(wsb->base + pl.ws_ab), e.stats_out, nullptr);
+                                       reinterpret_cast<float *>(wsb->base + pl.ws_ab), e.stats_out, nullptr,
+                                       reinterpret_cast<float *>(bias->base), 1.0, nullptr);
                 if (epi_kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL)
                     launch_bn_finalize(reinterpret_cast<float *>(wsb->base + pl.ws_partials), g.n, (int)pl.tiles_per_n,
-                                       g.cout, 1.0, e, reinterpret_cast<float *>(out->base), nullptr);
+                                       g.cout, 1.0, e, reinterpret_cast<float *>(out->base), nullptr,
+                                       reinterpret_cast<float *>(bias->base), nullptr);
                 ++replayed;
                 if (g_errors) break;
             }

@@ -231,3 +231,65 @@ def test_fused_softmax_beyond_one_workgroup(geo):
     ref = oracle.run_workload(wl, inp)
     err = max_err(out, ref.out.reshape(out.shape))
     assert err <= TOL, f"max|err| {err:.3e}"
+
+
+# ---------------------------------------------------------------- statistics with a large common offset
+
+@pytest.mark.parametrize("kind,geo", [
+    (W.EPI_RELU_GROUPNORM, (2, 24, 64, 9, 10, 11, 3, 1, 0, 0)),      # block sums (8-channel blocks)
+    (W.EPI_RELU_GROUPNORM, (2, 20, 30, 6, 7, 8, 3, 2, 1, 1)),        # per-channel sums (10 channels a group)
+    (W.EPI_SCALE_BN_TRAIN_AVGPOOL, (3, 16, 40, 6, 7, 8, 4, 2, 1, 0)),
+])
+def test_fused_statistics_with_large_bias(kind, geo):
+    """A bias of about 100 on every channel: the conv outputs sit ~150 standard
+    deviations from zero, so E[v^2] - mean^2 over fp32 sums of v would lose the
+    variance; the sums are taken around relu(bias) / scale*bias instead."""
+    n, cin, cout, d, h, w, k, s, p, op = geo
+    groups = 3 if cout == 30 else 8 if kind == W.EPI_RELU_GROUPNORM else 1
+    wl = W.Workload("bigbias", n, cin, cout, d, h, w, k=k, stride=s, pad=p, out_pad=op, bias=True, epi=kind,
+                    groups=groups, scale=1.5, seed=4700 + cout)
+    say(f"[case] large bias kind {kind} {geo}")
+    inp = W.make_inputs(wl)
+    inp = W.Inputs(inp.x, inp.w, (inp.b + np.float32(100.0)).astype(np.float32), inp.gamma, inp.beta, inp.rmean,
+                   inp.rvar)
+    out, st, rm, rv, _ = fused(wl, inp)
+    ref = oracle.run_workload(wl, inp)
+    assert max_err(out, ref.out.reshape(out.shape)) <= TOL
+    np.testing.assert_allclose(st, ref.stats.reshape(st.shape), rtol=1e-5, atol=1e-6)
+    if kind == W.EPI_SCALE_BN_TRAIN_AVGPOOL:
+        assert max_err(rm, ref.running[0]) <= TOL and max_err(rv, ref.running[1]) <= TOL
+
+
+@pytest.mark.parametrize("kind", [W.EPI_RELU_GROUPNORM, W.EPI_SCALE_BN_TRAIN_AVGPOOL, W.EPI_SCALE_BN_EVAL_AVGPOOL])
+def test_epilogue_only_statistics_with_large_offset(kind):
+    """A given y with a common offset of 100 (about 170 standard deviations):
+    the statistics pass sums v - pivot around a value of each row."""
+    import torch
+    n, c, dims = 2, 16, (9, 10, 12)
+    y, gamma, beta, rmean, rvar = y_case(n, c, dims, 900 + kind)
+    y = (y + np.float32(100.0)).astype(np.float32)
+    S = int(np.prod(dims))
+    groups, scale, eps, mom = 4, 1.25, 1e-5, 0.1
+    say(f"[case] epilogue_only large offset kind {kind}")
+    dy = to_dev(y)
+    pooled = kind != W.EPI_RELU_GROUPNORM
+    out = torch.full((n, c) if pooled else y.shape, float("nan"), device="cuda:0")
+    stats = torch.empty((n, groups, 2) if kind == W.EPI_RELU_GROUPNORM else (c, 2), device="cuda:0")
+    rm, rv = to_dev(rmean), to_dev(rvar)
+    g_, b_ = to_dev(gamma), to_dev(beta)  # kept alive: the epilogue holds only their addresses
+    epi = C.make_epilogue(kind, groups, eps, scale, g_, b_, stats, mom, rm, rv)
+    ws_bytes = C.convt3d_epilogue_workspace_size(n, c, S, epi)
+    ws = torch.empty(max(1, ws_bytes // 4), device="cuda:0")
+    C.convt3d_epilogue_only(dy, n, c, S, epi, out, ws, ws_bytes)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    y64 = y.astype(np.float64)
+    if kind == W.EPI_RELU_GROUPNORM:
+        want, st = oracle.relu_groupnorm(y64, groups, eps, gamma, beta)
+        np.testing.assert_allclose(stats.cpu().numpy(), st, rtol=1e-5, atol=1e-6)
+    elif kind == W.EPI_SCALE_BN_TRAIN_AVGPOOL:
+        want, st = oracle.scale_bn_avgpool(y64, scale, eps, gamma, beta)
+        np.testing.assert_allclose(stats.cpu().numpy(), st, rtol=1e-5, atol=1e-6)
+    else:
+        want = oracle.scale_bn_eval_avgpool(y64, scale, eps, gamma, beta, rmean, rvar)
+    assert max_err(got, want.reshape(got.shape)) <= TOL
