@@ -369,7 +369,8 @@ static int run_plan(const Plan &pl, const float *x, const void *w_packed, const 
         cp.wp = static_cast<const float *>(w_packed) + (size_t)gi * pl.packed_floats;
         cp.bias = bias ? bias + (size_t)gi * pl.cog : nullptr;
         cp.out = pooled ? out : out + (size_t)gi * pl.cog * pl.S;
-        cp.partials = partials ? partials + (size_t)gi * pl.cog * 2 : nullptr;
+        // channel-major partials: a group starts cog channel rows of tiles further
+        cp.partials = partials ? partials + (size_t)gi * pl.cog * pl.tiles_per_n * 2 : nullptr;
         if (timed(kTimedConv, stream, [&] { return launch_conv(pl, cp, stream); }) != (int)hipSuccess)
             return CONVT3D_ERR_LAUNCH;
     }

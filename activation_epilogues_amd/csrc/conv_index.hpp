@@ -217,9 +217,14 @@ CONVT3D_IX unsigned row_pair_bytes(int row, int Cout, int S) {
 // byte offset a lane gives a store that must not happen: past every range
 constexpr unsigned kDropOffset = 0xFFFFFFF8u;
 
-// ---- statistics partials [n][tile][Cout_total][2]: tile index of a work item
+// ---- statistics partials, channel-major [n][Cout_total][tile][2] (each
+// channel's tiles contiguous, the order the statistics merges read them):
+// tile index of a work item, and the float offset of a (sum, sum of squares)
 CONVT3D_IX int partial_tile(const ConvParams &P, int rho_d, int rho_h, int wgrp, int bx) {
     return ((rho_d * P.s3[1] + rho_h) * P.nwgroups + wgrp) * P.tiles_total + bx;
+}
+CONVT3D_IX size_t partial_offset(int n, int C_total, int c, int tiles, int tile) {
+    return (((size_t)n * C_total + c) * tiles + tile) * 2;
 }
 
 }  // namespace ix

@@ -51,7 +51,7 @@ struct ConvParams {
     const float *wp;      // packed weights
     const float *bias;    // may be null
     float *out;
-    float *partials;      // [n][tiles_per_n][cout][2] or null
+    float *partials;      // [n][cout][tiles_per_n][2] (channel-major) or null
     int N, Cin, Cout, D, H, W, Do, Ho, Wo;  // Cin, Cout: of one channel group
     int Cout_total;       // output channels of the whole conv (row stride of out and partials)
     int x_nstride;        // floats per sample of x (all groups' channels)

@@ -27,6 +27,7 @@
 
 #include <cmath>
 
+#include "conv_index.hpp"
 #include "convt3d_internal.hpp"
 
 namespace convt3d {
@@ -99,7 +100,7 @@ __device__ __forceinline__ double stat_pivot(const float *prow, const float *pbi
 }
 
 // GroupNorm statistics: one workgroup per (n, group); fp64 sums of the fp32
-// partials (layout [n][tile][C][2], sums of v - pivot(n, c)) in a fixed order,
+// partials (layout [n][C][tile][2], sums of v - pivot(n, c)) in a fixed order,
 // the pivots added back (sum v = sum d + cnt*p, sum v^2 = sum (d^2 + 2 p d) +
 // cnt*p^2 per summed channel), then mean, biased variance E[v^2] - mean^2 (in
 // fp64: the pivots keep the fp32 sums free of the mean's magnitude), rstd =
@@ -125,9 +126,10 @@ __global__ __launch_bounds__(kStatThreads) void gn_finalize_kernel(const float *
             v[u] = make_float2(0.0f, 0.0f);
             pv[u] = 0.0;
             if (i < items) {
-                const int t = i / cps, cc = (i - t * cps) * chan_step;
+                // tile fastest: each summed channel's tiles are contiguous
+                const int k = i / tiles_per_n, t = i - k * tiles_per_n, cc = k * chan_step;
                 v[u] = *reinterpret_cast<const float2 *>(partials +
-                                                          (((size_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2);
+                                                          ix::partial_offset(n, C, g * cpg + cc, tiles_per_n, t));
                 pv[u] = stat_pivot(prow, pbias, true, 1.0f, n, C, g * cpg + cc);
             }
         }
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(256) void normalize_kernel(const V *src, V *out, co
 }
 
 // BatchNorm (training) + average pool: one workgroup per channel.  partials
-// is [n][tile][C][2] of sums of z - pivot(n, c) and their squares, z = scale
+// is [n][C][tile][2] of sums of z - pivot(n, c) and their squares, z = scale
 // * y (the pivot added back in fp64 as in the GroupNorm merge).  Writes the
 // pooled [n, C] output, the batch statistics and, when both buffers are
 // given, the running statistics (unbiased variance folded in).
@@ -254,9 +256,10 @@ __global__ __launch_bounds__(kStatThreads) void bn_finalize_kernel(const float *
 #pragma unroll
         for (int u = 0; u < kStatUnroll; ++u) {
             const int i = i0 + u * (int)blockDim.x;  // i = n*tiles_per_n + t
-            v[u] = i < items ? *reinterpret_cast<const float2 *>(partials + ((size_t)i * C + c) * 2)
+            const int n = i / tiles_per_n, t = i - n * tiles_per_n;
+            v[u] = i < items ? *reinterpret_cast<const float2 *>(partials + ix::partial_offset(n, C, c, tiles_per_n, t))
                              : make_float2(0.0f, 0.0f);
-            pv[u] = prow && i < items ? (double)prow[(size_t)(i / tiles_per_n) * C + c] : 0.0;
+            pv[u] = prow && i < items ? (double)prow[(size_t)n * C + c] : 0.0;
         }
 #pragma unroll
         for (int u = 0; u < kStatUnroll; ++u) {
@@ -301,7 +304,7 @@ __global__ __launch_bounds__(kStatThreads) void bn_finalize_kernel(const float *
         double m = 0.0;
         if (n < N)
             for (int t = lane; t < tiles_per_n; t += 64)
-                m += (double)partials[(((size_t)n * tiles_per_n + t) * C + c) * 2];
+                m += (double)partials[ix::partial_offset(n, C, c, tiles_per_n, t)];
         for (int off = 32; off > 0; off >>= 1) m += __shfl_xor(m, off);
         if (n < N && lane == 0) {
             const double zbar = m / S + stat_pivot(prow, pbias, false, pscale, n, C, c);
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kStatThreads) void bn_finalize_kernel(const float *
 // n*C + c, with v = ReLU(mult*y) (RELU) or mult*y and the row's pivot p = v
 // of the row's first element (every workgroup of the row reads it; the first
 // chunk's writes it to pivots[row]); writes (sum d, sum d^2) to
-// partials[n][chunk][C][2], the layout the finalize kernels read.  The pivot
+// partials[n][C][chunk][2], the layout the finalize kernels read.  The pivot
 // is a value of the row, so a large common offset does not cancel in the fp32
 // sum of squares.
 template <class V, bool RELU>
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const V *y, int rows, in
         const float2 r = block_sum2(s1, s2, red);
         if (threadIdx.x == 0) {
             const int n = row / C, c = row - n * C;
-            float *pp = partials + (((size_t)n * chunks + blockIdx.x) * C + c) * 2;
+            float *pp = partials + ix::partial_offset(n, C, c, chunks, blockIdx.x);
             pp[0] = r.x;
             pp[1] = r.y;
             if (blockIdx.x == 0) pivots[row] = pv;
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(1024) void softmax_rows_kernel(const float *src, fl
     }
 }
 
-// Eval-mode BatchNorm + pool from per-row sums (partials [n][chunk][C][2] of
+// Eval-mode BatchNorm + pool from per-row sums (partials [n][C][chunk][2] of
 // (sum (y - pivot), -), pivots [n][C]): thread per (n, c), pooled mean
 // m = scale * (sum / S + pivot), then
 // out = (scale*m - rmean) / sqrt(rvar + eps) * gamma + beta.
@@ -535,7 +538,7 @@ __global__ __launch_bounds__(256) void bn_eval_rows_kernel(const float *partials
     if (i >= N * C) return;
     const int n = i / C, c = i - n * C;
     double sum = 0.0;
-    for (int t = 0; t < chunks; ++t) sum += (double)partials[(((size_t)n * chunks + t) * C + c) * 2];
+    for (int t = 0; t < chunks; ++t) sum += (double)partials[ix::partial_offset(n, C, c, chunks, t)];
     const double m = (double)scale * (sum / S + (double)pivots[i]);
     const double ga = gamma ? (double)gamma[c] : 1.0, be = beta ? (double)beta[c] : 0.0;
     const double mu = rmean ? (double)rmean[c] : 0.0, var = rvar ? (double)rvar[c] : 1.0;

@@ -715,7 +715,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                     t1 += red[(w * CO32 + row) * 2 + 0];
                     t2 += red[(w * CO32 + row) * 2 + 1];
                 }
-                float *pp = P.partials + (((size_t)n * P.tiles_per_n + tile) * P.Cout_total + grp * Cout + co) * 2;
+                float *pp = P.partials + ix::partial_offset(n, P.Cout_total, grp * Cout + co, P.tiles_per_n, tile);
                 pp[0] = t1;
                 pp[1] = t2;
             }

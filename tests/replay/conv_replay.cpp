@@ -381,7 +381,7 @@ int replay_conv(const Plan &pl, const ConvParams &P) {
                     const int co = wi.co_tile * CO32 + row;
                     if (co >= Cout) continue;
                     if (blk8 && (row & 7) != 0) continue;
-                    const int64_t pi = (((int64_t)n * P.tiles_per_n + tile) * P.Cout_total + (int64_t)grp * Cout + co) * 2;
+                    const int64_t pi = (int64_t)ix::partial_offset(n, P.Cout_total, grp * Cout + co, P.tiles_per_n, tile);
                     mark_write(bp, P.partials, pi, "partial store");
                     mark_write(bp, P.partials, pi + 1, "partial store");
                 }
@@ -429,7 +429,7 @@ int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int
         for (int g = 0; g < G; ++g)
             for (int t = 0; t < tiles_per_n; ++t)
                 for (int cc = 0; cc < cpg; cc += chan_step) {
-                    const int64_t i = (((int64_t)n * tiles_per_n + t) * C + g * cpg + cc) * 2;
+                    const int64_t i = (int64_t)ix::partial_offset(n, C, g * cpg + cc, tiles_per_n, t);
                     check_written(bp, partials, i, "GroupNorm partial read");
                     check_written(bp, partials, i + 1, "GroupNorm partial read");
                 }
@@ -454,11 +454,13 @@ int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, dou
     if (prow) in_buf(find_buf(prow), prow, 0, (int64_t)N * C, "pivot read");
     if (pbias) in_buf(find_buf(pbias), pbias, 0, C, "bias pivot read");
     Buf *bp = find_buf(partials);
-    for (int64_t i = 0; i < (int64_t)N * tiles_per_n; ++i)
-        for (int c = 0; c < C; ++c) {
-            check_written(bp, partials, (i * C + c) * 2, "BatchNorm partial read");
-            check_written(bp, partials, (i * C + c) * 2 + 1, "BatchNorm partial read");
-        }
+    for (int n = 0; n < N; ++n)
+        for (int t = 0; t < tiles_per_n; ++t)
+            for (int c = 0; c < C; ++c) {
+                const int64_t i = (int64_t)ix::partial_offset(n, C, c, tiles_per_n, t);
+                check_written(bp, partials, i, "BatchNorm partial read");
+                check_written(bp, partials, i + 1, "BatchNorm partial read");
+            }
     in_buf(find_buf(out), out, 0, (int64_t)N * C, "pooled output write");
     if (e.stats_out) in_buf(find_buf(e.stats_out), e.stats_out, 0, (int64_t)C * 2, "BatchNorm stats write");
     if (e.running_mean) in_buf(find_buf(e.running_mean), e.running_mean, 0, C, "running mean");
@@ -640,7 +642,7 @@ int main(int argc, char **argv) {
                     cp.bias = reinterpret_cast<float *>(bias->base) + (size_t)gi * pl.cog;
                     cp.out = pooled ? reinterpret_cast<float *>(out->base)
                                     : reinterpret_cast<float *>(out->base) + (size_t)gi * pl.cog * pl.S;
-                    cp.partials = stats_k ? reinterpret_cast<float *>(wsb->base + pl.ws_partials) + (size_t)gi * pl.cog * 2
+                    cp.partials = stats_k ? reinterpret_cast<float *>(wsb->base + pl.ws_partials) + (size_t)gi * pl.cog * pl.tiles_per_n * 2
                                           : nullptr;
                     replay_conv(pl, cp);
                 }
