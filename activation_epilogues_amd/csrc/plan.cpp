@@ -266,6 +266,7 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
     // pass finishes
     const bool softmax = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID && pl->cb_total <= 4 && pl->G == 1;
     pl->softmax_pass = e->kind == CONVT3D_EPI_SOFTMAX_SIGMOID && !softmax;
+    const bool no_y_store = e->kind == CONVT3D_EPI_SCALE_BN_TRAIN_AVGPOOL;
 
     const int sd = pl->s3[0], sh = pl->s3[1], sw = pl->s3[2];
     const int ins[3] = {g->d, g->h, g->w};
@@ -448,8 +449,10 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                         const int ext[3] = {sgd.b - sgd.a, sgh.b - sgh.a, sgw.b - sgw.a};
                         RChoice bestr{};
                         bestr.cost = 1e300;
-                        // rows of at least 16 positions keep LDS reads and stores contiguous
-                        const int TQw_min = std::min(ext[2], 16);
+                        // rows of at least 16 positions keep LDS reads and stores contiguous;
+                        // the BatchNorm-pool epilogue stores no y, so its boxes may be narrower
+                        // (a 1-wide box gives a w border its exact taps)
+                        const int TQw_min = no_y_store ? 1 : std::min(ext[2], 16);
                         for (int TQw = TQw_min; TQw <= std::min(ext[2], PT); ++TQw) {
                             for (int TQh = 1; TQh <= std::min(ext[1], PT / TQw); ++TQh) {
                                 // boxes that leave a whole position block empty are skipped

@@ -339,14 +339,16 @@ def test_plan_string_selects_the_same_plan(monkeypatch):
         assert again == info, wl.name
 
 
-@pytest.mark.parametrize("name", ["k3s1_gn", "k5s1_bnpool"])
-def test_one_border_tiled_with_the_interior_cuts_padding(monkeypatch, name):
+@pytest.mark.parametrize("name,margin", [("k3s1_gn", 0.96), ("k5s1_bnpool", 0.99)])
+def test_one_border_tiled_with_the_interior_cuts_padding(monkeypatch, name, margin):
     """k3 over 32 inputs gives 34 outputs per dim and k5 over 16 or 32 gives 20
     or 36: a 2 + 32 (4 + 16, 4 + 32) segmentation lets the boxes divide the long
     segment, where low border / interior / high border leaves an interior of
     30 (12, 28) that they do not.  The plan keeps one border inside the
     interior (border_split bit 3 + d or 6 + d) and issues fewer MACs than the
-    same variant and wave grid with every border on its own."""
+    same variant and wave grid with every border on its own.  (The BatchNorm-
+    pool epilogue stores no y, so its border boxes may be narrower than 16 and
+    the three-way split loses less there.)"""
     wl = W.BY_NAME[name]
     e = C.make_epilogue(wl.epi, wl.groups, wl.eps, wl.scale)
     monkeypatch.delenv("CONVT3D_PLAN", raising=False)
@@ -358,7 +360,7 @@ def test_one_border_tiled_with_the_interior_cuts_padding(monkeypatch, name):
     three = C.convt3d_get_plan_info(geom_of(wl), e)
     assert three["border_split"] == 7
     assert three["valid_macs"] == info["valid_macs"]
-    assert info["issued_macs"] < 0.96 * three["issued_macs"]
+    assert info["issued_macs"] < margin * three["issued_macs"]
 
 
 def test_sigmoid_polynomial_matches_its_generator():
