@@ -25,6 +25,7 @@
 //                            then BatchNorm with the running statistics.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "conv_index.hpp"
@@ -717,10 +718,20 @@ __global__ __launch_bounds__(256) void eval_finalize_kernel(const EvalGeom E, co
 // ---------------------------------------------------------------------------
 // launchers
 
+// Threads of a statistics merge over `items` partial-sum pairs: enough waves
+// for kStatUnroll pairs in flight per thread, up to kStatThreads.  A short
+// merge (the standalone passes' few chunks per row) runs as one wave, which
+// finishes sooner than a full workgroup of idle threads.
+static int stat_threads(int64_t items) {
+    const int64_t waves = (items + 64 * kStatUnroll - 1) / (64 * kStatUnroll);
+    return (int)std::min<int64_t>(kStatThreads, std::max<int64_t>(1, waves) * 64);
+}
+
 int launch_gn_finalize(const float *partials, int N, int tiles_per_n, int C, int G, int chan_step, double count,
                        float eps, const float *gamma, const float *beta, float *ab, float *stats_out,
                        const float *prow, const float *pbias, double S, void *stream) {
-    hipLaunchKernelGGL(gn_finalize_kernel, dim3(N * G), dim3(kStatThreads), 0, (hipStream_t)stream, partials,
+    const int threads = stat_threads((int64_t)tiles_per_n * (C / G / chan_step));
+    hipLaunchKernelGGL(gn_finalize_kernel, dim3(N * G), dim3(threads), 0, (hipStream_t)stream, partials,
                        tiles_per_n, C, G, chan_step, eps, gamma, beta, ab, stats_out, count, prow, pbias,
                        (double)chan_step * S);
     return (int)hipGetLastError();
@@ -766,7 +777,9 @@ int launch_normalize(const float *src, float *out, const float *ab, int rows, in
 
 int launch_bn_finalize(const float *partials, int N, int tiles_per_n, int C, double S, const convt3d_epilogue &e,
                        float *out, const float *prow, const float *pbias, void *stream) {
-    hipLaunchKernelGGL(bn_finalize_kernel, dim3(C), dim3(kStatThreads), 0, (hipStream_t)stream, partials, N,
+    // and at least one wave per sample for the pooled output's per-sample sums
+    const int threads = std::max(stat_threads((int64_t)N * tiles_per_n), std::min(kStatThreads, 64 * N));
+    hipLaunchKernelGGL(bn_finalize_kernel, dim3(C), dim3(threads), 0, (hipStream_t)stream, partials, N,
                        tiles_per_n, C, S, e.eps, e.gamma, e.beta, out, e.stats_out, e.momentum, e.running_mean,
                        e.running_var, prow, pbias, e.scale);
     return (int)hipGetLastError();
