@@ -27,11 +27,11 @@ constexpr int kEvalTargetBlocks = 2048;  // eval-mode bin sums: workgroups to ai
 constexpr int kTuneCandidates = 12;
 constexpr int kTuneBorderAlternatives = 8;
 
-// sigmoid(p) for a softmax probability p in [0, 1]: the degree-6 Chebyshev
-// interpolant of sigmoid on [0, 1] in the monomial basis, float32 (Horner's
-// rule; |error| < 1e-7; sigmoid_poly.py beside the kernels prints them).
-constexpr float kSigmoidPoly[7] = {5.000000000e-01f,  2.500010431e-01f, -1.699157474e-05f, -2.072521672e-02f,
-                                   -3.389832564e-04f, 2.655707300e-03f, -5.169519573e-04f};
+// sigmoid(p) for a softmax probability p in [0, 1]: sigmoid(p) - 1/2 is odd,
+// approximated by p * (r0 + r1 p^2 + r2 p^4 + r3 p^6), the Chebyshev series of
+// sigmoid - 1/2 on [-1, 1] truncated after T7, float32 (|error| < 1.2e-7 with
+// Horner's rule in p^2; sigmoid_poly.py beside the kernels prints them).
+constexpr float kSigmoidOdd[4] = {2.499994040e-01f, -2.082532272e-02f, 2.053756500e-03f, -1.693251979e-04f};
 
 // Per-dimension stride-phase description.  Output index o = s*q + rho; the
 // taps that reach it are t = r + ts*j (j = 0..J-1) from input i = q + c - e*j,

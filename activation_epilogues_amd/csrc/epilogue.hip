@@ -431,8 +431,8 @@ __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out,
 // channel row of the group is one coalesced access of 256*VEC bytes.  The
 // waves combine their maxima and sums of exponentials through LDS in a fixed
 // order.  A workgroup holds blockDim / (64*WPP) position groups.  sigmoid of
-// the probability e/sum is the polynomial of kSigmoidPoly, evaluated in e with
-// coefficients scaled by powers of 1/sum.  out may equal src (each thread
+// the probability q = e/sum is 1/2 + q R(q^2), R the polynomial of
+// kSigmoidOdd, evaluated in e^2 with coefficients scaled by powers of 1/sum.  out may equal src (each thread
 // writes only what it read).  NT: non-temporal loads (tensors past the
 // last-level cache); the output, which nothing here reads again, is stored
 // non-temporally.  S is counted in VEC-vectors.
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(1024) void softmax_rows_kernel(const float *src, fl
                 else v[c] = p[(size_t)c * S];
             }
         }
-        float m[VEC], l[VEC], d[VEC][7];
+        float m[VEC], l[VEC], d[VEC][4];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             m[e] = v[0][e];
@@ -502,12 +502,12 @@ __global__ __launch_bounds__(1024) void softmax_rows_kernel(const float *src, fl
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float inv = __builtin_amdgcn_rcpf(l[e]);
-            d[e][0] = kSigmoidPoly[0];
+            const float inv2 = inv * inv;
             float ik = inv;
 #pragma unroll
-            for (int k = 1; k < 7; ++k) {
-                d[e][k] = kSigmoidPoly[k] * ik;
-                ik *= inv;
+            for (int k = 0; k < 4; ++k) {
+                d[e][k] = kSigmoidOdd[k] * ik;
+                ik *= inv2;
             }
         }
         vec_t *o = reinterpret_cast<vec_t *>(out) + ((size_t)n * C + c0) * S + s;
@@ -517,10 +517,11 @@ __global__ __launch_bounds__(1024) void softmax_rows_kernel(const float *src, fl
             vec_t y;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                float t = d[e][6];
+                const float x = v[c][e], x2 = x * x;
+                float t = d[e][3];
 #pragma unroll
-                for (int k = 5; k >= 0; --k) t = fmaf(t, v[c][e], d[e][k]);
-                y[e] = t;
+                for (int k = 2; k >= 0; --k) t = fmaf(t, x2, d[e][k]);
+                y[e] = fmaf(t, x, 0.5f);
             }
             __builtin_nontemporal_store(y, o + (size_t)c * S);
         }

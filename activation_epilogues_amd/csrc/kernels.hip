@@ -245,6 +245,23 @@ void convt3d_mfma_kernel(const ConvParams P) {
     // the d-overhang at a region's end (d is the slowest index), runs no MFMAs
     const bool wave_live = min(vol, TQd_e * plane) > wpos * PBW * 32;
 
+    // softmax kernels with up to two co blocks per wave start each accumulator
+    // at its channel's bias (-inf for rows past Cout, whose packed weights are
+    // zero): the softmax then needs no separate bias pass.  The same 16*CBW
+    // values for every phase group, held in registers (with four co blocks
+    // they would cost an occupancy step; those add the bias in the epilogue).
+    constexpr bool BI = SM && CBW <= 2;
+    float binit[BI ? CBW : 1][16];
+    if constexpr (BI) {
+#pragma unroll
+        for (int c = 0; c < CBW; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = ix::acc_row(cb0 * 32, c, r) + 4 * half;
+                binit[c][r] = row < P.Cout ? (P.bias ? P.bias[grp * P.Cout + row] : 0.0f) : -INFINITY;
+            }
+    }
+
   for (int pgi = 0; pgi < npg; ++pgi) {
     const int pg = pg0 + pgi;
     const int rho_h = pg % sh;
@@ -264,7 +281,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
             for (int pb = 0; pb < PBW; ++pb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[p][c][pb][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[p][c][pb][r] = BI ? binit[BI ? c : 0][r] : 0.0f;
 
     bool work = Jd > 0 && Jh > 0 && w_taps && jd_lo <= jd_hi && jh_lo <= jh_hi;
     {
@@ -490,17 +507,20 @@ void convt3d_mfma_kernel(const ConvParams P) {
     if constexpr (SM) {
         // Channel softmax + sigmoid.  The wave holds every channel of its columns
         // (planner: WCO == 1 and CBW*32 >= Cout); lane l and lane l^32 hold
-        // complementary halves.  Bias first (padding rows -> -inf, so they add 0).
+        // complementary halves.  Bias first (padding rows -> -inf, so they add
+        // 0), unless the accumulators started at it.
+        if constexpr (!BI) {
 #pragma unroll
-        for (int c = 0; c < CBW; ++c)
+            for (int c = 0; c < CBW; ++c)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float bco = row_ok(c, r) ? bias_of(c, r, 0.0f) : -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const float bco = row_ok(c, r) ? bias_of(c, r, 0.0f) : -INFINITY;
 #pragma unroll
-                for (int p = 0; p < NPH; ++p)
+                    for (int p = 0; p < NPH; ++p)
 #pragma unroll
-                    for (int pb = 0; pb < PBW; ++pb) acc[p][c][pb][r] += bco;
-            }
+                        for (int pb = 0; pb < PBW; ++pb) acc[p][c][pb][r] += bco;
+                }
+        }
         // exp(x) = 2^(x*log2 e) on the hardware exp2, 1/x on the hardware
         // reciprocal (about 1 ulp each); the max is taken on the scaled values.
         constexpr float kLog2e = 1.4426950408889634f;
@@ -526,28 +546,29 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         sum += e;
                     }
                 sum += __shfl_xor(sum, 32);
-                // sigmoid(q) for the probability q = e/sum in [0, 1]: the degree-6
-                // Chebyshev interpolant of sigmoid on [0, 1] (|error| < 1e-7; the
+                // sigmoid(q) for the probability q = e/sum in [0, 1]: 1/2 + q R(q^2)
+                // with the odd polynomial of kSigmoidOdd (|error| < 1.2e-7; the
                 // coefficients are printed by sigmoid_poly.py beside this file),
-                // sum_k c_k q^k = sum_k (c_k / sum^k) e^k by Horner's rule in e.
+                // as 1/2 + e R'(e^2) with R' = sum_k (r_k / sum^(2k+1)) (e^2)^k.
                 const float inv = __builtin_amdgcn_rcpf(sum);
-                float d[7];
-                d[0] = kSigmoidPoly[0];
+                const float inv2 = inv * inv;
+                float d[4];
                 float ik = inv;
 #pragma unroll
-                for (int k = 1; k < 7; ++k) {
-                    d[k] = kSigmoidPoly[k] * ik;
-                    ik *= inv;
+                for (int k = 0; k < 4; ++k) {
+                    d[k] = kSigmoidOdd[k] * ik;
+                    ik *= inv2;
                 }
 #pragma unroll
                 for (int c = 0; c < CBW; ++c)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float e = acc[p][c][pb][r];
-                        float y = d[6];
+                        const float e2 = e * e;
+                        float t = d[3];
 #pragma unroll
-                        for (int k = 5; k >= 0; --k) y = fmaf(y, e, d[k]);
-                        acc[p][c][pb][r] = y;
+                        for (int k = 2; k >= 0; --k) t = fmaf(t, e2, d[k]);
+                        acc[p][c][pb][r] = fmaf(t, e, 0.5f);
                     }
             }
         // stores: bounds-checked non-temporal buffer stores, one descriptor per

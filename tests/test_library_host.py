@@ -366,8 +366,8 @@ def test_one_border_tiled_with_the_interior_cuts_padding(monkeypatch, name, marg
 def test_sigmoid_polynomial_matches_its_generator():
     """The softmax epilogues' sigmoid coefficients (one table, shared by the
     fused and the standalone kernels) are the ones sigmoid_poly.py derives, and
-    their float32 Horner evaluation stays within 1e-7 of the definition on
-    [0, 1]."""
+    their float32 evaluation 1/2 + p R(p^2) stays within 1.2e-7 (two units in
+    the last place of a result in [0.5, 0.74]) of the definition on [0, 1]."""
     import importlib.util
     csrc = os.path.join(ROOT, "activation_epilogues_amd", "csrc")
     spec = importlib.util.spec_from_file_location("sigmoid_poly", os.path.join(csrc, "sigmoid_poly.py"))
@@ -375,13 +375,13 @@ def test_sigmoid_polynomial_matches_its_generator():
     spec.loader.exec_module(sp)
     want = sp.coefficients()
     src = open(os.path.join(csrc, "convt3d_internal.hpp")).read()
-    m = re.search(r"kSigmoidPoly\[7\]\s*=\s*\{([^}]*)\}", src)
+    m = re.search(r"kSigmoidOdd\[4\]\s*=\s*\{([^}]*)\}", src)
     assert m
     got = np.array([float(t.strip().rstrip("f")) for t in m.group(1).split(",")], dtype=np.float32)
     assert np.array_equal(got, want)
     p = np.linspace(0.0, 1.0, 100001).astype(np.float32)
-    err = np.abs(sp.horner32(got, p).astype(np.float64) - 1.0 / (1.0 + np.exp(-p.astype(np.float64)))).max()
-    assert err < 1e-7
+    err = np.abs(sp.eval32(got, p).astype(np.float64) - 1.0 / (1.0 + np.exp(-p.astype(np.float64)))).max()
+    assert err < 1.2e-7
 
 
 def test_plan_cache_keys_on_every_override(monkeypatch):
