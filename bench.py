@@ -162,14 +162,14 @@ def torch_comparison(wl, call, x, w, b, gamma, beta, rmean, rvar, fused_ms, reps
            "reps": reps, "note": "PyTorch-ROCm (MIOpen) fp32, TF32 off; context only"}
     if has_tail:
         # convt3d_epilogue_only alone on a resident y: its passes move
-        # (reads, writes) x |y| bytes: GN (2, 1), softmax (1, 1) up to 64
+        # (reads, writes) x |y| bytes: GN (2, 1), softmax (1, 1) up to 1024
         # channels (held in registers) else (2, 1), BN (1, 0)
         y = conv()
         out = torch.empty((wl.n, wl.cout), device=x.device) if pooled else torch.empty_like(y)
         ep_ms = timed(lambda: C.convt3d_epilogue_only(y, wl.n, wl.cout, S, epi, out, ws, ws_bytes))
         if pooled:
             passes = 1
-        elif wl.epi == W.EPI_SOFTMAX_SIGMOID and wl.cout <= 64:
+        elif wl.epi == W.EPI_SOFTMAX_SIGMOID and wl.cout <= 1024:
             passes = 2
         else:
             passes = 3
@@ -305,9 +305,10 @@ def measure(wl, args, log=print):
     kernels["pass"] = "second pass of the same steps, every kernel bracketed by HIP events"
     if prof_all["normalize_ms"] > 0:
         # the output pass moves |y| per read and per write: GroupNorm's
-        # normalise and the register-held softmax read once and write once;
-        # the softmax over more than 64 channels reads twice
-        passes = 3 if (wl.epi == W.EPI_SOFTMAX_SIGMOID and wl.cout > 64) else 2
+        # normalise and the softmax over up to 1024 channels (held in the
+        # registers of one position group) read once and write once; the
+        # softmax over more channels reads twice
+        passes = 3 if (wl.epi == W.EPI_SOFTMAX_SIGMOID and wl.cout > 1024) else 2
         norm_bytes = passes * 4.0 * call.out.numel()
         kernels["normalize_GBps"] = round(norm_bytes / (kernels["normalize_ms"] * 1e-3) / 1e9, 1)
         kernels["normalize_frac_hbm"] = round(kernels["normalize_GBps"] / PEAK_HBM_GBS, 4)
