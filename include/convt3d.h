@@ -247,8 +247,9 @@ int convt3d_autotune(const float *x, const void *w_packed, const float *bias,
  * the training one updates the running statistics as convt3d_fused does (the
  * count M is n * spatial).  CONVT3D_EPI_NONE is rejected
  * (CONVT3D_ERR_UNSUPPORTED).  Same numerics as the fused epilogues; y is read
- * twice for GroupNorm and softmax (statistics, then the output pass) and once
- * for BatchNorm.  Enqueued on stream, no waiting. */
+ * twice for GroupNorm (statistics, then the output pass), once for softmax
+ * over up to 1024 channels (twice above that: running maximum and sum, then
+ * the output) and once for BatchNorm.  Enqueued on stream, no waiting. */
 size_t convt3d_epilogue_workspace_size(int32_t n, int32_t c, int64_t spatial, const convt3d_epilogue *epi);
 int convt3d_epilogue_only(const float *y, int32_t n, int32_t c, int64_t spatial,
                           const convt3d_epilogue *epi, float *out, void *workspace,
