@@ -441,7 +441,17 @@ def measure_epilogue_only(wl, args, log=print):
     nbytes = passes * 4.0 * y.numel()
     gbps = nbytes / (ms * 1e-3) / 1e9
     kern = {k: round(prof[k] / args.steps, 4) for k in ("reduce_ms", "finalize_ms", "normalize_ms")}
-    log(f"[bench] {wl.name} epilogue only: {ms:.4f} ms/call, {gbps:.0f} GB/s")
+    # each HBM pass on its own (its kernel's HIP-event time): the statistics
+    # pass reads |y|; the output pass (GroupNorm's normalise, the softmax)
+    # reads |y| (twice for the softmax above 1024 channels) and writes |y|
+    pass_bytes = {"reduce_ms": 4.0 * y.numel(),
+                  "normalize_ms": (passes - (1 if wl.epi == W.EPI_RELU_GROUPNORM else 0)) * 4.0 * y.numel()}
+    per_pass = {}
+    for k, b in pass_bytes.items():
+        if kern[k] > 0:
+            r = b / (kern[k] * 1e-3) / 1e9
+            per_pass[k.replace("_ms", "")] = {"ms": kern[k], "GBps": round(r, 1), "frac_hbm": round(r / PEAK_HBM_GBS, 4)}
+    log(f"[bench] {wl.name} epilogue only: {ms:.4f} ms/call, {gbps:.0f} GB/s; per pass {per_pass}")
     in_place = None
     if not pooled:
         # the same calls with out == y (the API allows it); y's values change
@@ -466,7 +476,8 @@ def measure_epilogue_only(wl, args, log=print):
         "metric": "convt3d_epilogue_only HBM rate on a resident conv output",
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_call": round(ms, 4), "higher_is_better": True, "frac_hbm": round(gbps / PEAK_HBM_GBS, 4),
-        "y_passes": passes, "bytes_per_call": nbytes, "kernels_ms": kern, "in_place": in_place,
+        "y_passes": passes, "bytes_per_call": nbytes, "kernels_ms": kern, "per_pass": per_pass,
+        "in_place": in_place,
         "config": {"workload": wl.name, "y": list(y.shape), "epilogue": W.EPI_NAMES[wl.epi], "out": "separate buffer"},
         "dtype": "f32", "data": "the workload's own conv output (synthetic seeded inputs)",
     }
@@ -522,7 +533,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+              "(a batch split with one all-reduce of the BatchNorm sums is the design); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch  # noqa: F401  (loads torch's HIP runtime before the library)

@@ -40,3 +40,13 @@ def test_committed_summaries_parse():
         assert nbytes is None or nbytes > 0
         if nbytes is not None and kernel == "convt3d_mfma_kernel":
             assert plan is not None and plan.count(",") == 6
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    """--gpus N > 1 stops before touching a GPU, with a status of 2 and a message."""
+    import subprocess
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
