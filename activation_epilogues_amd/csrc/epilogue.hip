@@ -432,11 +432,10 @@ __global__ __launch_bounds__(256) void softmax_pass_kernel(const V *src, V *out,
 // waves combine their maxima and sums of exponentials through LDS in a fixed
 // order.  A workgroup holds blockDim / (64*WPP) position groups.  sigmoid of
 // the probability q = e/sum is 1/2 + q R(q^2), R the polynomial of
-// kSigmoidOdd, evaluated in e^2 with coefficients scaled by powers of 1/sum.
-// out may equal src (each thread writes only what it read).  NT:
-// non-temporal loads (tensors past the last-level cache); the output, which
-// nothing here reads again, is stored non-temporally.  S is counted in
-// VEC-vectors.
+// kSigmoidOdd, evaluated in e^2 with coefficients scaled by powers of 1/sum.  out may equal src (each thread
+// writes only what it read).  NT: non-temporal loads (tensors past the
+// last-level cache); the output, which nothing here reads again, is stored
+// non-temporally.  S is counted in VEC-vectors.
 template <int CR, int VEC, bool NT>
 __global__ __launch_bounds__(1024) void softmax_rows_kernel(const float *src, float *out, int N, int C, int S,
                                                             int WPP) {
