@@ -216,7 +216,7 @@ const char *convt3d_status_string(int status) {
         case CONVT3D_ERR_WORKSPACE: return "workspace missing or smaller than convt3d_workspace_size";
         case CONVT3D_ERR_UNSUPPORTED: return "unsupported epilogue or geometry combination";
         case CONVT3D_ERR_LAUNCH: return "HIP kernel launch failed";
-        case CONVT3D_ERR_TOO_LARGE: return "tensor too large (more than 2^31 elements)";
+        case CONVT3D_ERR_TOO_LARGE: return "tensor too large (more than 2^31 elements, or an input plane D*H*W over 2^29)";
         case CONVT3D_ERR_ALIAS: return "out overlaps x";
         case CONVT3D_ERR_SCRATCH: return "the plan needs more workspace than the static scratch of convt3d_fused_noalloc";
         default: return "unknown status";

@@ -217,6 +217,29 @@ CONVT3D_IX unsigned row_pair_bytes(int row, int Cout, int S) {
 // byte offset a lane gives a store that must not happen: past every range
 constexpr unsigned kDropOffset = 0xFFFFFFF8u;
 
+// ---- halo staging: raw buffer loads of one channel chunk (CI_T channel
+// planes from the chunk's first channel, CI_T * D*H*W * 4 bytes, the plane
+// offset of each channel in the scalar offset), or, when that range passes
+// 2^31 bytes, of one channel plane per descriptor (range 4 * D*H*W, no scalar
+// offset).  A halo position outside the input gets this byte offset, past
+// either range whether or not the scalar offset is added before the range
+// check, and reads as zero.  The planner keeps D*H*W at or below 2^29, so both
+// ranges stay at or below 2^31 bytes and the offset plus a plane offset below
+// 2^32.
+constexpr unsigned kHaloOutside = 0x80000000u;
+static_assert(kMaxChunkPlanes <= (int64_t(1) << 29) && kMaxInputPlane <= (int64_t(1) << 29),
+              "staging ranges and the outside offset must fit 32 bits");
+// a 64-bit address from its two 32-bit halves (each read from the first
+// lane into a scalar register), both zero-extended
+CONVT3D_IX uint64_t join_halves(unsigned hi, unsigned lo) { return ((uint64_t)hi << 32) | (uint64_t)lo; }
+// range of the chunk descriptor (0: one descriptor per plane instead)
+CONVT3D_IX unsigned chunk_range_bytes(int CI_T, int DHWin) { return 4u * (unsigned)CI_T * (unsigned)DHWin; }
+// byte offset of halo position (id, ih, iw) in a channel plane, or kHaloOutside
+CONVT3D_IX unsigned halo_src_off(int id, int ih, int iw, int D, int H, int W) {
+    const bool inside = (unsigned)id < (unsigned)D && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
+    return inside ? (unsigned)((id * H + ih) * W + iw) * 4u : kHaloOutside;
+}
+
 // ---- statistics partials, channel-major [n][Cout_total][tile][2] (each
 // channel's tiles contiguous, the order the statistics merges read them):
 // tile index of a work item, and the float offset of a (sum, sum of squares)

@@ -19,6 +19,12 @@ constexpr int kMaxLdsBytes = 80 * 1024;  // at least two workgroups per CU
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs (256 CUs), one L2 each
 constexpr int64_t kL2Bytes = 4 << 20;    // L2 per XCD
 constexpr int kRowStatChunk = 8192;      // vector elements per workgroup in the statistics pass over y
+// The conv kernel's halo staging addresses a chunk of CI_T input channel
+// planes with 32-bit byte offsets when CI_T * D*H*W is at most
+// kMaxChunkPlanes, else one channel plane per descriptor; input planes D*H*W
+// stay at or below kMaxInputPlane.
+constexpr int64_t kMaxChunkPlanes = int64_t(1) << 29;
+constexpr int64_t kMaxInputPlane = int64_t(1) << 29;
 constexpr int kEvalMaxK = 31;            // eval-mode BN: kernel size limit (bins per dim <= 2k+1)
 constexpr int kEvalMaxBins = 2 * kEvalMaxK + 1;
 constexpr int kEvalTargetBlocks = 2048;  // eval-mode bin sums: workgroups to aim for
@@ -70,6 +76,7 @@ struct ConvParams {
     int rg_off[kMaxRegions + 1];
     int tiles_total;      // rg_off[nreg]
     int CI_T;             // input channels per LDS chunk (multiple of 8)
+    int plane_desc;       // 1: CI_T * D*H*W > kMaxChunkPlanes, staging loads take one descriptor per plane
     int octets;           // ceil(Cin / 8)
     int nchunks;          // ceil(octets * 8 / CI_T)
     int cb_total;         // ceil(Cout / 32)

@@ -22,6 +22,7 @@
 #include <atomic>
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "conv_index.hpp"
 #include "convt3d_internal.hpp"
@@ -192,44 +193,60 @@ void convt3d_mfma_kernel(const ConvParams P) {
     const float *xn = P.x + (size_t)n * P.x_nstride + (size_t)grp * P.xg;
 
     // ---- halo staging.  Thread t takes halo positions t, t + 256, ...; for each
-    // position inside the input it loads the 8 channels of every octet of the
-    // chunk (one address, channel planes apart) and writes them as two 16-byte
-    // LDS stores.  Positions outside the input are never written: when the box
-    // crosses the input border (or Cin is not a multiple of 8) the buffer is
-    // cleared once, and those positions stay zero for every chunk.
-    const bool clear = lo_d < 0 || lo_d + HD > P.D || lo_h < 0 || lo_h + HH > P.H || lo_w < 0 ||
-                       lo_w + HW > P.W || (P.Cin & 7) != 0;
-    if (clear) {
-        float4 *l4 = reinterpret_cast<float4 *>(lds);
-        const int n4 = (P.CI_T * SLAB) >> 2;
-        for (int i = tid; i < n4; i += kBlockThreads) l4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        __syncthreads();
-    }
+    // it loads the 8 channels of every octet of the chunk and writes them as
+    // two 16-byte LDS stores.  The loads are raw buffer loads: one descriptor
+    // over the chunk's channel planes, formed once per chunk, with each
+    // channel's plane offset in a scalar register and the position's byte
+    // offset as the one vector operand.  (When the chunk's planes exceed what
+    // 32-bit offsets reach, plain global loads with 64-bit addresses instead.)
+    // A position outside the input gets an offset past the range and reads
+    // zero; channels past Cin (a last, partial octet) are not
+    // loaded and stage zero.  Every position of every chunk is written, so the
+    // buffer needs no clearing.
     const int inc_w = kBlockThreads % HW, inc_h = (kBlockThreads / HW) % HH, inc_d = kBlockThreads / (HW * HH);
-    auto stage = [&](int chunk) {
+    const unsigned plane_bytes = 4u * (unsigned)DHWin;
+    auto stage_t = [&](int chunk, auto per_plane) {
+        constexpr bool kPlanes = decltype(per_plane)::value;
         int t = tid;  // opaque: the digits are formed here, not kept live across the MFMA loop
         asm volatile("" : "+v"(t));
         int w = t % HW, h = (t / HW) % HH, d = t / (HW * HH);
         const int oct0 = chunk * G4;
+        // descriptors are formed from a base read into scalar registers (a
+        // descriptor in vector registers needs a loop over its distinct values
+        // at every load); the chunk's is formed here, outside the position loop
+        auto scalar_ptr = [](uint64_t a) -> void * {
+            // readfirstlane returns int: each half is taken as unsigned before
+            // widening (a sign-extended low half would corrupt the high bits)
+            return reinterpret_cast<void *>(ix::join_halves((unsigned)__builtin_amdgcn_readfirstlane((int)(a >> 32)),
+                                                            (unsigned)__builtin_amdgcn_readfirstlane((int)a)));
+        };
+        const uint64_t xc = reinterpret_cast<uint64_t>(xn + (size_t)oct0 * 8 * DHWin);
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            scalar_ptr(xc), (short)0, (int)ix::chunk_range_bytes(kPlanes ? 0 : P.CI_T, DHWin), 0x00020000);
+        auto load = [&](int ch, unsigned vo) -> float {  // channel ch of the chunk at byte offset vo
+            if constexpr (kPlanes) {
+                return vo != ix::kHaloOutside ? reinterpret_cast<const float *>(xc)[(size_t)ch * DHWin + (vo >> 2)]
+                                              : 0.0f;
+            } else {
+                return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, vo, ch * plane_bytes, 0));
+            }
+        };
+        const int cin_left = __builtin_amdgcn_readfirstlane(P.Cin - oct0 * 8);
         for (int pos = t; pos < SLAB; pos += kBlockThreads) {
-            const int id = lo_d + d, ih = lo_h + h, iw = lo_w + w;
-            if ((unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H && (unsigned)iw < (unsigned)P.W) {
-                const int voff = (id * P.H + ih) * P.W + iw;
-                for (int g = 0; g < G4; ++g) {
-                    const int ci0 = (oct0 + g) * 8;
-                    const float *src = xn + (size_t)ci0 * DHWin + voff;
-                    float v[8];
-                    if (ci0 + 8 <= P.Cin) {
+            const unsigned vo = ix::halo_src_off(lo_d + d, lo_h + h, lo_w + w, P.D, P.H, P.W);
+            for (int g = 0; g < G4; ++g) {
+                const int nch = cin_left - 8 * g;  // channels of the octet that exist (may be <= 0 past Cin)
+                float v[8];
+                if (nch >= 8) {
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) v[c] = src[(size_t)c * DHWin];
-                    } else {
+                    for (int c = 0; c < 8; ++c) v[c] = load(8 * g + c, vo);
+                } else {
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) v[c] = ci0 + c < P.Cin ? src[(size_t)c * DHWin] : 0.0f;
-                    }
-                    float4 *l4 = reinterpret_cast<float4 *>(lds);
-                    l4[ix::stage_lds_index(g, SLAB, pos, 0)] = make_float4(v[0], v[2], v[4], v[6]);
-                    l4[ix::stage_lds_index(g, SLAB, pos, 1)] = make_float4(v[1], v[3], v[5], v[7]);
+                    for (int c = 0; c < 8; ++c) v[c] = c < nch ? load(8 * g + c, vo) : 0.0f;
                 }
+                float4 *l4 = reinterpret_cast<float4 *>(lds);
+                l4[ix::stage_lds_index(g, SLAB, pos, 0)] = make_float4(v[0], v[2], v[4], v[6]);
+                l4[ix::stage_lds_index(g, SLAB, pos, 1)] = make_float4(v[1], v[3], v[5], v[7]);
             }
             w += inc_w;
             if (w >= HW) { w -= HW; ++h; }
@@ -237,6 +254,10 @@ void convt3d_mfma_kernel(const ConvParams P) {
             if (h >= HH) { h -= HH; ++d; }
             d += inc_d;
         }
+    };
+    auto stage = [&](int chunk) {
+        if (P.plane_desc) stage_t(chunk, std::true_type{});
+        else stage_t(chunk, std::false_type{});
     };
     stage(0);
     __syncthreads();

@@ -261,6 +261,8 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
         out->push_back(*pl);
         return CONVT3D_OK;
     }
+    // the conv kernel stages input channel planes through 32-bit buffer offsets
+    if ((int64_t)g->d * g->h * g->w > kMaxInputPlane) return CONVT3D_ERR_TOO_LARGE;
     // the in-register softmax needs every channel in one workgroup (<= 4 blocks
     // of 32, one channel group); beyond that the conv stores y and a second
     // pass finishes
@@ -699,6 +701,7 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     for (int r = 0; r <= kMaxRegions; ++r) cp->rg_off[r] = pl.rg_off[r];
     cp->tiles_total = pl.tiles_total;
     cp->CI_T = pl.CI_T; cp->octets = pl.octets; cp->nchunks = pl.nchunks;
+    cp->plane_desc = (int64_t)pl.CI_T * pl.g.d * pl.g.h * pl.g.w > kMaxChunkPlanes;
     cp->cb_total = pl.cb_total;
     cp->WCO = pl.WCO; cp->WPOS = pl.WPOS;
     cp->co_tiles = pl.co_tiles; cp->nwgroups = pl.nwgroups;

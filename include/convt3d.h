@@ -120,7 +120,8 @@ enum convt3d_status {
     CONVT3D_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than required         */
     CONVT3D_ERR_UNSUPPORTED = 6,   /* epilogue kind unknown or not valid for the call */
     CONVT3D_ERR_LAUNCH = 7,        /* HIP reported an error when launching            */
-    CONVT3D_ERR_TOO_LARGE = 8,     /* a tensor exceeds 2^31 elements                  */
+    CONVT3D_ERR_TOO_LARGE = 8,     /* a tensor exceeds 2^31 elements, or (conv path)  */
+                                   /* an input channel plane D*H*W exceeds 2^29       */
     CONVT3D_ERR_ALIAS = 9,         /* out overlaps x                                  */
     CONVT3D_ERR_SCRATCH = 10       /* convt3d_fused_noalloc: the plan needs more workspace than the
                                       library's static scratch (CONVT3D_NOALLOC_SCRATCH_BYTES) */

@@ -6,7 +6,7 @@
 // each address the kernel would form -- through the same index functions the
 // convolution kernel calls (conv_index.hpp) -- against the buffers the caller
 // handed in: LDS inside the workgroup's dynamic allocation (and never read
-// before it was cleared or staged), global reads inside x / the packed
+// before it was staged), global reads inside x / the packed
 // weights / bias / the partials, every output and partial sum written exactly
 // once, and the statistics merges reading only partials the conv wrote.
 // No value is computed.  Built with -fsanitize=address,undefined, so the host
@@ -193,11 +193,14 @@ int replay_conv(const Plan &pl, const ConvParams &P) {
         const int cb0w = wi.co_tile * CO_T;
         if (g_full) ldsv.assign(lds_floats / 4 + 1, 0);
 
-        const bool clear = lo_d < 0 || lo_d + HD > P.D || lo_h < 0 || lo_h + HH > P.H || lo_w < 0 ||
-                           lo_w + HW > P.W || (P.Cin & 7) != 0;
-        if (clear && g_full)
-            for (int i = 0; i < halo4; ++i) ldsv[i] = 1;
         const int inc_w = kBlockThreads % HW, inc_h = (kBlockThreads / HW) % HH, inc_d = kBlockThreads / (HW * HH);
+        const unsigned plane_bytes = 4u * (unsigned)DHWin;
+        if ((int64_t)DHWin > kMaxInputPlane) fail("input plane of %d voxels", DHWin);
+        if (P.plane_desc != ((int64_t)P.CI_T * DHWin > kMaxChunkPlanes))
+            fail("plane descriptors %d for a chunk of %d planes of %d", P.plane_desc, P.CI_T, DHWin);
+        // one descriptor over the chunk (scalar offset: the channel's plane) or one per plane
+        const uint64_t range = P.plane_desc ? plane_bytes : ix::chunk_range_bytes(P.CI_T, DHWin);
+        if (range > (uint64_t(1) << 31)) fail("staging range %" PRIu64 " bytes", range);
         auto stage = [&](int chunk) {
             const int oct0 = chunk * G4;
             for (int t = 0; t < kBlockThreads; ++t) {
@@ -205,24 +208,38 @@ int replay_conv(const Plan &pl, const ConvParams &P) {
                 for (int pos = t; pos < SLAB; pos += kBlockThreads) {
                     if ((d * HH + h) * HW + w != pos) fail("staging digits (%d,%d,%d) != position %d", d, h, w, pos);
                     const int id = lo_d + d, ih = lo_h + h, iw = lo_w + w;
-                    if ((unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H && (unsigned)iw < (unsigned)P.W) {
-                        const int voff = (id * P.H + ih) * P.W + iw;
-                        for (int g = 0; g < G4; ++g) {
-                            const int ci0 = (oct0 + g) * 8;
-                            const int clast = std::min(8, P.Cin - ci0);  // channels read
-                            if (clast > 0) {
+                    const bool inside =
+                        (unsigned)id < (unsigned)P.D && (unsigned)ih < (unsigned)P.H && (unsigned)iw < (unsigned)P.W;
+                    const unsigned vo = ix::halo_src_off(id, ih, iw, P.D, P.H, P.W);
+                    for (int g = 0; g < G4; ++g) {
+                        const int ci0 = (oct0 + g) * 8;
+                        const int nch = std::min(8, P.Cin - ci0);  // channels loaded
+                        for (int c = 0; c < nch; ++c) {
+                            const int ch = 8 * g + c;  // channel of the chunk
+                            // descriptor base (floats from the chunk's first plane)
+                            // and the load's buffer offset: in the range exactly
+                            // when the position is inside the input, with or
+                            // without the scalar offset, and never wrapping
+                            const int64_t base = P.plane_desc ? (int64_t)ch * DHWin : 0;
+                            const uint64_t so = P.plane_desc ? 0u : (uint64_t)ch * plane_bytes;
+                            const uint64_t vso = (uint64_t)vo + so;
+                            if (vso >= (uint64_t(1) << 32)) fail("staging offset %" PRIu64 " wraps", vso);
+                            if (inside != (vso < range) || inside != (vo < range))
+                                fail("staging offset %" PRIu64 " (position %s) against range %" PRIu64, vso,
+                                     inside ? "inside" : "outside", range);
+                            if (inside && (g_full || pos == t || pos + kBlockThreads >= SLAB)) {
+                                const int64_t rel = base + (int64_t)(vso / 4);  // floats from the chunk's first plane
                                 const int64_t off = (int64_t)n * P.x_nstride + (int64_t)grp * P.xg +
-                                                    (int64_t)ci0 * DHWin + voff;
-                                if (g_full || pos == t || pos + kBlockThreads >= SLAB) {
-                                    in_buf(bx_, P.x, off, 1, "x read (first channel)");
-                                    in_buf(bx_, P.x, off + (int64_t)(clast - 1) * DHWin, 1, "x read (last channel)");
-                                }
+                                                    (int64_t)oct0 * 8 * DHWin + rel;
+                                if (c == 0 || c == nch - 1) in_buf(bx_, P.x, off, 1, "x read");
+                                if (rel != (int64_t)(ci0 - oct0 * 8 + c) * DHWin + (vo / 4))
+                                    fail("staging offset %" PRIu64 " is not channel %d's", vso, ci0 + c);
                             }
-                            for (int half = 0; half < 2; ++half) {
-                                const int li = ix::stage_lds_index(g, SLAB, pos, half);
-                                if (li < 0 || li >= halo4) fail("staging LDS float4 %d outside the halo (%d)", li, halo4);
-                                else if (g_full) ldsv[li] = 1;
-                            }
+                        }
+                        for (int half = 0; half < 2; ++half) {
+                            const int li = ix::stage_lds_index(g, SLAB, pos, half);
+                            if (li < 0 || li >= halo4) fail("staging LDS float4 %d outside the halo (%d)", li, halo4);
+                            else if (g_full) ldsv[li] = 1;
                         }
                     }
                     w += inc_w;
@@ -541,6 +558,13 @@ int main(int argc, char **argv) {
     (void)argv;
     char line[1024];
     int failed = 0, cases = 0;
+    // the staging descriptor's base is rebuilt from two 32-bit halves: a low
+    // half with bit 31 set must not spill into the high half
+    if (ix::join_halves(0x7f12u, 0x80000004u) != 0x7f1280000004ull ||
+        ix::join_halves(0u, 0xffffffffu) != 0xffffffffull) {
+        std::printf("FAIL join_halves does not zero-extend\n");
+        ++failed;
+    }
     while (std::fgets(line, sizeof line, stdin)) {
         if (line[0] == '#' || line[0] == '\n') continue;
         char name[128], penv[128], lenv[32], mode[16];
