@@ -498,8 +498,24 @@ void convt3d_mfma_kernel(const ConvParams P) {
     auto row_u = [&](int c, int r) { return ix::acc_row(row0, c, r); };
     auto row_ok = [&](int c, int r) { return rows_full || row_u(c, r) + 4 * half < Cout; };
     auto rowp = [&](int c, int r) { return outb + (size_t)row_u(c, r) * S * 4; };
-    auto bias_of = [&](int c, int r, float dflt) {  // bias of the lane's row c, r (dflt: no bias)
-        return P.bias ? P.bias[grp * Cout + row_u(c, r) + 4 * half] : dflt;
+    // the bias of the lane's rows 4q .. 4q+3 of co block c (0 without bias and
+    // for rows past Cout): the four loads are issued together and waited for
+    // once.  The group offset is made opaque here so the loads stay in the
+    // epilogue, not hoisted above the MFMA loop.
+    auto bias_rows4 = [&](int c, int q, float (&bv)[4]) {
+        if (P.bias) {
+            int gofs = grp * Cout;
+            asm volatile("" : "+s"(gofs));
+            const float *b = P.bias + gofs;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = row_u(c, 4 * q + i) + 4 * half;
+                bv[i] = rows_full || row < Cout ? b[row] : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = 0.0f;
+        }
     };
     // the stores of one accumulator row (c, r) of position block pb.  The
     // softmax kernels write the final output, which nothing here reads again:
@@ -531,11 +547,14 @@ void convt3d_mfma_kernel(const ConvParams P) {
         // complementary halves.  Bias first (padding rows -> -inf, so they add
         // 0), unless the accumulators started at it.
         if constexpr (!BI) {
+            // one row at a time: loading them in groups costs these kernels
+            // (four co blocks, tight on registers) an occupancy step
 #pragma unroll
             for (int c = 0; c < CBW; ++c)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float bco = row_ok(c, r) ? bias_of(c, r, 0.0f) : -INFINITY;
+                    const float bo = P.bias ? P.bias[grp * Cout + row_u(c, r) + 4 * half] : 0.0f;
+                    const float bco = row_ok(c, r) ? bo : -INFINITY;
 #pragma unroll
                     for (int p = 0; p < NPH; ++p)
 #pragma unroll
@@ -660,6 +679,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
             for (int c = 0; c < CBW; ++c)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                    float bv[4];
+                    bias_rows4(c, q, bv);
                     const bool bok = row_ok(c, 4 * q);  // whole block in range (Cout % 8 == 0)
                     // the block's pivot: relu(bias) of its first channel (wave-uniform)
                     const float pvt = bok && P.bias ? fmaxf(P.bias[grp * Cout + row0 + c * 32 + 8 * q], 0.0f) : 0.0f;
@@ -667,7 +688,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
                         const int r = 4 * q + rr;
-                        const float bco = bok ? bias_of(c, r, 0.0f) : 0.0f;
+                        const float bco = bok ? bv[rr] : 0.0f;
                         char *rp = rowp(c, r);
 #pragma unroll
                         for (int pb = 0; pb < PBW; ++pb) {
@@ -698,12 +719,21 @@ void convt3d_mfma_kernel(const ConvParams P) {
         for (int c = 0; c < CBW; ++c) {
             // per-row sums x[r] (sum) and x[16 + r] (sum of squares) of the lane
             float x[32];
+            float bv[4];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                // BatchNorm sums z - scale*bias = scale*acc: its bias stays out
+                if (r % 4 == 0) {
+                    if (bn) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) bv[i] = 0.0f;
+                    } else {
+                        bias_rows4(c, r / 4, bv);
+                    }
+                }
                 const bool cok = row_ok(c, r);
-                // BatchNorm sums z - scale*bias = scale*acc: its bias stays out;
                 // GroupNorm sums relu(acc + bias) - relu(bias)
-                const float bco = cok && !bn ? bias_of(c, r, 0.0f) : 0.0f;
+                const float bco = cok ? bv[r % 4] : 0.0f;
                 float a1 = 0.0f, a2 = 0.0f;
                 char *rp = rowp(c, r);
 #pragma unroll
