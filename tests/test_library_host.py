@@ -290,6 +290,10 @@ def test_size_limits():
     # whole output and whole input beyond 2^31 elements
     assert status(C.make_geom(11, 1, 1, 590, 590, 590, 1)) == 8              # 11 * 590^3 > 2^31
     assert status(C.make_geom(1, 11, 1, 590, 590, 590, 1)) == 8
+    # input channel planes: the halo staging's 32-bit buffer offsets reach
+    # 2^29 voxels (k = 1 with a large pad keeps the output small)
+    assert status(C.make_geom(1, 1, 1, 1024, 1024, 512, 1, 1, (250, 250, 200))) == 0   # 2^29 voxels
+    assert status(C.make_geom(1, 1, 1, 1024, 1024, 513, 1, 1, (250, 250, 200))) == 8   # past 2^29
     # packed weights
     assert status(C.make_geom(1, 1024, 1024, 2, 2, 2, 16)) == 8
     assert C.convt3d_packed_weight_bytes(C.make_geom(1, 1024, 1024, 2, 2, 2, 16)) == 0
