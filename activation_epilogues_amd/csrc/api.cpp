@@ -96,6 +96,15 @@ int cached_entry(const convt3d_geom *g, const convt3d_epilogue *e, CacheEntry *o
     }
     {
         std::lock_guard<std::mutex> lk(g_mu);
+        // another thread may have planned (and since tuned) this key while the
+        // lock was released: keep its entry rather than a second, untuned one
+        for (auto it = g_cache.begin(); it != g_cache.end(); ++it)
+            if (it->first == key) {
+                *out = it->second;
+                out->plan.e = *e;
+                if (it != g_cache.begin()) g_cache.splice(g_cache.begin(), g_cache, it);
+                return CONVT3D_OK;
+            }
         g_cache.emplace_front(key, ent);
         if (g_cache.size() > 64) g_cache.pop_back();
     }

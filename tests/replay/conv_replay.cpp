@@ -31,8 +31,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <memory>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "conv_index.hpp"
@@ -553,9 +555,89 @@ static void check_coverage(Buf *out, int64_t elems) {
         }
 }
 
+// "threads" mode: the host calls that plan (plan info, workspace size,
+// output size) from several threads at once, every thread walking the cases
+// in its own order, so each geometry is first planned by whichever thread
+// gets there first; then a serial pass (cache hits) must give every thread's
+// results.  Built with -fsanitize=thread, this checks the plan cache for data
+// races.
+struct PlanResult {
+    int st;
+    convt3d_plan_info info;
+    size_t ws;
+    int64_t oelems;
+    bool operator==(const PlanResult &o) const {
+        return st == o.st && ws == o.ws && oelems == o.oelems &&
+               std::memcmp(&info, &o.info, sizeof(info)) == 0;
+    }
+};
+
+static PlanResult plan_once(const convt3d_geom &g, const convt3d_epilogue &e) {
+    PlanResult r;
+    std::memset(&r, 0, sizeof(r));
+    r.st = convt3d_get_plan_info(&g, &e, &r.info);
+    r.ws = convt3d_workspace_size(&g, &e);
+    r.oelems = convt3d_output_elems(&g, &e);
+    return r;
+}
+
+static int threads_main(int nthreads) {
+    std::vector<std::pair<convt3d_geom, convt3d_epilogue>> cases;
+    char line[1024];
+    while (std::fgets(line, sizeof line, stdin)) {
+        if (line[0] == '#' || line[0] == '\n') continue;
+        char name[128], penv[128], lenv[32], mode[16];
+        convt3d_geom g{};
+        int epi_kind, gn_groups;
+        const int got = std::sscanf(line,
+                                    "%127s %d %d %d %d %d %d  %d %d %d  %d %d %d  %d %d %d  %d %d %d  %d %d %d  %d %d %d "
+                                    "%127s %31s %15s",
+                                    name, &g.n, &g.cin, &g.cout, &g.d, &g.h, &g.w, &g.k[0], &g.k[1], &g.k[2], &g.stride[0],
+                                    &g.stride[1], &g.stride[2], &g.pad[0], &g.pad[1], &g.pad[2], &g.out_pad[0],
+                                    &g.out_pad[1], &g.out_pad[2], &g.dilation[0], &g.dilation[1], &g.dilation[2],
+                                    &g.groups, &epi_kind, &gn_groups, penv, lenv, mode);
+        if (got != 28) {
+            std::printf("FAIL bad case line: %s", line);
+            return 1;
+        }
+        convt3d_epilogue e{};
+        e.kind = epi_kind;
+        e.groups = gn_groups;
+        e.eps = 1e-5f;
+        e.scale = 1.0f;
+        cases.emplace_back(g, e);
+    }
+    const int nc = (int)cases.size();
+    std::vector<std::vector<PlanResult>> res(nthreads, std::vector<PlanResult>(nc));
+    std::atomic<int> ready{0};
+    std::vector<std::thread> pool;
+    for (int t = 0; t < nthreads; ++t)
+        pool.emplace_back([&, t]() {
+            ready.fetch_add(1);
+            while (ready.load() < nthreads) std::this_thread::yield();  // start together
+            for (int i = 0; i < nc; ++i) {
+                const int c = (i + t * 3) % nc;
+                res[t][c] = plan_once(cases[c].first, cases[c].second);
+            }
+        });
+    for (auto &th : pool) th.join();
+    int failed = 0;
+    for (int c = 0; c < nc; ++c) {
+        const PlanResult want = plan_once(cases[c].first, cases[c].second);
+        for (int t = 0; t < nthreads; ++t)
+            if (!(res[t][c] == want)) {
+                std::printf("FAIL case %d: thread %d planned status %d variant %d ws %zu, serial %d variant %d ws %zu\n",
+                            c, t, res[t][c].st, res[t][c].info.variant, res[t][c].ws, want.st, want.info.variant,
+                            want.ws);
+                ++failed;
+            }
+    }
+    std::printf("%d cases x %d threads, %d mismatches\n", nc, nthreads, failed);
+    return failed ? 1 : 0;
+}
+
 int main(int argc, char **argv) {
-    (void)argc;
-    (void)argv;
+    if (argc > 1 && std::strcmp(argv[1], "threads") == 0) return threads_main(argc > 2 ? std::atoi(argv[2]) : 8);
     char line[1024];
     int failed = 0, cases = 0;
     // the staging descriptor's base is rebuilt from two 32-bit halves: a low

@@ -45,6 +45,20 @@ def harness(tmp_path_factory):
     return exe
 
 
+@pytest.fixture(scope="module")
+def harness_tsan(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("g++ or the ROCm headers are missing")
+    exe = str(tmp_path_factory.mktemp("replay_tsan") / "conv_replay_tsan")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-fno-omit-frame-pointer", "-pthread",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-I", "/opt/rocm/include",
+           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "api.cpp"), SRC, "-o", exe]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-4000:]
+    return exe
+
+
 def case_line(name, wl, plan_env="-", ploop_env="-", mode="full"):
     t = W.triple
     k, s, p, op, dl = (t(v) for v in (wl.k, wl.stride, wl.pad, wl.out_pad, wl.dilation))
@@ -128,3 +142,23 @@ def test_named_workloads_full_size(harness):
     tuner are covered by the small cases above)."""
     lines = [case_line(wl.name, wl, mode="one") for wl in W.WORKLOADS + W.EXTRA_WORKLOADS]
     run(harness, lines, timeout=900)
+
+
+def test_concurrent_planning_under_thread_sanitizer(harness_tsan):
+    """Eight host threads plan the named workloads and random general
+    geometries at once (each geometry first planned by whichever thread gets
+    there), under ThreadSanitizer: no data race is reported, and every thread's
+    plan, workspace and output sizes equal a serial lookup afterwards."""
+    rng = np.random.default_rng(4242)
+    lines = [case_line(wl.name, wl) for wl in W.WORKLOADS + W.EXTRA_WORKLOADS]
+    while len(lines) < 24:
+        wl = W.random_general_geometry(rng, max_in=7, max_ch=40, epi=len(lines) % 4)
+        lines.append(case_line(f"r{len(lines)}", wl))
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 second_deadlock_stack=1")
+    env.pop("CONVT3D_PLAN", None)
+    env.pop("CONVT3D_PHASE_LOOP", None)
+    res = subprocess.run([harness_tsan, "threads", "8"], input="\n".join(lines) + "\n", capture_output=True,
+                         text=True, timeout=600, env=env)
+    assert "WARNING: ThreadSanitizer" not in res.stderr, res.stderr[-6000:]
+    assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-3000:]
+    assert "0 mismatches" in res.stdout, res.stdout[-2000:]
