@@ -35,6 +35,41 @@ __device__ __forceinline__ v16f mfma32x32x2(float a, float b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Cross-lane sums and maxima without the LDS crossbar: gfx950's lane-half
+// swaps (v_permlane32_swap: lanes l and l ^ 32; v_permlane16_swap: rows of 16
+// lanes, l and l ^ 16) and DPP row rotations.  The swap of v with itself
+// leaves v's lower half in both halves of the first result and its upper half
+// in both halves of the second, so their sum (or maximum) is v + v[l ^ 32] in
+// every lane, the same bits as adding the partner's value.
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v + v of lane l - N within its row of 16 lanes (DPP row rotation)
+template <int N>
+__device__ __forceinline__ float add_row_ror(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+// Sum over the wave's 64 lanes.  Every lane ends with a sum of all 64 values,
+// but the rotations add them in an order that depends on the lane: only one
+// lane's result is to be used.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = add_xor32(v);
+    v = add_xor16(v);
+    v = add_row_ror<8>(v);
+    v = add_row_ror<4>(v);
+    v = add_row_ror<2>(v);
+    return add_row_ror<1>(v);
+}
+
 // ---------------------------------------------------------------------------
 // Weight pre-pack of one channel group.  Packed order per phase:
 // [co_block][octet][tap][lane][4] (as float4 groups [co_block][octet*ntaps +
@@ -573,7 +608,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                 for (int c = 0; c < CBW; ++c)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[p][c][pb][r]);
-                m = fmaxf(m, __shfl_xor(m, 32));
+                m = max_xor32(m);
                 const float ml = m * kLog2e;
                 float sum = 0.0f;
 #pragma unroll
@@ -585,7 +620,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         acc[p][c][pb][r] = e;
                         sum += e;
                     }
-                sum += __shfl_xor(sum, 32);
+                sum = add_xor32(sum);
                 // sigmoid(q) for the probability q = e/sum in [0, 1]: 1/2 + q R(q^2)
                 // with the odd polynomial of kSigmoidOdd (|error| < 1.2e-7; the
                 // coefficients are printed by sigmoid_poly.py beside this file),
@@ -655,7 +690,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
     } else {
         // bias (+ReLU) and store, or scale; per-channel sums over the tile: the
         // lane's columns, then the 32 columns of each half (xor-shuffle
-        // butterfly, or per 8-channel block for GroupNorm), then the waves
+        // butterfly, or per 8-channel block for GroupNorm: lane-half swaps and
+        // row rotations over the whole wave), then the waves
         // (LDS), one (sum, sum of squares) per (tile, channel).  The sums are
         // of v - pivot with a per-channel pivot near the channel's values, so
         // a large common offset does not cancel in the fp32 sum of squares:
@@ -703,11 +739,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
                             if (bok) store_row(rp, pb, v);
                         }
                     }
-#pragma unroll
-                    for (int off = 32; off >= 1; off >>= 1) {
-                        b1 += __shfl_xor(b1, off);
-                        b2 += __shfl_xor(b2, off);
-                    }
+                    b1 = wave_sum(b1);  // lane 0's sums are the block's
+                    b2 = wave_sum(b2);
                     if (lane == 0 && bok) {
                         const int row = (wco * CBW + c) * 32 + 8 * q;
                         red[(wpos * CO32 + row) * 2 + 0] = b1;
