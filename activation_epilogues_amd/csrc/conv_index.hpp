@@ -23,15 +23,17 @@ CONVT3D_IX int imin(int a, int b) { return a < b ? a : b; }
 CONVT3D_IX int imax(int a, int b) { return a > b ? a : b; }
 
 // floor / ceil of a / b for b > 0 and any sign of a (tap ranges with
-// dilation; b is wave-uniform and 1 without dilation)
+// dilation; b is wave-uniform: 1 without dilation, a power of two for the
+// usual dilations, where an arithmetic shift is the floor)
 CONVT3D_IX int floor_div_any(int a, int b) {
     if (b == 1) return a;
+    if ((b & (b - 1)) == 0) return a >> __builtin_ctz((unsigned)b);
     return a >= 0 ? a / b : -((-a + b - 1) / b);
 }
 CONVT3D_IX int ceil_div_any(int a, int b) { return -floor_div_any(-a, b); }
 
 // ---- workgroup -> work item.  Workgroups are handed to the XCDs round-robin
-// (dispatch index i runs on XCD i % nxcd), each XCD with its own L2.  The
+// (dispatch index i runs on XCD i % kNumXcd), each XCD with its own L2.  The
 // dispatch index bid is mapped to a linear work index so that every XCD gets
 // one contiguous range; the halo overlap of neighbouring tiles then hits in
 // one L2.  Within it either the (co tile, phase) index varies fastest (those
@@ -46,9 +48,22 @@ struct WorkItem {
     int n, grp;   // sample, channel group
 };
 
+// a / d and a % d for a wave-uniform d > 0; d == 1, the usual case for the
+// channel-group, co-tile and w-phase-group counts, needs no division
+CONVT3D_IX void divmod_uniform(int a, int d, int &q, int &r) {
+    if (d == 1) {
+        q = a;
+        r = 0;
+        return;
+    }
+    q = a / d;
+    r = a - q * d;
+}
+
 CONVT3D_IX WorkItem work_item(const ConvParams &P, int bid, int gx, int gy, int gz) {
     const int total = gx * gy * gz;
-    const int nx = P.nxcd, q = total / nx, r = total % nx;
+    constexpr int nx = kNumXcd;
+    const int q = total / nx, r = total % nx;
     const int xcd = bid % nx, idx = bid / nx;
     const int lin = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
     int bx, by;
@@ -62,12 +77,9 @@ CONVT3D_IX WorkItem work_item(const ConvParams &P, int bid, int gx, int gy, int 
     const int nz = lin / (gx * gy);  // grid z = sample * G + group
     WorkItem w;
     w.bx = bx;
-    w.grp = nz % P.G;
-    w.n = nz / P.G;
-    w.co_tile = by % P.co_tiles;
-    by /= P.co_tiles;
-    w.wgrp = by % P.nwgroups;
-    w.pg = by / P.nwgroups;
+    divmod_uniform(nz, P.G, w.n, w.grp);
+    divmod_uniform(by, P.co_tiles, by, w.co_tile);
+    divmod_uniform(by, P.nwgroups, w.pg, w.wgrp);
     return w;
 }
 

@@ -83,7 +83,6 @@ struct ConvParams {
     int WCO, WPOS;        // wave grid
     int co_tiles;
     int nwgroups;         // w-phase groups per (rho_d, rho_h): s / NPH
-    int nxcd;             // XCDs the workgroups are dealt over round-robin
     int order;            // 0: (co tile, phase) index fastest, 1: tile fastest
     int phase_loop;       // 1: each workgroup loops over all (rho_d, rho_h) groups
     int red_off;          // LDS float offset of the epilogue's reduction scratch

@@ -706,7 +706,6 @@ void fill_conv_params(const Plan &pl, ConvParams *cp) {
     cp->WCO = pl.WCO; cp->WPOS = pl.WPOS;
     cp->co_tiles = pl.co_tiles; cp->nwgroups = pl.nwgroups;
 
-    cp->nxcd = kNumXcd;
     cp->order = pl.order;
     cp->phase_loop = pl.phase_loop; cp->red_off = pl.red_off;
     cp->epi = pl.softmax_pass ? CONVT3D_EPI_NONE : pl.e.kind;
