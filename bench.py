@@ -45,15 +45,22 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 METRIC = "ConvTranspose3d+epilogue GFLOP/s and ms/forward; % FP32 MFMA peak"
 CSRC = os.path.join(ROOT, "activation_epilogues_amd", "csrc")
 # source file of each kernel a roofline line is given for
-KERNEL_SRC = {"convt3d_mfma_kernel": os.path.join(CSRC, "kernels.hip"),
-              "eval_binsum_kernel": os.path.join(CSRC, "epilogue.hip")}
+# the sources each profiled kernel's code is built from: its file and the
+# headers whose code it inlines
+KERNEL_SRC = {"convt3d_mfma_kernel": [os.path.join(CSRC, f) for f in
+                                      ("kernels.hip", "conv_index.hpp", "convt3d_internal.hpp")],
+              "eval_binsum_kernel": [os.path.join(CSRC, f) for f in
+                                     ("epilogue.hip", "conv_index.hpp", "convt3d_internal.hpp")]}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash(kernel: str = "convt3d_mfma_kernel") -> str:
-    """Hash of the HIP source file `kernel` is built from."""
-    with open(KERNEL_SRC[kernel], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources `kernel` is built from (in a fixed order)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRC[kernel]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(workload: str, kernel: str = "convt3d_mfma_kernel"):
