@@ -19,6 +19,9 @@ constexpr int kMaxLdsBytes = 80 * 1024;  // at least two workgroups per CU
 constexpr int kNumXcd = 8;               // MI355X: 8 XCDs (256 CUs), one L2 each
 constexpr int64_t kL2Bytes = 4 << 20;    // L2 per XCD
 constexpr int kRowStatChunk = 8192;      // vector elements per workgroup in the statistics pass over y
+// Register-prefetch kernels hold the next chunk's halo (one octet) in
+// registers: at most kRpPositions halo positions per thread.
+constexpr int kRpPositions = 10;
 // The conv kernel's halo staging addresses a chunk of CI_T input channel
 // planes with 32-bit byte offsets when CI_T * D*H*W is at most
 // kMaxChunkPlanes, else one channel plane per descriptor; input planes D*H*W
@@ -161,6 +164,7 @@ struct Variant {
     bool softmax;        // compiled with the softmax epilogue (else NONE / GN / BN)
     int waves_per_simd;  // register-limited occupancy of the compiled kernel
     bool phase_loop;     // also compiled with the (rho_d, rho_h) phase-group loop
+    bool prefetch = false;  // register prefetch of the next channel chunk (one octet per chunk)
 };
 extern const Variant kVariants[];
 extern const int kNumVariants;

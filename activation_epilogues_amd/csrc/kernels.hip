@@ -140,8 +140,8 @@ __global__ __launch_bounds__(256) void prepack_kernel(const PackParams P) {
 // to 170 VGPRs (three waves) rather than being held to 128 (four), where an
 // earlier form spilled in its chunk prologue; it now needs about 125 and runs
 // four waves per SIMD.
-template <int CBW, int NPH, int PBW, bool SM, bool PL>
-__global__ __launch_bounds__(kBlockThreads, (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
+template <int CBW, int NPH, int PBW, bool SM, bool PL, bool RP>
+__global__ __launch_bounds__(kBlockThreads, RP ? 2 : (SM && CBW == 4) ? (NPH * PBW == 1 ? 2 : 1)
                                           : (CBW * NPH * PBW <= 2) ? 6
                                           : (CBW * NPH * PBW <= 4) ? 3
                                           : (CBW * NPH * PBW <= 8) ? 2 : 1)
@@ -297,6 +297,71 @@ void convt3d_mfma_kernel(const ConvParams P) {
     stage(0);
     __syncthreads();
 
+    // ---- register prefetch of the next channel chunk (RP kernels: one octet
+    // per chunk, at most kRpPositions halo positions per thread, 32-bit plane
+    // offsets; the planner keeps to these).  The loads of chunk k + 1 are
+    // issued during chunk k's last MFMA groups, after those groups' A operands
+    // are in registers, so nothing in the MFMA loop waits for them; after the
+    // chunk's barrier they are written to LDS as staging would write them.
+    // Every thread issues the same kRpPositions x 8 loads: positions past the
+    // slab and channels past Cin take an offset past the range and load zero.
+    static_assert(!RP || (CBW == 1 && NPH == 1 && PBW >= 4 && !SM && !PL), "prefetch builds: one form only");
+    constexpr int RPN = RP ? kRpPositions : 1;
+    float pf[RPN][8];
+    // the thread's next halo position (digits w, h, d) and the chunk's
+    // descriptor, set by prefetch_begin; prefetch_part issues the loads of the
+    // thread's positions [i0, i1)
+    int pw = 0, ph_ = 0, pd = 0, pnch = 0;
+    uint64_t pxc = 0;
+    auto prefetch_begin = [&](int chunk) {
+        int t = tid;  // opaque, as in staging
+        asm volatile("" : "+v"(t));
+        pw = t % HW;
+        ph_ = (t / HW) % HH;
+        pd = t / (HW * HH);
+        pxc = reinterpret_cast<uint64_t>(xn + (size_t)chunk * 8 * DHWin);
+        pnch = __builtin_amdgcn_readfirstlane(P.Cin - chunk * 8);
+    };
+    auto prefetch_part = [&](auto i0c, auto i1c) {
+        constexpr int i0 = decltype(i0c)::value, i1 = decltype(i1c)::value;
+        const __amdgpu_buffer_rsrc_t pxr = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>(ix::join_halves((unsigned)__builtin_amdgcn_readfirstlane((int)(pxc >> 32)),
+                                                     (unsigned)__builtin_amdgcn_readfirstlane((int)pxc))),
+            (short)0, (int)ix::chunk_range_bytes(8, DHWin), 0x00020000);
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+            const int pos = tid + i * kBlockThreads;
+            const unsigned vo = pos < SLAB ? ix::halo_src_off(lo_d + pd, lo_h + ph_, lo_w + pw, P.D, P.H, P.W)
+                                           : ix::kHaloOutside;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                pf[i][c] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(pxr, c < pnch ? vo : ix::kHaloOutside, c * plane_bytes, 0));
+            pw += inc_w;
+            if (pw >= HW) { pw -= HW; ++ph_; }
+            ph_ += inc_h;
+            if (ph_ >= HH) { ph_ -= HH; ++pd; }
+            pd += inc_d;
+        }
+    };
+    constexpr int RPH = RPN / 2;  // the loads go out in two bursts of at most 40 (the wait counter holds 63)
+    auto prefetch = [&](int chunk) {
+        prefetch_begin(chunk);
+        prefetch_part(std::integral_constant<int, 0>{}, std::integral_constant<int, RPH>{});
+        prefetch_part(std::integral_constant<int, RPH>{}, std::integral_constant<int, RPN>{});
+    };
+    auto write_prefetched = [&]() {
+        float4 *l4 = reinterpret_cast<float4 *>(lds);
+#pragma unroll
+        for (int i = 0; i < RPN; ++i) {
+            const int pos = tid + i * kBlockThreads;
+            if (pos < SLAB) {
+                l4[ix::stage_lds_index(0, SLAB, pos, 0)] = make_float4(pf[i][0], pf[i][2], pf[i][4], pf[i][6]);
+                l4[ix::stage_lds_index(0, SLAB, pos, 1)] = make_float4(pf[i][1], pf[i][3], pf[i][5], pf[i][7]);
+            }
+        }
+    };
+
     // a wave whose position blocks all lie past the box volume, or wholly in
     // the d-overhang at a region's end (d is the slowest index), runs no MFMAs
     const bool wave_live = min(vol, TQd_e * plane) > wpos * PBW * 32;
@@ -351,7 +416,8 @@ void convt3d_mfma_kernel(const ConvParams P) {
             if constexpr (!PL) {
                 if (chunk > 0) {  // stage the next chunk while the workgroup waits
                     __syncthreads();
-                    stage(chunk);
+                    if constexpr (RP) write_prefetched();
+                    else stage(chunk);
                     __syncthreads();
                 }
             }
@@ -359,6 +425,7 @@ void convt3d_mfma_kernel(const ConvParams P) {
             // (vector-ALU heavy) epilogue (measured +2 %; the other epilogues
             // lose 1-2 % because their staging waves then wait longer)
             if constexpr (SM) __builtin_amdgcn_s_setprio(1);
+            bool pf_done = false;  // RP: this wave has issued the next chunk's prefetch
 #pragma unroll
             for (int p = 0; p < NPH; ++p) {
                 if (!wave_live || Jw[p] == 0 || jw_lo[p] > jw_hi[p]) continue;
@@ -435,7 +502,13 @@ void convt3d_mfma_kernel(const ConvParams P) {
                             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one LDS read
                         }
                     };
-                    for (int it = 0; it < n_it; it += 2) {
+                    // RP kernels before a further chunk: the loop stops at an even
+                    // group count n_main, leaving the last groups (up to kTail + 1)
+                    // to a tail that prefetches the next chunk
+                    constexpr int kTail = 4;
+                    const bool tail_pf = RP && chunk + 1 < P.nchunks;
+                    const int n_main = tail_pf ? (n_it > kTail ? ((n_it - kTail) & ~1) : 0) : n_it;
+                    for (int it = 0; it < n_main; it += 2) {
                         if (it + 1 < n_it) next_group(giB, boB); else { giB = giA; boB = boA; }
 #pragma unroll
                         for (int c = 0; c < CBW; ++c) aB[c] = aload(c, giB);
@@ -449,6 +522,45 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         __builtin_amdgcn_sched_barrier(0);
                         group_mfma(aB, boA);
                         __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if constexpr (RP) {
+                        if (tail_pf) {
+                            // aA and bq hold group n_main; load the A operands of the
+                            // (up to kTail) groups after it and wait for them, then
+                            // issue the prefetch in two bursts between the tail's
+                            // groups: no MFMA of the tail waits on a vector load
+                            const int nt = n_it - n_main;  // 1 .. kTail + 1
+                            float4 at[kTail][CBW];
+                            int bo[kTail + 1];
+                            bo[0] = boA;
+#pragma unroll
+                            for (int j = 1; j <= kTail; ++j) {
+                                bo[j] = bo[j - 1];
+                                if (j < nt) {
+                                    int gi;
+                                    next_group(gi, bo[j]);
+#pragma unroll
+                                    for (int c = 0; c < CBW; ++c) at[j - 1][c] = aload(c, gi);
+                                }
+                            }
+                            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tail's A operands
+                            __builtin_amdgcn_sched_barrier(0);
+                            prefetch_begin(chunk + 1);
+                            prefetch_part(std::integral_constant<int, 0>{}, std::integral_constant<int, RPH>{});
+                            pf_done = true;
+                            __builtin_amdgcn_sched_barrier(0);
+                            group_mfma(aA, nt > 1 ? bo[1] : bo[0]);
+                            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                            for (int j = 1; j <= kTail; ++j) {
+                                if (j == kTail / 2) {
+                                    prefetch_part(std::integral_constant<int, RPH>{}, std::integral_constant<int, RPN>{});
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
+                                if (j < nt) group_mfma(at[j - 1], j + 1 < nt ? bo[j + 1] : bo[j]);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
                     }
                 } else {
                     // Two B register sets: the next group's B is read before this
@@ -486,6 +598,10 @@ void convt3d_mfma_kernel(const ConvParams P) {
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
+            }
+            if constexpr (RP) {
+                // waves that ran no MFMAs still stage their share of the next chunk
+                if (chunk + 1 < P.nchunks && !pf_done) prefetch(chunk + 1);
             }
             if constexpr (SM) __builtin_amdgcn_s_setprio(0);
         }
@@ -869,9 +985,9 @@ int launch_prepack(const Plan &pl, const float *w, float *wp, void *stream) {
     return (int)hipGetLastError();
 }
 
-template <int CBW, int NPH, int PBW, bool SM, bool PL>
+template <int CBW, int NPH, int PBW, bool SM, bool PL, bool RP = false>
 static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
-    auto fn = convt3d_mfma_kernel<CBW, NPH, PBW, SM, PL>;
+    auto fn = convt3d_mfma_kernel<CBW, NPH, PBW, SM, PL, RP>;
     // the dynamic-LDS limit is a per-device attribute of the function: set it
     // once on every device the kernel runs on (bit d: done on device d)
     static std::atomic<uint64_t> attr_done{0};
@@ -893,6 +1009,12 @@ static int launch_conv_t(const Plan &pl, const ConvParams &cp, void *stream) {
 int launch_conv(const Plan &pl, const ConvParams &cp, void *stream) {
     const Variant v = kVariants[pl.variant];
     const bool pl_ = pl.phase_loop != 0;
+    // the register-prefetch build (its own variant entry)
+    if (v.prefetch) {
+        if (v.CBW == 1 && v.NPH == 1 && v.PBW == 4 && !v.softmax && !pl_)
+            return launch_conv_t<1, 1, 4, false, false, true>(pl, cp, stream);
+        return (int)hipErrorInvalidValue;
+    }
 #define CONVT3D_VARIANT(a, b, c, d) \
     if (v.CBW == a && v.NPH == b && v.PBW == c && v.softmax == d && !pl_) \
         return launch_conv_t<a, b, c, d, false>(pl, cp, stream);

@@ -41,6 +41,9 @@ const Variant kVariants[] = {
     {2, 1, 4, true, 2, false},  {2, 2, 2, true, 2, true},   {2, 1, 2, true, 3, true},
     {2, 2, 1, true, 3, true},
     {4, 1, 2, true, 1, false},  {4, 2, 1, true, 1, true},   {4, 1, 1, true, 3, true},
+    // register prefetch of the next channel chunk, for layers whose halo (not
+    // registers) holds the CU to two workgroups: a two-wave register budget
+    {1, 1, 4, false, 2, false, true},
 };
 const int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -559,6 +562,15 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
                     continue;
                 CI_T = force[5];
             }
+            if (v.prefetch) {
+                // one octet per chunk whose halo fits kRpPositions per thread, 32-bit
+                // plane offsets, and a further chunk to prefetch
+                if (pl->octets < 2 || max_slab > kRpPositions * kBlockThreads ||
+                    (int64_t)kOctet * g->d * g->h * g->w > kMaxChunkPlanes ||
+                    (forced && force[5] > 0 && force[5] != kOctet))
+                    continue;
+                CI_T = lds_of(kOctet) <= kMaxLdsBytes ? kOctet : 0;
+            }
             if (CI_T == 0) continue;
             const int nchunks = (int)ceil_div(CI_pad, CI_T);
             const int64_t grid = nn * co_tiles * (ploop ? 1 : sd * sh) * nwg * tiles_total;
@@ -571,7 +583,9 @@ int plan_candidates(const convt3d_geom *g, const convt3d_epilogue *e, int max_k,
             // exposed staging waits: co-resident workgroups advance in lockstep on
             // the shared MFMA pipe, so a stage idles the CU (measured about 2000 CU
             // cycles = 250k MAC-equivalents per chunk and workgroup)
-            double cost = cost_regions + (double)grid * kStageWaitMacs * nchunks;
+            // (a prefetching kernel waits in full only for its first chunk)
+            const double waits = v.prefetch ? 1.0 + 0.25 * (nchunks - 1) : (double)nchunks;
+            double cost = cost_regions + (double)grid * kStageWaitMacs * waits;
             cost *= rounds * slots / (double)grid;
             // few waves per SIMD hide less latency; fewer MFMA tiles per wave mean
             // more operand traffic per MFMA

@@ -188,6 +188,10 @@ int replay_conv(const Plan &pl, const ConvParams &P) {
         int jw_lo[2], jw_hi[2];
         for (int p = 0; p < NPH; ++p) ix::tap_range(tb.q0w, tb.TQw_e, cw[p], ew, Jw[p], P.W, jw_lo[p], jw_hi[p]);
         const int SLAB = HD * HH * HW, slab2 = 2 * SLAB;
+        // a register-prefetch kernel stages every later chunk from kRpPositions
+        // positions per thread: the halo must fit them, one octet per chunk
+        if (v.prefetch && (SLAB > kRpPositions * kBlockThreads || P.CI_T != kOctet || P.plane_desc || PL))
+            fail("prefetch kernel: halo of %d positions, chunk %d, plane descriptors %d", SLAB, P.CI_T, P.plane_desc);
         const int halo4 = (P.CI_T * SLAB) >> 2;  // float4s of the staged chunk
         if (halo4 * 4 > P.red_off) fail("halo of %d floats overlaps the reduction scratch at %d", halo4 * 4, P.red_off);
         const int vol = TQd * TQh * TQw, plane = TQh * TQw;

@@ -23,6 +23,7 @@ VARIANTS = [
     (1, 1, 4, True, False), (1, 1, 2, True, True), (1, 2, 2, True, True),
     (2, 1, 4, True, False), (2, 2, 2, True, True), (2, 1, 2, True, True), (2, 2, 1, True, True),
     (4, 1, 2, True, False), (4, 2, 1, True, True), (4, 1, 1, True, True),
+    (1, 1, 4, False, False),  # the register-prefetch build of the next channel chunk
 ]
 CASES = [(vi, 0) for vi in range(len(VARIANTS))] + [(vi, 1) for vi, v in enumerate(VARIANTS) if v[4]]
 
@@ -116,4 +117,18 @@ def test_forced_border_segmentation_matches_oracle(k, stride, split, monkeypatch
     info = C.convt3d_get_plan_info(geom_of(wl), e)
     say(f"[case] border split {split} k {k} s {stride} epi {W.EPI_NAMES[wl.epi]} plan {C.plan_string(info)}")
     assert info["border_split"] == split
+    run_and_check(wl)
+
+
+def test_prefetch_build_on_a_grouped_dilated_layer(monkeypatch):
+    """The register-prefetch build on the shape it is for: four channel groups
+    of 16 input channels (two chunks each), dilation 2, ragged sizes."""
+    from activation_epilogues_amd import convt3d as C
+    wl = W.Workload("rp_g4_dl2", 2, 64, 128, 9, 10, 11, k=3, dilation=2, conv_groups=4, bias=False,
+                    epi=W.EPI_RELU_GROUPNORM, groups=8, seed=7400)
+    monkeypatch.setenv("CONVT3D_PLAN", f"{len(VARIANTS) - 1},-1,-1,-1,-1,-1")
+    monkeypatch.setenv("CONVT3D_PHASE_LOOP", "0")
+    info = C.convt3d_get_plan_info(geom_of(wl), C.make_epilogue(wl.epi, wl.groups))
+    say(f"[case] prefetch build, grouped dilated layer, plan {C.plan_string(info)}")
+    assert info["variant"] == len(VARIANTS) - 1 and info["ci_chunk"] == 8
     run_and_check(wl)

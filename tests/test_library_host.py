@@ -404,6 +404,22 @@ def test_plan_cache_keys_on_every_override(monkeypatch):
     monkeypatch.setenv("CONVT3D_ORDER", "1")
     assert C.convt3d_get_plan_info(g, e)["xcd_order"] == 1
 
+PREFETCH_VARIANT = 15  # the register-prefetch build in the library's variant table
+
+
+def test_prefetch_build_needs_a_second_chunk(monkeypatch):
+    """The register-prefetch kernel takes one octet of input channels per
+    chunk and needs a further chunk to prefetch: forced on a layer with one
+    octet it has no plan; with two it runs 8-channel chunks."""
+    monkeypatch.setenv("CONVT3D_PLAN", f"{PREFETCH_VARIANT},-1,-1,-1,-1,-1")
+    monkeypatch.setenv("CONVT3D_PHASE_LOOP", "0")
+    e = C.make_epilogue(1, 4)
+    with pytest.raises(C.Convt3dError):
+        C.convt3d_get_plan_info(C.make_geom(2, 8, 32, 6, 6, 6, 3), e)
+    info = C.convt3d_get_plan_info(C.make_geom(2, 16, 32, 6, 6, 6, 3), e)
+    assert (info["variant"], info["ci_chunk"], info["pos_blocks_per_wave"]) == (PREFETCH_VARIANT, 8, 4)
+
+
 def test_profile_kind_mask_is_checked():
     """convt3d_profile_begin_kinds takes a nonzero subset of the kernel kinds;
     a session with nothing recorded ends with every duration 0."""
